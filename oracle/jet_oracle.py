@@ -1,0 +1,250 @@
+"""Plain fp64 CPU oracle for teacher-forced candidate-likelihood scoring.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or execute this
+module: only the tests, the package's smoke check and the benchmark's CPU-baseline leg do.
+It shares no code with the HIP library; the two meet only at the seeded input arrays.
+
+What it computes, in the pages' order (citations name the page and its equation/section):
+
+  z[r, v]   = sum_i H[r, i] W[v, i]                      projection of a predictor state
+                                                         through the LM head (JET paper,
+                                                         Eq. 1; FastJEV Sec. 3.3,
+                                                         candidate-preserving readout)
+  LSE_r     = log sum_{v in V} exp z[r, v]               full-vocabulary denominator
+                                                         (JET paper, Eq. 1 and Eq. 2)
+  l_k       = z[row_k, y_k] - LSE_{row_k}                token log-probability (JET Eq. 2)
+  s(c)      = sum_t l_{c,t}                              chain rule (JET Eq. 3; gemma-e2b
+                                                         doc, "Candidate likelihoods")
+  q(c)      = exp(s(c)/T) / sum_j exp(s(c_j)/T)          candidate-set normalisation (JET
+                                                         Eq. 4; gemma-e2b doc; nimble page,
+                                                         Execution step 6)
+  argmax    lowest index among the maxima of s/T         fixed tie order (JET Eq. 5)
+  q(true)   q at the "true" candidate                    binary rule (JET, decision rules;
+                                                         nimble page: booleans default to
+                                                         [false, true])
+  E         = sum_i i q(i)                               ordinal rule (JET, decision rules)
+  NLL_gold  = -log sum_{c: text(c) = gold} q(c)          gold NLL over equal-text labels
+                                                         (JET, labels vs answer text)
+  restricted: softmax over a field's allowed-token logits divided by T
+                                                         (nimble page, Execution steps 5-6)
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  * T scales candidate scores only, once, before the candidate softmax; token
+    log-probabilities are never tempered (JET says tokens are scored without temperature;
+    the gemma-e2b doc and the nimble page apply T to candidate scores).
+  * "Fixed ordering" for ties = supplied candidate order, lowest index wins.  The decision
+    is taken on float32-rounded a = s/T, the precision the GPU kernel decides in, so both
+    sides see the same exact ties; top-two gaps are reported in fp64.
+  * Binary "true" index: per-question index if given, else 1 for K == 2 ([false, true]),
+    else none (NaN).
+  * Gold NLL uses the same q as the decision (so T is included), natural log; +inf when
+    no candidate carries the gold text.
+Floating point: inputs are widened exactly (fp32 -> fp64; bf16 bits -> fp32 -> fp64), all
+arithmetic is fp64.  numpy's matmul (a library primitive) forms the dot products.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LN2 = math.log(2.0)
+
+
+# ----------------------------------------------------------------------------------------
+# operand widening
+# ----------------------------------------------------------------------------------------
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of an input operand to fp64.  bf16 values arrive as their 16 bits."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ----------------------------------------------------------------------------------------
+# readout: logits, full-vocabulary log-normaliser, token log-probabilities
+# ----------------------------------------------------------------------------------------
+
+def logits(H64: np.ndarray, W64: np.ndarray) -> np.ndarray:
+    """z[r, v] = <H[r], W[v]> for every predictor row r and vocabulary entry v
+    (JET paper, Eq. 1: the logit of token v given the context and the candidate prefix;
+    FastJEV Sec. 3.3: each predictor node is projected through the LM head)."""
+    return H64 @ W64.T
+
+
+def logsumexp_rows(z: np.ndarray) -> np.ndarray:
+    """LSE_r = m_r + log sum_v exp(z[r, v] - m_r) with m_r = max_v z[r, v]
+    (JET paper, Eq. 2: the numerically stable form of the log-probability's denominator;
+    the denominator runs over the full vocabulary, Eq. 1)."""
+    m = z.max(axis=1, keepdims=True)
+    return m[:, 0] + np.log(np.exp(z - m).sum(axis=1))
+
+
+def token_logprobs(z_at_target: np.ndarray, lse_of_row: np.ndarray) -> np.ndarray:
+    """l_k = z[row_k, y_k] - LSE_{row_k} (JET paper, Eq. 2)."""
+    return z_at_target - lse_of_row
+
+
+def candidate_scores(tok_logp: np.ndarray, cand_tok_off: np.ndarray) -> np.ndarray:
+    """s(c) = sum of the candidate's token log-probabilities, in token order, with no
+    length normalisation and no extra tokens (JET paper, Eq. 3 and the remarks after
+    Eq. 4; gemma-e2b doc, "Candidate likelihoods")."""
+    n = len(cand_tok_off) - 1
+    s = np.empty(n, dtype=np.float64)
+    for c in range(n):
+        s[c] = float(np.sum(tok_logp[cand_tok_off[c]:cand_tok_off[c + 1]]))
+    return s
+
+
+# ----------------------------------------------------------------------------------------
+# candidate-set decisions
+# ----------------------------------------------------------------------------------------
+
+def _lse(a: np.ndarray) -> float:
+    m = float(np.max(a))
+    if m == -math.inf:
+        return -math.inf
+    return m + math.log(float(np.sum(np.exp(a - m))))
+
+
+def decide_question(s: np.ndarray, T: float, text_id=None, gold_text=None, true_idx=None) -> dict:
+    """Decisions for one question from its candidates' sequence scores s.
+
+    q = softmax(s / T) over the supplied candidates (JET Eq. 4, gemma-e2b doc, nimble
+    Execution step 6 with temperature applied once to candidate scores); argmax with the
+    lowest index winning ties (JET Eq. 5); q(true) (binary rule); E = sum_i i q_i with
+    levels 0..K-1 (ordinal rule); gold NLL = -log of the summed q of every candidate whose
+    text equals the gold text (JET, labels vs answer text), computed as
+    LSE(a) - LSE(a over gold-text candidates)."""
+    K = len(s)
+    a = np.asarray(s, dtype=np.float64) / float(T)
+    M = float(np.max(a))
+    e = np.exp(a - M)
+    Z = float(np.sum(e))
+    q = e / Z
+    a32 = a.astype(np.float32)
+    argmax = int(np.flatnonzero(a32 == a32.max())[0])
+    qs = np.sort(q)[::-1]
+    gap = float(qs[0] - qs[1]) if K >= 2 else math.inf
+    if true_idx is None:
+        t = 1 if K == 2 else -1
+    else:
+        t = int(true_idx)
+    q_true = float(q[t]) if 0 <= t < K else math.nan
+    expect = float(np.sum(np.arange(K, dtype=np.float64) * q))
+    if text_id is None or gold_text is None:
+        nll = math.nan
+    else:
+        g = np.asarray(text_id) == gold_text
+        nll = math.inf if not g.any() else _lse(a) - _lse(a[g])
+    return dict(q=q, argmax=argmax, gap=gap, q_true=q_true, expect=expect, nll=nll)
+
+
+def decide(s: np.ndarray, q_cand_off: np.ndarray, T: float, cand_text_id=None,
+           q_gold_text_id=None, q_true_idx=None) -> dict:
+    """decide_question over every question; a question with any NaN candidate score (a
+    candidate not computed in a sampled run) gets NaN outputs and argmax -1."""
+    n_q = len(q_cand_off) - 1
+    out = dict(q=np.full(len(s), np.nan), argmax=np.full(n_q, -1, np.int64),
+               gap=np.full(n_q, np.nan), q_true=np.full(n_q, np.nan),
+               expect=np.full(n_q, np.nan), nll=np.full(n_q, np.nan))
+    for g in range(n_q):
+        c0, c1 = int(q_cand_off[g]), int(q_cand_off[g + 1])
+        sg = s[c0:c1]
+        if np.isnan(sg).any():
+            continue
+        r = decide_question(
+            sg, T,
+            None if cand_text_id is None else cand_text_id[c0:c1],
+            None if q_gold_text_id is None else int(q_gold_text_id[g]),
+            None if q_true_idx is None else int(q_true_idx[g]))
+        out["q"][c0:c1] = r["q"]
+        for k in ("argmax", "gap", "q_true", "expect", "nll"):
+            out[k][g] = r[k]
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# full problem
+# ----------------------------------------------------------------------------------------
+
+def score(p: dict, rows=None) -> dict:
+    """Score a whole problem (a dict as built by the workloads package).
+
+    rows: None for every row, or an index array of the predictor rows to compute (sampled
+    parity at full size); tokens on other rows get NaN, and so does everything built on
+    them.  Returns fp64 arrays: lse (per row, NaN if not computed), tok_logp, cand_s,
+    cand_q, q_argmax, q_gap, q_true, q_expect, q_nll.
+    """
+    n_rows = int(p["n_rows"])
+    tok_target = np.asarray(p["tok_target"], dtype=np.int64)
+    n_tok = len(tok_target)
+    tok_row = (np.arange(n_tok, dtype=np.int64) if p.get("tok_row") is None
+               else np.asarray(p["tok_row"], dtype=np.int64))
+    rows = np.arange(n_rows) if rows is None else np.unique(np.asarray(rows, dtype=np.int64))
+    W64 = widen(p["W"], p["w_dtype"])
+    H64 = widen(np.asarray(p["H"])[rows], p["h_dtype"])
+    lse = np.full(n_rows, np.nan)
+    z_tgt = np.full(n_tok, np.nan)
+    where = np.full(n_rows, -1, dtype=np.int64)
+    where[rows] = np.arange(len(rows))
+    blk = 64
+    for b0 in range(0, len(rows), blk):
+        z = logits(H64[b0:b0 + blk], W64)
+        lse[rows[b0:b0 + blk]] = logsumexp_rows(z)
+        sel = np.flatnonzero((where[tok_row] >= b0) & (where[tok_row] < b0 + blk))
+        z_tgt[sel] = z[where[tok_row[sel]] - b0, tok_target[sel]]
+    tok_logp = token_logprobs(z_tgt, lse[tok_row])
+    cand_s = candidate_scores(tok_logp, np.asarray(p["cand_tok_off"]))
+    dec = decide(cand_s, np.asarray(p["q_cand_off"]), p["T"], p.get("cand_text_id"),
+                 p.get("q_gold_text_id"), p.get("q_true_idx"))
+    return dict(lse=lse, tok_logp=tok_logp, cand_s=cand_s, cand_q=dec["q"],
+                q_argmax=dec["argmax"], q_gap=dec["gap"], q_true=dec["q_true"],
+                q_expect=dec["expect"], q_nll=dec["nll"])
+
+
+# ----------------------------------------------------------------------------------------
+# restricted vocabulary (allowed code tokens)
+# ----------------------------------------------------------------------------------------
+
+def build_union(field_ids: np.ndarray, field_off: np.ndarray, V: int):
+    """Sorted unique union of every field's allowed ids and, per slot, its index in the
+    union (nimble page, Execution step 5: gather only the allowed head rows and project
+    onto their union; each field then selects its own subset)."""
+    ids = np.asarray(field_ids, dtype=np.int64)
+    if ids.size and (ids.min() < 0 or ids.max() >= V):
+        raise ValueError("allowed id outside [0, V)")
+    union = np.unique(ids)
+    slot_uidx = np.searchsorted(union, ids)
+    return union.astype(np.int32), slot_uidx.astype(np.int32)
+
+
+def score_restricted(rp: dict) -> dict:
+    """Per field f with row r and allowed ids j: b_j = z[r, j]; q = softmax(b / T) over the
+    field's allowed ids; argmax with the lowest index winning ties, decided on
+    float32-rounded b / T (nimble page, Execution step 6; scaling applied once before the
+    softmax, "V2 probability default").  No full-vocabulary normaliser is involved
+    ("Correctness and limits": full-vocabulary probabilities are not part of this path)."""
+    fo = np.asarray(rp["field_off"])
+    ids = np.asarray(rp["field_ids"], dtype=np.int64)
+    rows = np.asarray(rp["field_row"], dtype=np.int64)
+    H64 = widen(rp["H"], rp["h_dtype"])
+    W64 = widen(np.asarray(rp["W"])[ids], rp["w_dtype"]) if ids.size else np.zeros((0, rp["d"]))
+    n_f = len(fo) - 1
+    logit = np.empty(len(ids))
+    qv = np.empty(len(ids))
+    am = np.empty(n_f, dtype=np.int64)
+    gap = np.empty(n_f)
+    for f in range(n_f):
+        a0, a1 = int(fo[f]), int(fo[f + 1])
+        b = W64[a0:a1] @ H64[rows[f]]
+        logit[a0:a1] = b
+        r = decide_question(b, rp["T"])
+        qv[a0:a1] = r["q"]
+        am[f] = r["argmax"]
+        gap[f] = r["gap"]
+    return dict(slot_logit=logit, slot_q=qv, field_argmax=am, field_gap=gap)

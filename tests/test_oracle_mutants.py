@@ -1,0 +1,148 @@
+"""Planted mistakes in the oracle (on the CPU) must each be caught by some pin.
+
+Each mutant replaces one oracle function with a plausibly wrong variant (a dropped term, a
+wrong sign, a wrong index, a transposed or reversed operand, a wrong tie rule...).  The
+test asserts that at least one pin of tests/test_oracle_pins.py fails under it, which is
+the evidence that the pins constrain every step of the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.jet_oracle as jom
+from tests import test_oracle_pins as pins
+
+
+def _lse_no_shift(z):
+    return np.log(np.exp(z).sum(axis=1))
+
+
+def _lse_sign(z):
+    m = z.max(axis=1, keepdims=True)
+    return m[:, 0] - np.log(np.exp(z - m).sum(axis=1))
+
+
+def _lse_drop_max(z):
+    m = z.max(axis=1, keepdims=True)
+    return np.log(np.exp(z - m).sum(axis=1))
+
+
+def _lse_partial_vocab(z):
+    z = z[:, :-1]
+    m = z.max(axis=1, keepdims=True)
+    return m[:, 0] + np.log(np.exp(z - m).sum(axis=1))
+
+
+def _logp_sign(zt, lse):
+    return lse - zt
+
+
+def _logits_reversed_vocab(H, W):
+    return (H @ W.T)[:, ::-1]
+
+
+def _logits_transposed(H, W):
+    n = min(H.shape[1], W.shape[0])
+    return H[:, :n] @ W[:n, :n].T if H.shape[0] else H @ W.T
+
+
+def _scores_mean(tok_logp, off):
+    n = len(off) - 1
+    return np.array([float(np.mean(tok_logp[off[c]:off[c + 1]])) for c in range(n)])
+
+
+def _scores_drop_last(tok_logp, off):
+    n = len(off) - 1
+    return np.array([float(np.sum(tok_logp[off[c]:max(off[c], off[c + 1] - 1)])) for c in range(n)])
+
+
+_orig_decide_question = jom.decide_question
+
+
+def _decide_T_times(s, T, *a, **k):
+    return _orig_decide_question(np.asarray(s) * float(T) * float(T), T, *a, **k)
+
+
+def _decide_last_tie(s, T, *a, **k):
+    r = _orig_decide_question(s, T, *a, **k)
+    a32 = (np.asarray(s, np.float64) / T).astype(np.float32)
+    r["argmax"] = int(np.flatnonzero(a32 == a32.max())[-1])
+    return r
+
+
+def _decide_levels_from_one(s, T, *a, **k):
+    r = _orig_decide_question(s, T, *a, **k)
+    r["expect"] = float(np.sum(np.arange(1, len(s) + 1) * r["q"]))
+    return r
+
+
+def _decide_gold_first_only(s, T, text_id=None, gold_text=None, true_idx=None):
+    r = _orig_decide_question(s, T, text_id, gold_text, true_idx)
+    if text_id is not None and gold_text is not None:
+        g = np.flatnonzero(np.asarray(text_id) == gold_text)
+        r["nll"] = math.inf if len(g) == 0 else -math.log(r["q"][g[0]])
+    return r
+
+
+def _decide_true_first(s, T, text_id=None, gold_text=None, true_idx=None):
+    r = _orig_decide_question(s, T, text_id, gold_text, true_idx)
+    if true_idx is None and len(s) == 2:
+        r["q_true"] = float(r["q"][0])
+    return r
+
+
+def _decide_no_temperature(s, T, *a, **k):
+    return _orig_decide_question(s, 1.0, *a, **k)
+
+
+def _widen_bad_shift(a, dtype):
+    if dtype == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+        return bits.view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def _union_unsorted(ids, off, V):
+    u, su = np.unique(np.asarray(ids)), None
+    u = u[::-1].copy()
+    su = np.array([int(np.flatnonzero(u == x)[0]) for x in ids], dtype=np.int32)
+    return u.astype(np.int32), su
+
+
+MUTANTS = {
+    "lse_without_max_shift": ("logsumexp_rows", _lse_no_shift),
+    "lse_sign_error": ("logsumexp_rows", _lse_sign),
+    "lse_dropped_max_term": ("logsumexp_rows", _lse_drop_max),
+    "lse_missing_vocab_entry": ("logsumexp_rows", _lse_partial_vocab),
+    "logprob_sign_flip": ("token_logprobs", _logp_sign),
+    "logits_reversed_vocab_index": ("logits", _logits_reversed_vocab),
+    "logits_transposed_operand": ("logits", _logits_transposed),
+    "length_normalised_scores": ("candidate_scores", _scores_mean),
+    "scores_drop_last_token": ("candidate_scores", _scores_drop_last),
+    "temperature_multiplies": ("decide_question", _decide_T_times),
+    "temperature_ignored": ("decide_question", _decide_no_temperature),
+    "tie_goes_to_last": ("decide_question", _decide_last_tie),
+    "ordinal_levels_from_one": ("decide_question", _decide_levels_from_one),
+    "gold_nll_not_summed": ("decide_question", _decide_gold_first_only),
+    "binary_true_is_first": ("decide_question", _decide_true_first),
+    "bf16_widen_wrong_shift": ("widen", _widen_bad_shift),
+    "union_not_sorted": ("build_union", _union_unsorted),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(jom, attr, fn)
+    import oracle
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as e:  # any failure (assertion, shape error, overflow) counts
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches the planted mistake {name}"
