@@ -1,0 +1,263 @@
+// C ABI of libjet: host-side validation, execution planning and launch sequencing.
+// Every check here runs on the host before anything is enqueued; a failing call
+// enqueues nothing.  The device kernels bounds-check every index themselves.
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "jet_internal.h"
+
+namespace jet {
+
+int small_group_size(int variant);
+
+namespace {
+
+constexpr int kMaxD = 65536;
+constexpr int kMaxV = 1 << 30;
+constexpr int kSmallWaves = 2048;  // 256 CUs x 8 resident waves
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+jet_status check_dims(jet_dtype h_dtype, jet_dtype w_dtype, int n_rows, int V, int d,
+                      const void* H, const void* W, float T) {
+  if (!(w_dtype == JET_BF16 && (h_dtype == JET_BF16 || h_dtype == JET_F32)) &&
+      !(w_dtype == JET_F32 && h_dtype == JET_F32))
+    return JET_E_DTYPE;
+  if (n_rows < 0 || V < 1 || V > kMaxV || d < 32 || d > kMaxD || d % 32 != 0) return JET_E_SHAPE;
+  if (!W || (n_rows > 0 && !H)) return JET_E_NULL;
+  if (!aligned16(W) || !aligned16(H)) return JET_E_SHAPE;
+  if (!std::isfinite(T) || !(T > 0.f)) return JET_E_TEMP;
+  return JET_OK;
+}
+
+jet_status check_problem(const jet_problem* p) {
+  if (!p) return JET_E_NULL;
+  jet_status st = check_dims(p->h_dtype, p->w_dtype, p->n_rows, p->V, p->d, p->H, p->W, p->T);
+  if (st != JET_OK) return st;
+  if (p->n_tok < 0 || p->n_cand < 0 || p->n_q < 0) return JET_E_SHAPE;
+  if (p->n_cand < p->n_q || p->n_tok < p->n_cand) return JET_E_SHAPE;  // K >= 1, m_c >= 1
+  if (p->n_tok > 0 && p->n_rows == 0) return JET_E_SHAPE;
+  if (!p->tok_row && p->n_tok > p->n_rows) return JET_E_SHAPE;
+  if (p->n_rows > (1 << 21)) return JET_E_SHAPE;
+  if (p->n_tok > 0 && !p->tok_target) return JET_E_NULL;
+  if (p->n_cand > 0 && !p->cand_tok_off) return JET_E_NULL;
+  if (p->n_q > 0 && !p->q_cand_off) return JET_E_NULL;
+  return JET_OK;
+}
+
+jet_status check_outputs(const jet_problem* p, const jet_outputs* o) {
+  if (!o) return JET_E_NULL;
+  if (p->n_tok > 0 && !o->tok_logp) return JET_E_NULL;
+  if (p->n_cand > 0 && (!o->cand_s || !o->cand_q)) return JET_E_NULL;
+  if (p->n_q > 0 && !o->q_argmax) return JET_E_NULL;
+  return JET_OK;
+}
+
+}  // namespace
+
+bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
+  *pl = Plan{};
+  pl->variant = p->w_dtype == JET_F32 ? VAR_SMALL_F32 : VAR_SMALL_BF16;
+  pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
+  pl->row_tile = 32;
+  pl->n_rtiles = (p->n_rows + 31) / 32;
+  pl->vgroup = small_group_size(pl->variant);
+  pl->n_vgroups = (p->V + pl->vgroup - 1) / pl->vgroup;
+  int gx = (pl->n_vgroups + 3) / 4;
+  gx = std::max(1, std::min(gx, kSmallWaves / 4));
+  pl->grid_x = gx;
+  pl->n_parts = gx;
+  pl->n_buckets = (long long)pl->n_rtiles * pl->n_vgroups;
+  size_t off = 0;
+  const size_t rows = (size_t)p->n_rows, d = (size_t)p->d, ntok = (size_t)p->n_tok;
+  pl->off_hhi = off;
+  if (pl->hilo) off += al256(rows * d * 2);
+  pl->off_hlo = off;
+  if (pl->hilo) off += al256(rows * d * 2);
+  pl->off_ztgt = off;
+  off += al256(ntok * 4);
+  pl->off_part = off;
+  off += al256((size_t)pl->n_parts * rows * 8);
+  pl->off_lse = off;
+  off += al256(rows * 4);
+  pl->off_bcount = off;
+  off += al256((size_t)(pl->n_buckets + 1) * 4);
+  pl->off_boff = off;
+  off += al256((size_t)(pl->n_buckets + 1) * 4);
+  pl->off_btok = off;
+  off += al256(ntok * 4);
+  pl->off_bpos = off;
+  off += al256(ntok * 4);
+  pl->off_flags = off;
+  off += 256;
+  pl->total = off;
+  return true;
+}
+
+}  // namespace jet
+
+using namespace jet;
+
+extern "C" {
+
+const char* jet_status_string(jet_status s) {
+  switch (s) {
+    case JET_OK: return "ok";
+    case JET_E_NULL: return "a required pointer is NULL";
+    case JET_E_SHAPE: return "a size is out of range or an operand is misaligned";
+    case JET_E_DTYPE: return "unsupported operand type combination";
+    case JET_E_INDEX: return "an index is out of range or offsets are malformed";
+    case JET_E_TEMP: return "temperature must be finite and > 0";
+    case JET_E_WORKSPACE: return "workspace is NULL, too small or not 256-byte aligned";
+    case JET_E_HIP: return "a HIP runtime call failed";
+  }
+  return "unknown status";
+}
+
+size_t jet_score_workspace_size(const jet_problem* p) {
+  if (check_problem(p) != JET_OK) return 0;
+  Plan pl;
+  make_plan(p, true, &pl);
+  return pl.total;
+}
+
+jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o, void* workspace,
+                              size_t workspace_bytes, void* stream, void* ev_before,
+                              void* ev_after) {
+  jet_status st = check_problem(p);
+  if (st != JET_OK) return st;
+  if ((st = check_outputs(p, o)) != JET_OK) return st;
+  Plan pl;
+  make_plan(p, true, &pl);
+  if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u)) return JET_E_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  ScoreArgs a;
+  a.p = p;
+  a.o = o;
+  a.plan = &pl;
+  a.ws = ws;
+  a.lse = o->row_lse ? o->row_lse : reinterpret_cast<float*>(ws + pl.off_lse);
+  a.flags = o->dev_flags ? o->dev_flags : reinterpret_cast<int32_t*>(ws + pl.off_flags);
+  a.stream = static_cast<hipStream_t>(stream);
+  if (launch_prep(a) != hipSuccess) return JET_E_HIP;
+  if (ev_before && hipEventRecord(static_cast<hipEvent_t>(ev_before), a.stream) != hipSuccess)
+    return JET_E_HIP;
+  if (p->n_rows > 0 && launch_project(a) != hipSuccess) return JET_E_HIP;
+  if (ev_after && hipEventRecord(static_cast<hipEvent_t>(ev_after), a.stream) != hipSuccess)
+    return JET_E_HIP;
+  if (launch_merge(a) != hipSuccess) return JET_E_HIP;
+  if (launch_decide(a) != hipSuccess) return JET_E_HIP;
+  return JET_OK;
+}
+
+jet_status jet_score(const jet_problem* p, const jet_outputs* o, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return jet_score_profiled(p, o, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+jet_status jet_validate_host(const jet_problem* p) {
+  jet_status st = check_problem(p);
+  if (st != JET_OK) return st;
+  for (int k = 0; k < p->n_tok; ++k) {
+    const int r = p->tok_row ? p->tok_row[k] : k;
+    if (r < 0 || r >= p->n_rows) return JET_E_INDEX;
+    if (p->tok_target[k] < 0 || p->tok_target[k] >= p->V) return JET_E_INDEX;
+  }
+  if (p->n_cand > 0) {
+    if (p->cand_tok_off[0] != 0 || p->cand_tok_off[p->n_cand] != p->n_tok) return JET_E_INDEX;
+    for (int c = 0; c < p->n_cand; ++c)
+      if (p->cand_tok_off[c + 1] <= p->cand_tok_off[c]) return JET_E_INDEX;
+  }
+  if (p->n_q > 0) {
+    if (p->q_cand_off[0] != 0 || p->q_cand_off[p->n_q] != p->n_cand) return JET_E_INDEX;
+    for (int g = 0; g < p->n_q; ++g) {
+      const int K = p->q_cand_off[g + 1] - p->q_cand_off[g];
+      if (K < 1) return JET_E_INDEX;
+      if (p->q_true_idx && (p->q_true_idx[g] < -1 || p->q_true_idx[g] >= K)) return JET_E_INDEX;
+    }
+  } else if (p->n_cand != 0) {
+    return JET_E_INDEX;
+  }
+  return JET_OK;
+}
+
+jet_status jet_build_union(const int32_t* field_ids, const int32_t* field_off, int32_t n_fields,
+                           int32_t V, int32_t* union_ids, int32_t* n_union, int32_t* slot_uidx) {
+  if (!field_off || !n_union) return JET_E_NULL;
+  if (n_fields < 0 || V < 1) return JET_E_SHAPE;
+  if (field_off[0] != 0) return JET_E_INDEX;
+  for (int f = 0; f < n_fields; ++f)
+    if (field_off[f + 1] <= field_off[f]) return JET_E_INDEX;
+  const int n_slots = field_off[n_fields];
+  if (n_slots > 0 && (!field_ids || !union_ids || !slot_uidx)) return JET_E_NULL;
+  std::vector<int32_t> u(field_ids, field_ids + n_slots);
+  for (int32_t x : u)
+    if (x < 0 || x >= V) return JET_E_INDEX;
+  std::sort(u.begin(), u.end());
+  u.erase(std::unique(u.begin(), u.end()), u.end());
+  for (int j = 0; j < n_slots; ++j)
+    slot_uidx[j] = (int32_t)(std::lower_bound(u.begin(), u.end(), field_ids[j]) - u.begin());
+  std::copy(u.begin(), u.end(), union_ids);
+  *n_union = (int32_t)u.size();
+  return JET_OK;
+}
+
+static jet_status check_restricted(const jet_restricted_problem* p) {
+  if (!p) return JET_E_NULL;
+  jet_status st = check_dims(p->h_dtype, p->w_dtype, p->n_rows, p->V, p->d, p->H, p->W, p->T);
+  if (st != JET_OK) return st;
+  if (p->n_union < 0 || p->n_fields < 0 || p->n_slots < p->n_fields) return JET_E_SHAPE;
+  if (p->n_fields > 0 && (p->n_union < 1 || p->n_rows < 1)) return JET_E_SHAPE;
+  if (p->n_union > p->V) return JET_E_SHAPE;
+  if (p->n_rows > (1 << 21)) return JET_E_SHAPE;
+  if (p->n_union > 0 && !p->union_ids) return JET_E_NULL;
+  if (p->n_fields > 0 && (!p->field_row || !p->field_slot_off || !p->slot_uidx)) return JET_E_NULL;
+  return JET_OK;
+}
+
+size_t jet_restricted_workspace_size(const jet_restricted_problem* p) {
+  if (check_restricted(p) != JET_OK) return 0;
+  RestrictedPlan pl;
+  make_restricted_plan(p, &pl);
+  return pl.total;
+}
+
+jet_status jet_score_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  jet_status st = check_restricted(p);
+  if (st != JET_OK) return st;
+  if (!o) return JET_E_NULL;
+  if (p->n_fields > 0 && (!o->slot_logit || !o->slot_q || !o->field_argmax)) return JET_E_NULL;
+  RestrictedPlan pl;
+  make_restricted_plan(p, &pl);
+  if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u)) return JET_E_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* flags = o->dev_flags ? o->dev_flags : reinterpret_cast<int32_t*>(ws + pl.off_flags);
+  if (launch_restricted(p, o, &pl, ws, flags, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return JET_E_HIP;
+  return JET_OK;
+}
+
+jet_status jet_validate_restricted_host(const jet_restricted_problem* p) {
+  jet_status st = check_restricted(p);
+  if (st != JET_OK) return st;
+  for (int j = 0; j < p->n_union; ++j) {
+    if (p->union_ids[j] < 0 || p->union_ids[j] >= p->V) return JET_E_INDEX;
+    if (j > 0 && p->union_ids[j] <= p->union_ids[j - 1]) return JET_E_INDEX;
+  }
+  if (p->n_fields > 0) {
+    if (p->field_slot_off[0] != 0 || p->field_slot_off[p->n_fields] != p->n_slots) return JET_E_INDEX;
+    for (int f = 0; f < p->n_fields; ++f) {
+      if (p->field_slot_off[f + 1] <= p->field_slot_off[f]) return JET_E_INDEX;
+      if (p->field_row[f] < 0 || p->field_row[f] >= p->n_rows) return JET_E_INDEX;
+    }
+    for (int j = 0; j < p->n_slots; ++j)
+      if (p->slot_uidx[j] < 0 || p->slot_uidx[j] >= p->n_union) return JET_E_INDEX;
+  }
+  return JET_OK;
+}
+
+}  // extern "C"

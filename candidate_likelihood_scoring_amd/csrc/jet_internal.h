@@ -1,0 +1,105 @@
+// Internal declarations shared by the HIP translation units of libjet.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "../../include/jet.h"
+
+namespace jet {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// bf16 round-to-nearest-even of an fp32 value (NaN stays a quiet NaN).
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Merge two online-logsumexp states (m = running max, s = sum of exp(z - m)).
+// Symmetric in its arguments bit-for-bit (max and + commute), so xor-shuffle trees give
+// every lane the same result.
+__device__ inline void lse_merge(float& m, float& s, float m2, float s2) {
+  float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * exp2f((m - M) * kLog2e) + s2 * exp2f((m2 - M) * kLog2e);
+  m = M;
+}
+
+__device__ inline void flag_or(int32_t* flags, uint32_t bit) {
+  if (flags) atomicOr(flags, (int32_t)bit);
+}
+
+// ------------------------------------------------------------------------------------
+// Execution plan of one jet_score call (derived from the scalars only)
+// ------------------------------------------------------------------------------------
+enum Variant { VAR_SMALL_BF16 = 0, VAR_SMALL_F32 = 1, VAR_TILED_BF16 = 2 };
+
+struct Plan {
+  int variant;
+  bool hilo;          // fp32 H split into bf16 hi + lo
+  int row_tile;       // rows per projection tile (bucketing granularity over rows)
+  int n_rtiles;
+  int vgroup;         // vocabulary entries per bucket (a multiple of the kernel's tile)
+  int n_vgroups;
+  int grid_x;         // projection workgroups along the vocabulary
+  int n_parts;        // (m, s) partials per row
+  long long n_buckets;
+  // workspace byte offsets
+  size_t off_hhi, off_hlo, off_ztgt, off_part, off_lse, off_bcount, off_boff, off_btok, off_bpos,
+      off_flags, total;
+};
+
+bool make_plan(const jet_problem* p, bool want_lse_buffer, Plan* plan);
+
+// ------------------------------------------------------------------------------------
+// Launchers (each returns hipSuccess or the launch error)
+// ------------------------------------------------------------------------------------
+struct ScoreArgs {
+  const jet_problem* p;
+  const jet_outputs* o;
+  const Plan* plan;
+  char* ws;
+  float* lse;        // row LSE buffer (caller's row_lse or workspace)
+  int32_t* flags;    // device flag word (caller's or workspace)
+  hipStream_t stream;
+};
+
+hipError_t launch_prep(const ScoreArgs& a);
+hipError_t launch_project(const ScoreArgs& a);
+hipError_t launch_merge(const ScoreArgs& a);
+hipError_t launch_decide(const ScoreArgs& a);
+
+struct RestrictedPlan {
+  bool hilo;
+  size_t off_wu, off_hhi, off_hlo, off_z, off_flags, total;
+};
+bool make_restricted_plan(const jet_restricted_problem* p, RestrictedPlan* plan);
+hipError_t launch_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
+                             const RestrictedPlan* plan, char* ws, int32_t* flags,
+                             hipStream_t stream);
+
+// H fp32 -> (hi, lo) bf16 split, shared by both paths.
+hipError_t launch_split(const float* H, long long n_elems, uint16_t* hi, uint16_t* lo,
+                        hipStream_t stream);
+
+// Projection core used by the restricted path: Z[row][u] = <H[row], Wu[u]> for all rows and
+// union entries (bf16 head rows; H bf16 or split fp32).
+hipError_t launch_project_store_bf16(const uint16_t* Wu, int U, int d, const uint16_t* Hhi,
+                                     const uint16_t* Hlo, int n_rows, float* Z,
+                                     hipStream_t stream);
+hipError_t launch_project_store_f32(const float* Wu, int U, int d, const float* H, int n_rows,
+                                    float* Z, hipStream_t stream);
+
+}  // namespace jet

@@ -1,0 +1,198 @@
+/*
+ * jet.h - C ABI of the MI355X (gfx950) candidate-likelihood scoring library.
+ *
+ * The library implements the readout of teacher-forced candidate scoring:
+ *
+ *   z[r, v]  = <H[r, :], W[v, :]>                 LM-head projection of predictor row r
+ *   LSE_r    = log sum_{v < V} exp z[r, v]          full-vocabulary normaliser
+ *   l_k      = z[row_k, y_k] - LSE_{row_k}          token log-probability
+ *   s(c)     = sum of l_k over the candidate's tokens (chain rule, no length normalisation)
+ *   q(c)     = softmax over the question's candidates of s(c) / T
+ *   argmax   lowest candidate index among the maxima of s / T
+ *   q(true), E = sum_i i q(i), gold NLL = -log sum_{text(c) = gold} q(c)
+ *
+ * as defined by "JET: Justification Evaluation in Transformer" (Eq. 1-5 and the decision
+ * rules after them), the gemma-e2b "Parallel decision inference" doc ("Candidate
+ * likelihoods", "Output contracts"), FastJEV Sec. 3.3 ("Candidate Preserving Readout":
+ * project each predictor node once, normalise over the full vocabulary, gather along
+ * candidate paths) and, for the restricted-vocabulary entry point, the nimble page
+ * "Parallel constrained scoring in MLX" (Execution, steps 5-6).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named in a *_problem / *_outputs struct are DEVICE pointers owned by the
+ *    caller, except where a comment says HOST.  Nothing is allocated, freed or
+ *    synchronised by the library; all work is enqueued on the caller's stream
+ *    (a hipStream_t passed as void*, NULL = the null stream).
+ *  - Matrices are row-major and densely packed: H[n_rows][d], W[V][d].
+ *  - bf16 operands are IEEE bfloat16 bit patterns (uint16); fp32 are IEEE binary32.
+ *  - Supported operand types: (W bf16, H bf16), (W bf16, H fp32: H is split exactly
+ *    into two bf16 terms so the product keeps about 16 significant bits of H), and
+ *    (W fp32, H fp32).  Anything else returns JET_E_DTYPE.
+ *  - d must be a positive multiple of 32 (at most 65536); V >= 1; counts >= 0.
+ *  - Errors: functions return a negative jet_status and enqueue nothing.  Only scalars
+ *    and pointers are checked on the host, since index arrays live on the device; use
+ *    jet_validate_host (host copies) to check indices.  On the device every index is
+ *    bounds-checked: an out-of-range row, target or offset never causes an out-of-bounds
+ *    access; it sets a bit in *dev_flags (when given) and yields NaN in the affected
+ *    outputs.  Outputs are defined only when the status is JET_OK and *dev_flags is 0.
+ *  - The library is stateless and re-entrant; calls on different streams may overlap if
+ *    their workspaces differ.
+ */
+#ifndef JET_H
+#define JET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define JET_API __attribute__((visibility("default")))
+#else
+#define JET_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JET_OK = 0,
+  JET_E_NULL = -1,      /* a required pointer is NULL                                  */
+  JET_E_SHAPE = -2,     /* a size is out of range (negative count, d % 32 != 0, ...)    */
+  JET_E_DTYPE = -3,     /* unsupported operand type combination                         */
+  JET_E_INDEX = -4,     /* host validation: index out of range or offsets not monotone  */
+  JET_E_TEMP = -5,      /* T is not finite or not > 0                                   */
+  JET_E_WORKSPACE = -6, /* workspace NULL, smaller than the size query, or misaligned   */
+  JET_E_HIP = -7,       /* a HIP runtime call (launch, event record) failed             */
+} jet_status;
+
+typedef enum { JET_F32 = 0, JET_BF16 = 1 } jet_dtype;
+
+/* Device flag bits written to *dev_flags (OR-ed; the buffer is cleared by each call). */
+#define JET_FLAG_BAD_ROW 1u      /* tok_row[k] outside [0, n_rows)                        */
+#define JET_FLAG_BAD_TARGET 2u   /* tok_target[k] outside [0, V)                          */
+#define JET_FLAG_BAD_OFFSETS 4u  /* cand_tok_off / q_cand_off / field offsets malformed   */
+#define JET_FLAG_BAD_TRUE_IDX 8u /* q_true_idx[q] outside [-1, K_q)                       */
+#define JET_FLAG_BAD_UNION 16u   /* union id / slot index / field row out of range        */
+
+/* Full-vocabulary problem (JET Eq. 1-5).  Token k is scored from predictor row
+ * tok_row[k] against target tok_target[k]; tokens [cand_tok_off[c], cand_tok_off[c+1])
+ * form candidate c in order; candidates [q_cand_off[g], q_cand_off[g+1]) form question g
+ * in their fixed tie order.  One row may serve many tokens: e.g. the shared prefix row
+ * scores the first token of every candidate (JET, hybrid execution) and one field row
+ * scores every single-token choice of that field (gemma-e2b doc). */
+typedef struct {
+  const void* H;             /* [n_rows][d] predictor hidden states                      */
+  jet_dtype h_dtype;
+  int32_t n_rows;
+  const void* W;             /* [V][d] LM head (tied embedding) rows                     */
+  jet_dtype w_dtype;
+  int32_t V;
+  int32_t d;
+  const int32_t* tok_row;    /* [n_tok] row of token k; NULL: token k uses row k          */
+  const int32_t* tok_target; /* [n_tok] target id in [0, V)                                */
+  int32_t n_tok;
+  const int32_t* cand_tok_off; /* [n_cand+1]: 0 = off[0] < off[1] < ... = n_tok (m_c >= 1) */
+  int32_t n_cand;
+  const int32_t* q_cand_off;   /* [n_q+1]: 0 = off[0] < ... = n_cand (K_g >= 1)            */
+  int32_t n_q;
+  const int32_t* cand_text_id;   /* [n_cand] optional: equal id = identical answer text   */
+  const int32_t* q_gold_text_id; /* [n_q] optional: text id of the gold answer            */
+  const int32_t* q_true_idx;     /* [n_q] optional: local index of "true", -1 = none;
+                                    NULL: index 1 when K_g == 2 ([false, true]), else none */
+  float T;                       /* candidate temperature, finite and > 0 (default 1)     */
+} jet_problem;
+
+/* Outputs of jet_score (device buffers, fp32 unless noted).  Required: tok_logp, cand_s,
+ * cand_q, q_argmax.  Optional outputs may be NULL. */
+typedef struct {
+  float* tok_logp;     /* [n_tok]  l_k                                                     */
+  float* row_lse;      /* [n_rows] LSE_r (optional)                                        */
+  float* cand_s;       /* [n_cand] s(c)                                                    */
+  float* cand_q;       /* [n_cand] q(c)                                                    */
+  int32_t* q_argmax;   /* [n_q] local index of the decision (lowest index wins ties)      */
+  float* q_true;       /* [n_q] q(true); NaN when the question has no true index (opt.)   */
+  float* q_expect;     /* [n_q] sum_i i q(i), levels 0..K-1 in supplied order (optional)  */
+  float* q_gold_nll;   /* [n_q] -log sum_{text = gold} q; NaN without text ids, +inf when
+                          no candidate has the gold text (optional)                        */
+  float* q_confidence; /* [n_q] 1 - H(q) / ln K, 1 when K = 1 (optional)                  */
+  float* q_mass;       /* [n_q] sum_c exp s(c): full-vocabulary probability mass of the
+                          complete candidate sequences (optional)                          */
+  int32_t* dev_flags;  /* [1] JET_FLAG_* bits met on the device (optional)                 */
+} jet_outputs;
+
+/* Bytes of device workspace jet_score needs for this problem (depends only on the
+ * problem's scalars: sizes and dtypes).  0 when the problem is invalid. */
+JET_API size_t jet_score_workspace_size(const jet_problem* p);
+
+/* Enqueue the whole path: operand staging, fused projection + online full-vocabulary
+ * logsumexp + target capture (logits never stored), the deterministic merge of the
+ * per-chunk normalisers, token log-probabilities, candidate sums and per-question
+ * decisions.  workspace: device memory of at least jet_score_workspace_size(p) bytes,
+ * 256-byte aligned, not shared with a concurrent call.  Results are bitwise
+ * reproducible for identical inputs and do not depend on a row's position. */
+JET_API jet_status jet_score(const jet_problem* p, const jet_outputs* o, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* jet_score, additionally recording ev_before and ev_after (hipEvent_t as void*, may be
+ * NULL) on the stream immediately before and after the projection kernel, so a caller
+ * can time the dominant kernel alone. */
+JET_API jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o, void* workspace,
+                              size_t workspace_bytes, void* stream, void* ev_before,
+                              void* ev_after);
+
+/* Host-side validation of a problem whose index arrays (tok_row, tok_target,
+ * cand_tok_off, q_cand_off, q_true_idx) are HOST pointers; H and W are not read.
+ * Returns JET_OK or the first error found. */
+JET_API jet_status jet_validate_host(const jet_problem* p);
+
+/* Restricted-vocabulary scoring (nimble page, Execution steps 5-6): gather only the
+ * allowed head rows (their sorted union), project the rows onto the union and take each
+ * field's softmax over its own allowed ids at temperature T.  The full-vocabulary
+ * normaliser is never computed, so there are no token log-probabilities. */
+
+/* HOST: build the sorted unique union of every field's allowed ids and, per slot, the
+ * index of its id in the union.  field_ids[field_off[n_fields]] and field_off[n_fields+1]
+ * are inputs; union_ids must hold field_off[n_fields] entries; slot_uidx likewise.
+ * Returns JET_E_INDEX for an id outside [0, V) or malformed offsets. */
+JET_API jet_status jet_build_union(const int32_t* field_ids, const int32_t* field_off, int32_t n_fields,
+                           int32_t V, int32_t* union_ids, int32_t* n_union, int32_t* slot_uidx);
+
+typedef struct {
+  const void* H;                /* [n_rows][d]                                              */
+  jet_dtype h_dtype;
+  int32_t n_rows;
+  const void* W;                /* [V][d]                                                   */
+  jet_dtype w_dtype;
+  int32_t V;
+  int32_t d;
+  const int32_t* union_ids;     /* [n_union] sorted unique ids in [0, V)                    */
+  int32_t n_union;
+  const int32_t* field_row;     /* [n_fields] row of H scored for field f                  */
+  const int32_t* field_slot_off;/* [n_fields+1] monotone, K_f >= 1, last = n_slots          */
+  const int32_t* slot_uidx;     /* [n_slots] index into union_ids of slot j's allowed id   */
+  int32_t n_fields;
+  int32_t n_slots;
+  float T;                      /* finite, > 0                                              */
+} jet_restricted_problem;
+
+typedef struct {
+  float* slot_logit;      /* [n_slots] z[field_row[f], union_ids[slot_uidx[j]]]             */
+  float* slot_q;          /* [n_slots] softmax over the field's slots of slot_logit / T     */
+  int32_t* field_argmax;  /* [n_fields] local slot index of the decision (lowest wins ties) */
+  int32_t* dev_flags;     /* [1] optional                                                   */
+} jet_restricted_outputs;
+
+JET_API size_t jet_restricted_workspace_size(const jet_restricted_problem* p);
+JET_API jet_status jet_score_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
+                                void* workspace, size_t workspace_bytes, void* stream);
+/* Host-side validation of a restricted problem whose index arrays are HOST pointers. */
+JET_API jet_status jet_validate_restricted_host(const jet_restricted_problem* p);
+
+/* Static description of a status code. */
+JET_API const char* jet_status_string(jet_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JET_H */

@@ -1,0 +1,205 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol, the
+ctypes structs match the C layout, host validation and the union builder behave, and
+invalid scalars are rejected before anything touches the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as jo
+import workloads as wl
+from candidate_likelihood_scoring_amd import _lib, api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jet.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"JET_API\s+[\w\s\*]+?\b(jet_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 9
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (jet_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    assert set(names) == set(_lib.EXPORTS), "ctypes table out of sync with include/jet.h"
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+_STRUCTS = {
+    "jet_problem": _lib.JetProblem, "jet_outputs": _lib.JetOutputs,
+    "jet_restricted_problem": _lib.JetRestrictedProblem,
+    "jet_restricted_outputs": _lib.JetRestrictedOutputs,
+}
+
+
+def test_struct_layout_matches_header(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
+    for cname, cls in _STRUCTS.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-o", str(exe), str(src)], check=True)
+    got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    for line in got:
+        if not line:
+            continue
+        cname, field, val = line.split()
+        cls = _STRUCTS[cname]
+        want = ctypes.sizeof(cls) if field == "sizeof" else getattr(cls, field).offset
+        assert int(val) == want, (cname, field, val, want)
+
+
+def test_status_strings(lib):
+    for code in range(-7, 1):
+        assert lib.jet_status_string(code)
+
+
+def _p(**kw):
+    p = wl.make_problem(V=50, d=32, n_q=3, K=(1, 4), lengths=(1, 3), layout="prefix", seed=3, **kw)
+    return p
+
+
+def _validate(p, **over):
+    args = dict(tok_target=p["tok_target"], cand_tok_off=p["cand_tok_off"], q_cand_off=p["q_cand_off"],
+                n_rows=p["n_rows"], V=p["V"], d=p["d"], T=p["T"], tok_row=p["tok_row"],
+                q_true_idx=p.get("q_true_idx"), h_dtype=0, w_dtype=1)
+    args.update(over)
+    return api.validate(**args)
+
+
+def test_validate_host_accepts_generated_problems():
+    for name in ("tiny", "tiny_tie", "binary_enum", "multi_token", "large_batch"):
+        p = wl.make_config(name, with_weights=False)
+        w_dtype = 0 if p["w_dtype"] == "f32" else 1
+        h_dtype = 0 if p["h_dtype"] == "f32" else 1
+        assert _validate(p, h_dtype=h_dtype, w_dtype=w_dtype) == 0, name
+
+
+def test_validate_host_rejects_bad_indices():
+    p = _p()
+    E_INDEX, E_SHAPE, E_TEMP, E_DTYPE = -4, -2, -5, -3
+    t = p["tok_target"].copy(); t[0] = p["V"]
+    assert _validate(p, tok_target=t) == E_INDEX
+    t = p["tok_target"].copy(); t[-1] = -1
+    assert _validate(p, tok_target=t) == E_INDEX
+    r = p["tok_row"].copy(); r[1] = p["n_rows"]
+    assert _validate(p, tok_row=r) == E_INDEX
+    c = p["cand_tok_off"].copy(); c[1] = c[0]
+    assert _validate(p, cand_tok_off=c) == E_INDEX  # empty candidate (m_c = 0)
+    c = p["cand_tok_off"].copy(); c[-1] += 1
+    assert _validate(p, cand_tok_off=c, tok_target=np.append(p["tok_target"], 0),
+                     tok_row=np.append(p["tok_row"], 0)) == 0
+    q = p["q_cand_off"].copy(); q[1] = 0
+    assert _validate(p, q_cand_off=q) == E_INDEX  # empty question (K = 0)
+    K = np.diff(p["q_cand_off"])
+    assert _validate(p, q_true_idx=np.full(len(K), -1, np.int32)) == 0
+    assert _validate(p, q_true_idx=K.astype(np.int32)) == E_INDEX
+    assert _validate(p, T=0.0) == E_TEMP
+    assert _validate(p, T=float("nan")) == E_TEMP
+    assert _validate(p, T=float("inf")) == E_TEMP
+    assert _validate(p, d=48) == E_SHAPE
+    assert _validate(p, V=0) == E_SHAPE
+    assert _validate(p, h_dtype=1, w_dtype=0) == E_DTYPE
+
+
+def test_build_union_matches_oracle():
+    rng = np.random.default_rng(2)
+    for trial in range(5):
+        n_f = int(rng.integers(1, 40))
+        K = rng.integers(1, 27, size=n_f)
+        off = np.concatenate([[0], np.cumsum(K)]).astype(np.int32)
+        ids = rng.integers(0, 1000, size=int(off[-1])).astype(np.int32)
+        u, s = api.build_union(ids, off, 1000)
+        ou, os_ = jo.build_union(ids, off, 1000)
+        assert np.array_equal(u, ou) and np.array_equal(s, os_)
+    for name in ("restricted", "restricted_max"):
+        rp = wl.make_config(name, with_weights=False)
+        u, s = api.build_union(rp["field_ids"], rp["field_off"], rp["V"])
+        ou, os_ = jo.build_union(rp["field_ids"], rp["field_off"], rp["V"])
+        assert np.array_equal(u, ou) and np.array_equal(s, os_)
+    assert len(api.build_union(wl.make_config("restricted_max", with_weights=False)["field_ids"],
+                               wl.make_config("restricted_max", with_weights=False)["field_off"],
+                               248320)[0]) == 832
+    with pytest.raises(_lib.JetError):
+        api.build_union(np.array([1, 1000], np.int32), np.array([0, 2], np.int32), 1000)
+    with pytest.raises(_lib.JetError):
+        api.build_union(np.array([1, 2], np.int32), np.array([0, 0, 2], np.int32), 1000)
+
+
+def test_validate_restricted_host():
+    union = np.array([2, 5, 9], np.int32)
+    ok = dict(union_ids=union, field_row=np.array([0, 1], np.int32),
+              field_slot_off=np.array([0, 2, 3], np.int32), slot_uidx=np.array([0, 2, 1], np.int32),
+              n_rows=2, V=10, d=32)
+    assert api.validate_restricted(**ok) == 0
+    assert api.validate_restricted(**{**ok, "union_ids": np.array([2, 2, 9], np.int32)}) == -4
+    assert api.validate_restricted(**{**ok, "slot_uidx": np.array([0, 3, 1], np.int32)}) == -4
+    assert api.validate_restricted(**{**ok, "field_row": np.array([0, 2], np.int32)}) == -4
+    assert api.validate_restricted(**{**ok, "T": -1.0}) == -5
+
+
+def test_score_rejects_invalid_scalars_without_a_device(lib):
+    """Scalar and workspace checks return before any device call, so they run here."""
+    h = np.zeros(64, np.float32)
+    p = _lib.JetProblem()
+    p.H, p.h_dtype, p.n_rows = h.ctypes.data, 0, 1
+    p.W, p.w_dtype, p.V, p.d = h.ctypes.data, 1, 2, 32
+    tgt = np.zeros(1, np.int32)
+    off = np.array([0, 1], np.int32)
+    p.tok_target, p.n_tok = tgt.ctypes.data, 1
+    p.cand_tok_off, p.n_cand = off.ctypes.data, 1
+    p.q_cand_off, p.n_q = off.ctypes.data, 1
+    p.T = 1.0
+    o = _lib.JetOutputs()
+    f = np.zeros(4, np.float32)
+    o.tok_logp = o.cand_s = o.cand_q = o.q_argmax = f.ctypes.data
+    assert lib.jet_score_workspace_size(ctypes.byref(p)) > 0
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -6
+    p.T = -1.0
+    assert lib.jet_score_workspace_size(ctypes.byref(p)) == 0
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -5
+    p.T = 1.0
+    p.d = 40
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -2
+    p.d = 32
+    p.w_dtype, p.h_dtype = 0, 1
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -3
+    p.w_dtype, p.h_dtype = 1, 0
+    o.cand_q = None
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -1
+    o.cand_q = f.ctypes.data
+    p.n_cand = 0  # fewer candidates than questions: a question would be empty
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -2
+    p.n_cand = 1
+    ws = np.zeros(1 << 20, np.uint8)
+    mis = ws.ctypes.data + 1
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), mis, 1 << 19, None) == -6
+
+
+def test_workspace_size_is_monotone_in_problem_size(lib):
+    sizes = []
+    for n_rows in (1, 32, 33, 1000):
+        p = _lib.JetProblem()
+        h = np.zeros(16, np.float32)
+        p.H, p.h_dtype, p.n_rows = h.ctypes.data, 0, n_rows
+        p.W, p.w_dtype, p.V, p.d = h.ctypes.data, 1, 248320, 2560
+        p.T = 1.0
+        sizes.append(lib.jet_score_workspace_size(ctypes.byref(p)))
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes)

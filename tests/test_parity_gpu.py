@@ -1,0 +1,249 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (needs an MI355X).
+
+Small and ragged problems are compared element by element on every output.  The five
+workloads run at their full sizes in the configuration the benchmark times; the large ones
+are compared on sampled rows the oracle computes one by one, plus properties that hold at
+any size (flags clear, q sums to one, duplicates bitwise equal, run-to-run determinism).
+"""
+import numpy as np
+import pytest
+
+import oracle as jo
+import workloads as wl
+from tests.parity import Q_TOL, compare, log, tol_logp
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def jet():
+    from candidate_likelihood_scoring_amd import problem
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return problem
+
+
+def _run(jet, p, **kw):
+    out = jet.to_numpy(jet.score_problem(jet.to_device(p, "cuda"), **kw))
+    torch.cuda.synchronize()
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# small problems: full element-by-element parity
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_tie"])
+def test_tiny(jet, name):
+    p = wl.make_config(name)
+    log(f"[gpu] {name}")
+    out = _run(jet, p)
+    ref = jo.score(p)
+    log(f"[gpu] {name} errs {compare(p, out, ref, name)}")
+    if name == "tiny_tie":
+        co = p["cand_tok_off"]
+        assert out["cand_s"][2] == out["cand_s"][3]  # identical inputs: bitwise equal
+        assert out["cand_q"][2] == out["cand_q"][3]
+        assert np.array_equal(out["tok_logp"][co[2]:co[3]], out["tok_logp"][co[3]:co[4]])
+        if out["q_argmax"][0] in (2, 3):
+            assert out["q_argmax"][0] == 2  # lowest index wins the tie
+
+
+RAGGED = [
+    dict(V=4099, d=64, n_q=7, K=(1, 9), lengths=(1, 5), layout="prefix", seed=11),
+    dict(V=10007, d=256, n_q=12, K=(2, 20), lengths=(1, 4), layout="own", seed=12),
+    dict(V=6151, d=96, n_q=40, K=(1, 26), layout="field", seed=13, T=2.0),
+    dict(V=5003, d=128, n_q=9, K=(1, 12), lengths=(1, 6), layout="prefix", seed=14, h_dtype="bf16",
+         dups=2),
+    dict(V=3001, d=64, n_q=6, K=(1, 8), lengths=(1, 7), layout="own", seed=15, w_dtype="f32"),
+    dict(V=2053, d=32, n_q=30, K=(1, 70), lengths=(1, 3), layout="prefix", seed=16, T=0.7),
+    dict(V=33, d=32, n_q=3, K=(1, 5), lengths=(1, 3), layout="prefix", seed=17),
+    dict(V=1, d=32, n_q=2, K=(1, 3), lengths=(1, 2), layout="own", seed=18),
+    dict(V=64, d=32, n_q=1, K=1, lengths=1, layout="field", seed=19),
+    dict(V=4096, d=256, n_q=8, K=(2, 5), lengths=(1, 3), layout="own", seed=20, w_dtype="f32",
+         n_extra_rows=0, w_std=0.5),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[f"ragged{i}" for i in range(len(RAGGED))])
+def test_ragged(jet, case):
+    p = wl.make_problem(**case)
+    log(f"[gpu] ragged {case} rows={p['n_rows']} tok={len(p['tok_target'])}")
+    out = _run(jet, p)
+    ref = jo.score(p)
+    log(f"[gpu] errs {compare(p, out, ref, str(case))}")
+
+
+def test_true_index_and_gold(jet):
+    p = wl.make_problem(V=3000, d=64, n_q=10, K=(2, 6), lengths=(1, 3), layout="prefix", seed=31, dups=1)
+    K = np.diff(p["q_cand_off"])
+    rng = np.random.default_rng(0)
+    p["q_true_idx"] = np.array([rng.integers(-1, k) for k in K], dtype=np.int32)
+    p["q_gold_text_id"][0] = 999  # gold text absent -> +inf
+    out = _run(jet, p)
+    ref = jo.score(p)
+    compare(p, out, ref, "true_idx")
+    assert np.isinf(out["q_gold_nll"][0])
+
+
+def test_empty_problem(jet):
+    p = wl.make_problem(V=100, d=32, n_q=0, seed=2, n_extra_rows=3)
+    out = _run(jet, p)
+    ref = jo.score(p)
+    assert out["dev_flags"][0] == 0
+    assert np.max(np.abs(out["row_lse"] - ref["lse"])) < 2e-3
+
+
+def test_bad_indices_set_flags_without_faulting(jet):
+    """Out-of-range rows/targets and malformed offsets are bounds-checked on the device."""
+    p = wl.make_problem(V=500, d=32, n_q=4, K=(2, 4), lengths=(1, 3), layout="prefix", seed=41)
+    q = dict(p)
+    q["tok_target"] = p["tok_target"].copy()
+    q["tok_target"][0] = p["V"] + 7
+    out = _run(jet, q)
+    assert out["dev_flags"][0] & 2
+    assert np.isnan(out["tok_logp"][0])
+    q = dict(p)
+    q["tok_row"] = p["tok_row"].copy()
+    q["tok_row"][1] = p["n_rows"] + 100
+    out = _run(jet, q)
+    assert out["dev_flags"][0] & 1
+    q = dict(p)
+    q["cand_tok_off"] = p["cand_tok_off"].copy()
+    q["cand_tok_off"][2] = q["cand_tok_off"][1]  # an empty candidate
+    out = _run(jet, q)
+    assert out["dev_flags"][0] & 4
+    q = dict(p)
+    K = np.diff(p["q_cand_off"])
+    q["q_true_idx"] = (K + 3).astype(np.int32)
+    out = _run(jet, q)
+    assert out["dev_flags"][0] & 8
+
+
+def test_deterministic(jet):
+    p = wl.make_problem(V=20011, d=256, n_q=20, K=(2, 10), lengths=(1, 5), layout="prefix", seed=51)
+    a = _run(jet, p)
+    b = _run(jet, p)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+# ----------------------------------------------------------------------------------------
+# the five workloads at full size
+# ----------------------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def binary_enum():
+    return wl.binary_enum()
+
+
+def test_binary_enum_full(jet, binary_enum):
+    p = binary_enum
+    log("[gpu] binary_enum full")
+    out = _run(jet, p)
+    ref = jo.score(p)
+    log(f"[gpu] binary_enum errs {compare(p, out, ref, 'binary_enum')}")
+
+
+@pytest.mark.parametrize("kind", ["wide", "planted"])
+def test_stress(jet, kind):
+    p = wl.stress(kind)
+    log(f"[gpu] stress {kind}")
+    out = _run(jet, p)
+    ref = jo.score(p)
+    log(f"[gpu] stress {kind} errs {compare(p, out, ref, kind)}")
+
+
+def _rows_of_questions(p, qs):
+    co, qo = p["cand_tok_off"], p["q_cand_off"]
+    tok_row = np.arange(len(p["tok_target"])) if p["tok_row"] is None else p["tok_row"]
+    rows = []
+    for g in qs:
+        t0, t1 = co[qo[g]], co[qo[g + 1]]
+        rows.append(tok_row[t0:t1])
+    return np.unique(np.concatenate(rows))
+
+
+def _full_size_properties(p, out):
+    qo = p["q_cand_off"]
+    assert out["dev_flags"][0] == 0
+    assert np.all(np.isfinite(out["tok_logp"])) and np.all(out["tok_logp"] < 0)
+    sums = np.add.reduceat(out["cand_q"].astype(np.float64), qo[:-1])
+    assert np.max(np.abs(sums - 1.0)) < 1e-5
+    co = p["cand_tok_off"]
+    s_from_l = np.add.reduceat(out["tok_logp"].astype(np.float64), co[:-1])
+    assert np.max(np.abs(s_from_l - out["cand_s"])) < 1e-3
+    K = np.diff(qo)
+    assert np.all((out["q_argmax"] >= 0) & (out["q_argmax"] < K))
+
+
+def test_multi_token_full_sampled(jet):
+    p = wl.multi_token()
+    log(f"[gpu] multi_token rows={p['n_rows']} tok={len(p['tok_target'])}")
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    # duplicates: bitwise-equal log-probs for bitwise-equal rows at other positions
+    for dst, src in p["dup_row_pairs"]:
+        assert np.array_equal(out["row_lse"][dst], out["row_lse"][src])
+    # sampled parity: main questions 0 and 5 and their ordinal/binary subsets (same rows)
+    rows = _rows_of_questions(p, [0, 5])
+    log(f"[gpu] multi_token oracle on {len(rows)} rows")
+    ref = jo.score(p, rows=rows)
+    errs = compare(p, out, ref, "multi_token", sampled=True)
+    log(f"[gpu] multi_token errs {errs}")
+    assert errs["argmax_checked"] >= 2
+
+
+def test_large_batch_full_sampled(jet):
+    p = wl.large_batch()
+    log(f"[gpu] large_batch rows={p['n_rows']}")
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    rows = _rows_of_questions(p, [0, 101, 257, 511])
+    log(f"[gpu] large_batch oracle on {len(rows)} rows")
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] large_batch errs {compare(p, out, ref, 'large_batch', sampled=True)}")
+
+
+@pytest.mark.parametrize("max_variant", [False, True])
+def test_restricted(jet, max_variant):
+    rp = wl.restricted(max_variant=max_variant)
+    log(f"[gpu] restricted max={max_variant}")
+    rd = jet.restricted_to_device(rp, "cuda")
+    ou, os_ = jo.build_union(rp["field_ids"], rp["field_off"], rp["V"])
+    assert np.array_equal(rd["host_union"], ou) and np.array_equal(rd["host_slot_uidx"], os_)
+    out = jet.to_numpy(jet.score_restricted_problem(rd))
+    torch.cuda.synchronize()
+    assert out["dev_flags"][0] == 0
+    ref = jo.score_restricted(rp)
+    dl = np.max(np.abs(out["slot_logit"] - ref["slot_logit"]))
+    dq = np.max(np.abs(out["slot_q"] - ref["slot_q"]))
+    assert dl <= 2e-3 and dq <= Q_TOL, (dl, dq)
+    dec = ref["field_gap"] > Q_TOL
+    assert np.array_equal(out["field_argmax"][dec], ref["field_argmax"][dec])
+    # against the full-vocabulary path on the same inputs (LSE cancels in the field softmax)
+    full = _run(jet, wl.restricted_as_full(rp))
+    assert np.max(np.abs(full["cand_q"] - out["slot_q"])) <= Q_TOL
+    assert np.array_equal(full["q_argmax"][dec], out["field_argmax"][dec])
+    log(f"[gpu] restricted errs logit={dl:.2e} q={dq:.2e}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(n_fields=5, V=1000, d=64, K=(1, 9), seed=3),
+    dict(n_fields=70, V=30011, d=256, K=(1, 26), seed=4, shared_rows=True, n_rows=9),
+    dict(n_fields=3, V=500, d=32, K=(2, 4), seed=5, h_dtype="bf16"),
+    dict(n_fields=4, V=700, d=64, K=(1, 5), seed=6, w_dtype="f32"),
+])
+def test_restricted_ragged(jet, case):
+    rp = wl.make_restricted(T=1.7, **case)
+    rd = jet.restricted_to_device(rp, "cuda")
+    out = jet.to_numpy(jet.score_restricted_problem(rd))
+    torch.cuda.synchronize()
+    ref = jo.score_restricted(rp)
+    tl = 1e-4 if rp["w_dtype"] == "f32" else 2e-3
+    assert out["dev_flags"][0] == 0
+    assert np.max(np.abs(out["slot_logit"] - ref["slot_logit"])) <= tl
+    assert np.max(np.abs(out["slot_q"] - ref["slot_q"])) <= Q_TOL
+    dec = ref["field_gap"] > Q_TOL
+    assert np.array_equal(out["field_argmax"][dec], ref["field_argmax"][dec])
