@@ -1,0 +1,272 @@
+"""Benchmark of the candidate-scoring hot path on one MI355X.
+
+A step is one jet_score call over one batch: fp32-H staging, the fused LM-head projection
+with online full-vocabulary logsumexp and target capture, the normaliser merge, token
+log-probabilities, candidate sums and per-question decisions (or, for the restricted
+workload, one jet_score_restricted call).  Inputs are synthetic, seeded, and resident in
+HBM before timing starts.
+
+Prints one JSON line: scored candidate tokens/s, the dominant kernel's roofline (its
+duration measured with HIP events that the library records around it on the same stream)
+and the fp64 oracle's throughput on this host's cores as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scored candidate tokens/sec (full-vocab LSE) + % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix peak
+MFMA_F32_PEAK_TFS = 157.3
+
+WORKLOADS = ("binary_enum", "multi_token", "large_batch", "restricted", "restricted_max", "tiny")
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# Sources that determine the dominant kernels' code; a traffic figure measured with
+# hardware counters is reported only while these are unchanged.
+KERNEL_SOURCES = ["candidate_likelihood_scoring_amd/csrc/k_project.hip",
+                  "candidate_likelihood_scoring_amd/csrc/jet_internal.h"]
+
+
+def _traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    scaled by the counters of a copy kernel of known size), if it was taken on the
+    current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_digest:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != _source_digest(KERNEL_SOURCES):
+        return None
+    return float(t.group(1))
+
+
+def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 30.0) -> dict:
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    if restricted:
+        t0 = time.perf_counter()
+        oracle.score_restricted(p)
+        dt = time.perf_counter() - t0
+        n = int(p["field_off"][-1])
+        return dict(value=n / dt, unit="scored candidate tokens/s", cores=int(cores), kind="oracle",
+                    sample=f"the whole batch ({n} allowed-token slots), 1 run, {dt:.2f} s")
+    n_tok = len(p["tok_target"])
+    tok_row = np.arange(n_tok) if p.get("tok_row") is None else np.asarray(p["tok_row"])
+    # Time one question first; then as many whole questions as fit the budget.
+    qo = p["q_cand_off"]
+    co = p["cand_tok_off"]
+
+    def rows_of(qs):
+        return np.unique(np.concatenate([tok_row[co[qo[g]]:co[qo[g + 1]]] for g in qs]))
+
+    n_q = len(qo) - 1
+    t0 = time.perf_counter()
+    oracle.score(p, rows=rows_of(range(min(n_q, 1))))
+    probe = time.perf_counter() - t0
+    n_rows = int(p["n_rows"])
+    sample_q = n_q
+    if probe * n_q > budget_s:
+        sample_q = max(1, int(budget_s / max(probe, 1e-3)))
+    qs = list(range(sample_q))
+    rows = rows_of(qs) if sample_q < n_q else None
+    t0 = time.perf_counter()
+    oracle.score(p, rows=rows)
+    dt = time.perf_counter() - t0
+    toks = int(co[qo[sample_q]]) if sample_q < n_q else n_tok
+    what = ("the whole batch" if sample_q == n_q else f"the first {sample_q} of {n_q} questions")
+    n_r = n_rows if rows is None else len(rows)
+    return dict(value=toks / dt, unit="scored candidate tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{what}: {toks} tokens on {n_r} predictor rows, 1 run, {dt:.2f} s")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=WORKLOADS, default="binary_enum")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a device copy of this many MiB first (counter calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from candidate_likelihood_scoring_amd import _lib, api, problem
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = _lib.load()
+    restricted = args.workload.startswith("restricted")
+
+    _log(f"[bench] generating {args.workload}")
+    p = wl.make_config(args.workload)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream or None
+    if restricted:
+        rd = problem.restricted_to_device(p, dev)
+        prob = api.make_restricted_problem(rd["H"], rd["W"], rd["union_ids"], rd["field_row"],
+                                           rd["field_slot_off"], rd["slot_uidx"], rd["T"])
+        need = api.restricted_workspace_size(prob)
+        ws = api.Workspace(dev)
+        base, size = ws.get(need)
+        out = dict(slot_logit=torch.empty(prob.n_slots, device=dev),
+                   slot_q=torch.empty(prob.n_slots, device=dev),
+                   field_argmax=torch.empty(prob.n_fields, dtype=torch.int32, device=dev),
+                   dev_flags=torch.zeros(1, dtype=torch.int32, device=dev))
+        o = _lib.JetRestrictedOutputs()
+        for name, _ in o._fields_:
+            setattr(o, name, out[name].data_ptr())
+
+        def step(ev=None):
+            st = lib.jet_score_restricted(ctypes.byref(prob), ctypes.byref(o), base, size, sh)
+            if st:
+                raise _lib.JetError(st, "jet_score_restricted")
+
+        n_tokens = prob.n_slots
+    else:
+        pd = problem.to_device(p, dev)
+        prob = api.make_problem(**pd)
+        need = api.score_workspace_size(prob)
+        ws = api.Workspace(dev)
+        base, size = ws.get(need)
+        out = api.alloc_outputs(prob, dev, optional=True)
+        o = api._outputs_struct(out)
+
+        def step(ev=None):
+            if ev is None:
+                st = lib.jet_score(ctypes.byref(prob), ctypes.byref(o), base, size, sh)
+            else:
+                st = lib.jet_score_profiled(ctypes.byref(prob), ctypes.byref(o), base, size, sh,
+                                            ev[0], ev[1])
+            if st:
+                raise _lib.JetError(st, "jet_score")
+
+        n_tokens = prob.n_tok
+        if args.workload == "multi_token":
+            n_tokens = int(p["n_primary_tok"])  # subset re-references are not new scored tokens
+
+    _log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    flags = int(out["dev_flags"][0].item())
+    assert flags == 0, f"device flags {flags}"
+
+    events = []
+    if not restricted:
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            events.append((a, b))
+        torch.cuda.synchronize()
+    _log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step((events[i][0].cuda_event, events[i][1].cuda_event) if events else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = n_tokens * args.steps / wall
+
+    V, d = int(p["V"]), int(p["d"])
+    w_elt = 4 if p["w_dtype"] == "f32" else 2
+    rows = int(p["n_rows"])
+    roofline = None
+    extra = {}
+    if events:
+        kms = np.array([a.elapsed_time(b) for a, b in events])
+        k_avg_s = float(kms.mean()) * 1e-3
+        extra["projection_kernel_ms_mean"] = round(float(kms.mean()), 5)
+        extra["projection_kernel_ms_min"] = round(float(kms.min()), 5)
+        flops = 2.0 * rows * d * V
+        h_bytes = rows * d * (4 if p["h_dtype"] == "f32" else 2)
+        alg_bytes = V * d * w_elt + h_bytes
+        intensity = flops / alg_bytes
+        kernel = "k_project_small"
+        if intensity < 300.0:
+            achieved = alg_bytes / k_avg_s / 1e9
+            roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                            frac=round(achieved / HBM_PEAK_GBS, 4),
+                            traffic=_traffic_from_profiles(kernel, args.workload))
+        else:
+            peak = MFMA_F32_PEAK_TFS if p["w_dtype"] == "f32" else MFMA_BF16_PEAK_TFS
+            achieved = flops / k_avg_s / 1e12
+            roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                            frac=round(achieved / peak, 4),
+                            traffic=_traffic_from_profiles(kernel, args.workload))
+        extra["kernel"] = kernel
+        extra["algorithmic_bytes_per_launch"] = int(alg_bytes)
+        extra["algorithmic_flop_per_launch"] = int(flops)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("[bench] timing the fp64 oracle on host cores")
+        cpu = _cpu_baseline(p, restricted)
+
+    dtype = "f32" if p["w_dtype"] == "f32" else "bf16"
+    config = dict(workload=args.workload, V=V, d=d, rows=rows, scored_tokens=int(n_tokens),
+                  head_dtype=p["w_dtype"], hidden_dtype=p["h_dtype"], T=p["T"],
+                  accumulate="fp32", seed_layout="workloads.synth")
+    if not restricted:
+        config.update(candidates=int(prob.n_cand), questions=int(prob.n_q))
+    line = dict(metric=METRIC, value=round(value, 1), unit="scored candidate tokens/s", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_per_step, 5),
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype=dtype,
+                data="synthetic", config=config, roofline=roofline, cpu_baseline=cpu, extra=extra)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

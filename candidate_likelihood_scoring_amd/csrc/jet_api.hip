@@ -9,13 +9,17 @@
 
 namespace jet {
 
-int small_group_size(int variant);
+int small_group_size(int variant, int d);
+int small_grid(int variant, int d, int n_groups, int max_waves);
 
 namespace {
 
 constexpr int kMaxD = 65536;
 constexpr int kMaxV = 1 << 30;
-constexpr int kSmallWaves = 2048;  // 256 CUs x 8 resident waves
+#ifndef JET_SMALL_WAVES
+#define JET_SMALL_WAVES 2048  // 256 CUs x 8 resident waves
+#endif
+constexpr int kSmallWaves = JET_SMALL_WAVES;
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -64,10 +68,9 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
   pl->row_tile = 32;
   pl->n_rtiles = (p->n_rows + 31) / 32;
-  pl->vgroup = small_group_size(pl->variant);
+  pl->vgroup = small_group_size(pl->variant, p->d);
   pl->n_vgroups = (p->V + pl->vgroup - 1) / pl->vgroup;
-  int gx = (pl->n_vgroups + 3) / 4;
-  gx = std::max(1, std::min(gx, kSmallWaves / 4));
+  const int gx = std::max(1, small_grid(pl->variant, p->d, pl->n_vgroups, kSmallWaves));
   pl->grid_x = gx;
   pl->n_parts = gx;
   pl->n_buckets = (long long)pl->n_rtiles * pl->n_vgroups;

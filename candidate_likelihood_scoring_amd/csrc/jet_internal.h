@@ -16,6 +16,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 // bf16 round-to-nearest-even of an fp32 value (NaN stays a quiet NaN).
 __device__ inline uint16_t f32_to_bf16_rne(float x) {

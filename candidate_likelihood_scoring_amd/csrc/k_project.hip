@@ -28,19 +28,8 @@ namespace {
 
 constexpr int kWpb = 4;  // waves per workgroup
 
-struct Frag32B {
-  uint4 x, y;
-};
-
-__device__ inline Frag32B ld32(const uint16_t* p) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-  Frag32B f;
-  f.x = q[0];
-  f.y = q[1];
-  return f;
-}
-
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ inline bf16x8 as_bf16x8v(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Vocabulary index (relative to the tile) held by register i of lane half h.
 __device__ inline int tile_m(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
@@ -89,7 +78,7 @@ __device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int n, in
     const int r = tok_row ? tok_row[k] : k;
     const int lv = tok_target[k] - v0;
     const int mm = lv & 31;
-    if (n == r - row0 && half == ((mm >> 2) & 1)) {
+    if (lv >= 0 && lv < 32 * NT && n == r - row0 && half == ((mm >> 2) & 1)) {
       const int tt = lv >> 5, ii = ((mm >> 3) << 2) | (mm & 3);
       float val = 0.f;
 #pragma unroll
@@ -104,6 +93,7 @@ __device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int n, in
 
 // Merge the two lane halves, then the workgroup's waves in wave order; store one partial
 // per row of the tile.
+template <int NW = kWpb>
 __device__ inline void store_partial(float m_run, float s_run, int n, int half, int wid,
                                      int row0, int n_rows, float2* __restrict__ part,
                                      float2 (*red)[32]) {
@@ -117,7 +107,7 @@ __device__ inline void store_partial(float m_run, float s_run, int n, int half, 
   if (threadIdx.x < 32) {
     float m = red[0][n].x, s = red[0][n].y;
 #pragma unroll
-    for (int w = 1; w < kWpb; ++w) lse_merge(m, s, red[w][n].x, red[w][n].y);
+    for (int w = 1; w < NW; ++w) lse_merge(m, s, red[w][n].x, red[w][n].y);
     const int row = row0 + n;
     if (row < n_rows) part[(size_t)blockIdx.x * n_rows + row] = make_float2(m, s);
   }
@@ -139,67 +129,97 @@ __device__ inline void epilogue_store(const Acc<NT>& acc, int v0, int V, int n, 
 }
 
 // ------------------------------------------------------------------------------------
+// K pipeline.  A stage holds one KB-wide block of k: lane half h covers
+// [kb + h*KB/2, kb + h*KB/2 + KB/2), i.e. KB bytes (bf16) of its W row and of its H row.
+// S stages rotate through registers; loads are issued S-1 blocks ahead of use and are
+// never predicated (a block past the end re-reads the last block, which the caches
+// serve), so the compiler can wait for exactly the block it is about to consume.
+// ------------------------------------------------------------------------------------
+template <int KB>
+struct FragK {
+  uint4 v[KB / 16];
+};
+
+template <int KB>
+__device__ inline FragK<KB> ldk(const uint16_t* p) {
+  FragK<KB> f;
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int j = 0; j < KB / 16; ++j) f.v[j] = q[j];
+  return f;
+}
+
+// ------------------------------------------------------------------------------------
 // bf16 head
 // ------------------------------------------------------------------------------------
-template <int NT, bool HILO, bool STORE>
+template <int NT, int KB, int S, bool HILO, bool STORE>
 __global__ __launch_bounds__(256) void k_project_small_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ Hhi,
     const uint16_t* __restrict__ Hlo, int n_rows, int n_groups, const int* __restrict__ b_off,
     const int* __restrict__ b_tok, const int* __restrict__ tok_row,
     const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
     float* __restrict__ Z) {
+  static_assert(KB % 32 == 0 && S >= 2, "stage shape");
   __shared__ float2 red[kWpb][32];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n = lane & 31, half = lane >> 5;
   const int rt = blockIdx.y, row0 = rt * 32;
   const int hrow = min(row0 + n, n_rows - 1);
-  const uint16_t* hp = Hhi + (size_t)hrow * d + half * 16;
-  const uint16_t* lp = HILO ? Hlo + (size_t)hrow * d + half * 16 : nullptr;
+  const uint16_t* hp = Hhi + (size_t)hrow * d + half * (KB / 2);
+  const uint16_t* lp = HILO ? Hlo + (size_t)hrow * d + half * (KB / 2) : nullptr;
   const long long nw = (long long)gridDim.x * kWpb;
   const long long w = (long long)blockIdx.x * kWpb + wid;
   const int g0 = (int)(w * n_groups / nw), g1 = (int)((w + 1) * n_groups / nw);
+  const int nkb = d / KB;
   float m_run = -INFINITY, s_run = 0.f;
 
   for (int g = g0; g < g1; ++g) {
     const int v0 = g * (32 * NT);
     const uint16_t* wp[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) wp[t] = W + (size_t)min(v0 + 32 * t + n, V - 1) * d + half * 16;
+    for (int t = 0; t < NT; ++t)
+      wp[t] = W + (size_t)min(v0 + 32 * t + n, V - 1) * d + half * (KB / 2);
     Acc<NT> acc;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc.t[t] = f32x16{};
 
-    Frag32B a0[NT], a1[NT], bh0, bh1, bl0, bl1;
-#define JET_LOAD(A, BH, BL, KB)                                    \
-  {                                                                \
-    _Pragma("unroll") for (int t = 0; t < NT; ++t) A[t] = ld32(wp[t] + (KB)); \
-    BH = ld32(hp + (KB));                                          \
-    if (HILO) BL = ld32(lp + (KB));                                \
-  }
-#define JET_MMA(A, BH, BL)                                                                   \
-  {                                                                                          \
-    _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                         \
-      acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[t].x), as_bf16x8(BH.x), \
-                                                        acc.t[t], 0, 0, 0);                  \
-      if (HILO)                                                                              \
-        acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[t].x),                \
-                                                          as_bf16x8(BL.x), acc.t[t], 0, 0, 0); \
-      acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[t].y), as_bf16x8(BH.y), \
-                                                        acc.t[t], 0, 0, 0);                  \
-      if (HILO)                                                                              \
-        acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[t].y),                \
-                                                          as_bf16x8(BL.y), acc.t[t], 0, 0, 0); \
-    }                                                                                        \
-  }
-    JET_LOAD(a0, bh0, bl0, 0);
-    for (int kb = 0; kb < d; kb += 64) {
-      if (kb + 32 < d) JET_LOAD(a1, bh1, bl1, kb + 32);
-      JET_MMA(a0, bh0, bl0);
-      if (kb + 64 < d) JET_LOAD(a0, bh0, bl0, kb + 64);
-      if (kb + 32 < d) JET_MMA(a1, bh1, bl1);
+    FragK<KB> A[S][NT], BH[S], BL[S];
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) {
+      const int off = min(s, nkb - 1) * KB;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) A[s][t] = ldk<KB>(wp[t] + off);
+      BH[s] = ldk<KB>(hp + off);
+      if (HILO) BL[s] = ldk<KB>(lp + off);
     }
-#undef JET_LOAD
-#undef JET_MMA
+    for (int i = 0; i < nkb; i += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int ls = (s + S - 1) % S;
+        const int off = min(i + s + S - 1, nkb - 1) * KB;
+        // Keep each stage's loads ahead of its matrix ops and in source order, so every
+        // path into the loop sees the same number of younger loads at each wait.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) A[ls][t] = ldk<KB>(wp[t] + off);
+        BH[ls] = ldk<KB>(hp + off);
+        if (HILO) BL[ls] = ldk<KB>(lp + off);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + s < nkb) {
+#pragma unroll
+          for (int j = 0; j < KB / 16; ++j)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(A[s][t].v[j]), as_bf16x8(BH[s].v[j]), acc.t[t], 0, 0, 0);
+              if (HILO)
+                acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(A[s][t].v[j]), as_bf16x8(BL[s].v[j]), acc.t[t], 0, 0, 0);
+            }
+        }
+      }
+    }
     if (STORE)
       epilogue_store<NT>(acc, v0, V, n, half, row0, n_rows, Z);
     else
@@ -210,9 +230,123 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 }
 
 // ------------------------------------------------------------------------------------
-// fp32 head and fp32 hidden states: v_mfma_f32_32x32x2_f32, one k per lane half per
-// step; lane half h loads 4 consecutive k (a float4) of its row per 8-wide block and
-// step j uses k = kb + 4 h + j.
+// Streaming kernel for d % 128 == 0 (the HBM-bound small-row case).
+//
+// Every global load is lane-contiguous: 16 lanes cover 256 contiguous bytes of one row and
+// an instruction reads four rows, i.e. 8 whole cache lines per 1 KB.  (Loading operands
+// directly in the matrix-core layout instead touches 32-64 lines per instruction, and the
+// per-line cost then bounds the stream well below HBM bandwidth.)  The workgroup's waves
+// advance through K in lockstep, 128 k per stage:
+//   * each wave owns one 32-row tile of the head and moves each stage of it through its
+//     own LDS tile into the MFMA A layout;
+//   * the 32 x 128 stage of H (hi and lo planes) is loaded once per workgroup, each wave
+//     fetching WPB-th of it, into a double-buffered LDS stage shared by all waves.
+// LDS chunk (row r, 16-byte chunk c) of a 32x128 bf16 tile lives at r * 16 + (c ^ (r & 7)):
+// eight consecutive rows at the same c fall into eight different 16-byte bank groups, so
+// the row-wise writes and the column-wise fragment reads are both conflict-free.
+// K permutation inside a stage: lane half h, MFMA step j covers k = kb + 64 h + 8 j + e,
+// i.e. chunk 8 h + j of the row, for both operands.  Register stages rotate S deep; loads
+// run S-1 stages ahead and are never predicated (a stage past the end re-reads the last
+// one), so the compiler waits exactly for the stage it consumes.
+// ------------------------------------------------------------------------------------
+template <int WPB, int S, bool HILO>
+__global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
+    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ Hhi,
+    const uint16_t* __restrict__ Hlo, int n_rows, int n_groups, const int* __restrict__ b_off,
+    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part) {
+  constexpr int KC = 128;                 // k per stage
+  constexpr int NP = HILO ? 2 : 1;        // H planes
+  constexpr int HQ = NP * 8 / WPB;        // H load instructions per wave per stage
+  static_assert(HQ >= 1 && (NP * 8) % WPB == 0, "H stage split");
+  __shared__ u32x4 wt[WPB][512];          // per-wave 32-row head tile
+  __shared__ u32x4 hb[2][NP][512];        // H stage, double buffered
+  __shared__ float2 red[WPB][32];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n = lane & 31, half = lane >> 5;
+  const int lrow = lane >> 4, lch = lane & 15;
+  const int rt = blockIdx.y, row0 = rt * 32;
+  const int g0 = (int)((long long)blockIdx.x * n_groups / gridDim.x);
+  const int g1 = (int)((long long)(blockIdx.x + 1) * n_groups / gridDim.x);
+  const int nst = d / KC;
+  u32x4* my = wt[wid];
+  float m_run = -INFINITY, s_run = 0.f;
+
+  // H load instruction i of this wave: plane hq / 8, stage rows 4 (hq % 8) + lrow
+  int h_plane[HQ], h_r[HQ];
+  const uint16_t* h_src[HQ];
+#pragma unroll
+  for (int i = 0; i < HQ; ++i) {
+    const int hq = wid * HQ + i;
+    h_plane[i] = hq >> 3;
+    h_r[i] = 4 * (hq & 7) + lrow;
+    h_src[i] = (HILO && h_plane[i] ? Hlo : Hhi) + (size_t)min(row0 + h_r[i], n_rows - 1) * d + lch * 8;
+  }
+
+  for (int g = g0; g < g1; ++g) {
+    const int v0 = g * (WPB * 32) + wid * 32;
+    Acc<1> acc;
+    acc.t[0] = f32x16{};
+    u32x4 R[S][8], Hr[S][HQ];
+#define JET_STAGE_LOAD(SLOT, ST)                                                            \
+  {                                                                                         \
+    const int ko_ = (ST) * KC + lch * 8;                                                    \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) R[SLOT][q] = *reinterpret_cast<const u32x4*>( \
+        W + (size_t)min(v0 + 4 * q + lrow, V - 1) * d + ko_);                               \
+    _Pragma("unroll") for (int i = 0; i < HQ; ++i) Hr[SLOT][i] =                             \
+        *reinterpret_cast<const u32x4*>(h_src[i] + (ST) * KC);                              \
+  }
+#define JET_STAGE_MMA(SLOT, ST)                                                             \
+  {                                                                                         \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                         \
+      const int r = 4 * q + lrow;                                                           \
+      my[r * 16 + (lch ^ (r & 7))] = R[SLOT][q];                                            \
+    }                                                                                       \
+    u32x4* hbuf = &hb[(ST) & 1][0][0];                                                      \
+    _Pragma("unroll") for (int i = 0; i < HQ; ++i)                                          \
+        hbuf[h_plane[i] * 512 + h_r[i] * 16 + (lch ^ (h_r[i] & 7))] = Hr[SLOT][i];          \
+    __syncthreads();                                                                        \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
+      const int c = ((half * 8 + j) ^ (n & 7)) + n * 16;                                    \
+      const bf16x8 a = as_bf16x8v(my[c]);                                                   \
+      acc.t[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[c]), acc.t[0], 0, 0, 0); \
+      if (HILO)                                                                             \
+        acc.t[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[512 + c]), acc.t[0], 0, 0, 0); \
+    }                                                                                       \
+  }
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      JET_STAGE_LOAD(s, min(s, nst - 1));
+    }
+    // Main loop over a multiple of S stages: every prefetched slot is consumed, so no load
+    // sits behind a condition (which would let it sink to its use).
+    const int nmain = nst - nst % S;
+    for (int st0 = 0; st0 < nmain; st0 += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        JET_STAGE_LOAD((s + S - 1) % S, min(st0 + s + S - 1, nst - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        JET_STAGE_MMA(s, st0 + s);
+      }
+    }
+    // The last nst % S (< S) stages are already in slots 0 .. nst % S - 1.
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nst - nmain) JET_STAGE_MMA(s, nmain + s);  // uniform over the workgroup
+#undef JET_STAGE_MMA
+#undef JET_STAGE_LOAD
+    epilogue_lse<1>(acc, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
+                    tok_target, z_tgt, m_run, s_run);
+  }
+  store_partial<WPB>(m_run, s_run, n, half, wid, row0, n_rows, part, red);
+}
+
+// ------------------------------------------------------------------------------------
+// fp32 head and fp32 hidden states: v_mfma_f32_32x32x2_f32 takes one k per lane half.
+// A stage is a 16-wide block: lane half h loads 8 consecutive k (two float4) of its row,
+// k = kb + 8 h + 4 q + c for float4 q and component c; each component is one MFMA step.
 // ------------------------------------------------------------------------------------
 template <int NT, bool STORE>
 __global__ __launch_bounds__(256) void k_project_small_f32(
@@ -220,45 +354,63 @@ __global__ __launch_bounds__(256) void k_project_small_f32(
     int n_groups, const int* __restrict__ b_off, const int* __restrict__ b_tok,
     const int* __restrict__ tok_row, const int* __restrict__ tok_target,
     float* __restrict__ z_tgt, float2* __restrict__ part, float* __restrict__ Z) {
+  constexpr int KB = 16, S = 2;
   __shared__ float2 red[kWpb][32];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n = lane & 31, half = lane >> 5;
   const int rt = blockIdx.y, row0 = rt * 32;
   const int hrow = min(row0 + n, n_rows - 1);
-  const float* hp = H + (size_t)hrow * d + half * 4;
+  const float* hp = H + (size_t)hrow * d + half * (KB / 2);
   const long long nw = (long long)gridDim.x * kWpb;
   const long long w = (long long)blockIdx.x * kWpb + wid;
   const int g0 = (int)(w * n_groups / nw), g1 = (int)((w + 1) * n_groups / nw);
+  const int nkb = d / KB;
   float m_run = -INFINITY, s_run = 0.f;
   for (int g = g0; g < g1; ++g) {
     const int v0 = g * (32 * NT);
     const float* wp[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) wp[t] = W + (size_t)min(v0 + 32 * t + n, V - 1) * d + half * 4;
+    for (int t = 0; t < NT; ++t)
+      wp[t] = W + (size_t)min(v0 + 32 * t + n, V - 1) * d + half * (KB / 2);
     Acc<NT> acc;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc.t[t] = f32x16{};
-    float4 a0[NT], a1[NT], b0, b1;
-    auto load = [&](float4* A, float4& B, int kb) {
+    float4 A[S][NT][2], B[S][2];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) A[t] = *reinterpret_cast<const float4*>(wp[t] + kb);
-      B = *reinterpret_cast<const float4*>(hp + kb);
-    };
-    auto mma = [&](const float4* A, const float4& B) {
+    for (int s = 0; s < S - 1; ++s) {
+      const int off = min(s, nkb - 1) * KB;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[t].x, B.x, acc.t[t], 0, 0, 0);
-        acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[t].y, B.y, acc.t[t], 0, 0, 0);
-        acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[t].z, B.z, acc.t[t], 0, 0, 0);
-        acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[t].w, B.w, acc.t[t], 0, 0, 0);
+        A[s][t][0] = *reinterpret_cast<const float4*>(wp[t] + off);
+        A[s][t][1] = *reinterpret_cast<const float4*>(wp[t] + off + 4);
       }
-    };
-    load(a0, b0, 0);
-    for (int kb = 0; kb < d; kb += 16) {
-      if (kb + 8 < d) load(a1, b1, kb + 8);
-      mma(a0, b0);
-      if (kb + 16 < d) load(a0, b0, kb + 16);
-      if (kb + 8 < d) mma(a1, b1);
+      B[s][0] = *reinterpret_cast<const float4*>(hp + off);
+      B[s][1] = *reinterpret_cast<const float4*>(hp + off + 4);
+    }
+    for (int i = 0; i < nkb; i += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int ls = (s + S - 1) % S;
+        const int off = min(i + s + S - 1, nkb - 1) * KB;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          A[ls][t][0] = *reinterpret_cast<const float4*>(wp[t] + off);
+          A[ls][t][1] = *reinterpret_cast<const float4*>(wp[t] + off + 4);
+        }
+        B[ls][0] = *reinterpret_cast<const float4*>(hp + off);
+        B[ls][1] = *reinterpret_cast<const float4*>(hp + off + 4);
+        if (i + s < nkb) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].x, B[s][q].x, acc.t[t], 0, 0, 0);
+              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].y, B[s][q].y, acc.t[t], 0, 0, 0);
+              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].z, B[s][q].z, acc.t[t], 0, 0, 0);
+              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].w, B[s][q].w, acc.t[t], 0, 0, 0);
+            }
+        }
+      }
     }
     if (STORE)
       epilogue_store<NT>(acc, v0, V, n, half, row0, n_rows, Z);
@@ -271,12 +423,28 @@ __global__ __launch_bounds__(256) void k_project_small_f32(
 
 }  // namespace
 
-// Tiles per vocabulary group of the small-row kernels (a group is 32 * NT entries).  Two
-// tiles keep the bf16 kernel at 2 resident waves per SIMD.
+// Shape of the small-row bf16 kernel: NT 32-row tiles per vocabulary group (a group is
+// 32 * NT entries), KB-wide k blocks, S pipeline stages.
 #ifndef JET_SMALL_NT
 #define JET_SMALL_NT 2
 #endif
+#ifndef JET_SMALL_KB
+#define JET_SMALL_KB 32
+#endif
+#ifndef JET_SMALL_S
+#define JET_SMALL_S 3
+#endif
+#ifndef JET_STREAM_WPB
+#define JET_STREAM_WPB 8
+#endif
+#ifndef JET_STREAM_S
+#define JET_STREAM_S 2
+#endif
+constexpr int kStreamWPB = JET_STREAM_WPB;
+constexpr int kStreamS = JET_STREAM_S;
 constexpr int kSmallNT = JET_SMALL_NT;
+constexpr int kSmallKB = JET_SMALL_KB;
+constexpr int kSmallS = JET_SMALL_S;
 constexpr int kSmallNTf32 = 2;
 
 hipError_t launch_project(const ScoreArgs& a) {
@@ -287,17 +455,32 @@ hipError_t launch_project(const ScoreArgs& a) {
   float* z_tgt = reinterpret_cast<float*>(a.ws + pl.off_ztgt);
   float2* part = reinterpret_cast<float2*>(a.ws + pl.off_part);
   dim3 grid(pl.grid_x, pl.n_rtiles), block(256);
-  if (pl.variant == VAR_SMALL_BF16) {
+  if (pl.variant == VAR_SMALL_BF16 && p->d % 128 == 0) {
+    const uint16_t* W = static_cast<const uint16_t*>(p->W);
+    dim3 sblock(kStreamWPB * 64);
+    if (pl.hilo) {
+      const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
+      const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
+      hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, kStreamS, true>), grid, sblock, 0,
+                         a.stream, W, p->V, p->d, hhi, hlo, p->n_rows, pl.n_vgroups, b_off, b_tok,
+                         p->tok_row, p->tok_target, z_tgt, part);
+    } else {
+      const uint16_t* h = static_cast<const uint16_t*>(p->H);
+      hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, kStreamS, false>), grid, sblock, 0,
+                         a.stream, W, p->V, p->d, h, nullptr, p->n_rows, pl.n_vgroups, b_off,
+                         b_tok, p->tok_row, p->tok_target, z_tgt, part);
+    }
+  } else if (pl.variant == VAR_SMALL_BF16) {
     const uint16_t* W = static_cast<const uint16_t*>(p->W);
     if (pl.hilo) {
       const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
       const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
-      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, true, false>), grid, block, 0, a.stream,
+      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, true, false>), grid, block, 0, a.stream,
                          W, p->V, p->d, hhi, hlo, p->n_rows, pl.n_vgroups, b_off, b_tok,
                          p->tok_row, p->tok_target, z_tgt, part, nullptr);
     } else {
       const uint16_t* h = static_cast<const uint16_t*>(p->H);
-      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, false, false>), grid, block, 0,
+      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, false, false>), grid, block, 0,
                          a.stream, W, p->V, p->d, h, nullptr, p->n_rows, pl.n_vgroups, b_off,
                          b_tok, p->tok_row, p->tok_target, z_tgt, part, nullptr);
     }
@@ -312,7 +495,21 @@ hipError_t launch_project(const ScoreArgs& a) {
   return hipGetLastError();
 }
 
-int small_group_size(int variant) { return 32 * (variant == VAR_SMALL_F32 ? kSmallNTf32 : kSmallNT); }
+// Vocabulary entries per group (the bucketing unit) and workgroups of the small-row path.
+int small_group_size(int variant, int d) {
+  if (variant == VAR_SMALL_F32) return 32 * kSmallNTf32;
+  return d % 128 == 0 ? 32 * kStreamWPB : 32 * kSmallNT;
+}
+
+int small_grid(int variant, int d, int n_groups, int max_waves) {
+  if (variant == VAR_SMALL_BF16 && d % 128 == 0) {
+    int wg = max_waves / kStreamWPB;
+    return n_groups < wg ? n_groups : wg;
+  }
+  int gx = (n_groups + kWpb - 1) / kWpb;
+  const int cap = max_waves / kWpb;
+  return gx < 1 ? 1 : (gx > cap ? cap : gx);
+}
 
 static int store_grid(int n_groups) {
   int g = (n_groups + kWpb - 1) / kWpb;
@@ -325,11 +522,11 @@ hipError_t launch_project_store_bf16(const uint16_t* Wu, int U, int d, const uin
   const int n_groups = (U + 31) / 32;
   dim3 grid(store_grid(n_groups), (n_rows + 31) / 32), block(256);
   if (Hlo)
-    hipLaunchKernelGGL((k_project_small_bf16<1, true, true>), grid, block, 0, stream, Wu, U, d,
+    hipLaunchKernelGGL((k_project_small_bf16<1, 32, 2, true, true>), grid, block, 0, stream, Wu, U, d,
                        Hhi, Hlo, n_rows, n_groups, nullptr, nullptr, nullptr, nullptr, nullptr,
                        nullptr, Z);
   else
-    hipLaunchKernelGGL((k_project_small_bf16<1, false, true>), grid, block, 0, stream, Wu, U, d,
+    hipLaunchKernelGGL((k_project_small_bf16<1, 32, 2, false, true>), grid, block, 0, stream, Wu, U, d,
                        Hhi, nullptr, n_rows, n_groups, nullptr, nullptr, nullptr, nullptr,
                        nullptr, nullptr, Z);
   return hipGetLastError();
