@@ -140,11 +140,14 @@ def main(argv=None) -> int:
     _log(f"[bench] generating {args.workload}")
     p = wl.make_config(args.workload)
     if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        # Counter calibration: an elementwise kernel that reads and writes exactly
+        # copy_probe_mib MiB each (torch's neg), run three times before the benchmark.
+        n = (args.copy_probe_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -233,7 +236,12 @@ def main(argv=None) -> int:
         h_bytes = rows * d * (4 if p["h_dtype"] == "f32" else 2)
         alg_bytes = V * d * w_elt + h_bytes
         intensity = flops / alg_bytes
-        kernel = "k_project_small"
+        if p["w_dtype"] == "f32":
+            kernel = "k_project_small_f32"
+        elif d % 128 == 0:
+            kernel = "k_project_wg_bf16"
+        else:
+            kernel = "k_project_small_bf16"
         if intensity < 300.0:
             achieved = alg_bytes / k_avg_s / 1e9
             roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",

@@ -66,6 +66,7 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   *pl = Plan{};
   pl->variant = p->w_dtype == JET_F32 ? VAR_SMALL_F32 : VAR_SMALL_BF16;
   pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
+  pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
   pl->row_tile = 32;
   pl->n_rtiles = (p->n_rows + 31) / 32;
   pl->vgroup = small_group_size(pl->variant, p->d);
@@ -76,10 +77,11 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   pl->n_buckets = (long long)pl->n_rtiles * pl->n_vgroups;
   size_t off = 0;
   const size_t rows = (size_t)p->n_rows, d = (size_t)p->d, ntok = (size_t)p->n_tok;
+  const bool split_buffers = pl->hilo && !pl->stream;
   pl->off_hhi = off;
-  if (pl->hilo) off += al256(rows * d * 2);
+  if (split_buffers) off += al256(rows * d * 2);
   pl->off_hlo = off;
-  if (pl->hilo) off += al256(rows * d * 2);
+  if (split_buffers) off += al256(rows * d * 2);
   pl->off_ztgt = off;
   off += al256(ntok * 4);
   pl->off_part = off;

@@ -18,12 +18,19 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
-// bf16 round-to-nearest-even of an fp32 value (NaN stays a quiet NaN).
+// bf16 round-to-nearest-even of an fp32 value (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32; NaN stays a NaN).
 __device__ inline uint16_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Exact two-term split of two fp32 values: hi = bf16(x), lo = bf16(x - hi), packed as
+// bf16 pairs (element 0 in the low half).  x - hi is exact in fp32.
+__device__ inline void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  const __bf16 la = (__bf16)(a - (float)ha), lb = (__bf16)(b - (float)hb);
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  lo = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
 }
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
@@ -50,6 +57,7 @@ enum Variant { VAR_SMALL_BF16 = 0, VAR_SMALL_F32 = 1, VAR_TILED_BF16 = 2 };
 struct Plan {
   int variant;
   bool hilo;          // fp32 H split into bf16 hi + lo
+  bool stream;        // streaming kernel (d % 128 == 0): splits fp32 H itself
   int row_tile;       // rows per projection tile (bucketing granularity over rows)
   int n_rtiles;
   int vgroup;         // vocabulary entries per bucket (a multiple of the kernel's tile)

@@ -166,8 +166,8 @@ __global__ __launch_bounds__(256) void k_decide(
 
 hipError_t launch_merge(const ScoreArgs& a) {
   const jet_problem* p = a.p;
-  if (p->n_rows == 0) return hipSuccess;
   const Plan& pl = *a.plan;
+  if (p->n_rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_merge, dim3((p->n_rows + 3) / 4), dim3(256), 0, a.stream,
                      reinterpret_cast<const float2*>(a.ws + pl.off_part), pl.n_parts, p->n_rows,
                      a.lse);

@@ -106,6 +106,70 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
   if (tid == 0 && flags) flags[0] = (int32_t)sflags;
 }
 
+// Counting sort in LDS when the buckets fit (one workgroup): counts, exclusive scan and
+// offsets never leave LDS until the final offsets are stored.
+constexpr int kLdsBuckets = 12288;
+
+__global__ __launch_bounds__(kPrepThreads) void k_bucket_lds(
+    const int* __restrict__ tok_row, const int* __restrict__ tok_target, int n_tok, int n_rows,
+    int V, int row_tile, int vgroup, int n_groups, int n_buckets, int* __restrict__ b_off,
+    int* __restrict__ b_tok, int* __restrict__ b_pos, float* __restrict__ z_tgt,
+    int32_t* __restrict__ flags) {
+  __shared__ int cnt[kLdsBuckets + 1];
+  __shared__ int sh[kPrepThreads];
+  __shared__ uint32_t sflags;
+  const int tid = threadIdx.x;
+  if (tid == 0) sflags = 0u;
+  for (int i = tid; i <= n_buckets; i += kPrepThreads) cnt[i] = 0;
+  __syncthreads();
+  uint32_t my_flags = 0u;
+  for (int k = tid; k < n_tok; k += kPrepThreads) {
+    z_tgt[k] = __builtin_nanf("");
+    const int r = tok_row ? tok_row[k] : k;
+    const int y = tok_target[k];
+    bool ok = true;
+    if (r < 0 || r >= n_rows) {
+      ok = false;
+      my_flags |= JET_FLAG_BAD_ROW;
+    }
+    if (y < 0 || y >= V) {
+      ok = false;
+      my_flags |= JET_FLAG_BAD_TARGET;
+    }
+    b_pos[k] = ok ? atomicAdd(&cnt[(r / row_tile) * n_groups + y / vgroup], 1) : -1;
+  }
+  if (my_flags) atomicOr(&sflags, my_flags);
+  __syncthreads();
+  const int per = (n_buckets + kPrepThreads - 1) / kPrepThreads;
+  const int lo = tid * per, hi = min(lo + per, n_buckets);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += cnt[i];
+  sh[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kPrepThreads; off <<= 1) {
+    const int v = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? sh[tid - 1] : 0;
+  for (int i = lo; i < hi; ++i) {
+    const int c = cnt[i];
+    cnt[i] = run;
+    b_off[i] = run;
+    run += c;
+  }
+  if (tid == kPrepThreads - 1) b_off[n_buckets] = sh[kPrepThreads - 1];
+  __syncthreads();
+  for (int k = tid; k < n_tok; k += kPrepThreads) {
+    const int pos = b_pos[k];
+    if (pos < 0) continue;
+    const int r = tok_row ? tok_row[k] : k;
+    b_tok[cnt[(r / row_tile) * n_groups + tok_target[k] / vgroup] + pos] = k;
+  }
+  if (tid == 0 && flags) flags[0] = (int32_t)sflags;
+}
+
 __global__ __launch_bounds__(256) void k_split(const float* __restrict__ H, long long n,
                                                uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
   split_range(H, n, hi, lo, (long long)blockIdx.x * 256 + threadIdx.x, (long long)gridDim.x * 256);
@@ -124,7 +188,17 @@ hipError_t launch_prep(const ScoreArgs& a) {
   const Plan& pl = *a.plan;
   char* ws = a.ws;
   const long long n_h = (long long)p->n_rows * p->d;
-  const int nsb = pl.hilo ? split_blocks(n_h, kPrepThreads) : 0;
+  const bool need_split = pl.hilo && !pl.stream;
+  if (!need_split && pl.n_buckets <= kLdsBuckets) {
+    hipLaunchKernelGGL(k_bucket_lds, dim3(1), dim3(kPrepThreads), 0, a.stream, p->tok_row,
+                       p->tok_target, p->n_tok, p->n_rows, p->V, pl.row_tile, pl.vgroup,
+                       pl.n_vgroups, (int)pl.n_buckets, reinterpret_cast<int*>(ws + pl.off_boff),
+                       reinterpret_cast<int*>(ws + pl.off_btok),
+                       reinterpret_cast<int*>(ws + pl.off_bpos),
+                       reinterpret_cast<float*>(ws + pl.off_ztgt), a.flags);
+    return hipGetLastError();
+  }
+  const int nsb = need_split ? split_blocks(n_h, kPrepThreads) : 0;
   hipLaunchKernelGGL(k_prep, dim3(nsb + 1), dim3(kPrepThreads), 0, a.stream,
                      static_cast<const float*>(p->H), n_h,
                      reinterpret_cast<uint16_t*>(ws + pl.off_hhi),

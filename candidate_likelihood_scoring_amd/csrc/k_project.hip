@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kWpb = 4;  // waves per workgroup
 
+
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ inline bf16x8 as_bf16x8v(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -249,16 +250,16 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // run S-1 stages ahead and are never predicated (a stage past the end re-reads the last
 // one), so the compiler waits exactly for the stage it consumes.
 // ------------------------------------------------------------------------------------
-template <int WPB, int S, bool HILO>
+template <int WPB, int S, bool HF32>
 __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
-    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ Hhi,
-    const uint16_t* __restrict__ Hlo, int n_rows, int n_groups, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part) {
+    const uint16_t* __restrict__ W, int V, int d, const void* __restrict__ Hsrc, int n_rows,
+    int n_groups, const int* __restrict__ b_off, const int* __restrict__ b_tok,
+    const int* __restrict__ tok_row, const int* __restrict__ tok_target,
+    float* __restrict__ z_tgt, float2* __restrict__ part) {
   constexpr int KC = 128;                 // k per stage
-  constexpr int NP = HILO ? 2 : 1;        // H planes
-  constexpr int HQ = NP * 8 / WPB;        // H load instructions per wave per stage
-  static_assert(HQ >= 1 && (NP * 8) % WPB == 0, "H stage split");
+  constexpr int NP = HF32 ? 2 : 1;        // H planes in LDS (hi, lo)
+  constexpr int HQ = (HF32 ? 16 : 8) / WPB;  // H load instructions per wave per stage
+  static_assert(HQ >= 1 && (HF32 ? 16 : 8) % WPB == 0, "H stage split");
   __shared__ u32x4 wt[WPB][512];          // per-wave 32-row head tile
   __shared__ u32x4 hb[2][NP][512];        // H stage, double buffered
   __shared__ float2 red[WPB][32];
@@ -272,16 +273,21 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
   u32x4* my = wt[wid];
   float m_run = -INFINITY, s_run = 0.f;
 
-  // H load instruction i of this wave: plane hq / 8, stage rows 4 (hq % 8) + lrow
-  int h_plane[HQ], h_r[HQ];
-  const uint16_t* h_src[HQ];
+  // H stage loads.  bf16 H: instruction hq reads stage rows 4 hq + lane / 16, 16-byte chunk
+  // lane % 16.  fp32 H: instruction hq reads rows 2 hq + lane / 32, four values at
+  // 4 (lane % 32), i.e. half of chunk (lane % 32) / 2; they are split into bf16 hi and lo
+  // (hi = rne(x), lo = rne(x - hi)) on the way into LDS.
+  int h_r[HQ];
+  const char* h_src[HQ];
 #pragma unroll
   for (int i = 0; i < HQ; ++i) {
     const int hq = wid * HQ + i;
-    h_plane[i] = hq >> 3;
-    h_r[i] = 4 * (hq & 7) + lrow;
-    h_src[i] = (HILO && h_plane[i] ? Hlo : Hhi) + (size_t)min(row0 + h_r[i], n_rows - 1) * d + lch * 8;
+    h_r[i] = HF32 ? 2 * hq + (lane >> 5) : 4 * hq + lrow;
+    const int hrow = min(row0 + h_r[i], n_rows - 1);
+    h_src[i] = HF32 ? (const char*)((const float*)Hsrc + (size_t)hrow * d + (lane & 31) * 4)
+                    : (const char*)((const uint16_t*)Hsrc + (size_t)hrow * d + lch * 8);
   }
+  const int h_chunk = HF32 ? ((lane & 31) >> 1) : lch;
 
   for (int g = g0; g < g1; ++g) {
     const int v0 = g * (WPB * 32) + wid * 32;
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     _Pragma("unroll") for (int q = 0; q < 8; ++q) R[SLOT][q] = *reinterpret_cast<const u32x4*>( \
         W + (size_t)min(v0 + 4 * q + lrow, V - 1) * d + ko_);                               \
     _Pragma("unroll") for (int i = 0; i < HQ; ++i) Hr[SLOT][i] =                             \
-        *reinterpret_cast<const u32x4*>(h_src[i] + (ST) * KC);                              \
+        *reinterpret_cast<const u32x4*>(h_src[i] + (size_t)(ST) * KC * (HF32 ? 4 : 2));     \
   }
 #define JET_STAGE_MMA(SLOT, ST)                                                             \
   {                                                                                         \
@@ -303,14 +309,27 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
       my[r * 16 + (lch ^ (r & 7))] = R[SLOT][q];                                            \
     }                                                                                       \
     u32x4* hbuf = &hb[(ST) & 1][0][0];                                                      \
-    _Pragma("unroll") for (int i = 0; i < HQ; ++i)                                          \
-        hbuf[h_plane[i] * 512 + h_r[i] * 16 + (lch ^ (h_r[i] & 7))] = Hr[SLOT][i];          \
+    _Pragma("unroll") for (int i = 0; i < HQ; ++i) {                                        \
+      const int slot_ = h_r[i] * 16 + (h_chunk ^ (h_r[i] & 7));                             \
+      if (HF32) {                                                                           \
+        const u32x4 x = Hr[SLOT][i];                                                        \
+        uint32_t h01, l01, h23, l23;                                                        \
+        split_pair(__uint_as_float(x[0]), __uint_as_float(x[1]), h01, l01);                 \
+        split_pair(__uint_as_float(x[2]), __uint_as_float(x[3]), h23, l23);                 \
+        uint2* dh = reinterpret_cast<uint2*>(&hbuf[slot_]) + (lane & 1);                    \
+        uint2* dl = reinterpret_cast<uint2*>(&hbuf[512 + slot_]) + (lane & 1);              \
+        *dh = make_uint2(h01, h23);                                                         \
+        *dl = make_uint2(l01, l23);                                                         \
+      } else {                                                                              \
+        hbuf[slot_] = Hr[SLOT][i];                                                          \
+      }                                                                                     \
+    }                                                                                       \
     __syncthreads();                                                                        \
     _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
       const int c = ((half * 8 + j) ^ (n & 7)) + n * 16;                                    \
       const bf16x8 a = as_bf16x8v(my[c]);                                                   \
       acc.t[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[c]), acc.t[0], 0, 0, 0); \
-      if (HILO)                                                                             \
+      if (HF32)                                                                             \
         acc.t[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[512 + c]), acc.t[0], 0, 0, 0); \
     }                                                                                       \
   }
@@ -341,6 +360,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
                     tok_target, z_tgt, m_run, s_run);
   }
   store_partial<WPB>(m_run, s_run, n, half, wid, row0, n_rows, part, red);
+
 }
 
 // ------------------------------------------------------------------------------------
@@ -458,18 +478,14 @@ hipError_t launch_project(const ScoreArgs& a) {
   if (pl.variant == VAR_SMALL_BF16 && p->d % 128 == 0) {
     const uint16_t* W = static_cast<const uint16_t*>(p->W);
     dim3 sblock(kStreamWPB * 64);
-    if (pl.hilo) {
-      const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
-      const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
+    if (pl.hilo)
       hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, kStreamS, true>), grid, sblock, 0,
-                         a.stream, W, p->V, p->d, hhi, hlo, p->n_rows, pl.n_vgroups, b_off, b_tok,
+                         a.stream, W, p->V, p->d, p->H, p->n_rows, pl.n_vgroups, b_off, b_tok,
                          p->tok_row, p->tok_target, z_tgt, part);
-    } else {
-      const uint16_t* h = static_cast<const uint16_t*>(p->H);
+    else
       hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, kStreamS, false>), grid, sblock, 0,
-                         a.stream, W, p->V, p->d, h, nullptr, p->n_rows, pl.n_vgroups, b_off,
-                         b_tok, p->tok_row, p->tok_target, z_tgt, part);
-    }
+                         a.stream, W, p->V, p->d, p->H, p->n_rows, pl.n_vgroups, b_off, b_tok,
+                         p->tok_row, p->tok_target, z_tgt, part);
   } else if (pl.variant == VAR_SMALL_BF16) {
     const uint16_t* W = static_cast<const uint16_t*>(p->W);
     if (pl.hilo) {
