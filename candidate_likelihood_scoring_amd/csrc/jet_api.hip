@@ -20,6 +20,15 @@ constexpr int kMaxV = 1 << 30;
 #define JET_SMALL_WAVES 2048  // 256 CUs x 8 resident waves
 #endif
 constexpr int kSmallWaves = JET_SMALL_WAVES;
+// Row count above which the tiled (matrix-core bound) kernel replaces the streaming one.
+#ifndef JET_TILED_MIN_ROWS
+#define JET_TILED_MIN_ROWS 128
+#endif
+#ifndef JET_TILED_WGS
+#define JET_TILED_WGS 3072
+#endif
+constexpr int kTiledMinRows = JET_TILED_MIN_ROWS;
+constexpr int kTiledWorkgroups = JET_TILED_WGS;
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -66,13 +75,26 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   *pl = Plan{};
   pl->variant = p->w_dtype == JET_F32 ? VAR_SMALL_F32 : VAR_SMALL_BF16;
   pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
+  if (pl->variant == VAR_SMALL_BF16 && p->n_rows > kTiledMinRows && p->d % tiled_bk(pl->hilo) == 0)
+    pl->variant = VAR_TILED_BF16;
   pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
-  pl->row_tile = 32;
-  pl->n_rtiles = (p->n_rows + 31) / 32;
-  pl->vgroup = small_group_size(pl->variant, p->d);
-  pl->n_vgroups = (p->V + pl->vgroup - 1) / pl->vgroup;
-  const int gx = std::max(1, small_grid(pl->variant, p->d, pl->n_vgroups, kSmallWaves));
-  pl->grid_x = gx;
+  if (pl->variant == VAR_TILED_BF16) {
+    pl->row_tile = 256;
+    pl->n_rtiles = (p->n_rows + 255) / 256;
+    pl->vgroup = 256;
+    pl->n_vgroups = (p->V + 255) / 256;
+    // about kTiledWorkgroups workgroups in all, each sweeping a contiguous vocabulary range
+    int splits = (kTiledWorkgroups + pl->n_rtiles - 1) / pl->n_rtiles;
+    splits = std::max(1, std::min(splits, pl->n_vgroups));
+    pl->grid_x = splits;
+  } else {
+    pl->row_tile = 32;
+    pl->n_rtiles = (p->n_rows + 31) / 32;
+    pl->vgroup = small_group_size(pl->variant, p->d);
+    pl->n_vgroups = (p->V + pl->vgroup - 1) / pl->vgroup;
+    pl->grid_x = std::max(1, small_grid(pl->variant, p->d, pl->n_vgroups, kSmallWaves));
+  }
+  const int gx = pl->grid_x;
   pl->n_parts = gx;
   pl->n_buckets = (long long)pl->n_rtiles * pl->n_vgroups;
   size_t off = 0;

@@ -87,6 +87,8 @@ struct ScoreArgs {
 
 hipError_t launch_prep(const ScoreArgs& a);
 hipError_t launch_project(const ScoreArgs& a);
+hipError_t launch_project_tiled(const ScoreArgs& a);
+int tiled_bk(bool hilo);
 hipError_t launch_merge(const ScoreArgs& a);
 hipError_t launch_decide(const ScoreArgs& a);
 

@@ -470,6 +470,7 @@ constexpr int kSmallNTf32 = 2;
 hipError_t launch_project(const ScoreArgs& a) {
   const jet_problem* p = a.p;
   const Plan& pl = *a.plan;
+  if (pl.variant == VAR_TILED_BF16) return launch_project_tiled(a);
   const int* b_off = reinterpret_cast<const int*>(a.ws + pl.off_boff);
   const int* b_tok = reinterpret_cast<const int*>(a.ws + pl.off_btok);
   float* z_tgt = reinterpret_cast<float*>(a.ws + pl.off_ztgt);
