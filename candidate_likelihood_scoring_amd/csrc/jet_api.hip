@@ -22,7 +22,7 @@ constexpr int kMaxV = 1 << 30;
 constexpr int kSmallWaves = JET_SMALL_WAVES;
 // Row count above which the tiled (matrix-core bound) kernel replaces the streaming one.
 #ifndef JET_TILED_MIN_ROWS
-#define JET_TILED_MIN_ROWS 128
+#define JET_TILED_MIN_ROWS 256
 #endif
 #ifndef JET_TILED_WGS
 #define JET_TILED_WGS 3072
@@ -75,7 +75,12 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   *pl = Plan{};
   pl->variant = p->w_dtype == JET_F32 ? VAR_SMALL_F32 : VAR_SMALL_BF16;
   pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
-  if (pl->variant == VAR_SMALL_BF16 && p->n_rows > kTiledMinRows && p->d % tiled_bk(pl->hilo) == 0)
+  // tiled path: enough rows, whole stages, at least one full 256 x 256 tile, and operands
+  // addressable with 32-bit buffer offsets
+  if (pl->variant == VAR_SMALL_BF16 && p->n_rows >= kTiledMinRows && p->n_rows >= 256 &&
+      p->V >= 256 && p->d % tiled_bk(pl->hilo) == 0 &&
+      (unsigned long long)p->V * p->d * 2 < 0xffffffffull &&
+      (unsigned long long)p->n_rows * p->d * 2 < 0xffffffffull)
     pl->variant = VAR_TILED_BF16;
   pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
   if (pl->variant == VAR_TILED_BF16) {
@@ -83,8 +88,17 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     pl->n_rtiles = (p->n_rows + 255) / 256;
     pl->vgroup = 256;
     pl->n_vgroups = (p->V + 255) / 256;
-    // about kTiledWorkgroups workgroups in all, each sweeping a contiguous vocabulary range
-    int splits = (kTiledWorkgroups + pl->n_rtiles - 1) / pl->n_rtiles;
+    // About kTiledWorkgroups workgroups in all, each sweeping a contiguous vocabulary
+    // range.  Prefer a split count that makes the total a multiple of 256 (every CU gets
+    // the same number of workgroups and the XCD-aware placement applies).
+    const int R = pl->n_rtiles;
+    int splits = std::max(1, (kTiledWorkgroups + R - 1) / R);
+    int g = 256, a = R;
+    while (a) { const int t = g % a; g = a; a = t; }  // g = gcd(256, R)
+    int unit = 256 / g;
+    if (unit < 8) unit = 8;
+    const int snapped = std::max(unit, (splits + unit / 2) / unit * unit);
+    if (snapped <= pl->n_vgroups) splits = snapped;
     splits = std::max(1, std::min(splits, pl->n_vgroups));
     pl->grid_x = splits;
   } else {

@@ -242,9 +242,9 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 //     own LDS tile into the MFMA A layout;
 //   * the 32 x 128 stage of H (hi and lo planes) is loaded once per workgroup, each wave
 //     fetching WPB-th of it, into a double-buffered LDS stage shared by all waves.
-// LDS chunk (row r, 16-byte chunk c) of a 32x128 bf16 tile lives at r * 16 + (c ^ (r & 7)):
-// eight consecutive rows at the same c fall into eight different 16-byte bank groups, so
-// the row-wise writes and the column-wise fragment reads are both conflict-free.
+// LDS chunk (row r, 16-byte chunk c) of a 32x128 bf16 tile lives at r * 16 + (c ^ (r & 15)):
+// sixteen consecutive rows at the same c fall into sixteen different 16-byte bank groups,
+// so the row-wise writes and the column-wise fragment reads are both conflict-free.
 // K permutation inside a stage: lane half h, MFMA step j covers k = kb + 64 h + 8 j + e,
 // i.e. chunk 8 h + j of the row, for both operands.  Register stages rotate S deep; loads
 // run S-1 stages ahead and are never predicated (a stage past the end re-reads the last
@@ -306,11 +306,11 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
   {                                                                                         \
     _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                         \
       const int r = 4 * q + lrow;                                                           \
-      my[r * 16 + (lch ^ (r & 7))] = R[SLOT][q];                                            \
+      my[r * 16 + (lch ^ (r & 15))] = R[SLOT][q];                                            \
     }                                                                                       \
     u32x4* hbuf = &hb[(ST) & 1][0][0];                                                      \
     _Pragma("unroll") for (int i = 0; i < HQ; ++i) {                                        \
-      const int slot_ = h_r[i] * 16 + (h_chunk ^ (h_r[i] & 7));                             \
+      const int slot_ = h_r[i] * 16 + (h_chunk ^ (h_r[i] & 15));                             \
       if (HF32) {                                                                           \
         const u32x4 x = Hr[SLOT][i];                                                        \
         uint32_t h01, l01, h23, l23;                                                        \
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     }                                                                                       \
     __syncthreads();                                                                        \
     _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
-      const int c = ((half * 8 + j) ^ (n & 7)) + n * 16;                                    \
+      const int c = ((half * 8 + j) ^ (n & 15)) + n * 16;                                    \
       const bf16x8 a = as_bf16x8v(my[c]);                                                   \
       acc.t[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[c]), acc.t[0], 0, 0, 0); \
       if (HF32)                                                                             \

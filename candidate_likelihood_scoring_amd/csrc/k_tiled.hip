@@ -9,11 +9,19 @@
 // range of 256-entry vocabulary tiles.  Each wave computes a 128 x 128 quadrant (vocabulary
 // x rows) as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, i.e. 256 fp32 accumulators per lane.
 // K advances in BK-wide stages staged through LDS, double buffered: the next stage is
-// loaded into registers with lane-contiguous 16-byte loads (8 lanes cover one 128-byte row
-// segment) while the current stage feeds the matrix cores, then written to the other
-// buffer; one barrier per stage.  LDS chunk (row r, 16-byte chunk c) lives at
-// r * CH + (c ^ ((r / (8 / CH)) % CH)), which keeps the row-wise writes and the 32-row
-// fragment reads conflict-free.  Fragment k layout: lane half h, sub-step kk reads chunk
+// loaded into registers with lane-contiguous 16-byte buffer loads (8 lanes cover one
+// 128-byte row segment) while the current stage feeds the matrix cores, then written to
+// the other buffer; one barrier per stage.  Fragments of the next k sub-step are read
+// from LDS while the current sub-step's MFMAs run.  The last vocabulary tile (and row
+// tile) is shifted back to end exactly at V (n_rows), so every load is in bounds; the
+// overlap is masked in the epilogue and only the tile's own rows are reported.  LDS chunk (row r, 16-byte chunk c) lives at
+// r * CH + (c ^ f(r)) (lds_slot), which keeps the row-wise writes and the 32-row fragment
+// reads conflict-free.
+//
+// Workgroup placement: workgroup L runs on XCD L % 8, and each XCD runs about 32 at a time
+// (one per CU).  Launch index L is remapped so that those 32 form an SR x SS block of
+// (row tile, vocabulary split) pairs: the SR row tiles' H tiles are shared SS ways and the
+// SS splits' head tiles SR ways inside that XCD's L2.  Fragment k layout: lane half h, sub-step kk reads chunk
 // 2 kk + h of its row for both operands (any k permutation shared by A and B gives the
 // same dot product).
 //
@@ -29,10 +37,21 @@ constexpr int TBN = 256;  // rows per block tile
 
 __device__ inline int tm_of(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
+// XOR swizzle of 16-byte chunks, a function of row & 15 only: 16 consecutive rows read at
+// one chunk land in 16 different 16-byte bank groups, every aligned 8 rows in 8 different
+// ones, and 32-row tiles 32 * CH apart share one swizzle (so their addresses differ by an
+// immediate offset).
 template <int CH>
-__device__ inline int lds_slot(int r, int c) {
-  constexpr int RPL = 8 / CH;  // rows per 128-byte bank line
-  return r * CH + (c ^ ((r / RPL) % CH));
+__device__ inline int swz(int r) {
+  return CH == 8 ? ((r ^ ((r >> 3) & 1)) & 7) : (((r >> 1) ^ (r >> 2)) & 3);
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
 template <int NP>
@@ -40,12 +59,14 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
     const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, const int* __restrict__ b_off,
     const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part) {
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
+    int n_rtiles, int splits, int sr, int ss, int remap) {
   constexpr int BK = NP == 1 ? 64 : 32;
   constexpr int CH = BK / 8;          // 16-byte chunks per row per stage
   constexpr int KK = BK / 16;         // MFMA k sub-steps per stage
-  constexpr int LA = TBM * CH / 256;  // A chunks loaded per thread per stage
-  constexpr int LB = TBN * CH / 256;  // B chunks per plane per thread per stage
+  constexpr int RPI = 256 / CH;       // tile rows covered by one load round of 256 threads
+  constexpr int LA = TBM / RPI;       // A loads per thread per stage
+  constexpr int LB = TBN / RPI;       // B loads per plane per thread per stage
   __shared__ u32x4 sA[2][TBM * CH];
   __shared__ u32x4 sB[2][NP][TBN * CH];
   __shared__ float2 red[2][TBN];
@@ -53,32 +74,38 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int wm = wid & 1, wn = wid >> 1;
   const int n = lane & 31, h = lane >> 5;
-  const int rt = blockIdx.y, row0 = rt * TBN;
-  const int t0 = (int)((long long)blockIdx.x * n_vtiles / gridDim.x);
-  const int t1 = (int)((long long)(blockIdx.x + 1) * n_vtiles / gridDim.x);
+  int P = blockIdx.x;
+  if (remap) {  // total is a multiple of 256: 8 XCDs x 32 concurrent workgroups
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    P = (((slot >> 5) << 3) + xcd) * 32 + (slot & 31);
+  }
+  const int j = P / (sr * ss), w = P % (sr * ss);
+  const int jr = j / (splits / ss), js = j % (splits / ss);
+  const int rt = jr * sr + w / ss, split = js * ss + w % ss;
+  const int row_nom = rt * TBN;                    // first row this tile reports
+  const int row0 = min(row_nom, n_rows - TBN);     // rows loaded: [row0, row0 + 256), all valid
+  const int t0 = (int)((long long)split * n_vtiles / splits);
+  const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
   const int nk = d / BK;
+  const uint32_t rowb = (uint32_t)d * 2;           // bytes per row (head and H planes)
 
-  // global -> LDS mapping: chunk q = i * 256 + tid -> tile row q / CH, chunk q % CH
-  const uint16_t* hsrc[NP][LB];
-  int b_slot[LB];
+  // load-side mapping: thread tid loads chunk tid % CH of tile rows tid / CH + i * RPI
+  const int lr0 = tid / CH, lc = tid % CH;
+  const uint32_t lvoff = (uint32_t)lr0 * rowb + lc * 16;
+  const __amdgpu_buffer_rsrc_t rH0 = rsrc_of(H0, (uint32_t)n_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rH1 = rsrc_of(NP == 2 ? H1 : H0, (uint32_t)n_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
+  // LDS write slots: row lr0 + i * RPI keeps row & 15 within two patterns (i even / odd
+  // when RPI is 8-aligned), so slot = base + i * RPI * CH
+  const int wslot = lr0 * CH + (lc ^ swz<CH>(lr0));
+  // fragment read slot of sub-step kk: row (wm|wn)*128 + t*32 + n, chunk 2 kk + h
+  int ra_slot[KK], rb_slot[KK];
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int q = i * 256 + tid, r = q / CH, c = q % CH;
-    const size_t off = (size_t)min(row0 + r, n_rows - 1) * d + c * 8;
-    hsrc[0][i] = H0 + off;
-    if (NP == 2) hsrc[NP - 1][i] = H1 + off;
-    b_slot[i] = lds_slot<CH>(r, c);
-  }
-  int a_slot[LA], a_row[LA], a_c[LA];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int q = i * 256 + tid;
-    a_row[i] = q / CH;
-    a_c[i] = q % CH;
-    a_slot[i] = lds_slot<CH>(a_row[i], a_c[i]);
+  for (int kk = 0; kk < KK; ++kk) {
+    ra_slot[kk] = (wm * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
+    rb_slot[kk] = (wn * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
   }
 
-  // running (max, sum) of the lane's 4 rows: row0 + wn*128 + nt*32 + n
   float m_run[4], s_run[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
@@ -87,10 +114,10 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   }
 
   for (int vt = t0; vt < t1; ++vt) {
-    const int v0 = vt * TBM;
-    const uint16_t* wsrc[LA];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) wsrc[i] = W + (size_t)min(v0 + a_row[i], V - 1) * d + a_c[i] * 8;
+    const int v_nom = vt * TBM;
+    const int v0 = min(v_nom, V - TBM);            // entries loaded: [v0, v0 + 256)
+    const uint32_t wbase = (uint32_t)v0 * rowb + lvoff;
+    const uint32_t hbase = (uint32_t)row0 * rowb + lvoff;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -99,62 +126,64 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
 
     u32x4 ra[LA], rb[NP][LB];
-    // stage 0 -> buffer 0
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(wsrc[i]);
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int i = 0; i < LB; ++i) rb[p][i] = *reinterpret_cast<const u32x4*>(hsrc[p][i]);
-#pragma unroll
-    for (int i = 0; i < LA; ++i) sA[0][a_slot[i]] = ra[i];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int i = 0; i < LB; ++i) sB[0][p][b_slot[i]] = rb[p][i];
+#define JET_TILE_LOAD(KOFF)                                                                  \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < LA; ++i) ra[i] = bload(rW, wbase + (KOFF), i * RPI * rowb); \
+    _Pragma("unroll") for (int i = 0; i < LB; ++i) {                                         \
+      rb[0][i] = bload(rH0, hbase + (KOFF), i * RPI * rowb);                                 \
+      if (NP == 2) rb[NP - 1][i] = bload(rH1, hbase + (KOFF), i * RPI * rowb);               \
+    }                                                                                        \
+  }
+#define JET_TILE_STORE(BUF)                                                                  \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < LA; ++i) sA[BUF][wslot + i * RPI * CH] = ra[i];    \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p)                                           \
+      _Pragma("unroll") for (int i = 0; i < LB; ++i) sB[BUF][p][wslot + i * RPI * CH] = rb[p][i]; \
+  }
+    JET_TILE_LOAD(0);
+    JET_TILE_STORE(0);
     __syncthreads();
 
     for (int ks = 0; ks < nk; ++ks) {
       const int buf = ks & 1;
-      const int kn = min(ks + 1, nk - 1) * BK;  // next stage (re-reads the last at the end)
-#pragma unroll
-      for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + kn);
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int i = 0; i < LB; ++i) rb[p][i] = *reinterpret_cast<const u32x4*>(hsrc[p][i] + kn);
-
+      __builtin_amdgcn_sched_barrier(0);
+      JET_TILE_LOAD((uint32_t)min(ks + 1, nk - 1) * BK * 2);  // the last stage re-reads itself
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 fa[2][4], fb[2][NP][4];
+#define JET_FRAGS(SET, KK_)                                                                  \
+  {                                                                                          \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
+      fa[SET][t] = __builtin_bit_cast(bf16x8, sA[buf][ra_slot[KK_] + t * 32 * CH]);          \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p)                                           \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                          \
+        fb[SET][p][t] = __builtin_bit_cast(bf16x8, sB[buf][p][rb_slot[KK_] + t * 32 * CH]);  \
+  }
+      JET_FRAGS(0, 0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int c = 2 * kk + h;
-        bf16x8 fa[4], fb[NP][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          fa[mt] = __builtin_bit_cast(bf16x8, sA[buf][lds_slot<CH>(wm * 128 + mt * 32 + n, c)]);
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            fb[p][nt] = __builtin_bit_cast(bf16x8, sB[buf][p][lds_slot<CH>(wn * 128 + nt * 32 + n, c)]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < KK) JET_FRAGS((kk + 1) & 1, kk + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
             for (int p = 0; p < NP; ++p)
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[p][nt], acc[mt][nt], 0, 0, 0);
+              acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mt], fb[kk & 1][p][nt],
+                                                                   acc[mt][nt], 0, 0, 0);
       }
+#undef JET_FRAGS
+      __builtin_amdgcn_sched_barrier(0);
       // the other buffer was last read before the previous barrier
-#pragma unroll
-      for (int i = 0; i < LA; ++i) sA[buf ^ 1][a_slot[i]] = ra[i];
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int i = 0; i < LB; ++i) sB[buf ^ 1][p][b_slot[i]] = rb[p][i];
+      JET_TILE_STORE(buf ^ 1);
       __syncthreads();
     }
+#undef JET_TILE_LOAD
+#undef JET_TILE_STORE
 
-    // online logsumexp over this tile's 128 vocabulary entries per lane row
+    // online logsumexp over this tile's entries (the shifted last tile skips the ones
+    // before v_nom, which the previous tile counted)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float gm = -INFINITY;
@@ -162,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (v0 + wm * 128 + mt * 32 + tm_of(i, h) < V) gm = fmaxf(gm, acc[mt][nt][i]);
+          if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom) gm = fmaxf(gm, acc[mt][nt][i]);
       const float mn = fmaxf(m_run[nt], gm);
       if (mn != -INFINITY) {
         const float mb = mn * kLog2e;
@@ -171,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (v0 + wm * 128 + mt * 32 + tm_of(i, h) < V)
+            if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom)
               sum += exp2f(fmaf(acc[mt][nt][i], kLog2e, -mb));
         s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
         m_run[nt] = mn;
@@ -216,7 +245,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
     const int r = tid;  // 256 threads, 256 rows
     float m = red[0][r].x, s = red[0][r].y;
     lse_merge(m, s, red[1][r].x, red[1][r].y);
-    if (row0 + r < n_rows) part[(size_t)blockIdx.x * n_rows + row0 + r] = make_float2(m, s);
+    const int row = row0 + r;
+    if (row >= row_nom) part[(size_t)split * n_rows + row] = make_float2(m, s);
   }
 }
 
@@ -231,18 +261,37 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   const int* b_tok = reinterpret_cast<const int*>(a.ws + pl.off_btok);
   float* z_tgt = reinterpret_cast<float*>(a.ws + pl.off_ztgt);
   float2* part = reinterpret_cast<float2*>(a.ws + pl.off_part);
-  dim3 grid(pl.grid_x, pl.n_rtiles), block(256);
+  // super-tile shape for the XCD-aware placement
+  int sr = 1, ss = 1;
+  const int S = pl.grid_x, R = pl.n_rtiles;
+  const int total = S * R;
+  int remap = 0;
+  if (total % 256 == 0) {
+    const int cand[3][2] = {{4, 8}, {2, 16}, {1, 32}};
+    for (int i = 0; i < 3; ++i)
+      if (R % cand[i][0] == 0 && S % cand[i][1] == 0) {
+        sr = cand[i][0];
+        ss = cand[i][1];
+        remap = 1;
+        break;
+      }
+  }
+  if (!remap) {  // plain order: P = row tile * S + split
+    sr = 1;
+    ss = S;
+  }
+  dim3 grid(total), block(256);
   const uint16_t* W = static_cast<const uint16_t*>(p->W);
   if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
     hipLaunchKernelGGL((k_project_tiled_bf16<2>), grid, block, 0, a.stream, W, p->V, p->d, hhi,
                        hlo, p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target,
-                       z_tgt, part);
+                       z_tgt, part, R, S, sr, ss, remap);
   } else {
     hipLaunchKernelGGL((k_project_tiled_bf16<1>), grid, block, 0, a.stream, W, p->V, p->d,
                        static_cast<const uint16_t*>(p->H), nullptr, p->n_rows, pl.n_vgroups,
-                       b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part);
+                       b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
   }
   return hipGetLastError();
 }
