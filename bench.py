@@ -238,7 +238,7 @@ def main(argv=None) -> int:
         intensity = flops / alg_bytes
         if p["w_dtype"] == "f32":
             kernel = "k_project_small_f32"
-        elif rows > 128 and d % (32 if p["h_dtype"] == "f32" else 64) == 0:
+        elif rows >= 256 and V >= 256 and d % 64 == 0:
             kernel = "k_project_tiled_bf16"
         elif d % 128 == 0:
             kernel = "k_project_wg_bf16"

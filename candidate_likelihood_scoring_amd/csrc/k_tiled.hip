@@ -7,27 +7,39 @@
 //
 // Tiling (gfx950): a workgroup of 4 waves owns a 256-row tile of H and sweeps a contiguous
 // range of 256-entry vocabulary tiles.  Each wave computes a 128 x 128 quadrant (vocabulary
-// x rows) as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, i.e. 256 fp32 accumulators per lane.
-// K advances in BK-wide stages staged through LDS, double buffered: the next stage is
-// loaded into registers with lane-contiguous 16-byte buffer loads (8 lanes cover one
-// 128-byte row segment) while the current stage feeds the matrix cores, then written to
-// the other buffer; one barrier per stage.  Fragments of the next k sub-step are read
-// from LDS while the current sub-step's MFMAs run.  The last vocabulary tile (and row
-// tile) is shifted back to end exactly at V (n_rows), so every load is in bounds; the
-// overlap is masked in the epilogue and only the tile's own rows are reported.  LDS chunk (row r, 16-byte chunk c) lives at
-// r * CH + (c ^ f(r)) (lds_slot), which keeps the row-wise writes and the 32-row fragment
-// reads conflict-free.
+// x rows) as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, i.e. 256 fp32 accumulators per lane
+// (all AGPRs; one wave per SIMD).
+//
+// Pipeline: K advances in 32-wide stages; the stages of all the split's vocabulary tiles
+// form one stream, so the next tile's first stages are in flight during an epilogue.
+//  * global -> registers: lane-contiguous 16-byte buffer loads (4 lanes cover one 64-byte
+//    row segment), issued three stages ahead into two register sets;
+//  * registers -> LDS: a ring of three buffers; stage g + 2 is written while stage g
+//    computes, so the buffer of stage g + 1 was completed before the previous barrier and
+//    its first fragments are read before this stage's barrier (no read-after-barrier
+//    bubble); one barrier per stage;
+//  * every MFMA is followed by one memory instruction (fragment read, LDS write or global
+//    load), so with one wave per SIMD the memory traffic overlaps the matrix core instead
+//    of stalling its issue in bursts.
+// The last vocabulary tile (and row tile) is shifted back to end exactly at V (n_rows), so
+// every load is in bounds; the overlap is masked in the epilogue and only the tile's own
+// rows are reported.  LDS chunk (row r, 16-byte chunk c) lives at r * CH + (c ^ f(r)),
+// which keeps the row-wise writes and the 32-row fragment reads conflict-free.
 //
 // Workgroup placement: workgroup L runs on XCD L % 8, and each XCD runs about 32 at a time
 // (one per CU).  Launch index L is remapped so that those 32 form an SR x SS block of
 // (row tile, vocabulary split) pairs: the SR row tiles' H tiles are shared SS ways and the
-// SS splits' head tiles SR ways inside that XCD's L2.  Fragment k layout: lane half h, sub-step kk reads chunk
-// 2 kk + h of its row for both operands (any k permutation shared by A and B gives the
-// same dot product).
+// SS splits' head tiles SR ways inside that XCD's L2.  Fragment k layout: lane half h,
+// sub-step kk reads chunk 2 kk + h of its row for both operands (any k permutation shared
+// by A and B gives the same dot product).
 //
 // H in one bf16 plane (bf16 hidden states) or two (fp32 hidden states split into hi + lo,
-// each product accumulated twice); with two planes BK halves so a stage still fits.
+// each product accumulated twice).
 #include "jet_internal.h"
+
+#ifndef JET_TILED_NSET2
+#define JET_TILED_NSET2 2
+#endif
 
 namespace jet {
 namespace {
@@ -54,21 +66,47 @@ __device__ inline u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
-template <int NP>
+// One BK = 32 stage of the block tile: LA head chunks and NP * LB hidden-state chunks per
+// thread (16 bytes each), 16 KB per operand plane.
+constexpr int BK = 32;
+constexpr int CH = BK / 8;        // 16-byte chunks per row per stage
+constexpr int KK = BK / 16;       // MFMA k sub-steps per stage
+constexpr int RPI = 256 / CH;     // tile rows covered by one load round of 256 threads
+constexpr int LA = TBM / RPI;     // head loads per thread per stage
+constexpr int LB = TBN / RPI;     // hidden-state loads per plane per thread per stage
+constexpr int NBUF = 3;           // LDS ring depth
+constexpr int ASZ = TBM * CH;     // 16-byte slots per operand plane per buffer
+
+// Issue pattern of one MFMA sub-step: every MFMA is followed by one memory instruction
+// (LDS reads and writes first, spread evenly, then global loads), so with one wave per
+// SIMD the LDS and load traffic proceeds while the matrix core is busy instead of
+// stalling its issue in a burst.
+template <int I, int NM, int NR, int NW, int NV>
+__device__ __forceinline__ void mfma_interleave() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    constexpr int NL = NR + NW;
+    if constexpr (I < NL) {
+      constexpr bool wr = ((I + 1) * NW) / NL > (I * NW) / NL;
+      __builtin_amdgcn_sched_group_barrier(wr ? 0x200 : 0x100, 1, 0);  // DS write / read
+    } else if constexpr (I - NL < NV) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+    mfma_interleave<I + 1, NM, NR, NW, NV>();
+  }
+}
+
+template <int NP, int NSET>
 __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
     const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, const int* __restrict__ b_off,
     const int* __restrict__ b_tok, const int* __restrict__ tok_row,
     const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
     int n_rtiles, int splits, int sr, int ss, int remap) {
-  constexpr int BK = NP == 1 ? 64 : 32;
-  constexpr int CH = BK / 8;          // 16-byte chunks per row per stage
-  constexpr int KK = BK / 16;         // MFMA k sub-steps per stage
-  constexpr int RPI = 256 / CH;       // tile rows covered by one load round of 256 threads
-  constexpr int LA = TBM / RPI;       // A loads per thread per stage
-  constexpr int LB = TBN / RPI;       // B loads per plane per thread per stage
-  __shared__ u32x4 sA[2][TBM * CH];
-  __shared__ u32x4 sB[2][NP][TBN * CH];
+  static_assert(KK == 2 && (NSET == 1 || NSET == 2), "stage layout");
+  constexpr int BUFSZ = ASZ * (1 + NP);
+  constexpr int NST = LA + NP * LB;  // LDS stores per thread per stage
+  __shared__ u32x4 lds[NBUF * BUFSZ];
   __shared__ float2 red[2][TBN];
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -86,7 +124,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   const int row0 = min(row_nom, n_rows - TBN);     // rows loaded: [row0, row0 + 256), all valid
   const int t0 = (int)((long long)split * n_vtiles / splits);
   const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
-  const int nk = d / BK;
+  const int nk = d / BK;                           // even
   const uint32_t rowb = (uint32_t)d * 2;           // bytes per row (head and H planes)
 
   // load-side mapping: thread tid loads chunk tid % CH of tile rows tid / CH + i * RPI
@@ -95,15 +133,15 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   const __amdgpu_buffer_rsrc_t rH0 = rsrc_of(H0, (uint32_t)n_rows * rowb);
   const __amdgpu_buffer_rsrc_t rH1 = rsrc_of(NP == 2 ? H1 : H0, (uint32_t)n_rows * rowb);
   const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
-  // LDS write slots: row lr0 + i * RPI keeps row & 15 within two patterns (i even / odd
-  // when RPI is 8-aligned), so slot = base + i * RPI * CH
+  const uint32_t hrow = (uint32_t)row0 * rowb;
+  // LDS write slot: rows lr0 + i * RPI share row & 15, hence one swizzle
   const int wslot = lr0 * CH + (lc ^ swz<CH>(lr0));
-  // fragment read slot of sub-step kk: row (wm|wn)*128 + t*32 + n, chunk 2 kk + h
+  // fragment read slots of sub-step kk: row (wm|wn)*128 + t*32 + n, chunk 2 kk + h
   int ra_slot[KK], rb_slot[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     ra_slot[kk] = (wm * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
-    rb_slot[kk] = (wn * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
+    rb_slot[kk] = ASZ + (wn * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
   }
 
   float m_run[4], s_run[4];
@@ -113,97 +151,168 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
     s_run[nt] = 0.f;
   }
 
-  for (int vt = t0; vt < t1; ++vt) {
-    const int v_nom = vt * TBM;
-    const int v0 = min(v_nom, V - TBM);            // entries loaded: [v0, v0 + 256)
-    const uint32_t wbase = (uint32_t)v0 * rowb + lvoff;
-    const uint32_t hbase = (uint32_t)row0 * rowb + lvoff;
+  // The stages of all vocabulary tiles of this split form one stream g = 0 .. G - 1
+  // (tile t0 + g / nk, k block g % nk).  Stage g + 1 + NSET is loaded at the top of stage
+  // g; stage g + 2 is written to buffer (g + 2) % 3 while stage g computes.  Buffer
+  // (g + 1) % 3 was completed before the previous barrier, so the first fragments of stage
+  // g + 1 are read before this stage's barrier.  Past the end the cursor repeats the last
+  // stage (in bounds; never consumed).
+  const int G = (t1 - t0) * nk;
+  int lt = t0, lk = 0, lg = 0;  // load cursor: tile, k block, stream index
+  u32x4 ra[NSET][LA], rb[NSET][NP][LB];
+  uint32_t l_ws = 0, l_hs = 0;  // byte offsets of the stage being loaded
+#define JET_CURSOR()                                                                         \
+  {                                                                                          \
+    const uint32_t ko = (uint32_t)lk * (BK * 2);                                             \
+    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)min(lt * TBM, V - TBM) * rowb + ko);     \
+    l_hs = __builtin_amdgcn_readfirstlane(hrow + ko);                                        \
+    if (lg + 1 < G) {                                                                        \
+      ++lg;                                                                                  \
+      if (++lk == nk) {                                                                      \
+        lk = 0;                                                                              \
+        ++lt;                                                                                \
+      }                                                                                      \
+    }                                                                                        \
+  }
+  // loads u in [U0, U1) of the stage at the cursor into register set SET
+#define JET_LOADU(SET, U0, U1)                                                               \
+  {                                                                                          \
+    _Pragma("unroll") for (int u = (U0); u < (U1); ++u) {                                    \
+      if (u < LA) ra[SET][u] = bload(rW, lvoff, l_ws + u * RPI * rowb);                      \
+      else                                                                                   \
+        rb[SET][(u - LA) / LB][(u - LA) % LB] =                                              \
+            bload((u - LA) / LB ? rH1 : rH0, lvoff, l_hs + ((u - LA) % LB) * RPI * rowb);    \
+    }                                                                                        \
+  }
+#define JET_LOAD(SET)                                                                        \
+  {                                                                                          \
+    JET_CURSOR();                                                                            \
+    JET_LOADU(SET, 0, NST);                                                                  \
+  }
+  // stores u in [U0, U1) of register set SET into the buffer at slot offset BOFF
+#define JET_STORE(SET, BOFF, U0, U1)                                                         \
+  {                                                                                          \
+    _Pragma("unroll") for (int u = (U0); u < (U1); ++u) {                                    \
+      if (u < LA) lds[(BOFF) + wslot + u * RPI * CH] = ra[SET][u];                           \
+      else                                                                                   \
+        lds[(BOFF) + ASZ * (1 + (u - LA) / LB) + wslot + ((u - LA) % LB) * RPI * CH] =        \
+            rb[SET][(u - LA) / LB][(u - LA) % LB];                                           \
+    }                                                                                        \
+  }
+  bf16x8 fa[KK][4], fb[KK][NP][4];
+#define JET_FRAGS(F, BOFF, KK_)                                                              \
+  {                                                                                          \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
+      fa[F][t] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_] + t * 32 * CH]);       \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p)                                           \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                          \
+        fb[F][p][t] = __builtin_bit_cast(bf16x8,                                             \
+                                         lds[(BOFF) + p * ASZ + rb_slot[KK_] + t * 32 * CH]); \
+  }
+#define JET_MMA(F)                                                                           \
+  {                                                                                          \
+    _Pragma("unroll") for (int mt = 0; mt < 4; ++mt)                                         \
+      _Pragma("unroll") for (int nt = 0; nt < 4; ++nt)                                       \
+        _Pragma("unroll") for (int p = 0; p < NP; ++p)                                       \
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][mt], fb[F][p][nt],     \
+                                                               acc[mt][nt], 0, 0, 0);        \
+  }
+  // One stage.  SLOAD receives stage g + 1 + NSET (half its loads per sub-step), SSTORE
+  // (stage g + 2) is written to buffer (g + 2) % 3, half per sub-step with two sets, all in
+  // the second with one.  Sub-step 0 also reads the fragments of k sub-step 1; sub-step 1
+  // reads those of the next stage's sub-step 0.
+  constexpr int NRD = 4 + 4 * NP;                  // fragment reads per sub-step
+  constexpr int NW0 = NSET == 2 ? NST / 2 : 0;     // stores in sub-step 0
+#define JET_STAGE(SLOAD, SSTORE)                                                             \
+  {                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    JET_CURSOR();                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    JET_FRAGS(1, b_cur, 1);                                                                  \
+    JET_STORE(SSTORE, b_st, 0, NW0);                                                         \
+    JET_LOADU(SLOAD, 0, NST / 2);                                                            \
+    JET_MMA(0);                                                                              \
+    mfma_interleave<0, 16 * NP, NRD, NW0, NST / 2>();                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    JET_FRAGS(0, b_nxt, 0);                                                                  \
+    JET_STORE(SSTORE, b_st, NW0, NST);                                                       \
+    JET_LOADU(SLOAD, NST / 2, NST);                                                          \
+    JET_MMA(1);                                                                              \
+    mfma_interleave<0, 16 * NP, NRD, NST - NW0, NST - NST / 2>();                            \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    __syncthreads();                                                                         \
+    {                                                                                        \
+      const int b_old = b_cur;                                                               \
+      b_cur = b_nxt;                                                                         \
+      b_nxt = b_st;                                                                          \
+      b_st = b_old;                                                                          \
+    }                                                                                        \
+  }
 
+  // prologue: stages 0 and 1 into buffers 0 and 1, stage 2 (two sets) in flight
+  JET_LOAD(0);
+  JET_STORE(0, 0, 0, NST);
+  JET_LOAD(NSET - 1);
+  JET_STORE(NSET - 1, BUFSZ, 0, NST);
+  if (NSET == 2) JET_LOAD(0);
+  __syncthreads();
+  int b_cur = 0, b_nxt = BUFSZ, b_st = 2 * BUFSZ;  // slot offsets of buffers g, g+1, g+2 (mod 3)
+  JET_FRAGS(0, b_cur, 0);
+
+  for (int vt = t0; vt < t1; ++vt) {
     f32x16 acc[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
+    for (int kb = 0; kb < nk; kb += 2) {
+      JET_STAGE(NSET - 1, 0);  // even stage: loads into the second set, stores the first
+      JET_STAGE(0, NSET - 1);  // odd stage: loads into the first set, stores the second
+    }
 
-    u32x4 ra[LA], rb[NP][LB];
-#define JET_TILE_LOAD(KOFF)                                                                  \
-  {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < LA; ++i) ra[i] = bload(rW, wbase + (KOFF), i * RPI * rowb); \
-    _Pragma("unroll") for (int i = 0; i < LB; ++i) {                                         \
-      rb[0][i] = bload(rH0, hbase + (KOFF), i * RPI * rowb);                                 \
-      if (NP == 2) rb[NP - 1][i] = bload(rH1, hbase + (KOFF), i * RPI * rowb);               \
-    }                                                                                        \
-  }
-#define JET_TILE_STORE(BUF)                                                                  \
-  {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < LA; ++i) sA[BUF][wslot + i * RPI * CH] = ra[i];    \
-    _Pragma("unroll") for (int p = 0; p < NP; ++p)                                           \
-      _Pragma("unroll") for (int i = 0; i < LB; ++i) sB[BUF][p][wslot + i * RPI * CH] = rb[p][i]; \
-  }
-    JET_TILE_LOAD(0);
-    JET_TILE_STORE(0);
-    __syncthreads();
-
-    for (int ks = 0; ks < nk; ++ks) {
-      const int buf = ks & 1;
-      __builtin_amdgcn_sched_barrier(0);
-      JET_TILE_LOAD((uint32_t)min(ks + 1, nk - 1) * BK * 2);  // the last stage re-reads itself
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8 fa[2][4], fb[2][NP][4];
-#define JET_FRAGS(SET, KK_)                                                                  \
-  {                                                                                          \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
-      fa[SET][t] = __builtin_bit_cast(bf16x8, sA[buf][ra_slot[KK_] + t * 32 * CH]);          \
-    _Pragma("unroll") for (int p = 0; p < NP; ++p)                                           \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                          \
-        fb[SET][p][t] = __builtin_bit_cast(bf16x8, sB[buf][p][rb_slot[KK_] + t * 32 * CH]);  \
-  }
-      JET_FRAGS(0, 0);
+    // tile vt done: online logsumexp over its entries (the shifted last tile skips the ones
+    // before v_nom, which the previous tile counted)
+    const int v_nom = vt * TBM;
+    const int v0 = min(v_nom, V - TBM);
+    if (v0 == v_nom) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + 1 < KK) JET_FRAGS((kk + 1) & 1, kk + 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < 4; ++nt) {
+        float gm = m_run[nt];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mt], fb[kk & 1][p][nt],
-                                                                   acc[mt][nt], 0, 0, 0);
-      }
-#undef JET_FRAGS
-      __builtin_amdgcn_sched_barrier(0);
-      // the other buffer was last read before the previous barrier
-      JET_TILE_STORE(buf ^ 1);
-      __syncthreads();
-    }
-#undef JET_TILE_LOAD
-#undef JET_TILE_STORE
-
-    // online logsumexp over this tile's entries (the shifted last tile skips the ones
-    // before v_nom, which the previous tile counted)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float gm = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom) gm = fmaxf(gm, acc[mt][nt][i]);
-      const float mn = fmaxf(m_run[nt], gm);
-      if (mn != -INFINITY) {
-        const float mb = mn * kLog2e;
+          for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
+        const float mb = gm * kLog2e;  // gm is finite: the tile holds 256 finite logits
         float sum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
+          for (int i = 0; i < 16; ++i) sum += exp2f(fmaf(acc[mt][nt][i], kLog2e, -mb));
+        s_run[nt] = s_run[nt] * exp2f(m_run[nt] * kLog2e - mb) + sum;
+        m_run[nt] = gm;
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float gm = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom)
-              sum += exp2f(fmaf(acc[mt][nt][i], kLog2e, -mb));
-        s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
-        m_run[nt] = mn;
+            if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom) gm = fmaxf(gm, acc[mt][nt][i]);
+        const float mn = fmaxf(m_run[nt], gm);
+        if (mn != -INFINITY) {
+          const float mb = mn * kLog2e;
+          float sum = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom)
+                sum += exp2f(fmaf(acc[mt][nt][i], kLog2e, -mb));
+          s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
+          m_run[nt] = mn;
+        }
       }
     }
     // target capture: tokens whose (row tile, vocabulary tile) is this block tile
@@ -232,6 +341,13 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       }
     }
   }
+#undef JET_LOAD
+#undef JET_LOADU
+#undef JET_CURSOR
+#undef JET_STORE
+#undef JET_FRAGS
+#undef JET_MMA
+#undef JET_STAGE
 
   // merge lane halves, then the two vocabulary halves (wm = 0 then 1) of each row
 #pragma unroll
@@ -252,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 
 }  // namespace
 
-int tiled_bk(bool hilo) { return hilo ? 32 : 64; }
+int tiled_bk(bool) { return 2 * BK; }  // nk = d / BK must be even
 
 hipError_t launch_project_tiled(const ScoreArgs& a) {
   const jet_problem* p = a.p;
@@ -285,11 +401,11 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
-    hipLaunchKernelGGL((k_project_tiled_bf16<2>), grid, block, 0, a.stream, W, p->V, p->d, hhi,
+    hipLaunchKernelGGL((k_project_tiled_bf16<2, JET_TILED_NSET2>), grid, block, 0, a.stream, W, p->V, p->d, hhi,
                        hlo, p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target,
                        z_tgt, part, R, S, sr, ss, remap);
   } else {
-    hipLaunchKernelGGL((k_project_tiled_bf16<1>), grid, block, 0, a.stream, W, p->V, p->d,
+    hipLaunchKernelGGL((k_project_tiled_bf16<1, 2>), grid, block, 0, a.stream, W, p->V, p->d,
                        static_cast<const uint16_t*>(p->H), nullptr, p->n_rows, pl.n_vgroups,
                        b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
   }
