@@ -38,6 +38,10 @@ __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint3
 // Merge two online-logsumexp states (m = running max, s = sum of exp(z - m)).
 // Symmetric in its arguments bit-for-bit (max and + commute), so xor-shuffle trees give
 // every lane the same result.
+// Hardware base-2 exponential (v_exp_f32, about 1 ulp).  Results below 2^-126 may flush to
+// zero; used for the terms of a sum of exp(z - max), which always holds a term equal to 1.
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline void lse_merge(float& m, float& s, float m2, float s2) {
   float M = fmaxf(m, m2);
   if (M == -INFINITY) return;

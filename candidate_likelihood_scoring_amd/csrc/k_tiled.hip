@@ -77,25 +77,6 @@ constexpr int LB = TBN / RPI;     // hidden-state loads per plane per thread per
 constexpr int NBUF = 3;           // LDS ring depth
 constexpr int ASZ = TBM * CH;     // 16-byte slots per operand plane per buffer
 
-// Issue pattern of one MFMA sub-step: every MFMA is followed by one memory instruction
-// (LDS reads and writes first, spread evenly, then global loads), so with one wave per
-// SIMD the LDS and load traffic proceeds while the matrix core is busy instead of
-// stalling its issue in a burst.
-template <int I, int NM, int NR, int NW, int NV>
-__device__ __forceinline__ void mfma_interleave() {
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    constexpr int NL = NR + NW;
-    if constexpr (I < NL) {
-      constexpr bool wr = ((I + 1) * NW) / NL > (I * NW) / NL;
-      __builtin_amdgcn_sched_group_barrier(wr ? 0x200 : 0x100, 1, 0);  // DS write / read
-    } else if constexpr (I - NL < NV) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-    }
-    mfma_interleave<I + 1, NM, NR, NW, NV>();
-  }
-}
-
 template <int NP, int NSET>
 __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
@@ -209,13 +190,41 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
         fb[F][p][t] = __builtin_bit_cast(bf16x8,                                             \
                                          lds[(BOFF) + p * ASZ + rb_slot[KK_] + t * 32 * CH]); \
   }
-#define JET_MMA(F)                                                                           \
+  // One MFMA sub-step with its memory slots, in issue order: MFMA i (vocabulary tile
+  // i / (4 NP), row tile (i / NP) % 4, plane i % NP) is followed by memory slot i.  Slots
+  // 0 .. NL - 1 hold the fragment reads of the next sub-step (read set RF, buffer RBOFF,
+  // k sub-step RKK) with the NW LDS writes [W0, W0 + NW) of register set SSET spread evenly
+  // among them; the next NLD slots issue loads [L0, L0 + NLD) into register set LSET.
+  // Reads are ordered by first use: a0, all b, a1, a2, a3.
+#define JET_SUBSTEP(F, RF, RBOFF, RKK, SSET, W0, NW, LSET, L0, NLD)                           \
   {                                                                                          \
-    _Pragma("unroll") for (int mt = 0; mt < 4; ++mt)                                         \
-      _Pragma("unroll") for (int nt = 0; nt < 4; ++nt)                                       \
-        _Pragma("unroll") for (int p = 0; p < NP; ++p)                                       \
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][mt], fb[F][p][nt],     \
-                                                               acc[mt][nt], 0, 0, 0);        \
+    _Pragma("unroll") for (int i = 0; i < 16 * NP; ++i) {                                    \
+      acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(              \
+          fa[F][i / (4 * NP)], fb[F][i % NP][(i / NP) % 4], acc[i / (4 * NP)][(i / NP) % 4],  \
+          0, 0, 0);                                                                          \
+      constexpr int NL_ = NRD + (NW);                                                        \
+      if (i < NL_) {                                                                         \
+        const int nwb = (i * (NW)) / NL_;                                                    \
+        if (((i + 1) * (NW)) / NL_ > nwb) {                                                  \
+          JET_STORE(SSET, b_st, (W0) + nwb, (W0) + nwb + 1);                                 \
+        } else {                                                                             \
+          const int jr = i - nwb;                                                            \
+          if (jr == 0) {                                                                     \
+            fa[RF][0] = __builtin_bit_cast(bf16x8, lds[(RBOFF) + ra_slot[RKK]]);             \
+          } else if (jr <= 4 * NP) {                                                         \
+            const int pb = (jr - 1) % NP, tb = (jr - 1) / NP;                                \
+            fb[RF][pb][tb] = __builtin_bit_cast(                                             \
+                bf16x8, lds[(RBOFF) + pb * ASZ + rb_slot[RKK] + tb * 32 * CH]);              \
+          } else {                                                                           \
+            const int ta = jr - 4 * NP;                                                      \
+            fa[RF][ta] = __builtin_bit_cast(bf16x8, lds[(RBOFF) + ra_slot[RKK] + ta * 32 * CH]); \
+          }                                                                                  \
+        }                                                                                    \
+      } else if (i - NL_ < (NLD)) {                                                          \
+        JET_LOADU(LSET, (L0) + i - NL_, (L0) + i - NL_ + 1);                                 \
+      }                                                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+    }                                                                                        \
   }
   // One stage.  SLOAD receives stage g + 1 + NSET (half its loads per sub-step), SSTORE
   // (stage g + 2) is written to buffer (g + 2) % 3, half per sub-step with two sets, all in
@@ -223,23 +232,16 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   // reads those of the next stage's sub-step 0.
   constexpr int NRD = 4 + 4 * NP;                  // fragment reads per sub-step
   constexpr int NW0 = NSET == 2 ? NST / 2 : 0;     // stores in sub-step 0
+  static_assert(NRD + NW0 + NST / 2 <= 16 * NP &&
+                    NRD + (NST - NW0) + (NST - NST / 2) <= 16 * NP,
+                "every memory slot needs an MFMA");
 #define JET_STAGE(SLOAD, SSTORE)                                                             \
   {                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     JET_CURSOR();                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                       \
-    JET_FRAGS(1, b_cur, 1);                                                                  \
-    JET_STORE(SSTORE, b_st, 0, NW0);                                                         \
-    JET_LOADU(SLOAD, 0, NST / 2);                                                            \
-    JET_MMA(0);                                                                              \
-    mfma_interleave<0, 16 * NP, NRD, NW0, NST / 2>();                                        \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
-    JET_FRAGS(0, b_nxt, 0);                                                                  \
-    JET_STORE(SSTORE, b_st, NW0, NST);                                                       \
-    JET_LOADU(SLOAD, NST / 2, NST);                                                          \
-    JET_MMA(1);                                                                              \
-    mfma_interleave<0, 16 * NP, NRD, NST - NW0, NST - NST / 2>();                            \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
+    JET_SUBSTEP(0, 1, b_cur, 1, SSTORE, 0, NW0, SLOAD, 0, NST / 2);                          \
+    JET_SUBSTEP(1, 0, b_nxt, 0, SSTORE, NW0, NST - NW0, SLOAD, NST / 2, NST - NST / 2);      \
     __syncthreads();                                                                         \
     {                                                                                        \
       const int b_old = b_cur;                                                               \
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sum += exp2f(fmaf(acc[mt][nt][i], kLog2e, -mb));
+          for (int i = 0; i < 16; ++i) sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
         s_run[nt] = s_run[nt] * exp2f(m_run[nt] * kLog2e - mb) + sum;
         m_run[nt] = gm;
       }
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 #pragma unroll
             for (int i = 0; i < 16; ++i)
               if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom)
-                sum += exp2f(fmaf(acc[mt][nt][i], kLog2e, -mb));
+                sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
           s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
           m_run[nt] = mn;
         }
@@ -346,8 +348,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 #undef JET_CURSOR
 #undef JET_STORE
 #undef JET_FRAGS
-#undef JET_MMA
 #undef JET_STAGE
+#undef JET_SUBSTEP
 
   // merge lane halves, then the two vocabulary halves (wm = 0 then 1) of each row
 #pragma unroll
