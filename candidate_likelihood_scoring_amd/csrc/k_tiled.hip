@@ -37,8 +37,12 @@
 // each product accumulated twice).
 #include "jet_internal.h"
 
-#ifndef JET_TILED_NSET2
-#define JET_TILED_NSET2 2
+// Per plane count: 1 = stages are loaded straight into LDS, 0 = staged through registers
+#ifndef JET_TILED_DTL
+#define JET_TILED_DTL 1
+#endif
+#ifndef JET_TILED_DTL2
+#define JET_TILED_DTL2 0
 #endif
 
 namespace jet {
@@ -66,41 +70,182 @@ __device__ inline u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
-// One BK = 32 stage of the block tile: LA head chunks and NP * LB hidden-state chunks per
-// thread (16 bytes each), 16 KB per operand plane.
-constexpr int BK = 32;
-constexpr int CH = BK / 8;        // 16-byte chunks per row per stage
-constexpr int KK = BK / 16;       // MFMA k sub-steps per stage
-constexpr int RPI = 256 / CH;     // tile rows covered by one load round of 256 threads
-constexpr int LA = TBM / RPI;     // head loads per thread per stage
-constexpr int LB = TBN / RPI;     // hidden-state loads per plane per thread per stage
-constexpr int NBUF = 3;           // LDS ring depth
-constexpr int ASZ = TBM * CH;     // 16-byte slots per operand plane per buffer
+// Load 16 bytes per lane straight into LDS: lane l's bytes land at LDS byte address
+// m0 + 16 l.  Issued as inline assembly so that the compiler's own LDS reads are not made
+// to wait for every load in flight; completion is awaited explicitly (vm_wait) before
+// the barrier that publishes the buffer.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-template <int NP, int NSET>
+// Workgroup -> (row tile, vocabulary split).  Launch index L runs on XCD L % 8, and each XCD
+// runs about 32 workgroups at a time; with remap (launch size a multiple of 256) those 32
+// form an sr x ss block of (row tile, split) pairs sharing tiles in that XCD's L2.
+__device__ __forceinline__ void tile_assign(int sr, int ss, int splits, int remap, int& rt,
+                                            int& split) {
+  int P = blockIdx.x;
+  if (remap) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    P = (((slot >> 5) << 3) + xcd) * 32 + (slot & 31);
+  }
+  const int j = P / (sr * ss), w = P % (sr * ss);
+  const int jr = j / (splits / ss), js = j % (splits / ss);
+  rt = jr * sr + w / ss;
+  split = js * ss + w % ss;
+}
+
+// Fold the finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
+// this lane's rows and capture the logits of the tile's scored targets.  The shifted last
+// vocabulary tile skips the entries before v_nom, which the previous tile counted.
+__device__ __forceinline__ void tile_epilogue(
+    f32x16 (&acc)[4][4], float (&m_run)[4], float (&s_run)[4], int vt, int V, int wm, int wn,
+    int n, int h, int rt, int n_vtiles, int row0, const int* __restrict__ b_off,
+    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt) {
+  const int v_nom = vt * TBM;
+  const int v0 = min(v_nom, V - TBM);
+  if (v0 == v_nom) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float gm = m_run[nt];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
+      const float mb = gm * kLog2e;  // gm is finite: the tile holds 256 finite logits
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
+      s_run[nt] = s_run[nt] * exp2f(m_run[nt] * kLog2e - mb) + sum;
+      m_run[nt] = gm;
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float gm = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom) gm = fmaxf(gm, acc[mt][nt][i]);
+      const float mn = fmaxf(m_run[nt], gm);
+      if (mn != -INFINITY) {
+        const float mb = mn * kLog2e;
+        float sum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom)
+              sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
+        s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
+        m_run[nt] = mn;
+      }
+    }
+  }
+  // target capture: tokens whose (row tile, vocabulary tile) is this block tile
+  const int bkey = rt * n_vtiles + vt;
+  const int e0 = b_off[bkey], e1 = b_off[bkey + 1];
+  for (int e = e0; e < e1; ++e) {
+    const int k = b_tok[e];
+    const int lr = (tok_row ? tok_row[k] : k) - row0;
+    const int lv = tok_target[k] - v0;
+    if (lv < 0 || lv >= TBM || lr < 0 || lr >= TBN) continue;
+    if ((lv >> 7) != wm || (lr >> 7) != wn) continue;  // wave-uniform
+    const int tmt = (lv >> 5) & 3, tnt = (lr >> 5) & 3, mm = lv & 31;
+    if (n == (lr & 31) && h == ((mm >> 2) & 1)) {
+      const int ti = ((mm >> 3) << 2) | (mm & 3);
+      float val = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (mt == tmt && nt == tnt) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (i == ti) val = acc[mt][nt][i];
+          }
+      z_tgt[k] = val;
+    }
+  }
+}
+
+// Merge lane halves, then the two vocabulary halves (wm = 0 then 1) of each row, and write
+// the tile's (max, sum) partial for its own rows.
+__device__ __forceinline__ void tile_finish(float (&m_run)[4], float (&s_run)[4],
+                                            float2 (&red)[2][TBN], int tid, int wm, int wn, int n,
+                                            int h, int row0, int row_nom, int split, int n_rows,
+                                            float2* __restrict__ part) {
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const float m2 = __shfl_xor(m_run[nt], 32), s2 = __shfl_xor(s_run[nt], 32);
+    lse_merge(m_run[nt], s_run[nt], m2, s2);
+    if (h == 0) red[wm][wn * 128 + nt * 32 + n] = make_float2(m_run[nt], s_run[nt]);
+  }
+  __syncthreads();
+  {
+    const int r = tid;  // 256 threads, 256 rows
+    float m = red[0][r].x, s = red[0][r].y;
+    lse_merge(m, s, red[1][r].x, red[1][r].y);
+    const int row = row0 + r;
+    if (row >= row_nom) part[(size_t)split * n_rows + row] = make_float2(m, s);
+  }
+}
+
+// Stage shapes.  A stage is BK columns of K for the 256-row head tile and the 256-row
+// hidden-state tile (each of NP planes): CH = BK / 8 16-byte chunks per row, so one load
+// round of 256 threads covers RPI = 256 / CH rows with CH lanes per contiguous row segment.
+// Loads per CU per stage are limited by the number of L1 requests in flight, not bytes, so
+// the bf16 path uses BK = 64 (128-byte row segments, one full line per 8 lanes) with two
+// LDS buffers; the two-plane path keeps BK = 32 and a three-buffer ring, which is what the
+// 160 KB of LDS holds.
+#ifndef JET_TILED_BK1
+#define JET_TILED_BK1 64
+#endif
+#ifndef JET_TILED_NBUF1
+#define JET_TILED_NBUF1 2
+#endif
+template <int NP> struct TiledShape;
+template <> struct TiledShape<1> { static constexpr int BK = JET_TILED_BK1, NBUF = JET_TILED_NBUF1; };
+template <> struct TiledShape<2> { static constexpr int BK = 32, NBUF = 3; };
+
+template <int NP>
 __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
     const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, const int* __restrict__ b_off,
     const int* __restrict__ b_tok, const int* __restrict__ tok_row,
     const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
     int n_rtiles, int splits, int sr, int ss, int remap) {
-  static_assert(KK == 2 && (NSET == 1 || NSET == 2), "stage layout");
+  constexpr int BK = TiledShape<NP>::BK, NBUF = TiledShape<NP>::NBUF;
+  constexpr int CH = BK / 8;          // 16-byte chunks per row per stage
+  constexpr int KK = BK / 16;         // MFMA k sub-steps per stage
+  constexpr int RPI = 256 / CH;       // tile rows covered by one load round of 256 threads
+  constexpr int LA = TBM / RPI;       // head loads per thread per stage
+  constexpr int LB = TBN / RPI;       // hidden-state loads per plane per thread per stage
+  constexpr int ASZ = TBM * CH;       // 16-byte slots per operand plane per buffer
   constexpr int BUFSZ = ASZ * (1 + NP);
-  constexpr int NST = LA + NP * LB;  // LDS stores per thread per stage
+  constexpr int NST = LA + NP * LB;   // loads (and LDS stores) per thread per stage
+  constexpr int NRD = 4 + 4 * NP;     // fragment reads per sub-step
+  static_assert((NBUF == 2 || NBUF == 3) && KK % 2 == 0, "stage layout");
+  static_assert(NRD + 2 * ((NST + KK - 1) / KK) <= 16 * NP, "every memory slot needs an MFMA");
   __shared__ u32x4 lds[NBUF * BUFSZ];
   __shared__ float2 red[2][TBN];
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int wm = wid & 1, wn = wid >> 1;
   const int n = lane & 31, h = lane >> 5;
-  int P = blockIdx.x;
-  if (remap) {  // total is a multiple of 256: 8 XCDs x 32 concurrent workgroups
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    P = (((slot >> 5) << 3) + xcd) * 32 + (slot & 31);
-  }
-  const int j = P / (sr * ss), w = P % (sr * ss);
-  const int jr = j / (splits / ss), js = j % (splits / ss);
-  const int rt = jr * sr + w / ss, split = js * ss + w % ss;
+  int rt, split;
+  tile_assign(sr, ss, splits, remap, rt, split);
   const int row_nom = rt * TBN;                    // first row this tile reports
   const int row0 = min(row_nom, n_rows - TBN);     // rows loaded: [row0, row0 + 256), all valid
   const int t0 = (int)((long long)split * n_vtiles / splits);
@@ -133,14 +278,16 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   }
 
   // The stages of all vocabulary tiles of this split form one stream g = 0 .. G - 1
-  // (tile t0 + g / nk, k block g % nk).  Stage g + 1 + NSET is loaded at the top of stage
-  // g; stage g + 2 is written to buffer (g + 2) % 3 while stage g computes.  Buffer
-  // (g + 1) % 3 was completed before the previous barrier, so the first fragments of stage
-  // g + 1 are read before this stage's barrier.  Past the end the cursor repeats the last
-  // stage (in bounds; never consumed).
+  // (tile t0 + g / nk, k block g % nk).  Two register sets: at the top of stage g, stage
+  // g + NBUF - 1 (loaded during the previous stage) sits in one set and is written to LDS
+  // buffer (g + NBUF - 1) % NBUF during stage g, while stage g + NBUF is loaded into the
+  // other.  With three buffers, buffer (g + 1) % 3 was completed before the previous
+  // barrier, so the first fragments of stage g + 1 are read before this stage's barrier;
+  // with two they are read right after it.  Past the end the cursor repeats the last stage
+  // (in bounds; never consumed).
   const int G = (t1 - t0) * nk;
   int lt = t0, lk = 0, lg = 0;  // load cursor: tile, k block, stream index
-  u32x4 ra[NSET][LA], rb[NSET][NP][LB];
+  u32x4 ra[2][LA], rb[2][NP][LB];
   uint32_t l_ws = 0, l_hs = 0;  // byte offsets of the stage being loaded
 #define JET_CURSOR()                                                                         \
   {                                                                                          \
@@ -155,7 +302,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       }                                                                                      \
     }                                                                                        \
   }
-  // loads u in [U0, U1) of the stage at the cursor into register set SET
+  // loads u in [U0, U1) of the stage at the cursor into register set SET (u < LA: head
+  // rows, else plane (u - LA) / LB of the hidden states)
 #define JET_LOADU(SET, U0, U1)                                                               \
   {                                                                                          \
     _Pragma("unroll") for (int u = (U0); u < (U1); ++u) {                                    \
@@ -180,85 +328,86 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
             rb[SET][(u - LA) / LB][(u - LA) % LB];                                           \
     }                                                                                        \
   }
-  bf16x8 fa[KK][4], fb[KK][NP][4];
-#define JET_FRAGS(F, BOFF, KK_)                                                              \
+  bf16x8 fa[2][4], fb[2][NP][4];
+  // fragment read jr (0 .. NRD - 1) of sub-step KK_ into set F, in order of first use:
+  // a0, all b, a1, a2, a3
+#define JET_FRAG1(F, BOFF, KK_, JR)                                                          \
   {                                                                                          \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                            \
-      fa[F][t] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_] + t * 32 * CH]);       \
-    _Pragma("unroll") for (int p = 0; p < NP; ++p)                                           \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                          \
-        fb[F][p][t] = __builtin_bit_cast(bf16x8,                                             \
-                                         lds[(BOFF) + p * ASZ + rb_slot[KK_] + t * 32 * CH]); \
-  }
-  // One MFMA sub-step with its memory slots, in issue order: MFMA i (vocabulary tile
-  // i / (4 NP), row tile (i / NP) % 4, plane i % NP) is followed by memory slot i.  Slots
-  // 0 .. NL - 1 hold the fragment reads of the next sub-step (read set RF, buffer RBOFF,
-  // k sub-step RKK) with the NW LDS writes [W0, W0 + NW) of register set SSET spread evenly
-  // among them; the next NLD slots issue loads [L0, L0 + NLD) into register set LSET.
-  // Reads are ordered by first use: a0, all b, a1, a2, a3.
-#define JET_SUBSTEP(F, RF, RBOFF, RKK, SSET, W0, NW, LSET, L0, NLD)                           \
-  {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < 16 * NP; ++i) {                                    \
-      acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(              \
-          fa[F][i / (4 * NP)], fb[F][i % NP][(i / NP) % 4], acc[i / (4 * NP)][(i / NP) % 4],  \
-          0, 0, 0);                                                                          \
-      constexpr int NL_ = NRD + (NW);                                                        \
-      if (i < NL_) {                                                                         \
-        const int nwb = (i * (NW)) / NL_;                                                    \
-        if (((i + 1) * (NW)) / NL_ > nwb) {                                                  \
-          JET_STORE(SSET, b_st, (W0) + nwb, (W0) + nwb + 1);                                 \
-        } else {                                                                             \
-          const int jr = i - nwb;                                                            \
-          if (jr == 0) {                                                                     \
-            fa[RF][0] = __builtin_bit_cast(bf16x8, lds[(RBOFF) + ra_slot[RKK]]);             \
-          } else if (jr <= 4 * NP) {                                                         \
-            const int pb = (jr - 1) % NP, tb = (jr - 1) / NP;                                \
-            fb[RF][pb][tb] = __builtin_bit_cast(                                             \
-                bf16x8, lds[(RBOFF) + pb * ASZ + rb_slot[RKK] + tb * 32 * CH]);              \
-          } else {                                                                           \
-            const int ta = jr - 4 * NP;                                                      \
-            fa[RF][ta] = __builtin_bit_cast(bf16x8, lds[(RBOFF) + ra_slot[RKK] + ta * 32 * CH]); \
-          }                                                                                  \
-        }                                                                                    \
-      } else if (i - NL_ < (NLD)) {                                                          \
-        JET_LOADU(LSET, (L0) + i - NL_, (L0) + i - NL_ + 1);                                 \
-      }                                                                                      \
-      __builtin_amdgcn_sched_barrier(0);                                                     \
+    if ((JR) == 0) {                                                                         \
+      fa[F][0] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_]]);                     \
+    } else if ((JR) <= 4 * NP) {                                                             \
+      const int pb = ((JR) - 1) % NP, tb = ((JR) - 1) / NP;                                  \
+      fb[F][pb][tb] =                                                                        \
+          __builtin_bit_cast(bf16x8, lds[(BOFF) + pb * ASZ + rb_slot[KK_] + tb * 32 * CH]);  \
+    } else {                                                                                 \
+      const int ta = (JR) - 4 * NP;                                                          \
+      fa[F][ta] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_] + ta * 32 * CH]);     \
     }                                                                                        \
   }
-  // One stage.  SLOAD receives stage g + 1 + NSET (half its loads per sub-step), SSTORE
-  // (stage g + 2) is written to buffer (g + 2) % 3, half per sub-step with two sets, all in
-  // the second with one.  Sub-step 0 also reads the fragments of k sub-step 1; sub-step 1
-  // reads those of the next stage's sub-step 0.
-  constexpr int NRD = 4 + 4 * NP;                  // fragment reads per sub-step
-  constexpr int NW0 = NSET == 2 ? NST / 2 : 0;     // stores in sub-step 0
-  static_assert(NRD + NW0 + NST / 2 <= 16 * NP &&
-                    NRD + (NST - NW0) + (NST - NST / 2) <= 16 * NP,
-                "every memory slot needs an MFMA");
+#define JET_FRAGS(F, BOFF, KK_)                                                              \
+  {                                                                                          \
+    _Pragma("unroll") for (int jr_ = 0; jr_ < NRD; ++jr_) JET_FRAG1(F, BOFF, KK_, jr_);      \
+  }
+  // One stage in issue order.  Sub-step kk runs 16 NP MFMAs from fragment set kk & 1
+  // (vocabulary tile i / (4 NP), row tile (i / NP) % 4, plane i % NP); MFMA i is followed
+  // by memory slot i: first the fragment reads of the next sub-step (set (kk + 1) & 1; for
+  // the last sub-step those of the next stage, with three buffers) with this sub-step's
+  // share of the LDS stores spread evenly among them, then its share of the loads.
+  // SLOAD / SSTORE: the register sets being loaded / stored.
 #define JET_STAGE(SLOAD, SSTORE)                                                             \
   {                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     JET_CURSOR();                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                       \
-    JET_SUBSTEP(0, 1, b_cur, 1, SSTORE, 0, NW0, SLOAD, 0, NST / 2);                          \
-    JET_SUBSTEP(1, 0, b_nxt, 0, SSTORE, NW0, NST - NW0, SLOAD, NST / 2, NST - NST / 2);      \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                      \
+      const int u0 = kk * NST / KK, nu = (kk + 1) * NST / KK - u0;                           \
+      const int nrd = (kk + 1 < KK || NBUF == 3) ? NRD : 0;                                  \
+      const int nls = nrd + nu; /* LDS slots */                                              \
+      _Pragma("unroll") for (int i = 0; i < 16 * NP; ++i) {                                  \
+        acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(            \
+            fa[kk & 1][i / (4 * NP)], fb[kk & 1][i % NP][(i / NP) % 4],                      \
+            acc[i / (4 * NP)][(i / NP) % 4], 0, 0, 0);                                       \
+        if (i < nls) {                                                                       \
+          const int nwb = (i * nu) / nls;                                                    \
+          if (((i + 1) * nu) / nls > nwb) {                                                  \
+            JET_STORE(SSTORE, b_st, u0 + nwb, u0 + nwb + 1);                                 \
+          } else if (kk + 1 < KK) {                                                          \
+            JET_FRAG1((kk + 1) & 1, b_cur, kk + 1, i - nwb);                                 \
+          } else {                                                                           \
+            JET_FRAG1(0, b_nxt, 0, i - nwb);                                                 \
+          }                                                                                  \
+        } else if (i - nls < nu) {                                                           \
+          JET_LOADU(SLOAD, u0 + i - nls, u0 + i - nls + 1);                                  \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+      }                                                                                      \
+    }                                                                                        \
     __syncthreads();                                                                         \
-    {                                                                                        \
+    if (NBUF == 3) {                                                                         \
       const int b_old = b_cur;                                                               \
       b_cur = b_nxt;                                                                         \
       b_nxt = b_st;                                                                          \
       b_st = b_old;                                                                          \
+    } else {                                                                                 \
+      const int b_old = b_cur;                                                               \
+      b_cur = b_st;                                                                          \
+      b_st = b_old;                                                                          \
+      JET_FRAGS(0, b_cur, 0);                                                                \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
     }                                                                                        \
   }
 
-  // prologue: stages 0 and 1 into buffers 0 and 1, stage 2 (two sets) in flight
+  // prologue: stages 0 .. NBUF - 2 into buffers 0 .. NBUF - 2, stage NBUF - 1 in flight
   JET_LOAD(0);
   JET_STORE(0, 0, 0, NST);
-  JET_LOAD(NSET - 1);
-  JET_STORE(NSET - 1, BUFSZ, 0, NST);
-  if (NSET == 2) JET_LOAD(0);
+  if (NBUF == 3) {
+    JET_LOAD(1);
+    JET_STORE(1, BUFSZ, 0, NST);
+  }
+  JET_LOAD((NBUF - 1) & 1);
   __syncthreads();
-  int b_cur = 0, b_nxt = BUFSZ, b_st = 2 * BUFSZ;  // slot offsets of buffers g, g+1, g+2 (mod 3)
+  // slot offsets of the buffers of stages g, g + 1 (three buffers) and g + NBUF - 1
+  int b_cur = 0, b_nxt = BUFSZ, b_st = (NBUF - 1) * BUFSZ;
   JET_FRAGS(0, b_cur, 0);
 
   for (int vt = t0; vt < t1; ++vt) {
@@ -268,80 +417,12 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
     for (int kb = 0; kb < nk; kb += 2) {
-      JET_STAGE(NSET - 1, 0);  // even stage: loads into the second set, stores the first
-      JET_STAGE(0, NSET - 1);  // odd stage: loads into the first set, stores the second
+      JET_STAGE(NBUF & 1, (NBUF - 1) & 1);        // stage g even
+      JET_STAGE((NBUF - 1) & 1, NBUF & 1);        // stage g odd
     }
 
-    // tile vt done: online logsumexp over its entries (the shifted last tile skips the ones
-    // before v_nom, which the previous tile counted)
-    const int v_nom = vt * TBM;
-    const int v0 = min(v_nom, V - TBM);
-    if (v0 == v_nom) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float gm = m_run[nt];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
-        const float mb = gm * kLog2e;  // gm is finite: the tile holds 256 finite logits
-        float sum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
-        s_run[nt] = s_run[nt] * exp2f(m_run[nt] * kLog2e - mb) + sum;
-        m_run[nt] = gm;
-      }
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float gm = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom) gm = fmaxf(gm, acc[mt][nt][i]);
-        const float mn = fmaxf(m_run[nt], gm);
-        if (mn != -INFINITY) {
-          const float mb = mn * kLog2e;
-          float sum = 0.f;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom)
-                sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
-          s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
-          m_run[nt] = mn;
-        }
-      }
-    }
-    // target capture: tokens whose (row tile, vocabulary tile) is this block tile
-    const int bkey = rt * n_vtiles + vt;
-    const int e0 = b_off[bkey], e1 = b_off[bkey + 1];
-    for (int e = e0; e < e1; ++e) {
-      const int k = b_tok[e];
-      const int lr = (tok_row ? tok_row[k] : k) - row0;
-      const int lv = tok_target[k] - v0;
-      if (lv < 0 || lv >= TBM || lr < 0 || lr >= TBN) continue;
-      if ((lv >> 7) != wm || (lr >> 7) != wn) continue;  // wave-uniform
-      const int tmt = (lv >> 5) & 3, tnt = (lr >> 5) & 3, mm = lv & 31;
-      if (n == (lr & 31) && h == ((mm >> 2) & 1)) {
-        const int ti = ((mm >> 3) << 2) | (mm & 3);
-        float val = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            if (mt == tmt && nt == tnt) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i)
-                if (i == ti) val = acc[mt][nt][i];
-            }
-        z_tgt[k] = val;
-      }
-    }
+    tile_epilogue(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok, tok_row,
+                  tok_target, z_tgt);
   }
 #undef JET_LOAD
 #undef JET_LOADU
@@ -349,28 +430,241 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 #undef JET_STORE
 #undef JET_FRAGS
 #undef JET_STAGE
-#undef JET_SUBSTEP
+#undef JET_FRAG1
 
-  // merge lane halves, then the two vocabulary halves (wm = 0 then 1) of each row
+  tile_finish(m_run, s_run, red, tid, wm, wn, n, h, row0, row_nom, split, n_rows, part);
+}
+
+// ---------------------------------------------------------------------------------------
+// Direct-to-LDS variant: the same block tile, epilogue and placement, but every stage is
+// loaded by the buffer unit straight into its LDS buffer (no register staging, no LDS
+// store instructions).  Each load instruction fills 1 KB of a buffer: 64 / CH rows x CH
+// chunks; lane l fetches the chunk that the swizzled layout puts in slot l, i.e. logical
+// chunk (l % CH) ^ f(row).  Stage g + NBUF - 1 is fetched during stage g into buffer
+// (g - 1) % NBUF, which every wave finished reading before the previous barrier.  With PF
+// the first fragments of stage g + 1 are read before the barrier at the end of stage g,
+// so stage g + 1 must be complete one barrier earlier.
+#ifndef JET_DTL_BK1
+#define JET_DTL_BK1 64
+#endif
+#ifndef JET_DTL_NBUF1
+#define JET_DTL_NBUF1 2
+#endif
+#ifndef JET_DTL_PF1
+#define JET_DTL_PF1 0
+#endif
+template <int NP> struct DtlShape;
+template <> struct DtlShape<1> {
+  static constexpr int BK = JET_DTL_BK1, NBUF = JET_DTL_NBUF1, PF = JET_DTL_PF1;
+};
+#ifndef JET_DTL_PF2
+#define JET_DTL_PF2 1
+#endif
+template <> struct DtlShape<2> { static constexpr int BK = 32, NBUF = 3, PF = JET_DTL_PF2; };
+
+// loads issued in sub-step kk of a stage: as many as the slots left by its fragment reads
+// allow, earliest sub-steps first
+constexpr int dtl_nd(int kk, int KK, int ndma, int slots, int nrd, int nrd_last) {
+  int before = 0;
+  for (int k = 0; k < kk; ++k) {
+    const int cap = slots - (k + 1 < KK ? nrd : nrd_last);
+    const int left = ndma - before;
+    before += cap < left ? cap : left;
+  }
+  const int cap = slots - (kk + 1 < KK ? nrd : nrd_last);
+  const int left = ndma - before;
+  return cap < left ? cap : left;
+}
+constexpr int dtl_before(int kk, int KK, int ndma, int slots, int nrd, int nrd_last) {
+  int before = 0;
+  for (int k = 0; k < kk; ++k) before += dtl_nd(k, KK, ndma, slots, nrd, nrd_last);
+  return before;
+}
+
+template <int NP>
+__global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
+    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
+    const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, const int* __restrict__ b_off,
+    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
+    int n_rtiles, int splits, int sr, int ss, int remap) {
+  constexpr int BK = DtlShape<NP>::BK, NBUF = DtlShape<NP>::NBUF, PF = DtlShape<NP>::PF;
+  constexpr int D = NBUF - 1;         // stages fetched ahead
+  constexpr int CH = BK / 8;          // 16-byte chunks per row per stage
+  constexpr int KK = BK / 16;         // MFMA k sub-steps per stage
+  constexpr int RPD = 64 / CH;        // rows per load instruction
+  constexpr int ASZ = TBM * CH;       // 16-byte slots per operand plane per buffer
+  constexpr int BUFSZ = ASZ * (1 + NP);
+  constexpr int NDO = CH;             // load instructions per wave per operand plane per stage
+  constexpr int NDMA = (1 + NP) * NDO;
+  constexpr int NRD = 4 + 4 * NP;     // fragment reads per sub-step
+  constexpr int SLOTS = 16 * NP;      // MFMAs (memory slots) per sub-step
+  constexpr int NRD_LAST = PF ? NRD : 0;
+  static_assert(KK % 2 == 0 && NBUF >= 2 && NBUF <= 4 && (PF == 0 || NBUF >= 3), "stage layout");
+  static_assert(dtl_before(KK, KK, NDMA, SLOTS, NRD, NRD_LAST) == NDMA, "every load needs a slot");
+  static_assert(D - 1 - PF >= 0, "ring depth");
+  __shared__ u32x4 lds[NBUF * BUFSZ];
+  __shared__ float2 red[2][TBN];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid & 1, wn = wid >> 1;
+  const int n = lane & 31, h = lane >> 5;
+  int rt, split;
+  tile_assign(sr, ss, splits, remap, rt, split);
+  const int row_nom = rt * TBN;
+  const int row0 = min(row_nom, n_rows - TBN);
+  const int t0 = (int)((long long)split * n_vtiles / splits);
+  const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
+  const int nk = d / BK;                           // even
+  const uint32_t rowb = (uint32_t)d * 2;
+
+  const __amdgpu_buffer_rsrc_t rH0 = rsrc_of(H0, (uint32_t)n_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rH1 = rsrc_of(NP == 2 ? H1 : H0, (uint32_t)n_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
+  const uint32_t hrow = (uint32_t)row0 * rowb;
+  // load instruction jj of this wave (per plane) covers tile rows (jj * 4 + wid) * RPD + [0, RPD):
+  // lane l takes row (jj * 4 + wid) * RPD + l / CH, LDS slot (jj * 4 + wid) * 64 + l, which
+  // holds logical chunk (l % CH) ^ f(row); f depends on row & 15, the same for every jj
+  const int dr = wid * RPD + lane / CH;
+  const uint32_t dvoff = (uint32_t)dr * rowb + (uint32_t)(((lane % CH) ^ swz<CH>(dr)) * 16);
+  const uint32_t m0_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds +
+                           (uint32_t)wid * 1024u;
+  int ra_slot[KK], rb_slot[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    ra_slot[kk] = (wm * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
+    rb_slot[kk] = ASZ + (wn * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
+  }
+
+  float m_run[4], s_run[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    const float m2 = __shfl_xor(m_run[nt], 32), s2 = __shfl_xor(s_run[nt], 32);
-    lse_merge(m_run[nt], s_run[nt], m2, s2);
-    if (h == 0) red[wm][wn * 128 + nt * 32 + n] = make_float2(m_run[nt], s_run[nt]);
+    m_run[nt] = -INFINITY;
+    s_run[nt] = 0.f;
   }
+
+  const int G = (t1 - t0) * nk;
+  int lt = t0, lk = 0, lg = 0;  // load cursor
+  uint32_t l_ws = 0, l_hs = 0;
+#define JET_CURSOR()                                                                         \
+  {                                                                                          \
+    const uint32_t ko = (uint32_t)lk * (BK * 2);                                             \
+    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)min(lt * TBM, V - TBM) * rowb + ko);     \
+    l_hs = __builtin_amdgcn_readfirstlane(hrow + ko);                                        \
+    if (lg + 1 < G) {                                                                        \
+      ++lg;                                                                                  \
+      if (++lk == nk) {                                                                      \
+        lk = 0;                                                                              \
+        ++lt;                                                                                \
+      }                                                                                      \
+    }                                                                                        \
+  }
+  // load instruction q (0 .. NDMA - 1) of the stage at the cursor into buffer BI
+#define JET_DMA1(BI, Q)                                                                      \
+  {                                                                                          \
+    const int op_ = (Q) / NDO, jj_ = (Q) % NDO;                                              \
+    const uint32_t m0_ = m0_base + (uint32_t)(((BI) * BUFSZ + op_ * ASZ + jj_ * 256) * 16);   \
+    const uint32_t so_ = (op_ == 0 ? l_ws : l_hs) + (uint32_t)(jj_ * 4 * RPD) * rowb;         \
+    dma16(op_ == 0 ? rW : (op_ == 1 ? rH0 : rH1), dvoff, so_, m0_);                          \
+  }
+  bf16x8 fa[2][4], fb[2][NP][4];
+#define JET_FRAG1(F, BOFF, KK_, JR)                                                          \
+  {                                                                                          \
+    if ((JR) == 0) {                                                                         \
+      fa[F][0] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_]]);                     \
+    } else if ((JR) <= 4 * NP) {                                                             \
+      const int pb = ((JR) - 1) % NP, tb = ((JR) - 1) / NP;                                  \
+      fb[F][pb][tb] =                                                                        \
+          __builtin_bit_cast(bf16x8, lds[(BOFF) + pb * ASZ + rb_slot[KK_] + tb * 32 * CH]);  \
+    } else {                                                                                 \
+      const int ta = (JR) - 4 * NP;                                                          \
+      fa[F][ta] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_] + ta * 32 * CH]);     \
+    }                                                                                        \
+  }
+#define JET_FRAGS(F, BOFF, KK_)                                                              \
+  {                                                                                          \
+    _Pragma("unroll") for (int jr_ = 0; jr_ < NRD; ++jr_) JET_FRAG1(F, BOFF, KK_, jr_);      \
+  }
+  int bc = 0;  // buffer index of stage g
+#define JET_DSTAGE()                                                                         \
+  {                                                                                          \
+    const int b_nx = bc + 1 == NBUF ? 0 : bc + 1;       /* stage g + 1 */                    \
+    const int b_ld = bc == 0 ? NBUF - 1 : bc - 1;       /* stage g + NBUF - 1 */             \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    JET_CURSOR();                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                      \
+      const int nrd = kk + 1 < KK ? NRD : NRD_LAST;                                          \
+      const int nd = dtl_nd(kk, KK, NDMA, SLOTS, NRD, NRD_LAST);                             \
+      const int q0 = dtl_before(kk, KK, NDMA, SLOTS, NRD, NRD_LAST);                         \
+      const int nls = nrd + nd;                                                              \
+      _Pragma("unroll") for (int i = 0; i < SLOTS; ++i) {                                    \
+        acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(            \
+            fa[kk & 1][i / (4 * NP)], fb[kk & 1][i % NP][(i / NP) % 4],                      \
+            acc[i / (4 * NP)][(i / NP) % 4], 0, 0, 0);                                       \
+        if (i < nls) {                                                                       \
+          const int ndb = nd ? (i * nd) / nls : 0;                                           \
+          if (nd && ((i + 1) * nd) / nls > ndb) {                                            \
+            JET_DMA1(b_ld, q0 + ndb);                                                        \
+          } else if (kk + 1 < KK) {                                                          \
+            JET_FRAG1((kk + 1) & 1, bc * BUFSZ, kk + 1, i - ndb);                            \
+          } else {                                                                           \
+            JET_FRAG1(0, b_nx * BUFSZ, 0, i - ndb);                                          \
+          }                                                                                  \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+      }                                                                                      \
+    }                                                                                        \
+    vm_wait<(D - 1 - PF) * NDMA>();                                                          \
+    __syncthreads();                                                                         \
+    bc = b_nx;                                                                               \
+    if (!PF) {                                                                               \
+      JET_FRAGS(0, bc * BUFSZ, 0);                                                           \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+    }                                                                                        \
+  }
+
+  // prologue: stages 0 .. D - 1 into buffers 0 .. D - 1; stages 0 (and 1 with PF) complete
+#pragma unroll
+  for (int st = 0; st < D; ++st) {
+    JET_CURSOR();
+#pragma unroll
+    for (int q = 0; q < NDMA; ++q) JET_DMA1(st, q);
+  }
+  vm_wait<(D - 1 - PF) * NDMA>();
   __syncthreads();
-  {
-    const int r = tid;  // 256 threads, 256 rows
-    float m = red[0][r].x, s = red[0][r].y;
-    lse_merge(m, s, red[1][r].x, red[1][r].y);
-    const int row = row0 + r;
-    if (row >= row_nom) part[(size_t)split * n_rows + row] = make_float2(m, s);
+  JET_FRAGS(0, 0, 0);
+
+  for (int vt = t0; vt < t1; ++vt) {
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
+    for (int kb = 0; kb < nk; kb += 2) {
+      JET_DSTAGE();
+      JET_DSTAGE();
+    }
+    tile_epilogue(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok, tok_row,
+                  tok_target, z_tgt);
   }
+  vm_wait<0>();  // no load may land in LDS after the workgroup ends
+#undef JET_CURSOR
+#undef JET_DMA1
+#undef JET_FRAG1
+#undef JET_FRAGS
+#undef JET_DSTAGE
+  tile_finish(m_run, s_run, red, tid, wm, wn, n, h, row0, row_nom, split, n_rows, part);
 }
 
 }  // namespace
 
-int tiled_bk(bool) { return 2 * BK; }  // nk = d / BK must be even
+// d must be a multiple of two stages (the stage loop is unrolled by two)
+int tiled_bk(bool hilo) {
+  if (hilo) return 2 * (JET_TILED_DTL2 ? DtlShape<2>::BK : TiledShape<2>::BK);
+  return 2 * (JET_TILED_DTL ? DtlShape<1>::BK : TiledShape<1>::BK);
+}
 
 hipError_t launch_project_tiled(const ScoreArgs& a) {
   const jet_problem* p = a.p;
@@ -403,11 +697,11 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
-    hipLaunchKernelGGL((k_project_tiled_bf16<2, JET_TILED_NSET2>), grid, block, 0, a.stream, W, p->V, p->d, hhi,
+    hipLaunchKernelGGL((JET_TILED_DTL2 ? k_project_tiled_dtl<2> : k_project_tiled_bf16<2>), grid, block, 0, a.stream, W, p->V, p->d, hhi,
                        hlo, p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target,
                        z_tgt, part, R, S, sr, ss, remap);
   } else {
-    hipLaunchKernelGGL((k_project_tiled_bf16<1, 2>), grid, block, 0, a.stream, W, p->V, p->d,
+    hipLaunchKernelGGL((JET_TILED_DTL ? k_project_tiled_dtl<1> : k_project_tiled_bf16<1>), grid, block, 0, a.stream, W, p->V, p->d,
                        static_cast<const uint16_t*>(p->H), nullptr, p->n_rows, pl.n_vgroups,
                        b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
   }

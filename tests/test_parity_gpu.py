@@ -75,6 +75,48 @@ def test_ragged(jet, case):
     log(f"[gpu] errs {compare(p, out, ref, str(case))}")
 
 
+# Large-row (matrix-core) path: at least 256 rows and 256 entries, d a multiple of two
+# K stages (128 for bf16 hidden states, 64 for fp32).  Ragged row and vocabulary tails
+# exercise the shifted last tiles; the medium case gives every workgroup several
+# vocabulary tiles, so the stage stream runs across tile boundaries.
+TILED = [
+    dict(V=3001, d=128, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=61, h_dtype="bf16",
+         n_extra_rows=300),
+    dict(V=1283, d=256, n_q=25, K=(1, 12), lengths=(1, 5), layout="prefix", seed=62,
+         h_dtype="bf16", n_extra_rows=211),
+    dict(V=256, d=128, n_q=10, K=(2, 4), lengths=(1, 3), layout="own", seed=65, h_dtype="bf16",
+         n_extra_rows=256),
+    dict(V=2500, d=64, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=63, n_extra_rows=250),
+    dict(V=4099, d=192, n_q=20, K=(1, 10), lengths=(1, 4), layout="field", seed=64,
+         n_extra_rows=400, T=1.7),
+]
+
+
+@pytest.mark.parametrize("case", TILED, ids=[f"tiled{i}" for i in range(len(TILED))])
+def test_tiled(jet, case):
+    p = wl.make_problem(**case)
+    log(f"[gpu] tiled {case} rows={p['n_rows']} tok={len(p['tok_target'])}")
+    assert p["n_rows"] >= 256 and p["V"] >= 256
+    out = _run(jet, p)
+    ref = jo.score(p)
+    log(f"[gpu] errs {compare(p, out, ref, str(case))}")
+
+
+@pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
+def test_tiled_stream(jet, h_dtype):
+    p = wl.make_problem(V=131101, d=128, n_q=40, K=(2, 6), lengths=(1, 4), layout="prefix",
+                        seed=66, h_dtype=h_dtype, n_extra_rows=3000)
+    log(f"[gpu] tiled stream {h_dtype} rows={p['n_rows']} V={p['V']}")
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    # oracle on every referenced row plus the rows at each 256-row tile boundary and the tail
+    n = p["n_rows"]
+    edges = [r for b in range(0, n, 256) for r in (b, b + 1, b + 255) if r < n]
+    rows = np.unique(np.concatenate([np.asarray(p["tok_row"]), edges, np.arange(n - 3, n)]))
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] errs {compare(p, out, ref, 'tiled_stream', sampled=True)} on {len(rows)} rows")
+
+
 def test_true_index_and_gold(jet):
     p = wl.make_problem(V=3000, d=64, n_q=10, K=(2, 6), lengths=(1, 3), layout="prefix", seed=31, dups=1)
     K = np.diff(p["q_cand_off"])
