@@ -44,10 +44,15 @@ def _source_digest(files):
     return h.hexdigest()[:16]
 
 
-# Sources that determine the dominant kernels' code; a traffic figure measured with
+# Sources that determine each projection kernel's code; a traffic figure measured with
 # hardware counters is reported only while these are unchanged.
-KERNEL_SOURCES = ["candidate_likelihood_scoring_amd/csrc/k_project.hip",
-                  "candidate_likelihood_scoring_amd/csrc/jet_internal.h"]
+_SMALL_SRC = ["candidate_likelihood_scoring_amd/csrc/k_project.hip",
+              "candidate_likelihood_scoring_amd/csrc/jet_internal.h"]
+_TILED_SRC = ["candidate_likelihood_scoring_amd/csrc/k_tiled.hip",
+              "candidate_likelihood_scoring_amd/csrc/jet_internal.h"]
+KERNEL_SOURCES = {"k_project_wg_bf16": _SMALL_SRC, "k_project_small_bf16": _SMALL_SRC,
+                  "k_project_small_f32": _SMALL_SRC, "k_project_tiled_dtl": _TILED_SRC,
+                  "k_project_tiled_bf16": _TILED_SRC}
 
 
 def _traffic_from_profiles(kernel: str, workload: str):
@@ -60,7 +65,7 @@ def _traffic_from_profiles(kernel: str, workload: str):
     text = open(path).read()
     m = re.search(r"source_digest:\s*(\w+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != _source_digest(KERNEL_SOURCES):
+    if not m or not t or kernel not in KERNEL_SOURCES or m.group(1) != _source_digest(KERNEL_SOURCES[kernel]):
         return None
     return float(t.group(1))
 
@@ -236,14 +241,7 @@ def main(argv=None) -> int:
         h_bytes = rows * d * (4 if p["h_dtype"] == "f32" else 2)
         alg_bytes = V * d * w_elt + h_bytes
         intensity = flops / alg_bytes
-        if p["w_dtype"] == "f32":
-            kernel = "k_project_small_f32"
-        elif rows >= 256 and V >= 256 and d % 64 == 0:
-            kernel = "k_project_tiled_bf16"
-        elif d % 128 == 0:
-            kernel = "k_project_wg_bf16"
-        else:
-            kernel = "k_project_small_bf16"
+        kernel = api.projection_kernel(prob)
         if intensity < 300.0:
             achieved = alg_bytes / k_avg_s / 1e9
             roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",

@@ -66,6 +66,7 @@ EXPORTS = {
     "jet_score": (c_int, [POINTER(JetProblem), POINTER(JetOutputs), c_void_p, c_size_t, c_void_p]),
     "jet_score_profiled": (c_int, [POINTER(JetProblem), POINTER(JetOutputs), c_void_p, c_size_t,
                                    c_void_p, c_void_p, c_void_p]),
+    "jet_projection_kernel": (c_char_p, [POINTER(JetProblem)]),
     "jet_validate_host": (c_int, [POINTER(JetProblem)]),
     "jet_build_union": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, POINTER(c_int32),
                                 c_void_p]),

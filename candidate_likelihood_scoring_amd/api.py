@@ -97,6 +97,12 @@ def make_problem(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None
     return p
 
 
+def projection_kernel(prob: JetProblem) -> str | None:
+    """Name of the projection kernel jet_score launches for this problem (None if invalid)."""
+    r = _lib.load().jet_projection_kernel(ctypes.byref(prob))
+    return r.decode() if r else None
+
+
 def score_workspace_size(prob: JetProblem) -> int:
     return int(_lib.load().jet_score_workspace_size(ctypes.byref(prob)))
 

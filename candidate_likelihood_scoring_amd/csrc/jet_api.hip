@@ -158,6 +158,17 @@ const char* jet_status_string(jet_status s) {
   return "unknown status";
 }
 
+const char* jet_projection_kernel(const jet_problem* p) {
+  if (check_problem(p) != JET_OK) return nullptr;
+  Plan pl;
+  make_plan(p, true, &pl);
+  switch (pl.variant) {
+    case VAR_TILED_BF16: return tiled_kernel_name(pl.hilo);
+    case VAR_SMALL_F32: return "k_project_small_f32";
+    default: return pl.stream ? "k_project_wg_bf16" : "k_project_small_bf16";
+  }
+}
+
 size_t jet_score_workspace_size(const jet_problem* p) {
   if (check_problem(p) != JET_OK) return 0;
   Plan pl;

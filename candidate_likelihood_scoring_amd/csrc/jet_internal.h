@@ -93,6 +93,7 @@ hipError_t launch_prep(const ScoreArgs& a);
 hipError_t launch_project(const ScoreArgs& a);
 hipError_t launch_project_tiled(const ScoreArgs& a);
 int tiled_bk(bool hilo);
+const char* tiled_kernel_name(bool hilo);  // the tiled kernel launched for this plane count
 hipError_t launch_merge(const ScoreArgs& a);
 hipError_t launch_decide(const ScoreArgs& a);
 

@@ -104,7 +104,10 @@ __device__ __forceinline__ void tile_assign(int sr, int ss, int splits, int rema
 
 // Fold the finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
 // this lane's rows and capture the logits of the tile's scored targets.  The shifted last
-// vocabulary tile skips the entries before v_nom, which the previous tile counted.
+// vocabulary tile skips the entries before v_nom, which the previous tile counted: with
+// MASK_MFMA by adding -inf to them through the matrix core (the accumulators stay in
+// place and the fold has one path), otherwise with a masked copy of the fold.
+template <bool MASK_MFMA>
 __device__ __forceinline__ void tile_epilogue(
     f32x16 (&acc)[4][4], float (&m_run)[4], float (&s_run)[4], int vt, int V, int wm, int wn,
     int n, int h, int rt, int n_vtiles, int row0, const int* __restrict__ b_off,
@@ -112,24 +115,8 @@ __device__ __forceinline__ void tile_epilogue(
     const int* __restrict__ tok_target, float* __restrict__ z_tgt) {
   const int v_nom = vt * TBM;
   const int v0 = min(v_nom, V - TBM);
-  if (v0 == v_nom) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float gm = m_run[nt];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
-      const float mb = gm * kLog2e;  // gm is finite: the tile holds 256 finite logits
-      float sum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
-      s_run[nt] = s_run[nt] * exp2f(m_run[nt] * kLog2e - mb) + sum;
-      m_run[nt] = gm;
-    }
-  } else {
+  if (!MASK_MFMA && v0 != v_nom) {
+    // shifted last tile, masked per entry: skip the entries below v_nom
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float gm = -INFINITY;
@@ -151,6 +138,41 @@ __device__ __forceinline__ void tile_epilogue(
         s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
         m_run[nt] = mn;
       }
+    }
+  } else {
+    if (MASK_MFMA && v0 != v_nom) {
+      // Shifted last tile: entries below v_nom were counted by the previous tile.  One MFMA
+      // per 32 x 32 tile adds -inf to exactly those entries: A holds -inf at k = 0 for a
+      // dropped vocabulary entry (0 elsewhere), B holds 1 at k = 0 (0 elsewhere), so no
+      // 0 * inf is formed.  The tile's scored targets are all >= v_nom: capture is unaffected.
+      const int thr = v_nom - v0 - wm * 128;  // local entries below thr are dropped
+      bf16x8 bone = {};
+      if (h == 0) bone[0] = (__bf16)1.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        bf16x8 amask = {};
+        if (h == 0 && mt * 32 + n < thr) amask[0] = (__bf16)(-INFINITY);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(amask, bone, acc[mt][nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float gm = m_run[nt];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
+      // gm is -inf only when this half tile is entirely dropped and nothing came before
+      const float mb = gm == -INFINITY ? 0.f : gm * kLog2e;
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
+      s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + sum;
+      m_run[nt] = gm;
     }
   }
   // target capture: tokens whose (row tile, vocabulary tile) is this block tile
@@ -421,8 +443,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       JET_STAGE((NBUF - 1) & 1, NBUF & 1);        // stage g odd
     }
 
-    tile_epilogue(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok, tok_row,
-                  tok_target, z_tgt);
+    tile_epilogue<false>(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
+                         tok_row, tok_target, z_tgt);
   }
 #undef JET_LOAD
 #undef JET_LOADU
@@ -646,8 +668,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
       JET_DSTAGE();
       JET_DSTAGE();
     }
-    tile_epilogue(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok, tok_row,
-                  tok_target, z_tgt);
+    tile_epilogue<true>(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
+                        tok_row, tok_target, z_tgt);
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 #undef JET_CURSOR
@@ -664,6 +686,10 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
 int tiled_bk(bool hilo) {
   if (hilo) return 2 * (JET_TILED_DTL2 ? DtlShape<2>::BK : TiledShape<2>::BK);
   return 2 * (JET_TILED_DTL ? DtlShape<1>::BK : TiledShape<1>::BK);
+}
+
+const char* tiled_kernel_name(bool hilo) {
+  return (hilo ? JET_TILED_DTL2 : JET_TILED_DTL) ? "k_project_tiled_dtl" : "k_project_tiled_bf16";
 }
 
 hipError_t launch_project_tiled(const ScoreArgs& a) {

@@ -140,6 +140,13 @@ JET_API jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o
                               size_t workspace_bytes, void* stream, void* ev_before,
                               void* ev_after);
 
+/* Name of the projection kernel jet_score launches for this problem (the plan depends
+ * only on the problem's scalars), as profilers report it: "k_project_tiled_dtl",
+ * "k_project_tiled_bf16", "k_project_wg_bf16", "k_project_small_bf16" or
+ * "k_project_small_f32".  NULL when the problem is invalid.  Host only; the string is
+ * static. */
+JET_API const char* jet_projection_kernel(const jet_problem* p);
+
 /* Host-side validation of a problem whose index arrays (tok_row, tok_target,
  * cand_tok_off, q_cand_off, q_true_idx) are HOST pointers; H and W are not read.
  * Returns JET_OK or the first error found. */

@@ -203,3 +203,27 @@ def test_workspace_size_is_monotone_in_problem_size(lib):
         p.T = 1.0
         sizes.append(lib.jet_score_workspace_size(ctypes.byref(p)))
     assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
+
+
+def test_projection_kernel_choice(lib):
+    """The plan's kernel choice depends only on the problem's scalars (host-only call)."""
+    from candidate_likelihood_scoring_amd import api
+
+    h = np.zeros(16, np.float32)
+
+    def pick(n_rows, V, d, h_dtype, w_dtype, T=1.0):
+        p = _lib.JetProblem()
+        p.H, p.h_dtype, p.n_rows = h.ctypes.data, h_dtype, n_rows
+        p.W, p.w_dtype, p.V, p.d = h.ctypes.data, w_dtype, V, d
+        p.T = T
+        return api.projection_kernel(p)
+
+    F32, BF16 = 0, 1
+    assert pick(26546, 248320, 2560, BF16, BF16) == "k_project_tiled_dtl"
+    assert pick(3330, 262144, 1536, F32, BF16) == "k_project_tiled_bf16"
+    assert pick(32, 248320, 2560, F32, BF16) == "k_project_wg_bf16"
+    assert pick(1000, 5000, 192, BF16, BF16) == "k_project_small_bf16"  # d not whole tiled stages
+    assert pick(255, 5000, 256, BF16, BF16) == "k_project_wg_bf16"      # too few rows to tile
+    assert pick(300, 255, 256, BF16, BF16) == "k_project_wg_bf16"       # vocabulary below one tile
+    assert pick(32, 1000, 64, F32, F32) == "k_project_small_f32"
+    assert pick(32, 1000, 64, F32, BF16, T=-1.0) is None

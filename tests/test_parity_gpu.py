@@ -97,6 +97,9 @@ def test_tiled(jet, case):
     p = wl.make_problem(**case)
     log(f"[gpu] tiled {case} rows={p['n_rows']} tok={len(p['tok_target'])}")
     assert p["n_rows"] >= 256 and p["V"] >= 256
+    from candidate_likelihood_scoring_amd import api
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    assert kern.startswith("k_project_tiled"), kern
     out = _run(jet, p)
     ref = jo.score(p)
     log(f"[gpu] errs {compare(p, out, ref, str(case))}")
@@ -107,6 +110,9 @@ def test_tiled_stream(jet, h_dtype):
     p = wl.make_problem(V=131101, d=128, n_q=40, K=(2, 6), lengths=(1, 4), layout="prefix",
                         seed=66, h_dtype=h_dtype, n_extra_rows=3000)
     log(f"[gpu] tiled stream {h_dtype} rows={p['n_rows']} V={p['V']}")
+    from candidate_likelihood_scoring_amd import api
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    assert kern.startswith("k_project_tiled"), kern
     out = _run(jet, p)
     _full_size_properties(p, out)
     # oracle on every referenced row plus the rows at each 256-row tile boundary and the tail
