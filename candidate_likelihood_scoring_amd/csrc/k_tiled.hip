@@ -159,6 +159,12 @@ __device__ __forceinline__ void tile_epilogue(
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
+      // (direct-to-LDS kernel) the accumulators of row tile nt are read only from here on:
+      // one group of 64 values in VGPRs at a time instead of all 256
+      if (MASK_MFMA) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
+      }
       float gm = m_run[nt];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -527,6 +533,9 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
   static_assert(D - 1 - PF >= 0, "ring depth");
   __shared__ u32x4 lds[NBUF * BUFSZ];
   __shared__ float2 red[2][TBN];
+  // running (max, sum of exp) per wave, row tile and lane; kept in LDS between vocabulary
+  // tiles so that no registers stay live across the stage loop for them
+  __shared__ float2 runs[4][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -559,12 +568,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
     rb_slot[kk] = ASZ + (wn * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
   }
 
-  float m_run[4], s_run[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    m_run[nt] = -INFINITY;
-    s_run[nt] = 0.f;
-  }
+  for (int nt = 0; nt < 4; ++nt) runs[wid][nt][lane] = make_float2(-INFINITY, 0.f);
 
   const int G = (t1 - t0) * nk;
   int lt = t0, lk = 0, lg = 0;  // load cursor
@@ -668,8 +673,19 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
       JET_DSTAGE();
       JET_DSTAGE();
     }
-    tile_epilogue<true>(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
-                        tok_row, tok_target, z_tgt);
+    {
+      float m_run[4], s_run[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float2 r = runs[wid][nt][lane];
+        m_run[nt] = r.x;
+        s_run[nt] = r.y;
+      }
+      tile_epilogue<true>(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
+                          tok_row, tok_target, z_tgt);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) runs[wid][nt][lane] = make_float2(m_run[nt], s_run[nt]);
+    }
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 #undef JET_CURSOR
@@ -677,6 +693,13 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
 #undef JET_FRAG1
 #undef JET_FRAGS
 #undef JET_DSTAGE
+  float m_run[4], s_run[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const float2 r = runs[wid][nt][lane];
+    m_run[nt] = r.x;
+    s_run[nt] = r.y;
+  }
   tile_finish(m_run, s_run, red, tid, wm, wn, n, h, row0, row_nom, split, n_rows, part);
 }
 
