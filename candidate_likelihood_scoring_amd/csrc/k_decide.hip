@@ -13,7 +13,8 @@
 //     argmax: lowest index among the exact maxima of a (fixed order)
 //     q(true) = q at the true index (given, or 1 for K = 2)
 //     E = sum_i i q_i ;  gold NLL = (M + log Z) - (Mg + log Zg) over gold-text candidates
-//     confidence = 1 - H(q) / ln K (1 for K = 1) ; mass = sum_c exp s(c)
+//     confidence = 1 - H(q) / ln K (1 for K = 1) ; mass = sum_c exp s(c), summed as
+//     exp(max s) * sum_c exp(s(c) - max s) so that terms far below the largest keep their bits
 //   Candidates are handled lane-strided (candidate c by lane (c - c0) % 64), every sum
 //   runs in candidate order per lane and then through a fixed xor tree, so results are
 //   bitwise reproducible.
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void k_decide(
   }
   const int K = c1 - c0;
   // pass 1: token log-probabilities, candidate sums, running argmax
-  float best = -INFINITY;
+  float best = -INFINITY, smax = -INFINITY;
   int best_c = c1;  // sentinel: no finite candidate seen
   bool bad_off = false;
   for (int c = c0 + lane; c < c1; c += 64) {
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(256) void k_decide(
       }
     }
     cand_s[c] = s;
+    smax = fmaxf(smax, s);
     const float a = s / T;
     if (a > best || (a == best && c < best_c)) {
       best = a;
@@ -115,6 +117,7 @@ __global__ __launch_bounds__(256) void k_decide(
     }
   }
   const float M = best;
+  const float Ms = wave_max(smax);  // shift of the mass sum
   const bool have_text = cand_text_id && q_gold_text_id;
   const int gold = have_text ? q_gold_text_id[q] : 0;
   // pass 2: normalisers (all candidates; gold-text candidates)
@@ -140,13 +143,13 @@ __global__ __launch_bounds__(256) void k_decide(
     cand_q[c] = qc;
     e_part += (float)(c - c0) * qc;
     if (qc > 0.f) h_part -= qc * logf(qc);
-    mass_part += expf(s);
+    mass_part += expf(s - Ms);
     if (have_text && cand_text_id[c] == gold && Mg != -INFINITY) zg_part += expf(a - Mg);
     if (q_true && c - c0 == t_idx) q_true[q] = qc;
   }
   const float E = wave_sum(e_part);
   const float Hq = wave_sum(h_part);
-  const float mass = wave_sum(mass_part);
+  const float mass = Ms == -INFINITY ? 0.f : expf(Ms) * wave_sum(mass_part);
   const float Zg = wave_sum(zg_part);
   if (lane == 0) {
     q_argmax[q] = best_c < c1 ? best_c - c0 : -1;

@@ -141,7 +141,30 @@ def decide_question(s: np.ndarray, T: float, text_id=None, gold_text=None, true_
     else:
         g = np.asarray(text_id) == gold_text
         nll = math.inf if not g.any() else _lse(a) - _lse(a[g])
-    return dict(q=q, argmax=argmax, gap=gap, q_true=q_true, expect=expect, nll=nll)
+    return dict(q=q, argmax=argmax, gap=gap, q_true=q_true, expect=expect, nll=nll,
+                confidence=confidence(q), mass=allowed_mass(s))
+
+
+def confidence(q: np.ndarray) -> float:
+    """One minus the normalised entropy of the decision distribution (gemma-e2b doc,
+    "Output contracts": concentration of the distribution, not an accuracy estimate):
+    1 - H(q) / ln K with H(q) = -sum q_i ln q_i and 0 ln 0 = 0.  Reading: a single choice
+    (K = 1, where ln K = 0) is fully concentrated, confidence 1."""
+    q = np.asarray(q, dtype=np.float64)
+    K = len(q)
+    if K == 1:
+        return 1.0
+    nz = q[q > 0]
+    H = -float(np.sum(nz * np.log(nz)))
+    return 1.0 - H / math.log(K)
+
+
+def allowed_mass(s: np.ndarray) -> float:
+    """Full-vocabulary probability of the allowed choices (gemma-e2b doc, "Output
+    contracts"): the summed probabilities of the complete candidate sequences,
+    sum_c exp s(c); for single-token candidates, the probability of the allowed tokens."""
+    s = np.asarray(s, dtype=np.float64)
+    return float(np.sum(np.exp(s)))
 
 
 def decide(s: np.ndarray, q_cand_off: np.ndarray, T: float, cand_text_id=None,
@@ -151,7 +174,8 @@ def decide(s: np.ndarray, q_cand_off: np.ndarray, T: float, cand_text_id=None,
     n_q = len(q_cand_off) - 1
     out = dict(q=np.full(len(s), np.nan), argmax=np.full(n_q, -1, np.int64),
                gap=np.full(n_q, np.nan), q_true=np.full(n_q, np.nan),
-               expect=np.full(n_q, np.nan), nll=np.full(n_q, np.nan))
+               expect=np.full(n_q, np.nan), nll=np.full(n_q, np.nan),
+               confidence=np.full(n_q, np.nan), mass=np.full(n_q, np.nan))
     for g in range(n_q):
         c0, c1 = int(q_cand_off[g]), int(q_cand_off[g + 1])
         sg = s[c0:c1]
@@ -163,7 +187,7 @@ def decide(s: np.ndarray, q_cand_off: np.ndarray, T: float, cand_text_id=None,
             None if q_gold_text_id is None else int(q_gold_text_id[g]),
             None if q_true_idx is None else int(q_true_idx[g]))
         out["q"][c0:c1] = r["q"]
-        for k in ("argmax", "gap", "q_true", "expect", "nll"):
+        for k in ("argmax", "gap", "q_true", "expect", "nll", "confidence", "mass"):
             out[k][g] = r[k]
     return out
 
@@ -178,7 +202,7 @@ def score(p: dict, rows=None) -> dict:
     rows: None for every row, or an index array of the predictor rows to compute (sampled
     parity at full size); tokens on other rows get NaN, and so does everything built on
     them.  Returns fp64 arrays: lse (per row, NaN if not computed), tok_logp, cand_s,
-    cand_q, q_argmax, q_gap, q_true, q_expect, q_nll.
+    cand_q, q_argmax, q_gap, q_true, q_expect, q_nll, q_confidence, q_mass.
     """
     n_rows = int(p["n_rows"])
     tok_target = np.asarray(p["tok_target"], dtype=np.int64)
@@ -204,7 +228,8 @@ def score(p: dict, rows=None) -> dict:
                  p.get("q_gold_text_id"), p.get("q_true_idx"))
     return dict(lse=lse, tok_logp=tok_logp, cand_s=cand_s, cand_q=dec["q"],
                 q_argmax=dec["argmax"], q_gap=dec["gap"], q_true=dec["q_true"],
-                q_expect=dec["expect"], q_nll=dec["nll"])
+                q_expect=dec["expect"], q_nll=dec["nll"], q_confidence=dec["confidence"],
+                q_mass=dec["mass"])
 
 
 # ----------------------------------------------------------------------------------------

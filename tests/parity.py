@@ -7,6 +7,7 @@ evaluated by the oracle on the same bf16 bits; q: 1e-4) and the ones derived fro
   E         1e-4 * K (K - 1) / 2   (sum_i i q_i with each q_i within 1e-4)
   gold NLL  2 * m_max * tol_l / T  (difference of two log-sum-exps of s / T)
   mass      relative m_max * tol_l (sum_c exp s(c))
+  confidence  2 m_max tol_l / T + 1e-5 (first-order bound through the entropy)
 Decisions must match wherever the oracle's top-two gap in q exceeds 1e-4.
 """
 from __future__ import annotations
@@ -87,8 +88,19 @@ def compare(p: dict, out: dict, ref: dict, name: str = "", sampled: bool = False
         assert np.all(dn[fin] <= 2 * m_max_q[fin] * tl / T), (name, "nll", float(dn[fin].max()))
         errs["q_gold_nll"] = float(dn[fin].max()) if fin.any() else 0.0
     if "q_mass" in out:
-        mass_ref = np.array([np.sum(np.exp(ref["cand_s"][qo[g]:qo[g + 1]])) for g in range(len(K))])
+        # exp of scores each within m_c * tol_l: relative error m_max * tol_l (fp32 range only)
+        mass_ref = ref["q_mass"]
         rel = np.abs(out["q_mass"] - mass_ref) / np.maximum(mass_ref, 1e-300)
         ok = qmask & (mass_ref > 1e-30)
         assert np.all(rel[ok] <= m_max_q[ok] * tl + 1e-5), (name, "q_mass", float(rel[ok].max()))
+        errs["q_mass_rel"] = float(rel[ok].max()) if ok.any() else 0.0
+    if "q_confidence" in out:
+        # scores a_c within eps = m_max tol_l / T move each q_c by at most 2 eps q_c, so the
+        # entropy by at most 2 eps H <= 2 eps ln K: |d confidence| <= 2 eps (+ fp32 rounding)
+        dc = np.abs(out["q_confidence"].astype(np.float64) - ref["q_confidence"])
+        tol_c = 2.0 * m_max_q * tl / T + 1e-5
+        assert np.all(dc[qmask] <= tol_c[qmask]), (name, "q_confidence", float(dc[qmask].max()))
+        one = qmask & (K == 1)
+        assert np.all(out["q_confidence"][one] == 1.0), (name, "confidence of a single choice")
+        errs["q_confidence"] = float(dc[qmask].max()) if qmask.any() else 0.0
     return errs

@@ -110,6 +110,34 @@ def _union_unsorted(ids, off, V):
     return u.astype(np.int32), su
 
 
+def _conf_unnormalised(q):
+    q = np.asarray(q, np.float64)
+    nz = q[q > 0]
+    return 1.0 + float(np.sum(nz * np.log(nz)))
+
+
+def _conf_bits_not_normalised(q):
+    q = np.asarray(q, np.float64)
+    nz = q[q > 0]
+    return 1.0 + float(np.sum(nz * np.log2(nz)))
+
+
+def _conf_entropy_itself(q):
+    q = np.asarray(q, np.float64)
+    if len(q) == 1:
+        return 0.0
+    nz = q[q > 0]
+    return -float(np.sum(nz * np.log(nz))) / math.log(len(q))
+
+
+def _mass_tempered(s):
+    return float(np.sum(np.exp(np.asarray(s, np.float64) / 2.0)))
+
+
+def _mass_best_only(s):
+    return float(np.exp(np.max(np.asarray(s, np.float64))))
+
+
 MUTANTS = {
     "lse_without_max_shift": ("logsumexp_rows", _lse_no_shift),
     "lse_sign_error": ("logsumexp_rows", _lse_sign),
@@ -128,6 +156,11 @@ MUTANTS = {
     "binary_true_is_first": ("decide_question", _decide_true_first),
     "bf16_widen_wrong_shift": ("widen", _widen_bad_shift),
     "union_not_sorted": ("build_union", _union_unsorted),
+    "confidence_entropy_not_normalised": ("confidence", _conf_unnormalised),
+    "confidence_entropy_in_bits": ("confidence", _conf_bits_not_normalised),
+    "confidence_is_the_entropy": ("confidence", _conf_entropy_itself),
+    "mass_with_temperature": ("allowed_mass", _mass_tempered),
+    "mass_of_best_candidate_only": ("allowed_mass", _mass_best_only),
 }
 
 

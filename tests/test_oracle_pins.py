@@ -395,6 +395,41 @@ def pin_sampled_rows():
     assert np.all(np.isnan(r["tok_logp"][~on]))
 
 
+def pin_confidence_and_mass():
+    """Confidence = 1 - normalised entropy of q and allowed mass = full-vocabulary
+    probability of the allowed choices (gemma-e2b doc, "Output contracts").
+
+    JET's worked example: the two candidates' sequence likelihoods 0.06 and 0.02 give
+    mass 0.08, and q = (3/4, 1/4) has binary entropy 2 - (3/4) log2 3 bits, so the
+    confidence is (3/4) log2 3 - 1.  A zero head makes every single-token candidate
+    probability 1/V (mass K / V, uniform q, confidence 0); one overwhelming candidate makes
+    q one-hot (confidence 1); one choice is confidence 1; mass ignores the temperature."""
+    g = json.load(open(os.path.join(GOLDEN, "jet_worked_example.json")))
+    p_prefix = [0.3, 0.02, 0.5, 0.18]
+    p_row1 = [0.2, 0.3, 0.25, 0.25]
+    prob = _onehot_problem([np.log(p_prefix), np.log(p_row1)],
+                           [([0, 1], [0, 0]), ([0], [1])])
+    r = jo.score(prob)
+    _close(r["q_mass"], [sum(g["candidate_likelihoods"])], 5e-8, "worked-example mass")
+    _close(r["q_confidence"], [0.75 * math.log2(3.0) - 1.0], 1e-7, "worked-example confidence")
+    # zero head, single-token candidates: uniform over the question
+    p = _tiny_problem(23, V=1000, d=16, lengths=(1, 1), K=(2, 7))
+    p["W"] = np.zeros_like(p["W"])
+    r = jo.score(p)
+    K = np.diff(p["q_cand_off"])
+    _close(r["q_mass"], K / 1000.0, 1e-13, "zero-head mass K / V")
+    _close(r["q_confidence"], np.zeros(len(K)), 1e-13, "uniform q: confidence 0")
+    # one overwhelming candidate (score gap 5000 nats): q is exactly one-hot in fp64
+    assert jo.decide_question(np.array([-3.0, -5003.0, -5010.0]), 1.0)["confidence"] == 1.0
+    assert jo.decide_question(np.array([-3.0]), 1.0)["confidence"] == 1.0
+    s = np.array([-1.5, -2.25, -0.75, -4.0])
+    masses = {jo.decide_question(s, T)["mass"] for T in (0.5, 1.0, 2.0)}
+    assert len(masses) == 1 and abs(masses.pop() - float(np.exp(s).sum())) < 1e-15
+    # confidence does not depend on the order of the candidates
+    c = jo.decide_question(s, 1.3)["confidence"]
+    assert abs(jo.decide_question(s[::-1].copy(), 1.3)["confidence"] - c) < 1e-15
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
