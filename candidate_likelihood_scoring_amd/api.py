@@ -97,6 +97,24 @@ def make_problem(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None
     return p
 
 
+def build_predictor_trie(tok_target, cand_tok_off, q_cand_off):
+    """Host history trie (see jet_build_predictor_trie): returns (tok_node, node_tok) as
+    int32 numpy arrays; raises JetError on malformed input."""
+    tg = np.ascontiguousarray(np.asarray(tok_target), dtype=np.int32)
+    co = np.ascontiguousarray(np.asarray(cand_tok_off), dtype=np.int32)
+    qo = np.ascontiguousarray(np.asarray(q_cand_off), dtype=np.int32)
+    n_tok = int(co[-1]) if len(co) else 0
+    tok_node = np.empty(max(n_tok, 1), np.int32)
+    node_tok = np.empty(max(n_tok, 1), np.int32)
+    nn = ctypes.c_int32(0)
+    st = _lib.load().jet_build_predictor_trie(tg.ctypes.data, co.ctypes.data, len(co) - 1,
+                                              qo.ctypes.data, len(qo) - 1, tok_node.ctypes.data,
+                                              node_tok.ctypes.data, ctypes.byref(nn))
+    if st != 0:
+        raise _lib.JetError(st, "jet_build_predictor_trie")
+    return tok_node[:n_tok].copy(), node_tok[:nn.value].copy()
+
+
 def projection_kernel(prob: JetProblem) -> str | None:
     """Name of the projection kernel jet_score launches for this problem (None if invalid)."""
     r = _lib.load().jet_projection_kernel(ctypes.byref(prob))

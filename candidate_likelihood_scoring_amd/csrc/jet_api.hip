@@ -3,6 +3,7 @@
 // enqueues nothing.  The device kernels bounds-check every index themselves.
 #include <algorithm>
 #include <cmath>
+#include <unordered_map>
 #include <vector>
 
 #include "jet_internal.h"
@@ -156,6 +157,50 @@ const char* jet_status_string(jet_status s) {
     case JET_E_HIP: return "a HIP runtime call failed";
   }
   return "unknown status";
+}
+
+jet_status jet_build_predictor_trie(const int32_t* tok_target, const int32_t* cand_tok_off,
+                                    int32_t n_cand, const int32_t* q_cand_off, int32_t n_q,
+                                    int32_t* tok_node, int32_t* node_tok, int32_t* n_nodes) {
+  if (!cand_tok_off || !q_cand_off || !n_nodes || n_cand < 0 || n_q < 0) return JET_E_NULL;
+  if (cand_tok_off[0] != 0 || q_cand_off[0] != 0 || q_cand_off[n_q] != n_cand) return JET_E_SHAPE;
+  for (int32_t g = 0; g < n_q; ++g)
+    if (q_cand_off[g + 1] <= q_cand_off[g]) return JET_E_SHAPE;
+  for (int32_t c = 0; c < n_cand; ++c)
+    if (cand_tok_off[c + 1] <= cand_tok_off[c]) return JET_E_SHAPE;
+  const int32_t n_tok = cand_tok_off[n_cand];
+  if (n_tok > 0 && (!tok_target || !tok_node || !node_tok)) return JET_E_NULL;
+  for (int32_t k = 0; k < n_tok; ++k)
+    if (tok_target[k] < 0) return JET_E_INDEX;
+  // tree nodes in creation order; number[v] = predictor index of tree node v, or -1
+  std::vector<int32_t> number;
+  number.reserve((size_t)n_tok + n_q);
+  std::unordered_map<uint64_t, int32_t> child;
+  child.reserve((size_t)n_tok * 2 + 1);
+  int32_t nn = 0;
+  for (int32_t g = 0; g < n_q; ++g) {
+    const int32_t root = (int32_t)number.size();
+    number.push_back(-1);
+    for (int32_t c = q_cand_off[g]; c < q_cand_off[g + 1]; ++c) {
+      int32_t v = root;
+      for (int32_t k = cand_tok_off[c]; k < cand_tok_off[c + 1]; ++k) {
+        if (number[v] < 0) {
+          number[v] = nn;
+          node_tok[nn++] = k;
+        }
+        tok_node[k] = number[v];
+        const uint64_t key = ((uint64_t)(uint32_t)v << 32) | (uint32_t)tok_target[k];
+        auto it = child.find(key);
+        if (it == child.end()) {
+          it = child.emplace(key, (int32_t)number.size()).first;
+          number.push_back(-1);
+        }
+        v = it->second;
+      }
+    }
+  }
+  *n_nodes = nn;
+  return JET_OK;
 }
 
 const char* jet_projection_kernel(const jet_problem* p) {

@@ -152,6 +152,26 @@ JET_API const char* jet_projection_kernel(const jet_problem* p);
  * Returns JET_OK or the first error found. */
 JET_API jet_status jet_validate_host(const jet_problem* p);
 
+/* HOST: predictor-row deduplication by history-consistent merging (FastJEV Sec. 3.3,
+ * Eq. 4).  Token t of a candidate is predicted from the state after its preceding history
+ * (the question's context, then the candidate's tokens 0..t-1).  Histories form one tree
+ * per question, a child keyed by (parent node, token); depth fixes the position.  Tokens
+ * share a predictor node exactly when they belong to the same question and have identical
+ * preceding histories.
+ *   tok_target[n_tok], cand_tok_off[n_cand+1], q_cand_off[n_q+1]: the problem's token and
+ *     offset arrays (HOST copies; n_tok = cand_tok_off[n_cand]; offsets monotone from 0,
+ *     every candidate and question non-empty, targets >= 0).
+ *   tok_node[n_tok] (out): predictor node of each token, numbered 0.. in order of first use.
+ *   node_tok[n_tok] (out): node_tok[j] = first token predicted from node j (its row in a
+ *     one-row-per-token layout holds node j's state); entries >= *n_nodes are untouched.
+ *   *n_nodes (out): number of predictor nodes.
+ * Scoring with H' = rows of node_tok and tok_row = tok_node projects each node once and
+ * gives the same outputs when equal histories have equal states.  Returns JET_E_NULL,
+ * JET_E_SHAPE (malformed offsets) or JET_E_INDEX (a negative target) without writing. */
+JET_API jet_status jet_build_predictor_trie(const int32_t* tok_target, const int32_t* cand_tok_off,
+                                            int32_t n_cand, const int32_t* q_cand_off, int32_t n_q,
+                                            int32_t* tok_node, int32_t* node_tok, int32_t* n_nodes);
+
 /* Restricted-vocabulary scoring (nimble page, Execution steps 5-6): gather only the
  * allowed head rows (their sorted union), project the rows onto the union and take each
  * field's softmax over its own allowed ids at temperature T.  The full-vocabulary

@@ -9,9 +9,12 @@ from .jet_oracle import (  # noqa: F401
     build_union,
     candidate_scores,
     decide,
+    allowed_mass,
+    confidence,
     decide_question,
     logits,
     logsumexp_rows,
+    predictor_trie,
     score,
     score_restricted,
     token_logprobs,

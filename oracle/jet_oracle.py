@@ -273,3 +273,45 @@ def score_restricted(rp: dict) -> dict:
         am[f] = r["argmax"]
         gap[f] = r["gap"]
     return dict(slot_logit=logit, slot_q=qv, field_argmax=am, field_gap=gap)
+
+
+# ----------------------------------------------------------------------------------------
+# predictor-row deduplication (history trie)
+# ----------------------------------------------------------------------------------------
+
+def predictor_trie(tok_target, cand_tok_off, q_cand_off):
+    """History-consistent merging of candidate token sequences (FastJEV Sec. 3.3, Eq. 4).
+
+    Token t of a candidate is predicted from the state after its preceding history: the
+    question's context followed by the candidate's tokens 0 .. t-1.  Histories form a tree
+    per question: the root is the context, and the child of node v by token y is keyed by
+    (v, y); since every candidate starts at the same position, depth fixes the position, so
+    the key carries no separate position.  Two tokens share a predictor node exactly when
+    they belong to the same question and have identical preceding histories.
+
+    Returns (tok_node, node_tok): tok_node[k] is the predictor node of token k, numbered
+    0, 1, ... in order of first use over the tokens; node_tok[j] is the first token predicted
+    from node j (a row of the undeduplicated layout that holds node j's state)."""
+    tok_target = [int(x) for x in tok_target]
+    co = [int(x) for x in cand_tok_off]
+    qo = [int(x) for x in q_cand_off]
+    tok_node = [-1] * len(tok_target)
+    node_tok = []
+    number = {}      # tree node -> predictor index (assigned at first use)
+    child = {}       # (tree node, token) -> tree node
+    n_tree = 0
+    for g in range(len(qo) - 1):
+        root = ("root", g)
+        for c in range(qo[g], qo[g + 1]):
+            v = root
+            for k in range(co[c], co[c + 1]):
+                if v not in number:
+                    number[v] = len(node_tok)
+                    node_tok.append(k)
+                tok_node[k] = number[v]
+                key = (v, tok_target[k])
+                if key not in child:
+                    child[key] = n_tree
+                    n_tree += 1
+                v = child[key]
+    return np.array(tok_node, dtype=np.int64), np.array(node_tok, dtype=np.int64)

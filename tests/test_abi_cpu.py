@@ -227,3 +227,41 @@ def test_projection_kernel_choice(lib):
     assert pick(300, 255, 256, BF16, BF16) == "k_project_wg_bf16"       # vocabulary below one tile
     assert pick(32, 1000, 64, F32, F32) == "k_project_small_f32"
     assert pick(32, 1000, 64, F32, BF16, T=-1.0) is None
+
+
+def test_predictor_trie_matches_oracle():
+    """The library's history trie (host call) equals the oracle's, bit for bit."""
+    import oracle as jo
+    from candidate_likelihood_scoring_amd import api
+
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        n_q = int(rng.integers(1, 6))
+        tg, co, qo = [], [0], [0]
+        for g in range(n_q):
+            for c in range(int(rng.integers(1, 9))):
+                m = int(rng.integers(1, 6))
+                tg.extend(int(x) for x in rng.integers(0, 1 + trial % 4, size=m))
+                co.append(len(tg))
+            qo.append(len(co) - 1)
+        tn, nt = api.build_predictor_trie(tg, co, qo)
+        rtn, rnt = jo.predictor_trie(tg, co, qo)
+        assert np.array_equal(tn, rtn) and np.array_equal(nt, rnt)
+    p = wl.multi_token()
+    tn, nt = api.build_predictor_trie(p["tok_target"], p["cand_tok_off"], p["q_cand_off"])
+    rtn, rnt = jo.predictor_trie(p["tok_target"], p["cand_tok_off"], p["q_cand_off"])
+    assert np.array_equal(tn, rtn) and np.array_equal(nt, rnt)
+
+
+def test_predictor_trie_rejects_malformed_input():
+    from candidate_likelihood_scoring_amd import api
+
+    with pytest.raises(_lib.JetError) as e:
+        api.build_predictor_trie([1, 2], [0, 2], [0, 2])      # question end != n_cand
+    assert e.value.status == -2
+    with pytest.raises(_lib.JetError) as e:
+        api.build_predictor_trie([1, 2], [0, 2, 2], [0, 2])   # empty candidate
+    assert e.value.status == -2
+    with pytest.raises(_lib.JetError) as e:
+        api.build_predictor_trie([1, -2], [0, 2], [0, 1])     # negative target
+    assert e.value.status == -4

@@ -138,6 +138,41 @@ def _mass_best_only(s):
     return float(np.exp(np.max(np.asarray(s, np.float64))))
 
 
+def _trie_token_only_key(tok_target, cand_tok_off, q_cand_off):
+    """Child keyed by (question, token): forgets the parent history."""
+    co, qo = list(cand_tok_off), list(q_cand_off)
+    tok_node, node_tok, number = [-1] * len(tok_target), [], {}
+    for g in range(len(qo) - 1):
+        for c in range(qo[g], qo[g + 1]):
+            v = ("root", g)
+            for k in range(co[c], co[c + 1]):
+                if v not in number:
+                    number[v] = len(node_tok)
+                    node_tok.append(k)
+                tok_node[k] = number[v]
+                v = (g, int(tok_target[k]))
+    return np.array(tok_node), np.array(node_tok)
+
+
+def _trie_shared_root(tok_target, cand_tok_off, q_cand_off):
+    """One root for every question."""
+    n_cand = len(cand_tok_off) - 1
+    return _orig_trie(tok_target, cand_tok_off, np.array([0, n_cand]))
+
+
+_orig_trie = jom.predictor_trie
+
+
+def _trie_node_of_own_token(tok_target, cand_tok_off, q_cand_off):
+    """Token mapped to the node its own token creates, not to its preceding history."""
+    tn, nt = _orig_trie(tok_target, cand_tok_off, q_cand_off)
+    co = np.asarray(cand_tok_off)
+    out = tn.copy()
+    for c in range(len(co) - 1):
+        out[co[c]:co[c + 1] - 1] = tn[co[c] + 1:co[c + 1]]
+    return out, nt
+
+
 MUTANTS = {
     "lse_without_max_shift": ("logsumexp_rows", _lse_no_shift),
     "lse_sign_error": ("logsumexp_rows", _lse_sign),
@@ -161,6 +196,9 @@ MUTANTS = {
     "confidence_is_the_entropy": ("confidence", _conf_entropy_itself),
     "mass_with_temperature": ("allowed_mass", _mass_tempered),
     "mass_of_best_candidate_only": ("allowed_mass", _mass_best_only),
+    "trie_forgets_parent": ("predictor_trie", _trie_token_only_key),
+    "trie_one_root_for_all_questions": ("predictor_trie", _trie_shared_root),
+    "trie_token_uses_its_own_node": ("predictor_trie", _trie_node_of_own_token),
 }
 
 

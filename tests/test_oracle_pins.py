@@ -430,6 +430,66 @@ def pin_confidence_and_mass():
     assert abs(jo.decide_question(s[::-1].copy(), 1.3)["confidence"] - c) < 1e-15
 
 
+def _seq_arrays(questions):
+    """CSR arrays for a list of questions, each a list of candidate token tuples."""
+    tg, co, qo = [], [0], [0]
+    for cands in questions:
+        for seq in cands:
+            tg.extend(seq)
+            co.append(len(tg))
+        qo.append(len(co) - 1)
+    return np.array(tg), np.array(co), np.array(qo)
+
+
+def pin_predictor_trie():
+    """History-consistent merging (FastJEV Sec. 3.3, Eq. 4): a token's predictor is the node
+    of its preceding history; nodes are keyed by (parent, token) from a per-question root,
+    so equal tokens after different histories stay separate.
+
+    Worked by hand: question 0 has candidates (a b c), (a b d), (a e), (f b d); question 1
+    has (a b c).  Predictors: root0 for every first token; 'a' for b, b, e; 'ab' for c, d;
+    'f' for b; 'fb' for d (not 'ab': its parent differs); question 1 repeats nothing of
+    question 0.  Numbering follows first use."""
+    a, b, c, d, e, f = 10, 20, 30, 40, 50, 60
+    tg, co, qo = _seq_arrays([[(a, b, c), (a, b, d), (a, e), (f, b, d)], [(a, b, c)]])
+    tok_node, node_tok = jo.predictor_trie(tg, co, qo)
+    assert list(tok_node) == [0, 1, 2, 0, 1, 2, 0, 1, 0, 3, 4, 5, 6, 7], list(tok_node)
+    assert list(node_tok) == [0, 1, 2, 9, 10, 11, 12, 13], list(node_tok)
+    # brute force against the plain definition on random inputs with many repeats
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        qs = [[tuple(rng.integers(0, 3, size=rng.integers(1, 5))) for _ in range(rng.integers(1, 7))]
+              for _ in range(rng.integers(1, 4))]
+        tg, co, qo = _seq_arrays(qs)
+        tok_node, node_tok = jo.predictor_trie(tg, co, qo)
+        hist = []
+        for g, cands in enumerate(qs):
+            for seq in cands:
+                hist.extend((g, tuple(seq[:t])) for t in range(len(seq)))
+        n = len(hist)
+        for i in range(n):
+            for j in range(n):
+                assert (tok_node[i] == tok_node[j]) == (hist[i] == hist[j])
+        firsts = [int(np.flatnonzero(tok_node == v)[0]) for v in range(len(node_tok))]
+        assert firsts == sorted(firsts) and list(node_tok) == firsts
+
+
+def pin_deduplicated_scoring():
+    """Candidate-preserving readout (FastJEV Sec. 3.3): projecting each predictor node once
+    and gathering every token's log-probability through its node gives the same outputs as
+    one row per token, when equal histories have equal states (as a backbone gives them)."""
+    p = wl.shared_history_problem(V=400, d=16, n_q=4, K=(3, 7), lengths=(1, 4), seed=3)
+    full = jo.score(p)
+    tok_node, node_tok = jo.predictor_trie(p["tok_target"], p["cand_tok_off"], p["q_cand_off"])
+    assert len(node_tok) < p["n_rows"]
+    dd = dict(p, H=p["H"][node_tok], n_rows=len(node_tok), tok_row=tok_node.astype(np.int32))
+    red = jo.score(dd)
+    for k in ("tok_logp", "cand_s", "cand_q", "q_expect", "q_confidence", "q_mass"):
+        _close(red[k], full[k], 1e-12, f"dedup {k}")
+    assert np.array_equal(red["q_argmax"], full["q_argmax"])
+    _close(red["lse"], full["lse"][node_tok], 1e-12, "dedup lse")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

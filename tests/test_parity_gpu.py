@@ -123,6 +123,26 @@ def test_tiled_stream(jet, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, 'tiled_stream', sampled=True)} on {len(rows)} rows")
 
 
+@pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
+def test_deduplicated_rows(jet, h_dtype):
+    """Predictor-row deduplication (history trie built by the library on the host): scoring
+    one row per predictor node gives the full problem's outputs (FastJEV Sec. 3.3)."""
+    from candidate_likelihood_scoring_amd import api
+
+    p = wl.shared_history_problem(V=5003, d=128, n_q=40, K=(4, 12), lengths=(1, 6), alphabet=3,
+                                  h_dtype=h_dtype, seed=71)
+    tok_node, node_tok = api.build_predictor_trie(p["tok_target"], p["cand_tok_off"], p["q_cand_off"])
+    pd = dict(p, H=p["H"][node_tok], n_rows=len(node_tok), tok_row=tok_node)
+    log(f"[gpu] dedup {h_dtype}: {p['n_rows']} rows -> {pd['n_rows']} predictor nodes")
+    assert pd["n_rows"] < p["n_rows"]
+    ref = jo.score(p)
+    out_full = _run(jet, p)
+    out_dd = _run(jet, pd)
+    log(f"[gpu] full errs {compare(p, out_full, ref, 'dedup full')}")
+    ref_dd = dict(ref, lse=ref["lse"][node_tok])
+    log(f"[gpu] dedup errs {compare(pd, out_dd, ref_dd, 'dedup nodes')}")
+
+
 def test_true_index_and_gold(jet):
     p = wl.make_problem(V=3000, d=64, n_q=10, K=(2, 6), lengths=(1, 3), layout="prefix", seed=31, dups=1)
     K = np.diff(p["q_cand_off"])

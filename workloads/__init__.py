@@ -19,4 +19,5 @@ from .synth import (  # noqa: F401
     restricted_as_full,
     large_batch,
     stress,
+    shared_history_problem,
 )

@@ -397,6 +397,40 @@ def make_problem(V: int, d: int, n_q: int, K=(1, 8), lengths=(1, 4), layout: str
                    with_true_idx=False)
 
 
+def shared_history_problem(V: int, d: int, n_q: int, K=(2, 8), lengths=(1, 5), alphabet: int = 3,
+                           h_dtype: str = "f32", w_dtype: str = "bf16", T: float = 1.0,
+                           seed: int = 1, name: str = "shared_history") -> dict:
+    """Every token on its own row (tok_row = identity), with candidates that share leading
+    tokens: each question draws its candidates' tokens from `alphabet` ids of its own, so
+    histories repeat.  A row is the state after the token's preceding history within its
+    question, as a backbone would produce it: tokens with equal histories get bitwise-equal
+    rows (one seeded draw per distinct history)."""
+    rng = np.random.default_rng([seed, _TAG_STRUCT])
+    rint = lambda r: int(r) if np.isscalar(r) else int(rng.integers(r[0], r[1] + 1))  # noqa: E731
+    b = _Builder()
+    state_of_tok = []
+    states = {}
+    nrow = 0
+    for q in range(n_q):
+        ids = rng.choice(V, size=min(alphabet, V), replace=False)
+        Kq = rint(K)
+        for c in range(Kq):
+            m = rint(lengths)
+            tg = ids[rng.integers(0, len(ids), size=m)]
+            b.candidate(list(range(nrow, nrow + m)), tg, c)
+            nrow += m
+            for t in range(m):
+                key = (q, tuple(int(x) for x in tg[:t]))
+                state_of_tok.append(states.setdefault(key, len(states)))
+        b.end_question(int(rng.integers(0, Kq)), -1)
+    hseed = seed * 7919 + 29
+    Hs = hidden_states(len(states), d, hseed, h_dtype)
+    H = np.ascontiguousarray(Hs[np.asarray(state_of_tok, dtype=np.int64)])
+    W = head_weights(V, d, seed, w_dtype)
+    return _finish(name, V, d, nrow, b.arrays(), H, h_dtype, W, w_dtype, T, identity_rows=True,
+                   with_true_idx=False)
+
+
 def stress(kind: str = "wide", seed: int = 606, V: int = 248320, d: int = 2560) -> dict:
     """The binary/enum shape with peaked logits.
 
