@@ -131,6 +131,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", choices=WORKLOADS, default="binary_enum")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dedup", action="store_true",
+                    help="project one row per predictor node of the history trie (built on the "
+                         "host before timing) instead of one row per token")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a device copy of this many MiB first (counter calibration)")
     args = ap.parse_args(argv)
@@ -153,6 +156,21 @@ def main(argv=None) -> int:
 
     _log(f"[bench] generating {args.workload}")
     p = wl.make_config(args.workload)
+    trie = None
+    if args.dedup and not restricted:
+        # Rows of the deduplicated problem: the state of each predictor node, taken from the
+        # row of the first token it predicts (a backbone gives equal histories equal states).
+        t0 = time.perf_counter()
+        tok_node, node_tok = api.build_predictor_trie(p["tok_target"], p["cand_tok_off"],
+                                                      p["q_cand_off"])
+        build_ms = (time.perf_counter() - t0) * 1e3
+        tok_row = (np.arange(len(p["tok_target"])) if p.get("tok_row") is None
+                   else np.asarray(p["tok_row"]))
+        rows_before = int(p["n_rows"])
+        p = dict(p, H=np.ascontiguousarray(p["H"][tok_row[node_tok]]), n_rows=len(node_tok),
+                 tok_row=tok_node)
+        trie = dict(rows_before=rows_before, predictor_nodes=len(node_tok),
+                    host_build_ms=round(build_ms, 3))
     if args.copy_probe_mib:
         # Counter calibration: an elementwise kernel that reads and writes exactly
         # copy_probe_mib MiB each (torch's neg), run three times before the benchmark.
@@ -277,6 +295,9 @@ def main(argv=None) -> int:
                   accumulate="fp32", seed_layout="workloads.synth")
     if not restricted:
         config.update(candidates=int(prob.n_cand), questions=int(prob.n_q))
+    if trie is not None:
+        config.update(dedup=True)
+        extra["trie"] = trie
     line = dict(metric=METRIC, value=round(value, 1), unit="scored candidate tokens/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_per_step, 5),
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype=dtype,

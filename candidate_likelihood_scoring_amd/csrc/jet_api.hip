@@ -25,11 +25,7 @@ constexpr int kSmallWaves = JET_SMALL_WAVES;
 #ifndef JET_TILED_MIN_ROWS
 #define JET_TILED_MIN_ROWS 256
 #endif
-#ifndef JET_TILED_WGS
-#define JET_TILED_WGS 3072
-#endif
 constexpr int kTiledMinRows = JET_TILED_MIN_ROWS;
-constexpr int kTiledWorkgroups = JET_TILED_WGS;
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -89,18 +85,21 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     pl->n_rtiles = (p->n_rows + 255) / 256;
     pl->vgroup = 256;
     pl->n_vgroups = (p->V + 255) / 256;
-    // About kTiledWorkgroups workgroups in all, each sweeping a contiguous vocabulary
-    // range.  Prefer a split count that makes the total a multiple of 256 (every CU gets
-    // the same number of workgroups and the XCD-aware placement applies).
-    const int R = pl->n_rtiles;
-    int splits = std::max(1, (kTiledWorkgroups + R - 1) / R);
-    int g = 256, a = R;
-    while (a) { const int t = g % a; g = a; a = t; }  // g = gcd(256, R)
-    int unit = 256 / g;
-    if (unit < 8) unit = 8;
-    const int snapped = std::max(unit, (splits + unit / 2) / unit * unit);
-    if (snapped <= pl->n_vgroups) splits = snapped;
-    splits = std::max(1, std::min(splits, pl->n_vgroups));
+    // Split count S (vocabulary ranges per row tile), from a makespan estimate: R * S
+    // workgroups run in ceil(R S / 256) rounds on the 256 CUs, each taking ceil(n_vt / S)
+    // tiles plus about a quarter tile of per-workgroup overhead.  S a multiple of 8 lets
+    // the launch use the XCD-aware 4 x 8 placement (others pay an estimated 5%).
+    const int R = pl->n_rtiles, nvt = pl->n_vgroups;
+    int splits = 1;
+    double best = 1e300;
+    for (int S = 1; S <= std::min(nvt, 1024); ++S) {
+      const double rounds = std::ceil((double)R * S / 256.0);
+      const double t = rounds * ((nvt + S - 1) / S + 0.25) * (S % 8 ? 1.05 : 1.0);
+      if (t < best - 1e-9) {
+        best = t;
+        splits = S;
+      }
+    }
     pl->grid_x = splits;
   } else {
     pl->row_tile = 32;

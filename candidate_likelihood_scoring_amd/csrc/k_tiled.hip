@@ -88,7 +88,8 @@ __device__ __forceinline__ void vm_wait() {
 
 // Workgroup -> (row tile, vocabulary split).  Launch index L runs on XCD L % 8, and each XCD
 // runs about 32 workgroups at a time; with remap (launch size a multiple of 256) those 32
-// form an sr x ss block of (row tile, split) pairs sharing tiles in that XCD's L2.
+// form an sr x ss block of (row tile, split) pairs sharing tiles in that XCD's L2.  Indices
+// past the last real block decode to row tiles >= n_rtiles (padding).
 __device__ __forceinline__ void tile_assign(int sr, int ss, int splits, int remap, int& rt,
                                             int& split) {
   int P = blockIdx.x;
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   const int n = lane & 31, h = lane >> 5;
   int rt, split;
   tile_assign(sr, ss, splits, remap, rt, split);
+  if (rt >= n_rtiles) return;  // padding workgroup of the XCD-aware launch (uniform)
   const int row_nom = rt * TBN;                    // first row this tile reports
   const int row0 = min(row_nom, n_rows - TBN);     // rows loaded: [row0, row0 + 256), all valid
   const int t0 = (int)((long long)split * n_vtiles / splits);
@@ -543,6 +545,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
   const int n = lane & 31, h = lane >> 5;
   int rt, split;
   tile_assign(sr, ss, splits, remap, rt, split);
+  if (rt >= n_rtiles) return;  // padding workgroup of the XCD-aware launch (uniform)
   const int row_nom = rt * TBN;
   const int row0 = min(row_nom, n_rows - TBN);
   const int t0 = (int)((long long)split * n_vtiles / splits);
@@ -722,24 +725,17 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   const int* b_tok = reinterpret_cast<const int*>(a.ws + pl.off_btok);
   float* z_tgt = reinterpret_cast<float*>(a.ws + pl.off_ztgt);
   float2* part = reinterpret_cast<float2*>(a.ws + pl.off_part);
-  // super-tile shape for the XCD-aware placement
-  int sr = 1, ss = 1;
+  // XCD-aware placement when the split count allows 4 row tiles x 8 splits per XCD block:
+  // row tiles are padded to a multiple of 4 and the launch to a multiple of 256; padding
+  // workgroups (row tile >= R) exit at once.  Otherwise the plain order P = rt * S + split.
   const int S = pl.grid_x, R = pl.n_rtiles;
-  const int total = S * R;
-  int remap = 0;
-  if (total % 256 == 0) {
-    const int cand[3][2] = {{4, 8}, {2, 16}, {1, 32}};
-    for (int i = 0; i < 3; ++i)
-      if (R % cand[i][0] == 0 && S % cand[i][1] == 0) {
-        sr = cand[i][0];
-        ss = cand[i][1];
-        remap = 1;
-        break;
-      }
-  }
-  if (!remap) {  // plain order: P = row tile * S + split
-    sr = 1;
-    ss = S;
+  int sr = 1, ss = S, remap = 0, total = S * R;
+  if (S % 8 == 0) {
+    sr = 4;
+    ss = 8;
+    remap = 1;
+    const int r_pad = (R + 3) / 4 * 4;
+    total = (r_pad * S + 255) / 256 * 256;
   }
   dim3 grid(total), block(256);
   const uint16_t* W = static_cast<const uint16_t*>(p->W);
