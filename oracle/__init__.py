@@ -12,11 +12,13 @@ from .jet_oracle import (  # noqa: F401
     allowed_mass,
     confidence,
     decide_question,
+    decision_sensitivity,
     logits,
     logsumexp_rows,
     predictor_trie,
     score,
     score_restricted,
+    select_layers,
     token_logprobs,
     widen,
 )

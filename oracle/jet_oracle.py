@@ -315,3 +315,39 @@ def predictor_trie(tok_target, cand_tok_off, q_cand_off):
                     n_tree += 1
                 v = child[key]
     return np.array(tok_node, dtype=np.int64), np.array(node_tok, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------------------
+# decision sensitivity of layer skips
+# ----------------------------------------------------------------------------------------
+
+def decision_sensitivity(z, z_skip, seg_off, eps: float = 1e-8):
+    """Layer sensitivity (FastJEV Sec. 3.4, Eq. 5-6).
+
+    z[seg_off[x]:seg_off[x+1]] is input x's logit vector (candidates and abstention) and
+    z_skip[l] the same vector with layer l skipped.  With ctr(v) = v - mean(v) and
+    rms(v) = ||v|| / sqrt(m):
+        d[l, x] = rms(ctr(z_skip[l] - z)) / max(eps, rms(ctr(z)))   over input x's entries
+        J[l]    = mean over inputs of d[l, x].
+    Returns (d [n_layers, n_inputs], J [n_layers]) in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    zs = np.asarray(z_skip, dtype=np.float64).reshape(-1, len(z))
+    off = [int(o) for o in seg_off]
+    n_in, L = len(off) - 1, zs.shape[0]
+    d = np.empty((L, n_in))
+    for x in range(n_in):
+        a, b = off[x], off[x + 1]
+        zx = z[a:b]
+        den = max(eps, float(np.sqrt(np.mean((zx - zx.mean()) ** 2))))
+        for l in range(L):
+            delta = zs[l, a:b] - zx
+            d[l, x] = float(np.sqrt(np.mean((delta - delta.mean()) ** 2))) / den
+    return d, d.mean(axis=1)
+
+
+def select_layers(J, k: int):
+    """The k layers with the smallest J, ties resolved by layer index (FastJEV Sec. 3.4,
+    "Calibration Guided Selection"), listed in that order (smallest first)."""
+    J = np.asarray(J)
+    order = sorted(range(len(J)), key=lambda l: (J[l], l))
+    return np.array(order[:k], dtype=np.int64)

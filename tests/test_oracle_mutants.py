@@ -173,6 +173,35 @@ def _trie_node_of_own_token(tok_target, cand_tok_off, q_cand_off):
     return out, nt
 
 
+def _sens_variant(center=True, ddof=0, floor=True, reduce="mean"):
+    def f(z, z_skip, seg_off, eps=1e-8):
+        z = np.asarray(z, np.float64)
+        zs = np.asarray(z_skip, np.float64).reshape(-1, len(z))
+        off = [int(o) for o in seg_off]
+        d = np.empty((zs.shape[0], len(off) - 1))
+        for x in range(len(off) - 1):
+            a, b = off[x], off[x + 1]
+            zx = z[a:b]
+            c = (lambda v: v - v.mean()) if center else (lambda v: v)
+            rms = lambda v: math.sqrt(float(np.sum(v * v)) / max(len(v) - ddof, 1))  # noqa: E731
+            den = max(eps, rms(c(zx))) if floor else rms(c(zx))
+            for l in range(zs.shape[0]):
+                with np.errstate(all="ignore"):
+                    d[l, x] = rms(c(zs[l, a:b] - zx)) / den if den else math.inf
+        return d, (d.mean(axis=1) if reduce == "mean" else d.sum(axis=1))
+    return f
+
+
+def _select_ties_high(J, k):
+    order = sorted(range(len(J)), key=lambda l: (J[l], -l))
+    return np.array(order[:k], dtype=np.int64)
+
+
+def _select_largest(J, k):
+    order = sorted(range(len(J)), key=lambda l: (-J[l], l))
+    return np.array(order[:k], dtype=np.int64)
+
+
 MUTANTS = {
     "lse_without_max_shift": ("logsumexp_rows", _lse_no_shift),
     "lse_sign_error": ("logsumexp_rows", _lse_sign),
@@ -199,6 +228,12 @@ MUTANTS = {
     "trie_forgets_parent": ("predictor_trie", _trie_token_only_key),
     "trie_one_root_for_all_questions": ("predictor_trie", _trie_shared_root),
     "trie_token_uses_its_own_node": ("predictor_trie", _trie_node_of_own_token),
+    "sensitivity_not_centred": ("decision_sensitivity", _sens_variant(center=False)),
+    "sensitivity_sample_std": ("decision_sensitivity", _sens_variant(ddof=1)),
+    "sensitivity_no_eps_floor": ("decision_sensitivity", _sens_variant(floor=False)),
+    "sensitivity_J_summed": ("decision_sensitivity", _sens_variant(reduce="sum")),
+    "selection_ties_to_higher_layer": ("select_layers", _select_ties_high),
+    "selection_of_largest_scores": ("select_layers", _select_largest),
 }
 
 

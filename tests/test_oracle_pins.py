@@ -490,6 +490,54 @@ def pin_deduplicated_scoring():
     _close(red["lse"], full["lse"][node_tok], 1e-12, "dedup lse")
 
 
+def pin_decision_sensitivity():
+    """FastJEV Sec. 3.4, Eq. 5-6: d = rms(ctr(delta)) / max(eps, rms(ctr(z))), J = mean d.
+
+    By hand: z = (0, 1) has ctr (-1/2, 1/2), rms 1/2; a skip moving it to (0, 2) has
+    delta (0, 1), also rms 1/2 after centring, so d = 1; a skip adding the same amount to
+    every entry has d = 0 (a common shift changes no difference).  z constant has
+    rms(ctr z) = 0, so the denominator is eps.  d is unchanged by a per-input shift of z or
+    of the skipped logits (ctr removes it) and by scaling both by c > 0; J is the mean over
+    inputs; a pure-Python brute force agrees on random ragged inputs."""
+    d, J = jo.decision_sensitivity([0.0, 1.0], [[0.0, 2.0], [3.5, 4.5]], [0, 2])
+    _close(d[:, 0], [1.0, 0.0], 1e-15, "hand d")
+    d, _ = jo.decision_sensitivity([2.0, 2.0, 2.0], [[2.0, 2.0, 2.3]], [0, 3])
+    exp_num = math.sqrt(((0.3 - 0.1) ** 2 + 2 * 0.1 ** 2) / 3)
+    _close(d[0, 0], exp_num / 1e-8, 1e-6 * exp_num / 1e-8, "eps floor")
+    rng = np.random.default_rng(5)
+    off = np.concatenate([[0], np.cumsum(rng.integers(1, 9, size=6))])
+    z = rng.normal(size=off[-1])
+    zs = z + rng.normal(scale=0.3, size=(4, off[-1]))
+    d, J = jo.decision_sensitivity(z, zs, off)
+    shift = np.repeat(rng.normal(size=6) * 50, np.diff(off))
+    d2, _ = jo.decision_sensitivity(z + shift, zs + shift + rng.normal(size=(4, 1)) * 0, off)
+    _close(d2, d, 1e-9, "shift of z and skipped logits")
+    d3, _ = jo.decision_sensitivity(z, zs + np.repeat(rng.normal(size=6), np.diff(off)), off)
+    _close(d3, d, 1e-9, "shift of the skipped logits alone")
+    d4, _ = jo.decision_sensitivity(3.7 * z, 3.7 * zs, off)
+    _close(d4, d, 1e-12, "common scale")
+    _close(J, d.mean(axis=1), 0.0, "J is the mean")
+    for l in range(4):
+        for x in range(6):
+            a, b = int(off[x]), int(off[x + 1])
+            m = b - a
+            zm = math.fsum(z[a:b]) / m
+            dl = [zs[l, i] - z[i] for i in range(a, b)]
+            dm = math.fsum(dl) / m
+            num = math.sqrt(math.fsum((v - dm) ** 2 for v in dl) / m)
+            den = max(1e-8, math.sqrt(math.fsum((z[i] - zm) ** 2 for i in range(a, b)) / m))
+            assert abs(d[l, x] - num / den) <= 1e-12 * max(1.0, num / den)
+
+
+def pin_select_layers():
+    """The k smallest J with ties resolved by layer index (FastJEV Sec. 3.4)."""
+    J = [0.3, 0.1, 0.1, 0.5, 0.05]
+    assert list(jo.select_layers(J, 3)) == [4, 1, 2]
+    assert list(jo.select_layers(J, 2)) == [4, 1]
+    assert list(jo.select_layers(J, 0)) == []
+    assert list(jo.select_layers([1.0, 1.0, 1.0], 2)) == [0, 1]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
