@@ -67,6 +67,9 @@ EXPORTS = {
     "jet_score_profiled": (c_int, [POINTER(JetProblem), POINTER(JetOutputs), c_void_p, c_size_t,
                                    c_void_p, c_void_p, c_void_p]),
     "jet_projection_kernel": (c_char_p, [POINTER(JetProblem)]),
+    "jet_decision_sensitivity": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                         c_float, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p]),
     "jet_build_predictor_trie": (c_int, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                                          c_void_p, POINTER(c_int32)]),
     "jet_validate_host": (c_int, [POINTER(JetProblem)]),

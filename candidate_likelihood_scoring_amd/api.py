@@ -115,6 +115,32 @@ def build_predictor_trie(tok_target, cand_tok_off, q_cand_off):
     return tok_node[:n_tok].copy(), node_tok[:nn.value].copy()
 
 
+def decision_sensitivity(z: torch.Tensor, z_skip: torch.Tensor, seg_off: torch.Tensor, k: int,
+                         eps: float = 1e-8, stream=None) -> dict:
+    """Layer-skip sensitivity on the device (see jet_decision_sensitivity): z [n_values] and
+    z_skip [n_layers, n_values] float32, seg_off [n_inputs + 1] int32, all on one device.
+    Returns d [n_layers, n_inputs], J [n_layers], selected [k] and dev_flags [1]."""
+    dev = z.device
+    if z.dtype != torch.float32 or z_skip.dtype != torch.float32 or z.dim() != 1 or \
+            z_skip.dim() != 2 or z_skip.shape[1] != z.shape[0] or not z.is_contiguous() or \
+            not z_skip.is_contiguous() or z_skip.device != dev:
+        raise TypeError("z [n_values] and z_skip [n_layers, n_values]: contiguous float32, one device")
+    _check_i32("seg_off", seg_off, dev)
+    L, n_in = int(z_skip.shape[0]), int(seg_off.numel()) - 1
+    out = dict(d=torch.empty(L, max(n_in, 0), dtype=torch.float32, device=dev),
+               J=torch.empty(L, dtype=torch.float32, device=dev),
+               selected=torch.empty(max(k, 1), dtype=torch.int32, device=dev),
+               dev_flags=torch.zeros(1, dtype=torch.int32, device=dev))
+    sh = _stream_handle(stream)
+    st = _lib.load().jet_decision_sensitivity(
+        _ptr(z), _ptr(z_skip), _ptr(seg_off), n_in, int(z.numel()), L, float(eps), int(k),
+        _ptr(out["d"]), _ptr(out["J"]), _ptr(out["selected"]), _ptr(out["dev_flags"]), sh)
+    if st != 0:
+        raise JetError(st, "jet_decision_sensitivity")
+    out["selected"] = out["selected"][:k]
+    return out
+
+
 def projection_kernel(prob: JetProblem) -> str | None:
     """Name of the projection kernel jet_score launches for this problem (None if invalid)."""
     r = _lib.load().jet_projection_kernel(ctypes.byref(prob))

@@ -158,6 +158,20 @@ const char* jet_status_string(jet_status s) {
   return "unknown status";
 }
 
+jet_status jet_decision_sensitivity(const float* z, const float* z_skip, const int32_t* seg_off,
+                                    int32_t n_inputs, int32_t n_values, int32_t n_layers,
+                                    float eps, int32_t k, float* d, float* J, int32_t* selected,
+                                    int32_t* dev_flags, void* stream) {
+  if (!z || !z_skip || !seg_off || !d || !J || (k > 0 && !selected)) return JET_E_NULL;
+  if (n_inputs < 1 || n_values < 1 || n_layers < 1 || n_layers > sensitivity_max_layers() ||
+      k < 0 || k > n_layers || !std::isfinite(eps) || !(eps > 0.f))
+    return JET_E_SHAPE;
+  const hipError_t e = launch_sensitivity(z, z_skip, seg_off, n_inputs, n_values, n_layers, eps,
+                                          k, d, J, selected, dev_flags,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? JET_OK : JET_E_HIP;
+}
+
 jet_status jet_build_predictor_trie(const int32_t* tok_target, const int32_t* cand_tok_off,
                                     int32_t n_cand, const int32_t* q_cand_off, int32_t n_q,
                                     int32_t* tok_node, int32_t* node_tok, int32_t* n_nodes) {

@@ -93,7 +93,12 @@ hipError_t launch_prep(const ScoreArgs& a);
 hipError_t launch_project(const ScoreArgs& a);
 hipError_t launch_project_tiled(const ScoreArgs& a);
 int tiled_bk(bool hilo);
-const char* tiled_kernel_name(bool hilo);  // the tiled kernel launched for this plane count
+const char* tiled_kernel_name(bool hilo);
+int sensitivity_max_layers();
+hipError_t launch_sensitivity(const float* z, const float* z_skip, const int* seg_off,
+                              int n_inputs, int n_values, int n_layers, float eps, int k,
+                              float* d, float* J, int32_t* selected, int32_t* flags,
+                              hipStream_t stream);  // the tiled kernel launched for this plane count
 hipError_t launch_merge(const ScoreArgs& a);
 hipError_t launch_decide(const ScoreArgs& a);
 

@@ -215,6 +215,28 @@ JET_API jet_status jet_score_restricted(const jet_restricted_problem* p, const j
 /* Host-side validation of a restricted problem whose index arrays are HOST pointers. */
 JET_API jet_status jet_validate_restricted_host(const jet_restricted_problem* p);
 
+/* Decision sensitivity of layer skips (FastJEV Sec. 3.4, Eq. 5-6), for a calibration set
+ * of logit vectors (candidates and abstention, before any probability post-processing).
+ *   z[n_values]: the inputs' logits back to back; input x owns z[seg_off[x] .. seg_off[x+1]).
+ *   z_skip[n_layers][n_values]: the same logits with layer l skipped (row l).
+ *   seg_off[n_inputs+1]: device offsets, each segment non-empty and inside [0, n_values).
+ *   eps: floor of the denominator (the pages use 1e-8); finite and > 0.
+ * Outputs (device, caller-owned):
+ *   d[n_layers][n_inputs] = rms(ctr(z_skip[l] - z)) / max(eps, rms(ctr(z))) over input x's
+ *     entries, with ctr(v) = v - mean(v) and rms(v) = ||v|| / sqrt(m);
+ *   J[n_layers] = mean over inputs of d;
+ *   selected[k] = the k layers with the smallest J, ties resolved by layer index, in that
+ *     order (0 <= k <= n_layers; may be NULL when k = 0);
+ *   dev_flags[1] (optional) = JET_FLAG_BAD_OFFSETS if a segment is malformed (its d and the
+ *     J built on it are NaN; NaN ranks last).
+ * Results are bitwise reproducible.  Host checks: JET_E_NULL, JET_E_SHAPE (n_inputs < 1,
+ * n_values < 1, n_layers outside [1, 4096], k outside [0, n_layers], eps not finite > 0). */
+JET_API jet_status jet_decision_sensitivity(const float* z, const float* z_skip,
+                                            const int32_t* seg_off, int32_t n_inputs,
+                                            int32_t n_values, int32_t n_layers, float eps,
+                                            int32_t k, float* d, float* J, int32_t* selected,
+                                            int32_t* dev_flags, void* stream);
+
 /* Static description of a status code. */
 JET_API const char* jet_status_string(jet_status s);
 

@@ -265,3 +265,21 @@ def test_predictor_trie_rejects_malformed_input():
     with pytest.raises(_lib.JetError) as e:
         api.build_predictor_trie([1, -2], [0, 2], [0, 1])     # negative target
     assert e.value.status == -4
+
+
+def test_decision_sensitivity_host_checks(lib):
+    """Scalar checks return before anything is enqueued, so they run without a device."""
+    buf = np.zeros(64, np.float32)
+    off = np.array([0, 4], np.int32)
+    a = buf.ctypes.data
+
+    def call(n_in=1, n_val=4, L=2, eps=1e-8, k=1, sel=a, z=a):
+        return lib.jet_decision_sensitivity(z, a, off.ctypes.data, n_in, n_val, L, eps, k, a, a, sel,
+                                            None, None)
+
+    assert call(n_in=0) == -2
+    assert call(n_val=0) == -2
+    assert call(L=0) == -2 and call(L=4097) == -2
+    assert call(k=3) == -2 and call(k=-1) == -2
+    assert call(eps=0.0) == -2 and call(eps=float("nan")) == -2 and call(eps=float("inf")) == -2
+    assert call(sel=None) == -1 and call(z=None) == -1

@@ -143,6 +143,73 @@ def test_deduplicated_rows(jet, h_dtype):
     log(f"[gpu] dedup errs {compare(pd, out_dd, ref_dd, 'dedup nodes')}")
 
 
+@pytest.mark.parametrize("case", [dict(), dict(n_inputs=300, K=(1, 130), n_layers=61, seed=708),
+                                  dict(n_inputs=1, K=(1, 1), n_layers=3, seed=709, tie=None)],
+                         ids=["calib32", "ragged", "single"])
+def test_decision_sensitivity(jet, case):
+    """Layer-skip sensitivity (FastJEV Sec. 3.4, Eq. 5-6) against the oracle.  Tolerance per
+    d: fp32 centring loses u * (|mean| / rms of the centred values) for both vectors, with
+    u = 2^-24, plus the sums' own rounding; J within the mean of those; the selection must
+    match wherever the oracle's J separates the k-th and (k+1)-th layers by more than that."""
+    from candidate_likelihood_scoring_amd import api
+
+    c = wl.calibration_logits(**case)
+    L, n_in = c["n_layers"], c["n_inputs"]
+    z64, zs64, off = c["z"].astype(np.float64), c["z_skip"].astype(np.float64), c["seg_off"]
+    d_ref, J_ref = jo.decision_sensitivity(c["z"], c["z_skip"], off)
+    dev = "cuda"
+    for k in sorted({0, 1, min(6, L), L}):
+        out = api.decision_sensitivity(torch.from_numpy(c["z"]).to(dev),
+                                       torch.from_numpy(c["z_skip"]).to(dev),
+                                       torch.from_numpy(off).to(dev), k)
+        torch.cuda.synchronize()
+        assert int(out["dev_flags"][0]) == 0
+        d = out["d"].cpu().numpy().astype(np.float64)
+        J = out["J"].cpu().numpy().astype(np.float64)
+        sel = out["selected"].cpu().numpy()
+        u = 2.0 ** -24
+        tol = np.empty((L, n_in))
+        for x in range(n_in):
+            a, b = int(off[x]), int(off[x + 1])
+            zx = z64[a:b]
+            rz = max(1e-8, float(np.sqrt(np.mean((zx - zx.mean()) ** 2))))
+            for l in range(L):
+                dl = zs64[l, a:b] - zx
+                rd = float(np.sqrt(np.mean((dl - dl.mean()) ** 2)))
+                cm = abs(dl.mean()) / max(rd, 1e-30) + abs(zx.mean()) / rz
+                tol[l, x] = 8 * u * (4 + (b - a) ** 0.5 + cm) * d_ref[l, x] + 1e-30
+        err = np.abs(d - d_ref)
+        assert np.all(err <= tol), ("d", float((err / tol).max()))
+        tol_J = tol.mean(axis=1) + 4 * u * J_ref
+        assert np.all(np.abs(J - J_ref) <= tol_J), ("J", float(np.abs(J - J_ref).max()))
+        if c.get("n_layers") and case.get("tie", (4, 9)) is not None and L > 9:
+            assert J[4] == J[9] and np.array_equal(d[4], d[9])  # exact copies tie exactly
+        ref_sel = jo.select_layers(J_ref, k)
+        order = sorted(range(L), key=lambda l: (J_ref[l], l))
+        if k == 0 or k == L or J_ref[order[k]] - J_ref[order[k - 1]] > tol_J[order[k]] + tol_J[order[k - 1]]:
+            assert set(sel) == set(ref_sel), (k, sel, ref_sel)
+        # whatever the band, the selection is sorted by (J, index) in the kernel's own values
+        assert list(sel) == sorted(sel, key=lambda l: (J[l], l))
+        assert len(set(sel)) == k and all(J[s] <= J[o] for s in sel for o in set(range(L)) - set(sel))
+        log(f"[gpu] sensitivity {case} k={k}: max d err/tol {float((err / tol).max()):.3f}")
+
+
+def test_decision_sensitivity_bad_offsets_flag(jet):
+    """A segment outside [0, n_values) raises the offsets flag; its d is NaN and ranks last."""
+    from candidate_likelihood_scoring_amd import api
+
+    c = wl.calibration_logits(n_inputs=4, K=(3, 6), n_layers=5, seed=710, tie=None)
+    off = c["seg_off"].copy()
+    off[3] = off[4] + 7  # input 2 runs past the end, input 3 is inverted
+    out = api.decision_sensitivity(torch.from_numpy(c["z"]).cuda(), torch.from_numpy(c["z_skip"]).cuda(),
+                                   torch.from_numpy(off).cuda(), 5)
+    torch.cuda.synchronize()
+    assert int(out["dev_flags"][0]) & 4
+    d = out["d"].cpu().numpy()
+    assert np.all(np.isnan(d[:, 2])) and np.all(np.isnan(d[:, 3])) and np.all(np.isfinite(d[:, :2]))
+    assert sorted(out["selected"].cpu().numpy().tolist()) == [0, 1, 2, 3, 4]
+
+
 def test_true_index_and_gold(jet):
     p = wl.make_problem(V=3000, d=64, n_q=10, K=(2, 6), lengths=(1, 3), layout="prefix", seed=31, dups=1)
     K = np.diff(p["q_cand_off"])

@@ -20,4 +20,5 @@ from .synth import (  # noqa: F401
     large_batch,
     stress,
     shared_history_problem,
+    calibration_logits,
 )

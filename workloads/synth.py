@@ -431,6 +431,28 @@ def shared_history_problem(V: int, d: int, n_q: int, K=(2, 8), lengths=(1, 5), a
                    with_true_idx=False)
 
 
+def calibration_logits(n_inputs: int = 32, K=(2, 65), n_layers: int = 28, seed: int = 707,
+                       tie=(4, 9)) -> dict:
+    """A calibration set for layer-skip sensitivity: per input a logit vector of K entries
+    (candidates and abstention; 32 inputs of up to 64 candidates + 1 by default, the pages'
+    calibration size and candidate-set size), with a common offset per input, and per layer
+    the same vectors perturbed by a common shift plus layer noise of log-uniform scale in
+    [1e-2, 1].  Layer tie[1] is an exact copy of layer tie[0] (an exact tie)."""
+    rng = np.random.default_rng([seed, _TAG_STRUCT])
+    m = rng.integers(K[0], K[1] + 1, size=n_inputs)
+    off = np.concatenate([[0], np.cumsum(m)]).astype(np.int32)
+    n = int(off[-1])
+    z = (rng.normal(scale=3.0, size=n) + np.repeat(rng.normal(scale=20.0, size=n_inputs), m))
+    scale = 10.0 ** rng.uniform(-2.0, 0.0, size=n_layers)
+    zs = np.empty((n_layers, n))
+    for l in range(n_layers):
+        zs[l] = z + np.repeat(rng.normal(scale=5.0, size=n_inputs), m) + scale[l] * rng.normal(size=n)
+    if tie is not None:
+        zs[tie[1]] = zs[tie[0]]
+    return dict(z=z.astype(np.float32), z_skip=zs.astype(np.float32), seg_off=off,
+                n_layers=int(n_layers), n_inputs=int(n_inputs))
+
+
 def stress(kind: str = "wide", seed: int = 606, V: int = 248320, d: int = 2560) -> dict:
     """The binary/enum shape with peaked logits.
 
