@@ -13,8 +13,10 @@ from .jet_oracle import (  # noqa: F401
     confidence,
     decide_question,
     decision_sensitivity,
+    fit_temperature,
     logits,
     logsumexp_rows,
+    mean_gold_nll,
     predictor_trie,
     score,
     score_restricted,

@@ -351,3 +351,68 @@ def select_layers(J, k: int):
     J = np.asarray(J)
     order = sorted(range(len(J)), key=lambda l: (J[l], l))
     return np.array(order[:k], dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------------------
+# temperature fitting
+# ----------------------------------------------------------------------------------------
+
+def _labelled_matrix(s, q_cand_off, cand_text_id, q_gold_text_id):
+    """Labelled questions as padded rows: scores [n, Kmax] (-inf padding) and gold masks."""
+    s = np.asarray(s, dtype=np.float64)
+    qo = np.asarray(q_cand_off, dtype=np.int64)
+    text = np.asarray(cand_text_id)
+    K = np.diff(qo)
+    keep = []
+    for g in range(len(K)):
+        gold = int(q_gold_text_id[g])
+        if gold >= 0 and (text[qo[g]:qo[g + 1]] == gold).any():
+            keep.append(g)
+    Kmax = int(K.max()) if len(K) else 1
+    S = np.full((len(keep), Kmax), -np.inf)
+    G = np.zeros((len(keep), Kmax), dtype=bool)
+    for i, g in enumerate(keep):
+        S[i, :K[g]] = s[qo[g]:qo[g + 1]]
+        G[i, :K[g]] = text[qo[g]:qo[g + 1]] == int(q_gold_text_id[g])
+    return S, G
+
+
+def _row_lse(A):
+    m = A.max(axis=1, keepdims=True)
+    return m[:, 0] + np.log(np.exp(A - m).sum(axis=1))
+
+
+def mean_gold_nll(s, q_cand_off, cand_text_id, q_gold_text_id, T: float, _mat=None):
+    """Mean over labelled questions of the gold NLL at temperature T (the decision's q,
+    equal-text labels summed: LSE(s/T) - LSE(s/T over gold-text candidates)).  Questions
+    with no label (gold id < 0) or no candidate of the gold text are not counted.
+    Returns (mean, number of questions counted)."""
+    S, G = _mat if _mat is not None else _labelled_matrix(s, q_cand_off, cand_text_id, q_gold_text_id)
+    if len(S) == 0:
+        return math.nan, 0
+    A = S / float(T)
+    nll = _row_lse(A) - _row_lse(np.where(G, A, -np.inf))
+    return float(nll.mean()), len(S)
+
+
+def fit_temperature(s, q_cand_off, cand_text_id, q_gold_text_id, T_min: float = 1e-2,
+                    T_max: float = 1e2):
+    """The temperature minimising the mean gold NLL over [T_min, T_max] (gemma-e2b doc,
+    "Output contracts": temperature fitting; nimble "V2 probability default": T scales the
+    candidate scores once before the softmax).  The pages name the fit but not its method;
+    this is the plain minimiser: an 801-point log grid locates the basin, then a bounded
+    scalar minimisation in log T refines it.  Returns (T*, mean NLL at T*)."""
+    from scipy.optimize import minimize_scalar
+
+    mat = _labelled_matrix(s, q_cand_off, cand_text_id, q_gold_text_id)
+    f = lambda u: mean_gold_nll(None, None, None, None, math.exp(u), _mat=mat)[0]  # noqa: E731
+    lo, hi = math.log(T_min), math.log(T_max)
+    grid = np.linspace(lo, hi, 801)
+    vals = np.array([f(u) for u in grid])
+    if not np.isfinite(vals).any():
+        return math.nan, math.nan
+    i = int(np.nanargmin(vals))
+    a, b = grid[max(i - 1, 0)], grid[min(i + 1, len(grid) - 1)]
+    r = minimize_scalar(f, bounds=(a, b), method="bounded", options=dict(xatol=1e-12))
+    best_u, best_f = (r.x, r.fun) if r.fun <= vals[i] else (grid[i], vals[i])
+    return math.exp(best_u), float(best_f)

@@ -202,6 +202,35 @@ def _select_largest(J, k):
     return np.array(order[:k], dtype=np.int64)
 
 
+_orig_nll = jom.mean_gold_nll
+
+
+def _nll_first_gold_only(s, q_cand_off, cand_text_id, q_gold_text_id, T, _mat=None):
+    S, G = _mat if _mat is not None else jom._labelled_matrix(s, q_cand_off, cand_text_id, q_gold_text_id)
+    first = G & (np.cumsum(G, axis=1) == 1)
+    return _orig_nll(None, None, None, None, T, _mat=(S, first))
+
+
+def _nll_T_multiplies(s, q_cand_off, cand_text_id, q_gold_text_id, T, _mat=None):
+    return _orig_nll(s, q_cand_off, cand_text_id, q_gold_text_id, 1.0 / T, _mat=_mat)
+
+
+def _nll_counts_unlabelled(s, q_cand_off, cand_text_id, q_gold_text_id, T, _mat=None):
+    v, n = _orig_nll(s, q_cand_off, cand_text_id, q_gold_text_id, T, _mat=_mat)
+    if _mat is not None or q_gold_text_id is None:
+        return v, n
+    tot = len(q_gold_text_id)
+    return v * n / tot, tot
+
+
+def _fit_grid_only(s, q_cand_off, cand_text_id, q_gold_text_id, T_min=1e-2, T_max=1e2):
+    mat = jom._labelled_matrix(s, q_cand_off, cand_text_id, q_gold_text_id)
+    grid = np.linspace(math.log(T_min), math.log(T_max), 801)
+    vals = [_orig_nll(None, None, None, None, math.exp(u), _mat=mat)[0] for u in grid]
+    i = int(np.argmin(vals))
+    return math.exp(grid[i]), float(vals[i])
+
+
 MUTANTS = {
     "lse_without_max_shift": ("logsumexp_rows", _lse_no_shift),
     "lse_sign_error": ("logsumexp_rows", _lse_sign),
@@ -234,6 +263,10 @@ MUTANTS = {
     "sensitivity_J_summed": ("decision_sensitivity", _sens_variant(reduce="sum")),
     "selection_ties_to_higher_layer": ("select_layers", _select_ties_high),
     "selection_of_largest_scores": ("select_layers", _select_largest),
+    "nll_first_gold_only": ("mean_gold_nll", _nll_first_gold_only),
+    "nll_temperature_multiplies": ("mean_gold_nll", _nll_T_multiplies),
+    "nll_counts_unlabelled_questions": ("mean_gold_nll", _nll_counts_unlabelled),
+    "fit_without_refinement": ("fit_temperature", _fit_grid_only),
 }
 
 

@@ -538,6 +538,42 @@ def pin_select_layers():
     assert list(jo.select_layers([1.0, 1.0, 1.0], 2)) == [0, 1]
 
 
+def pin_temperature_fit():
+    """Temperature fitting = the T minimising the mean gold NLL (gemma-e2b doc, "Output
+    contracts"; T scales candidate scores once, nimble "V2 probability default").
+
+    Closed form: two binary questions with gold gaps +2 and -1 have mean NLL
+    f(b) = (log(1 + e^{-2b}) + log(1 + e^{b})) / 2 in b = 1/T; f'(b) = 0 gives
+    x^3 - x - 2 = 0 for x = e^b, whose real root is Cardano's
+    cbrt(1 + sqrt(26/27)) + cbrt(1 - sqrt(26/27)).  Scaling every score by c scales T* by c.
+    Equal-text gold labels sum their probabilities; unlabelled questions are not counted."""
+    s = np.array([0.0, -2.0, 0.0, 1.0])
+    qo, text, gold = np.array([0, 2, 4]), np.array([0, 1, 0, 1]), np.array([0, 0])
+    r = math.sqrt(26.0 / 27.0)
+    x = (1 + r) ** (1 / 3) + (1 - r) ** (1 / 3)
+    T_star = 1.0 / math.log(x)
+    assert abs(x ** 3 - x - 2) < 1e-12
+    T, f = jo.fit_temperature(s, qo, text, gold)
+    assert abs(T - T_star) < 1e-7 * T_star, (T, T_star)
+    for t in (0.5, 1.0, T_star, 7.0):
+        want = (math.log1p(math.exp(-2 / t)) + math.log1p(math.exp(1 / t))) / 2
+        assert abs(jo.mean_gold_nll(s, qo, text, gold, t)[0] - want) < 1e-14
+    T3, _ = jo.fit_temperature(3.0 * s, qo, text, gold)
+    assert abs(T3 - 3.0 * T_star) < 3e-7 * T_star
+    # equal-text labels sum; an unlabelled question changes nothing
+    s2, qo2, tx2 = np.array([1.0, 1.0, 0.0, 5.0, 2.0]), np.array([0, 3, 5]), np.array([0, 0, 1, 0, 1])
+    v, n = jo.mean_gold_nll(s2, qo2, tx2, np.array([0, -1]), 1.0)
+    assert n == 1 and abs(v - (math.log(2 * math.e + 1) - math.log(2 * math.e))) < 1e-14
+
+
+def test_planted_temperature_recovery():
+    """Statistical check of the fit (not a mutant pin): labels drawn at T0 = 2.179 by the
+    Gumbel-max trick over 4096 questions give a fitted T within 5% of T0."""
+    c = wl.labelled_questions(n_q=4096)
+    T, _ = jo.fit_temperature(c["cand_s"], c["q_cand_off"], c["cand_text_id"], c["q_gold_text_id"])
+    assert abs(T / c["T0"] - 1) < 0.05, T
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

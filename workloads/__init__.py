@@ -21,4 +21,5 @@ from .synth import (  # noqa: F401
     stress,
     shared_history_problem,
     calibration_logits,
+    labelled_questions,
 )

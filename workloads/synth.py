@@ -453,6 +453,29 @@ def calibration_logits(n_inputs: int = 32, K=(2, 65), n_layers: int = 28, seed: 
                 n_layers=int(n_layers), n_inputs=int(n_inputs))
 
 
+def labelled_questions(n_q: int = 4096, K=(2, 26), T0: float = 2.179078721266035,
+                       seed: int = 808, dup_text: float = 0.1, score_std: float = 3.0) -> dict:
+    """Candidate scores with gold labels drawn at a planted temperature T0 (default: the
+    fitted temperature one of the pages quotes).  Scores ~ N(0, score_std) per candidate;
+    the gold is argmax(s / T0 + Gumbel noise), which has the distribution softmax(s / T0)
+    (the Gumbel-max property), so no softmax is computed here.  With probability dup_text a
+    question has one candidate re-using another's text id (an equal-text label)."""
+    rng = np.random.default_rng([seed, _TAG_STRUCT])
+    Ks = rng.integers(K[0], K[1] + 1, size=n_q)
+    qo = np.concatenate([[0], np.cumsum(Ks)]).astype(np.int32)
+    s = rng.normal(scale=score_std, size=int(qo[-1]))
+    text = np.concatenate([np.arange(k) for k in Ks]).astype(np.int32)
+    gold = np.empty(n_q, np.int32)
+    for g in range(n_q):
+        a, b = int(qo[g]), int(qo[g + 1])
+        if b - a >= 2 and rng.random() < dup_text:
+            text[b - 1] = text[a]
+        pick = int(np.argmax(s[a:b] / T0 + rng.gumbel(size=b - a)))
+        gold[g] = text[a + pick]
+    return dict(cand_s=s.astype(np.float32), q_cand_off=qo, cand_text_id=text,
+                q_gold_text_id=gold, T0=float(T0))
+
+
 def stress(kind: str = "wide", seed: int = 606, V: int = 248320, d: int = 2560) -> dict:
     """The binary/enum shape with peaked logits.
 
