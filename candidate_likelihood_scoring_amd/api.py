@@ -141,6 +141,29 @@ def decision_sensitivity(z: torch.Tensor, z_skip: torch.Tensor, seg_off: torch.T
     return out
 
 
+def fit_temperature(cand_s: torch.Tensor, q_cand_off: torch.Tensor, cand_text_id: torch.Tensor,
+                    q_gold_text_id: torch.Tensor, T_min: float = 1e-2, T_max: float = 1e2,
+                    stream=None) -> dict:
+    """Fit the candidate-score temperature on the device (see jet_fit_temperature).
+    Returns T [1], nll [1] and dev_flags [1] (device tensors)."""
+    dev = cand_s.device
+    if cand_s.dtype != torch.float32 or not cand_s.is_contiguous():
+        raise TypeError("cand_s must be a contiguous float32 tensor")
+    for name, t in (("q_cand_off", q_cand_off), ("cand_text_id", cand_text_id),
+                    ("q_gold_text_id", q_gold_text_id)):
+        _check_i32(name, t, dev)
+    out = dict(T=torch.empty(1, dtype=torch.float32, device=dev),
+               nll=torch.empty(1, dtype=torch.float32, device=dev),
+               dev_flags=torch.zeros(1, dtype=torch.int32, device=dev))
+    st = _lib.load().jet_fit_temperature(
+        _ptr(cand_s), _ptr(q_cand_off), int(q_cand_off.numel()) - 1, int(cand_s.numel()),
+        _ptr(cand_text_id), _ptr(q_gold_text_id), float(T_min), float(T_max), _ptr(out["T"]),
+        _ptr(out["nll"]), _ptr(out["dev_flags"]), _stream_handle(stream))
+    if st != 0:
+        raise JetError(st, "jet_fit_temperature")
+    return out
+
+
 def projection_kernel(prob: JetProblem) -> str | None:
     """Name of the projection kernel jet_score launches for this problem (None if invalid)."""
     r = _lib.load().jet_projection_kernel(ctypes.byref(prob))

@@ -237,6 +237,25 @@ JET_API jet_status jet_decision_sensitivity(const float* z, const float* z_skip,
                                             int32_t k, float* d, float* J, int32_t* selected,
                                             int32_t* dev_flags, void* stream);
 
+/* Temperature fitting (gemma-e2b doc, "Output contracts"; nimble, "V2 probability
+ * default": T scales candidate scores once, before the softmax): the T in [T_min, T_max]
+ * minimising the mean over labelled questions of the gold NLL,
+ *   LSE(s/T) - LSE(s/T over the candidates whose text id equals the gold text id).
+ *   cand_s[n_cand] (device): candidate sequence scores s(c), e.g. jet_score's cand_s.
+ *   q_cand_off[n_q+1], cand_text_id[n_cand], q_gold_text_id[n_q] (device): as in
+ *     jet_problem; a question with gold id < 0 or no candidate of the gold text is not
+ *     counted; a malformed question raises JET_FLAG_BAD_OFFSETS and is skipped.
+ *   T_fit[1], nll_fit[1] (device out): the fitted T and the mean gold NLL there (NaN if no
+ *     question is counted); dev_flags[1] optional.
+ * Search: 64 temperatures evenly spaced in log T, narrowed six times around the argmin
+ * (lowest index on ties); one workgroup, bitwise reproducible.  Host checks: JET_E_NULL,
+ * JET_E_SHAPE (n_q < 1 or n_cand < 1), JET_E_TEMP (0 < T_min < T_max, both finite). */
+JET_API jet_status jet_fit_temperature(const float* cand_s, const int32_t* q_cand_off, int32_t n_q,
+                                       int32_t n_cand, const int32_t* cand_text_id,
+                                       const int32_t* q_gold_text_id, float T_min, float T_max,
+                                       float* T_fit, float* nll_fit, int32_t* dev_flags,
+                                       void* stream);
+
 /* Static description of a status code. */
 JET_API const char* jet_status_string(jet_status s);
 

@@ -283,3 +283,17 @@ def test_decision_sensitivity_host_checks(lib):
     assert call(k=3) == -2 and call(k=-1) == -2
     assert call(eps=0.0) == -2 and call(eps=float("nan")) == -2 and call(eps=float("inf")) == -2
     assert call(sel=None) == -1 and call(z=None) == -1
+
+
+def test_fit_temperature_host_checks(lib):
+    """Scalar checks return before anything is enqueued, so they run without a device."""
+    buf = np.zeros(16, np.float32)
+    a = buf.ctypes.data
+
+    def call(n_q=1, n_c=2, lo=0.01, hi=100.0, s=a):
+        return lib.jet_fit_temperature(s, a, n_q, n_c, a, a, lo, hi, a, a, None, None)
+
+    assert call(s=None) == -1
+    assert call(n_q=0) == -2 and call(n_c=0) == -2
+    assert call(lo=0.0) == -5 and call(lo=2.0, hi=1.0) == -5 and call(hi=float("inf")) == -5
+    assert call(lo=float("nan")) == -5

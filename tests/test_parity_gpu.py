@@ -210,6 +210,81 @@ def test_decision_sensitivity_bad_offsets_flag(jet):
     assert sorted(out["selected"].cpu().numpy().tolist()) == [0, 1, 2, 3, 4]
 
 
+def _fit_tolerance(s, qo, text, gold, T):
+    """fp32 error bound of the mean gold NLL at T: each question's two log-sum-exps over K
+    terms carry at most (2K + 8) u of their magnitude (u = 2^-24); 4x that, averaged."""
+    u = 2.0 ** -24
+    tot, n = 0.0, 0
+    for g in range(len(qo) - 1):
+        a = np.asarray(s[qo[g]:qo[g + 1]], np.float64) / T
+        m = np.asarray(text[qo[g]:qo[g + 1]]) == gold[g]
+        if gold[g] < 0 or not m.any():
+            continue
+        l1 = a.max() + np.log(np.exp(a - a.max()).sum())
+        l2 = a[m].max() + np.log(np.exp(a[m] - a[m].max()).sum())
+        tot += (2 * len(a) + 8) * u * (abs(l1) + abs(l2))
+        n += 1
+    return 4 * tot / max(n, 1)
+
+
+def _check_fit(s, qo, text, gold, out, T_min=1e-2, T_max=1e2, what="", ds=0.0):
+    """ds: bound on |GPU scores - oracle scores| when the fit ran on the GPU's own scores;
+    each log-sum-exp is 1-Lipschitz in its arguments, so the NLL moves by <= 2 ds / T."""
+    T_ref, f_ref = jo.fit_temperature(s, qo, text, gold, T_min, T_max)
+    T = float(out["T"][0])
+    nll = float(out["nll"][0])
+    assert int(out["dev_flags"][0]) == 0
+    f_at = jo.mean_gold_nll(s, qo, text, gold, T)[0]
+    tol = _fit_tolerance(s, qo, text, gold, T_ref)
+    shift = 2.0 * ds / min(T, T_ref)
+    assert f_at - f_ref <= 2 * tol + 2 * shift, (what, T, T_ref, f_at - f_ref, tol, shift)
+    assert abs(nll - f_at) <= tol + shift, (what, nll, f_at, tol, shift)
+    log(f"[gpu] fit {what}: T {T:.6f} (oracle {T_ref:.6f}), excess NLL {f_at - f_ref:.2e} "
+        f"(tol {2 * tol:.1e})")
+
+
+@pytest.mark.parametrize("case", ["planted", "closed_form", "partly_unlabelled"])
+def test_fit_temperature(jet, case):
+    """Temperature fitting against the oracle's minimiser, compared by the NLL it attains."""
+    from candidate_likelihood_scoring_amd import api
+
+    if case == "planted":
+        c = wl.labelled_questions(n_q=4096)
+        s, qo, text, gold = c["cand_s"], c["q_cand_off"], c["cand_text_id"], c["q_gold_text_id"]
+    elif case == "closed_form":
+        s = np.array([0.0, -2.0, 0.0, 1.0], np.float32)
+        qo, text, gold = (np.array([0, 2, 4], np.int32), np.array([0, 1, 0, 1], np.int32),
+                          np.array([0, 0], np.int32))
+    else:
+        c = wl.labelled_questions(n_q=300, K=(1, 9), seed=809)
+        s, qo, text = c["cand_s"], c["q_cand_off"], c["cand_text_id"]
+        gold = c["q_gold_text_id"].copy()
+        gold[::7] = -1          # unlabelled
+        gold[3::11] = 999       # no candidate of that text
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    for T_min, T_max in ((1e-2, 1e2), (0.5, 4.0)):
+        out = api.fit_temperature(t(s), t(qo), t(text), t(gold), T_min, T_max)
+        torch.cuda.synchronize()
+        _check_fit(s, qo, text, gold, out, T_min, T_max, f"{case} [{T_min}, {T_max}]")
+
+
+def test_fit_temperature_after_scoring(jet):
+    """The calibration chain: jet_score's candidate scores (on the device) feed the fit."""
+    from candidate_likelihood_scoring_amd import api
+
+    p = wl.make_problem(V=3001, d=64, n_q=60, K=(2, 7), lengths=(1, 3), layout="prefix", seed=81)
+    pdv = jet.to_device(p, "cuda")
+    out = jet.score_problem(pdv)
+    torch.cuda.synchronize()
+    ref = jo.score(p)
+    fit = api.fit_temperature(out["cand_s"], pdv["q_cand_off"], pdv["cand_text_id"],
+                              pdv["q_gold_text_id"])
+    torch.cuda.synchronize()
+    ds = float(np.max(np.abs(out["cand_s"].cpu().numpy().astype(np.float64) - ref["cand_s"])))
+    _check_fit(ref["cand_s"], p["q_cand_off"], p["cand_text_id"], p["q_gold_text_id"], fit,
+               what="after scoring", ds=ds)
+
+
 def test_true_index_and_gold(jet):
     p = wl.make_problem(V=3000, d=64, n_q=10, K=(2, 6), lengths=(1, 3), layout="prefix", seed=31, dups=1)
     K = np.diff(p["q_cand_off"])
