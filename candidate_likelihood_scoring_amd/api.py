@@ -155,10 +155,16 @@ def fit_temperature(cand_s: torch.Tensor, q_cand_off: torch.Tensor, cand_text_id
     out = dict(T=torch.empty(1, dtype=torch.float32, device=dev),
                nll=torch.empty(1, dtype=torch.float32, device=dev),
                dev_flags=torch.zeros(1, dtype=torch.int32, device=dev))
-    st = _lib.load().jet_fit_temperature(
-        _ptr(cand_s), _ptr(q_cand_off), int(q_cand_off.numel()) - 1, int(cand_s.numel()),
+    lib = _lib.load()
+    n_q = int(q_cand_off.numel()) - 1
+    need = int(lib.jet_fit_temperature_workspace_size(max(n_q, 1)))
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    base = (ws.data_ptr() + 255) & ~255
+    st = lib.jet_fit_temperature(
+        _ptr(cand_s), _ptr(q_cand_off), n_q, int(cand_s.numel()),
         _ptr(cand_text_id), _ptr(q_gold_text_id), float(T_min), float(T_max), _ptr(out["T"]),
-        _ptr(out["nll"]), _ptr(out["dev_flags"]), _stream_handle(stream))
+        _ptr(out["nll"]), _ptr(out["dev_flags"]), base, need, _stream_handle(stream))
+    out["_workspace"] = ws  # keeps the workspace alive until the caller drops the result
     if st != 0:
         raise JetError(st, "jet_fit_temperature")
     return out

@@ -172,18 +172,27 @@ jet_status jet_decision_sensitivity(const float* z, const float* z_skip, const i
   return e == hipSuccess ? JET_OK : JET_E_HIP;
 }
 
+size_t jet_fit_temperature_workspace_size(int32_t n_q) {
+  return n_q < 1 ? 0 : fit_temperature_workspace(n_q);
+}
+
 jet_status jet_fit_temperature(const float* cand_s, const int32_t* q_cand_off, int32_t n_q,
                                int32_t n_cand, const int32_t* cand_text_id,
                                const int32_t* q_gold_text_id, float T_min, float T_max,
-                               float* T_fit, float* nll_fit, int32_t* dev_flags, void* stream) {
+                               float* T_fit, float* nll_fit, int32_t* dev_flags, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (!cand_s || !q_cand_off || !cand_text_id || !q_gold_text_id || !T_fit || !nll_fit)
     return JET_E_NULL;
   if (n_q < 1 || n_cand < 1) return JET_E_SHAPE;
   if (!std::isfinite(T_min) || !std::isfinite(T_max) || !(T_min > 0.f) || !(T_max > T_min))
     return JET_E_TEMP;
+  if (!workspace || workspace_bytes < fit_temperature_workspace(n_q) ||
+      ((uintptr_t)workspace & 255u))
+    return JET_E_WORKSPACE;
   const hipError_t e = launch_fit_temperature(cand_s, q_cand_off, n_q, n_cand, cand_text_id,
                                               q_gold_text_id, T_min, T_max, T_fit, nll_fit,
-                                              dev_flags, static_cast<hipStream_t>(stream));
+                                              dev_flags, static_cast<char*>(workspace),
+                                              static_cast<hipStream_t>(stream));
   return e == hipSuccess ? JET_OK : JET_E_HIP;
 }
 

@@ -95,9 +95,10 @@ hipError_t launch_project_tiled(const ScoreArgs& a);
 int tiled_bk(bool hilo);
 const char* tiled_kernel_name(bool hilo);
 int sensitivity_max_layers();
+size_t fit_temperature_workspace(int n_q);
 hipError_t launch_fit_temperature(const float* s, const int* q_cand_off, int n_q, int n_cand,
                                   const int* text, const int* gold, float T_min, float T_max,
-                                  float* T_out, float* nll_out, int32_t* flags,
+                                  float* T_out, float* nll_out, int32_t* flags, char* ws,
                                   hipStream_t stream);
 hipError_t launch_sensitivity(const float* z, const float* z_skip, const int* seg_off,
                               int n_inputs, int n_values, int n_layers, float eps, int k,

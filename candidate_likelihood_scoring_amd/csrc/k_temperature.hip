@@ -3,120 +3,151 @@
 // probability default": T scales candidate scores once, before the softmax).  The gold NLL
 // is the decision's: LSE(s/T) - LSE(s/T over the candidates of the gold text).
 //
-// One workgroup of 16 waves.  Each round evaluates 64 temperatures spaced evenly in log T
-// over the current interval, one per lane: wave w takes questions w, w + 16, ... and every
-// lane accumulates its temperature's NLL over them in question order; the 16 wave partials
-// are added in wave order.  Wave 0 takes the argmin (lowest index on ties, NaN last) and
-// narrows the interval to the two neighbouring grid points.  Six rounds shrink the spacing
-// from ln(T_max / T_min) / 63 by (2/63)^5, below fp32 resolution of ln T.  Questions with
-// no label (gold id < 0) or no candidate of the gold text are not counted.
+// Each round evaluates 64 temperatures spaced evenly in log T over the current interval,
+// one per lane.  k_fit_partial: wave w of the launch takes questions w, w + W, ... (W waves
+// in all) and every lane accumulates its temperature's NLL over them in question order; a
+// workgroup adds its 4 waves in order into one partial per temperature.  k_fit_reduce (one
+// wave): adds the workgroups' partials in order, takes the argmin (lowest index on ties, NaN
+// last) and narrows the interval to the two neighbouring grid points, kept in the
+// workspace for the next round.  Six rounds shrink the spacing from ln(T_max / T_min) / 63
+// by (2/63)^5, below fp32 resolution of ln T.  Questions with no label (gold id < 0) or no
+// candidate of the gold text are not counted.  The result is bitwise reproducible.
+#include <algorithm>
+
 #include "jet_internal.h"
 
 namespace jet {
 namespace {
 
-constexpr int kGrid = 64, kRounds = 6, kWaves = 16;
+constexpr int kGrid = 64, kRounds = 6, kMaxBlocks = 256;
 
-__global__ __launch_bounds__(1024) void k_fit_temperature(
+__device__ inline float grid_point(float lo, float hi, int g) {
+  return lo + (hi - lo) * (float)g / (float)(kGrid - 1);
+}
+
+__global__ __launch_bounds__(256) void k_fit_partial(
     const float* __restrict__ s, const int* __restrict__ q_cand_off, int n_q, int n_cand,
-    const int* __restrict__ text, const int* __restrict__ gold, float lo0, float hi0,
-    float* __restrict__ T_out, float* __restrict__ nll_out, int32_t* __restrict__ flags) {
-  __shared__ float part[kWaves][kGrid];
-  __shared__ int cnt[kWaves];
-  __shared__ float iv[2];
-  const int tid = threadIdx.x, g = tid & 63, wv = tid >> 6;
-  if (tid == 0) {
-    iv[0] = lo0;
-    iv[1] = hi0;
-  }
-  __syncthreads();
+    const int* __restrict__ text, const int* __restrict__ gold, const float* __restrict__ iv,
+    float lo0, float hi0, float* __restrict__ part, int* __restrict__ cnt,
+    int32_t* __restrict__ flags) {
+  __shared__ float wpart[4][kGrid];
+  __shared__ int wcnt[4];
+  const int g = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const float lo = iv ? iv[0] : lo0, hi = iv ? iv[1] : hi0;
+  const float inv_t = expf(-grid_point(lo, hi, g));
+  const int W = gridDim.x * 4;
+  float acc = 0.f;
+  int used = 0;
   bool bad = false;
-  for (int round = 0; round < kRounds; ++round) {
-    const float lo = iv[0], hi = iv[1];
-    const float u = lo + (hi - lo) * (float)g / (float)(kGrid - 1);
-    const float inv_t = expf(-u);
-    float acc = 0.f;
-    int used = 0;
-    for (int q = wv; q < n_q; q += kWaves) {
-      const int c0 = q_cand_off[q], c1 = q_cand_off[q + 1];
-      if (c0 < 0 || c1 > n_cand || c1 <= c0) {
-        bad = true;
-        continue;
-      }
-      const int gt = gold[q];
-      if (gt < 0) continue;
-      float M = -INFINITY, Mg = -INFINITY;
-      for (int c = c0; c < c1; ++c) {
-        const float a = s[c] * inv_t;
-        M = fmaxf(M, a);
-        if (text[c] == gt) Mg = fmaxf(Mg, a);
-      }
-      if (Mg == -INFINITY) continue;  // no candidate of the gold text
-      float Z = 0.f, Zg = 0.f;
-      for (int c = c0; c < c1; ++c) {
-        const float a = s[c] * inv_t;
-        Z += expf(a - M);
-        if (text[c] == gt) Zg += expf(a - Mg);
-      }
-      acc += (M + logf(Z)) - (Mg + logf(Zg));
-      ++used;
+  for (int q = blockIdx.x * 4 + wv; q < n_q; q += W) {
+    const int c0 = q_cand_off[q], c1 = q_cand_off[q + 1];
+    if (c0 < 0 || c1 > n_cand || c1 <= c0) {
+      bad = true;
+      continue;
     }
-    part[wv][g] = acc;
-    if (g == 0) cnt[wv] = used;
-    __syncthreads();
-    if (wv == 0) {
-      float tot = 0.f;
-      int n = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        tot += part[w][g];
-        n += cnt[w];
-      }
-      const float f = n ? tot / (float)n : __builtin_nanf("");
-      float bv = f != f ? INFINITY : f;
-      int bi = g;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov < bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (g == bi) {
-        if (round + 1 < kRounds) {
-          const float step = (hi - lo) / (float)(kGrid - 1);
-          iv[0] = bi > 0 ? u - step : u;
-          iv[1] = bi < kGrid - 1 ? u + step : u;
-        } else {
-          T_out[0] = n ? expf(u) : __builtin_nanf("");
-          nll_out[0] = f;
-        }
-      }
+    const int gt = gold[q];
+    if (gt < 0) continue;
+    float M = -INFINITY, Mg = -INFINITY;
+    for (int c = c0; c < c1; ++c) {
+      const float a = s[c] * inv_t;
+      M = fmaxf(M, a);
+      if (text[c] == gt) Mg = fmaxf(Mg, a);
     }
-    __syncthreads();
+    if (Mg == -INFINITY) continue;  // no candidate of the gold text
+    float Z = 0.f, Zg = 0.f;
+    for (int c = c0; c < c1; ++c) {
+      const float a = s[c] * inv_t;
+      Z += expf(a - M);
+      if (text[c] == gt) Zg += expf(a - Mg);
+    }
+    acc += (M + logf(Z)) - (Mg + logf(Zg));
+    ++used;
   }
   if (bad && g == 0 && flags) flag_or(flags, JET_FLAG_BAD_OFFSETS);
+  wpart[wv][g] = acc;
+  if (g == 0) wcnt[wv] = used;
+  __syncthreads();
+  if (wv == 0) {
+    part[(size_t)blockIdx.x * kGrid + g] = ((wpart[0][g] + wpart[1][g]) + wpart[2][g]) + wpart[3][g];
+    if (g == 0) cnt[blockIdx.x] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+  }
+}
+
+__global__ __launch_bounds__(64) void k_fit_reduce(const float* __restrict__ part,
+                                                   const int* __restrict__ cnt, int nb,
+                                                   float* __restrict__ iv, float lo0, float hi0,
+                                                   int first, int last, float* __restrict__ T_out,
+                                                   float* __restrict__ nll_out) {
+  const int g = threadIdx.x;
+  const float lo = first ? lo0 : iv[0], hi = first ? hi0 : iv[1];
+  const float u = grid_point(lo, hi, g);
+  float tot = 0.f;
+  int n = 0;
+#pragma unroll 8
+  for (int b = 0; b < nb; ++b) {
+    tot += part[(size_t)b * kGrid + g];
+    n += cnt[b];
+  }
+  const float f = n ? tot / (float)n : __builtin_nanf("");
+  float bv = f != f ? INFINITY : f;
+  int bi = g;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ov < bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (g == bi) {  // every lane has read the interval above: the wave runs in lockstep
+    if (!last) {
+      const float step = (hi - lo) / (float)(kGrid - 1);
+      iv[0] = bi > 0 ? u - step : u;
+      iv[1] = bi < kGrid - 1 ? u + step : u;
+    } else {
+      T_out[0] = n ? expf(u) : __builtin_nanf("");
+      nll_out[0] = f;
+    }
+  }
 }
 
 __global__ void k_temp_clear(int32_t* __restrict__ flags) {
   if (threadIdx.x == 0) flags[0] = 0;
 }
 
+int fit_blocks(int n_q) { return std::max(1, std::min(kMaxBlocks, (n_q + 31) / 32)); }
+
 }  // namespace
+
+size_t fit_temperature_workspace(int n_q) {
+  const size_t nb = (size_t)fit_blocks(n_q);
+  return (nb * kGrid * 4 + 255) / 256 * 256 + (nb * 4 + 255) / 256 * 256 + 256;
+}
 
 hipError_t launch_fit_temperature(const float* s, const int* q_cand_off, int n_q, int n_cand,
                                   const int* text, const int* gold, float T_min, float T_max,
-                                  float* T_out, float* nll_out, int32_t* flags,
+                                  float* T_out, float* nll_out, int32_t* flags, char* ws,
                                   hipStream_t stream) {
   hipError_t e;
+  const int nb = fit_blocks(n_q);
+  float* part = reinterpret_cast<float*>(ws);
+  int* cnt = reinterpret_cast<int*>(ws + ((size_t)nb * kGrid * 4 + 255) / 256 * 256);
+  float* iv = reinterpret_cast<float*>(reinterpret_cast<char*>(cnt) + ((size_t)nb * 4 + 255) / 256 * 256);
   if (flags) {
     hipLaunchKernelGGL(k_temp_clear, dim3(1), dim3(64), 0, stream, flags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_fit_temperature, dim3(1), dim3(1024), 0, stream, s, q_cand_off, n_q, n_cand,
-                     text, gold, logf(T_min), logf(T_max), T_out, nll_out, flags);
-  return hipGetLastError();
+  const float lo0 = logf(T_min), hi0 = logf(T_max);
+  for (int round = 0; round < kRounds; ++round) {
+    hipLaunchKernelGGL(k_fit_partial, dim3(nb), dim3(256), 0, stream, s, q_cand_off, n_q, n_cand,
+                       text, gold, round ? iv : nullptr, lo0, hi0, part, cnt, flags);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fit_reduce, dim3(1), dim3(64), 0, stream, part, cnt, nb, iv, lo0, hi0,
+                       round == 0 ? 1 : 0, round + 1 == kRounds ? 1 : 0, T_out, nll_out);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace jet

@@ -247,14 +247,17 @@ JET_API jet_status jet_decision_sensitivity(const float* z, const float* z_skip,
  *     counted; a malformed question raises JET_FLAG_BAD_OFFSETS and is skipped.
  *   T_fit[1], nll_fit[1] (device out): the fitted T and the mean gold NLL there (NaN if no
  *     question is counted); dev_flags[1] optional.
+ *   workspace: device memory of at least jet_fit_temperature_workspace_size(n_q) bytes,
+ *     256-byte aligned, not shared with a concurrent call.
  * Search: 64 temperatures evenly spaced in log T, narrowed six times around the argmin
- * (lowest index on ties); one workgroup, bitwise reproducible.  Host checks: JET_E_NULL,
- * JET_E_SHAPE (n_q < 1 or n_cand < 1), JET_E_TEMP (0 < T_min < T_max, both finite). */
+ * (lowest index on ties); bitwise reproducible.  Host checks: JET_E_NULL, JET_E_SHAPE
+ * (n_q < 1 or n_cand < 1), JET_E_TEMP (0 < T_min < T_max, both finite), JET_E_WORKSPACE. */
+JET_API size_t jet_fit_temperature_workspace_size(int32_t n_q);
 JET_API jet_status jet_fit_temperature(const float* cand_s, const int32_t* q_cand_off, int32_t n_q,
                                        int32_t n_cand, const int32_t* cand_text_id,
                                        const int32_t* q_gold_text_id, float T_min, float T_max,
                                        float* T_fit, float* nll_fit, int32_t* dev_flags,
-                                       void* stream);
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 JET_API const char* jet_status_string(jet_status s);

@@ -290,10 +290,16 @@ def test_fit_temperature_host_checks(lib):
     buf = np.zeros(16, np.float32)
     a = buf.ctypes.data
 
-    def call(n_q=1, n_c=2, lo=0.01, hi=100.0, s=a):
-        return lib.jet_fit_temperature(s, a, n_q, n_c, a, a, lo, hi, a, a, None, None)
+    ws = np.zeros(1 << 20, np.uint8)
+    w = (ws.ctypes.data + 255) & ~255
+
+    def call(n_q=1, n_c=2, lo=0.01, hi=100.0, s=a, wsp=w, wsb=1 << 19):
+        return lib.jet_fit_temperature(s, a, n_q, n_c, a, a, lo, hi, a, a, None, wsp, wsb, None)
 
     assert call(s=None) == -1
     assert call(n_q=0) == -2 and call(n_c=0) == -2
     assert call(lo=0.0) == -5 and call(lo=2.0, hi=1.0) == -5 and call(hi=float("inf")) == -5
     assert call(lo=float("nan")) == -5
+    assert call(wsp=None) == -6 and call(wsp=w + 1) == -6 and call(wsb=16) == -6
+    assert lib.jet_fit_temperature_workspace_size(0) == 0
+    assert 0 < lib.jet_fit_temperature_workspace_size(10) <= lib.jet_fit_temperature_workspace_size(10 ** 6)
