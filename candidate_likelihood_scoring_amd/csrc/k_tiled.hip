@@ -88,17 +88,21 @@ __device__ __forceinline__ void vm_wait() {
 
 // Workgroup -> (row tile, vocabulary split).  Launch index L runs on XCD L % 8, and each XCD
 // runs about 32 workgroups at a time; with remap (launch size a multiple of 256) those 32
-// form an sr x ss block of (row tile, split) pairs sharing tiles in that XCD's L2.  Indices
-// past the last real block decode to row tiles >= n_rtiles (padding).
-__device__ __forceinline__ void tile_assign(int sr, int ss, int splits, int remap, int& rt,
-                                            int& split) {
+// form an sr x ss block of (row tile, split) pairs sharing tiles in that XCD's L2.  Blocks
+// are numbered row group first: the eight XCDs, which start blocks together, work on the
+// same vocabulary splits for different row groups, so a head tile fetched from HBM by one
+// XCD is found by the others in the last-level cache.  Blocks past the last real one decode
+// to row tiles >= n_rtiles or splits >= splits (padding).
+__device__ __forceinline__ void tile_assign(int n_rtiles, int sr, int ss, int splits, int remap,
+                                            int& rt, int& split) {
   int P = blockIdx.x;
   if (remap) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     P = (((slot >> 5) << 3) + xcd) * 32 + (slot & 31);
   }
   const int j = P / (sr * ss), w = P % (sr * ss);
-  const int jr = j / (splits / ss), js = j % (splits / ss);
+  const int n_rg = (n_rtiles + sr - 1) / sr;  // row groups; the last may hold padding
+  const int jr = j % n_rg, js = j / n_rg;
   rt = jr * sr + w / ss;
   split = js * ss + w % ss;
 }
@@ -274,8 +278,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   const int wm = wid & 1, wn = wid >> 1;
   const int n = lane & 31, h = lane >> 5;
   int rt, split;
-  tile_assign(sr, ss, splits, remap, rt, split);
-  if (rt >= n_rtiles) return;  // padding workgroup of the XCD-aware launch (uniform)
+  tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
+  if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
   const int row_nom = rt * TBN;                    // first row this tile reports
   const int row0 = min(row_nom, n_rows - TBN);     // rows loaded: [row0, row0 + 256), all valid
   const int t0 = (int)((long long)split * n_vtiles / splits);
@@ -493,15 +497,27 @@ template <> struct DtlShape<1> {
 template <> struct DtlShape<2> { static constexpr int BK = 32, NBUF = 3, PF = JET_DTL_PF2; };
 
 // loads issued in sub-step kk of a stage: as many as the slots left by its fragment reads
-// allow, earliest sub-steps first
+// allow, but at most JET_DTL_MAXD (or the even share, if that is larger), earliest sub-steps
+// first.  Six per sub-step (6, 6, 4, 0 for the bf16 stage) measured faster than packing
+// them into the first two sub-steps (8, 8, 0, 0), which stalls issue on the memory path,
+// and than an even spread (4, 4, 4, 4), which leaves the last loads too little lead.
+#ifndef JET_DTL_MAXD
+#define JET_DTL_MAXD 6
+#endif
+constexpr int dtl_cap(int k, int KK, int ndma, int slots, int nrd, int nrd_last) {
+  const int c = slots - (k + 1 < KK ? nrd : nrd_last);
+  const int even = (ndma + KK - 1) / KK;
+  const int m = JET_DTL_MAXD > even ? JET_DTL_MAXD : even;
+  return c < m ? c : m;
+}
 constexpr int dtl_nd(int kk, int KK, int ndma, int slots, int nrd, int nrd_last) {
   int before = 0;
   for (int k = 0; k < kk; ++k) {
-    const int cap = slots - (k + 1 < KK ? nrd : nrd_last);
+    const int cap = dtl_cap(k, KK, ndma, slots, nrd, nrd_last);
     const int left = ndma - before;
     before += cap < left ? cap : left;
   }
-  const int cap = slots - (kk + 1 < KK ? nrd : nrd_last);
+  const int cap = dtl_cap(kk, KK, ndma, slots, nrd, nrd_last);
   const int left = ndma - before;
   return cap < left ? cap : left;
 }
@@ -544,8 +560,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
   const int wm = wid & 1, wn = wid >> 1;
   const int n = lane & 31, h = lane >> 5;
   int rt, split;
-  tile_assign(sr, ss, splits, remap, rt, split);
-  if (rt >= n_rtiles) return;  // padding workgroup of the XCD-aware launch (uniform)
+  tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
+  if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
   const int row_nom = rt * TBN;
   const int row0 = min(row_nom, n_rows - TBN);
   const int t0 = (int)((long long)split * n_vtiles / splits);
@@ -622,6 +638,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
     const int b_nx = bc + 1 == NBUF ? 0 : bc + 1;       /* stage g + 1 */                    \
     const int b_ld = bc == 0 ? NBUF - 1 : bc - 1;       /* stage g + NBUF - 1 */             \
     __builtin_amdgcn_sched_barrier(0);                                                       \
+    if (!PF) JET_FRAGS(0, bc * BUFSZ, 0);                                                    \
     JET_CURSOR();                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                      \
@@ -649,10 +666,6 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
     vm_wait<(D - 1 - PF) * NDMA>();                                                          \
     __syncthreads();                                                                         \
     bc = b_nx;                                                                               \
-    if (!PF) {                                                                               \
-      JET_FRAGS(0, bc * BUFSZ, 0);                                                           \
-      __builtin_amdgcn_sched_barrier(0);                                                     \
-    }                                                                                        \
   }
 
   // prologue: stages 0 .. D - 1 into buffers 0 .. D - 1; stages 0 (and 1 with PF) complete
@@ -664,7 +677,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
   }
   vm_wait<(D - 1 - PF) * NDMA>();
   __syncthreads();
-  JET_FRAGS(0, 0, 0);
+  if (PF) JET_FRAGS(0, 0, 0);
 
   for (int vt = t0; vt < t1; ++vt) {
     f32x16 acc[4][4];
