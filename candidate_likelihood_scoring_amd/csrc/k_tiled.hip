@@ -177,11 +177,13 @@ __device__ __forceinline__ void tile_epilogue(
         for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
       // gm is -inf only when this half tile is entirely dropped and nothing came before
       const float mb = gm == -INFINITY ? 0.f : gm * kLog2e;
-      float sum = 0.f;
+      // four partial sums, so that consecutive exponentials do not wait on one another
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
+        for (int i = 0; i < 16; ++i) ps[i & 3] += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
+      const float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
       s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + sum;
       m_run[nt] = gm;
     }
@@ -387,8 +389,9 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   // by memory slot i: first the fragment reads of the next sub-step (set (kk + 1) & 1; for
   // the last sub-step those of the next stage, with three buffers) with this sub-step's
   // share of the LDS stores spread evenly among them, then its share of the loads.
-  // SLOAD / SSTORE: the register sets being loaded / stored.
-#define JET_STAGE(SLOAD, SSTORE)                                                             \
+  // SLOAD / SSTORE: the register sets being loaded / stored.  FIRST: the first stage of a
+  // vocabulary tile, whose first MFMA per accumulator block starts from zero.
+#define JET_STAGE(SLOAD, SSTORE, FIRST)                                                      \
   {                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     JET_CURSOR();                                                                            \
@@ -400,7 +403,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       _Pragma("unroll") for (int i = 0; i < 16 * NP; ++i) {                                  \
         acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(            \
             fa[kk & 1][i / (4 * NP)], fb[kk & 1][i % NP][(i / NP) % 4],                      \
-            acc[i / (4 * NP)][(i / NP) % 4], 0, 0, 0);                                       \
+            (FIRST) && kk == 0 && i % NP == 0 ? f32x16{} : acc[i / (4 * NP)][(i / NP) % 4], 0, \
+            0, 0);                                                                           \
         if (i < nls) {                                                                       \
           const int nwb = (i * nu) / nls;                                                    \
           if (((i + 1) * nu) / nls > nwb) {                                                  \
@@ -446,13 +450,11 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 
   for (int vt = t0; vt < t1; ++vt) {
     f32x16 acc[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
-    for (int kb = 0; kb < nk; kb += 2) {
-      JET_STAGE(NBUF & 1, (NBUF - 1) & 1);        // stage g even
-      JET_STAGE((NBUF - 1) & 1, NBUF & 1);        // stage g odd
+    JET_STAGE(NBUF & 1, (NBUF - 1) & 1, true);    // stage g even, first of the tile
+    JET_STAGE((NBUF - 1) & 1, NBUF & 1, false);   // stage g odd
+    for (int kb = 2; kb < nk; kb += 2) {
+      JET_STAGE(NBUF & 1, (NBUF - 1) & 1, false);
+      JET_STAGE((NBUF - 1) & 1, NBUF & 1, false);
     }
 
     tile_epilogue<false>(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
     _Pragma("unroll") for (int jr_ = 0; jr_ < NRD; ++jr_) JET_FRAG1(F, BOFF, KK_, jr_);      \
   }
   int bc = 0;  // buffer index of stage g
-#define JET_DSTAGE()                                                                         \
+#define JET_DSTAGE(FIRST)                                                                    \
   {                                                                                          \
     const int b_nx = bc + 1 == NBUF ? 0 : bc + 1;       /* stage g + 1 */                    \
     const int b_ld = bc == 0 ? NBUF - 1 : bc - 1;       /* stage g + NBUF - 1 */             \
@@ -649,7 +651,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
       _Pragma("unroll") for (int i = 0; i < SLOTS; ++i) {                                    \
         acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(            \
             fa[kk & 1][i / (4 * NP)], fb[kk & 1][i % NP][(i / NP) % 4],                      \
-            acc[i / (4 * NP)][(i / NP) % 4], 0, 0, 0);                                       \
+            (FIRST) && kk == 0 && i % NP == 0 ? f32x16{} : acc[i / (4 * NP)][(i / NP) % 4], 0, \
+            0, 0);                                                                           \
         if (i < nls) {                                                                       \
           const int ndb = nd ? (i * nd) / nls : 0;                                           \
           if (nd && ((i + 1) * nd) / nls > ndb) {                                            \
@@ -681,13 +684,13 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
 
   for (int vt = t0; vt < t1; ++vt) {
     f32x16 acc[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
-    for (int kb = 0; kb < nk; kb += 2) {
-      JET_DSTAGE();
-      JET_DSTAGE();
+    // the tile's first stage is peeled: the first MFMA of every accumulator block starts
+    // from an inline-constant zero, so the 256 accumulators are never cleared
+    JET_DSTAGE(true);
+    JET_DSTAGE(false);
+    for (int kb = 2; kb < nk; kb += 2) {
+      JET_DSTAGE(false);
+      JET_DSTAGE(false);
     }
     {
       float m_run[4], s_run[4];
