@@ -126,6 +126,9 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   off += al256(rows * 4);
   pl->off_bcount = off;
   off += al256((size_t)(pl->n_buckets + 1) * 4);
+  pl->n_btiles = std::max(1LL, (pl->n_buckets + kBucketScanTile - 1) / kBucketScanTile);
+  pl->off_btile = off;
+  off += al256((size_t)pl->n_btiles * 4);
   pl->off_boff = off;
   off += al256((size_t)(pl->n_buckets + 1) * 4);
   pl->off_btok = off;
@@ -266,6 +269,7 @@ jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o, void* 
   if ((st = check_outputs(p, o)) != JET_OK) return st;
   Plan pl;
   make_plan(p, true, &pl);
+  if (pl.n_btiles > kBucketMaxTiles) return JET_E_SHAPE;
   if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u)) return JET_E_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   ScoreArgs a;

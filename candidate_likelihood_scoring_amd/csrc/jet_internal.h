@@ -58,6 +58,10 @@ __device__ inline void flag_or(int32_t* flags, uint32_t bit) {
 // ------------------------------------------------------------------------------------
 enum Variant { VAR_SMALL_BF16 = 0, VAR_SMALL_F32 = 1, VAR_TILED_BF16 = 2 };
 
+// buckets per tile of the grid-wide bucket scan, and the most tiles its one-workgroup
+// second level takes (so at most 2^26 buckets)
+constexpr long long kBucketScanTile = 8192, kBucketMaxTiles = 8192;
+
 struct Plan {
   int variant;
   bool hilo;          // fp32 H split into bf16 hi + lo
@@ -69,9 +73,10 @@ struct Plan {
   int grid_x;         // projection workgroups along the vocabulary
   int n_parts;        // (m, s) partials per row
   long long n_buckets;
+  long long n_btiles; // bucket-count tiles of the grid-wide scan (kBucketScanTile buckets each)
   // workspace byte offsets
-  size_t off_hhi, off_hlo, off_ztgt, off_part, off_lse, off_bcount, off_boff, off_btok, off_bpos,
-      off_flags, total;
+  size_t off_hhi, off_hlo, off_ztgt, off_part, off_lse, off_bcount, off_btile, off_boff, off_btok,
+      off_bpos, off_flags, total;
 };
 
 bool make_plan(const jet_problem* p, bool want_lse_buffer, Plan* plan);

@@ -27,83 +27,135 @@ __device__ inline void split_range(const float* __restrict__ H, long long n, uin
   }
 }
 
-__device__ inline int ld_agent(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Counting sort over many buckets (more than fit in LDS), as a chain of grid-wide launches:
+// clear the counts, count (each token takes its slot in its bucket with an atomic add),
+// sum the counts per tile of kScanTile buckets, scan the tile sums (one workgroup), scan
+// inside each tile from its tile offset, scatter.  Every step is exact integer work, so the
+// offsets do not depend on scheduling; only the order of tokens inside a bucket does, which
+// nothing depends on.
+constexpr int kScanThreads = 1024, kScanPer = 8, kScanTile = kScanThreads * kScanPer;
+
+__global__ __launch_bounds__(256) void k_bk_clear(int* __restrict__ b_count, long long n,
+                                                  int32_t* __restrict__ flags) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    b_count[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && flags) flags[0] = 0;
 }
 
-__global__ __launch_bounds__(kPrepThreads) void k_prep(
-    const float* __restrict__ H, long long n_h, uint16_t* __restrict__ hhi,
-    uint16_t* __restrict__ hlo, int n_split_blocks, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, int n_tok, int n_rows, int V, int row_tile, int vgroup,
-    int n_groups, long long n_buckets, int* __restrict__ b_count, int* __restrict__ b_off,
-    int* __restrict__ b_tok, int* __restrict__ b_pos, float* __restrict__ z_tgt,
-    int32_t* __restrict__ flags) {
-  const int tid = threadIdx.x;
-  if ((int)blockIdx.x < n_split_blocks) {
-    split_range(H, n_h, hhi, hlo, (long long)blockIdx.x * kPrepThreads + tid,
-                (long long)n_split_blocks * kPrepThreads);
+__global__ __launch_bounds__(256) void k_bk_count(
+    const int* __restrict__ tok_row, const int* __restrict__ tok_target, int n_tok, int n_rows,
+    int V, int row_tile, int vgroup, int n_groups, int* __restrict__ b_count,
+    int* __restrict__ b_pos, float* __restrict__ z_tgt, int32_t* __restrict__ flags) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= n_tok) return;
+  z_tgt[k] = __builtin_nanf("");
+  const int r = tok_row ? tok_row[k] : k;
+  const int y = tok_target[k];
+  uint32_t bad = 0u;
+  if (r < 0 || r >= n_rows) bad |= JET_FLAG_BAD_ROW;
+  if (y < 0 || y >= V) bad |= JET_FLAG_BAD_TARGET;
+  if (bad) {
+    flag_or(flags, bad);
+    b_pos[k] = -1;
     return;
   }
-  __shared__ int sh[kPrepThreads];
-  __shared__ uint32_t sflags;
-  if (tid == 0) sflags = 0u;
-  for (long long i = tid; i <= n_buckets; i += kPrepThreads) b_count[i] = 0;
-  __threadfence();
+  b_pos[k] = atomicAdd(&b_count[(long long)(r / row_tile) * n_groups + y / vgroup], 1);
+}
+
+// block-wide exclusive scan of one value per thread (1024 threads); returns the exclusive
+// prefix and writes the block total to *total
+__device__ inline int block_exscan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[w] = x;
   __syncthreads();
-  uint32_t my_flags = 0u;
-  for (int k = tid; k < n_tok; k += kPrepThreads) {
-    z_tgt[k] = __builtin_nanf("");
-    const int r = tok_row ? tok_row[k] : k;
-    const int y = tok_target[k];
-    bool ok = true;
-    if (r < 0 || r >= n_rows) {
-      ok = false;
-      my_flags |= JET_FLAG_BAD_ROW;
+  if (tid < 64) {
+    int t = tid < kScanThreads / 64 ? sh[tid] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(t, off);
+      if (lane >= off) t += y;
     }
-    if (y < 0 || y >= V) {
-      ok = false;
-      my_flags |= JET_FLAG_BAD_TARGET;
+    if (tid < kScanThreads / 64) sh[64 + tid] = t;
+  }
+  __syncthreads();
+  const int before = w ? sh[64 + w - 1] : 0;
+  *total = sh[64 + kScanThreads / 64 - 1];
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_bk_tile_sums(const int* __restrict__ b_count,
+                                                               long long n, int* __restrict__ tile_sum) {
+  __shared__ int sh[128];
+  const long long base = (long long)blockIdx.x * kScanTile + (long long)threadIdx.x * kScanPer;
+  int v = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j)
+    if (base + j < n) v += b_count[base + j];
+  int total;
+  block_exscan(v, sh, &total);
+  if (threadIdx.x == 0) tile_sum[blockIdx.x] = total;
+}
+
+// exclusive scan of up to kScanTile tile sums, in place (one workgroup)
+__global__ __launch_bounds__(kScanThreads) void k_bk_scan_tiles(int* __restrict__ tile_sum,
+                                                                int n_tiles) {
+  __shared__ int sh[128];
+  const int base = threadIdx.x * kScanPer;
+  int v[kScanPer], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    v[j] = base + j < n_tiles ? tile_sum[base + j] : 0;
+    sum += v[j];
+  }
+  int total;
+  int run = block_exscan(sum, sh, &total);
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j)
+    if (base + j < n_tiles) {
+      tile_sum[base + j] = run;
+      run += v[j];
     }
-    int pos = -1;
-    if (ok) {
-      const long long key = (long long)(r / row_tile) * n_groups + y / vgroup;
-      pos = atomicAdd(&b_count[key], 1);
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_bk_offsets(const int* __restrict__ b_count,
+                                                             long long n_buckets,
+                                                             const int* __restrict__ tile_off,
+                                                             int* __restrict__ b_off) {
+  __shared__ int sh[128];
+  const long long base = (long long)blockIdx.x * kScanTile + (long long)threadIdx.x * kScanPer;
+  int v[kScanPer], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    v[j] = base + j < n_buckets ? b_count[base + j] : 0;
+    sum += v[j];
+  }
+  int total;
+  int run = tile_off[blockIdx.x] + block_exscan(sum, sh, &total);
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j)
+    if (base + j < n_buckets) {
+      b_off[base + j] = run;
+      run += v[j];
     }
-    b_pos[k] = pos;
-  }
-  if (my_flags) atomicOr(&sflags, my_flags);
-  __threadfence();
-  __syncthreads();
-  // exclusive scan of the counts
-  const long long per = (n_buckets + kPrepThreads - 1) / kPrepThreads;
-  const long long lo = (long long)tid * per;
-  const long long hi = lo + per < n_buckets ? lo + per : n_buckets;
-  int sum = 0;
-  for (long long i = lo; i < hi; ++i) sum += ld_agent(&b_count[i]);
-  sh[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kPrepThreads; off <<= 1) {
-    const int v = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += v;
-    __syncthreads();
-  }
-  int run = tid ? sh[tid - 1] : 0;
-  for (long long i = lo; i < hi; ++i) {
-    b_off[i] = run;
-    run += ld_agent(&b_count[i]);
-  }
-  if (tid == kPrepThreads - 1) b_off[n_buckets] = sh[kPrepThreads - 1];
-  __threadfence();
-  __syncthreads();
-  for (int k = tid; k < n_tok; k += kPrepThreads) {
-    const int pos = b_pos[k];
-    if (pos < 0) continue;
-    const int r = tok_row ? tok_row[k] : k;
-    const long long key = (long long)(r / row_tile) * n_groups + tok_target[k] / vgroup;
-    b_tok[ld_agent(&b_off[key]) + pos] = k;
-  }
-  if (tid == 0 && flags) flags[0] = (int32_t)sflags;
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) b_off[n_buckets] = tile_off[blockIdx.x] + total;
+}
+
+__global__ __launch_bounds__(256) void k_bk_scatter(
+    const int* __restrict__ tok_row, const int* __restrict__ tok_target, int n_tok,
+    int row_tile, int vgroup, int n_groups, const int* __restrict__ b_off,
+    const int* __restrict__ b_pos, int* __restrict__ b_tok) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= n_tok) return;
+  const int pos = b_pos[k];
+  if (pos < 0) return;
+  const int r = tok_row ? tok_row[k] : k;
+  b_tok[b_off[(long long)(r / row_tile) * n_groups + tok_target[k] / vgroup] + pos] = k;
 }
 
 // Counting sort in LDS when the buckets fit (one workgroup): counts, exclusive scan and
@@ -187,26 +239,43 @@ hipError_t launch_prep(const ScoreArgs& a) {
   const jet_problem* p = a.p;
   const Plan& pl = *a.plan;
   char* ws = a.ws;
-  const long long n_h = (long long)p->n_rows * p->d;
-  const bool need_split = pl.hilo && !pl.stream;
-  if (!need_split && pl.n_buckets <= kLdsBuckets) {
+  if (pl.hilo && !pl.stream) {
+    const hipError_t e = launch_split(static_cast<const float*>(p->H), (long long)p->n_rows * p->d,
+                                      reinterpret_cast<uint16_t*>(ws + pl.off_hhi),
+                                      reinterpret_cast<uint16_t*>(ws + pl.off_hlo), a.stream);
+    if (e != hipSuccess) return e;
+  }
+  int* b_count = reinterpret_cast<int*>(ws + pl.off_bcount);
+  int* b_tile = reinterpret_cast<int*>(ws + pl.off_btile);
+  int* b_off = reinterpret_cast<int*>(ws + pl.off_boff);
+  int* b_tok = reinterpret_cast<int*>(ws + pl.off_btok);
+  int* b_pos = reinterpret_cast<int*>(ws + pl.off_bpos);
+  float* z_tgt = reinterpret_cast<float*>(ws + pl.off_ztgt);
+  if (pl.n_buckets <= kLdsBuckets) {
     hipLaunchKernelGGL(k_bucket_lds, dim3(1), dim3(kPrepThreads), 0, a.stream, p->tok_row,
                        p->tok_target, p->n_tok, p->n_rows, p->V, pl.row_tile, pl.vgroup,
-                       pl.n_vgroups, (int)pl.n_buckets, reinterpret_cast<int*>(ws + pl.off_boff),
-                       reinterpret_cast<int*>(ws + pl.off_btok),
-                       reinterpret_cast<int*>(ws + pl.off_bpos),
-                       reinterpret_cast<float*>(ws + pl.off_ztgt), a.flags);
+                       pl.n_vgroups, (int)pl.n_buckets, b_off, b_tok, b_pos, z_tgt, a.flags);
     return hipGetLastError();
   }
-  const int nsb = need_split ? split_blocks(n_h, kPrepThreads) : 0;
-  hipLaunchKernelGGL(k_prep, dim3(nsb + 1), dim3(kPrepThreads), 0, a.stream,
-                     static_cast<const float*>(p->H), n_h,
-                     reinterpret_cast<uint16_t*>(ws + pl.off_hhi),
-                     reinterpret_cast<uint16_t*>(ws + pl.off_hlo), nsb, p->tok_row, p->tok_target,
-                     p->n_tok, p->n_rows, p->V, pl.row_tile, pl.vgroup, pl.n_vgroups, pl.n_buckets,
-                     reinterpret_cast<int*>(ws + pl.off_bcount), reinterpret_cast<int*>(ws + pl.off_boff),
-                     reinterpret_cast<int*>(ws + pl.off_btok), reinterpret_cast<int*>(ws + pl.off_bpos),
-                     reinterpret_cast<float*>(ws + pl.off_ztgt), a.flags);
+  static_assert(kScanTile == kBucketScanTile && kScanTile == kBucketMaxTiles, "scan shape");
+  const long long nb = pl.n_buckets;
+  const int n_tiles = (int)pl.n_btiles;  // <= kBucketMaxTiles, checked by the caller
+  const int tok_blocks = (p->n_tok + 255) / 256;
+  hipLaunchKernelGGL(k_bk_clear, dim3((unsigned)std::min<long long>((nb + 256) / 256, 4096)),
+                     dim3(256), 0, a.stream, b_count, nb + 1, a.flags);
+  if (tok_blocks > 0)
+    hipLaunchKernelGGL(k_bk_count, dim3(tok_blocks), dim3(256), 0, a.stream, p->tok_row,
+                       p->tok_target, p->n_tok, p->n_rows, p->V, pl.row_tile, pl.vgroup,
+                       pl.n_vgroups, b_count, b_pos, z_tgt, a.flags);
+  hipLaunchKernelGGL(k_bk_tile_sums, dim3(n_tiles), dim3(kScanThreads), 0, a.stream, b_count, nb,
+                     b_tile);
+  hipLaunchKernelGGL(k_bk_scan_tiles, dim3(1), dim3(kScanThreads), 0, a.stream, b_tile, n_tiles);
+  hipLaunchKernelGGL(k_bk_offsets, dim3(n_tiles), dim3(kScanThreads), 0, a.stream, b_count, nb,
+                     b_tile, b_off);
+  if (tok_blocks > 0)
+    hipLaunchKernelGGL(k_bk_scatter, dim3(tok_blocks), dim3(256), 0, a.stream, p->tok_row,
+                       p->tok_target, p->n_tok, pl.row_tile, pl.vgroup, pl.n_vgroups, b_off, b_pos,
+                       b_tok);
   return hipGetLastError();
 }
 
