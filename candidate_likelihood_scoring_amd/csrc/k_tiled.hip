@@ -44,6 +44,10 @@
 #ifndef JET_TILED_DTL2
 #define JET_TILED_DTL2 0
 #endif
+// bf16 hidden states: 1 = k_project_tiled_m16 (16 x 16 x 32 MFMAs)
+#ifndef JET_TILED_M16
+#define JET_TILED_M16 1
+#endif
 
 namespace jet {
 namespace {
@@ -722,6 +726,266 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
   tile_finish(m_run, s_run, red, tid, wm, wn, n, h, row0, row_nom, split, n_rows, part);
 }
 
+
+// ------------------------------------------------------------------------------------
+// bf16 hidden states on v_mfma_f32_16x16x32_bf16.  Same block tile, stage width (64), LDS
+// buffers, swizzle, load discipline and placement as k_project_tiled_dtl; each wave's
+// 128 x 128 quadrant is 8 x 8 blocks of 16 x 16 (4 accumulators per lane each).  Operand
+// layout: lane l supplies row (A) or column (B) l % 16 and k = 8 (l / 16) + j, so a stage's
+// k-step ks (32 wide) reads chunk 4 ks + l / 16; the swizzle depends on row & 15 = l % 16,
+// so the 16 lanes of a quarter-wave hit 16 different bank groups.  Output register i of
+// lane l holds vocabulary entry 4 (l / 16) + i and row l % 16 of its block.
+// ------------------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// Fold a finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
+// this lane's eight rows and capture the tile's scored targets (see tile_epilogue).
+__device__ __forceinline__ void tile_epilogue16(
+    f32x4 (&acc)[8][8], float (&m_run)[8], float (&s_run)[8], int vt, int V, int wm, int wn,
+    int r16, int q, int rt, int n_vtiles, int row0, const int* __restrict__ b_off,
+    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt) {
+  const int v_nom = vt * TBM;
+  const int v0 = min(v_nom, V - TBM);
+  if (v0 != v_nom) {
+    // shifted last tile: add -inf to the entries below v_nom through the matrix core
+    // (A: -inf at k = 0 for a dropped entry, B: 1 at k = 0; no 0 * inf is formed)
+    const int thr = v_nom - v0 - wm * 128;
+    bf16x8 bone = {};
+    if (q == 0) bone[0] = (__bf16)1.0f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      bf16x8 amask = {};
+      if (q == 0 && mt * 16 + r16 < thr) amask[0] = (__bf16)(-INFINITY);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(amask, bone, acc[mt][nt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
+    float gm = m_run[nt];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
+    const float mb = gm == -INFINITY ? 0.f : gm * kLog2e;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps[i] += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
+    s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    m_run[nt] = gm;
+  }
+  const int bkey = rt * n_vtiles + vt;
+  const int e0 = b_off[bkey], e1 = b_off[bkey + 1];
+  for (int e = e0; e < e1; ++e) {
+    const int k = b_tok[e];
+    const int lr = (tok_row ? tok_row[k] : k) - row0;
+    const int lv = tok_target[k] - v0;
+    if (lv < 0 || lv >= TBM || lr < 0 || lr >= TBN) continue;
+    if ((lv >> 7) != wm || (lr >> 7) != wn) continue;  // wave-uniform
+    const int tmt = (lv >> 4) & 7, tnt = (lr >> 4) & 7, ti = lv & 3;
+    if (r16 == (lr & 15) && q == ((lv >> 2) & 3)) {
+      float val = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          if (mt == tmt && nt == tnt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i == ti) val = acc[mt][nt][i];
+          }
+      z_tgt[k] = val;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
+    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H, int n_rows,
+    int n_vtiles, const int* __restrict__ b_off, const int* __restrict__ b_tok,
+    const int* __restrict__ tok_row, const int* __restrict__ tok_target,
+    float* __restrict__ z_tgt, float2* __restrict__ part, int n_rtiles, int splits, int sr,
+    int ss, int remap) {
+  constexpr int BK = 64, CH = 8, RPD = 64 / CH;
+  constexpr int ASZ = TBM * CH;  // 16-byte slots per operand half per buffer (32 KB)
+  constexpr int BUFSZ = 2 * ASZ;
+  constexpr int NDO = CH;        // load instructions per wave per operand per stage
+  __shared__ u32x4 lds[2 * BUFSZ];
+  __shared__ float2 red[2][TBN];
+  __shared__ float2 runs[4][8][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid & 1, wn = wid >> 1;
+  const int r16 = lane & 15, q = lane >> 4;
+  int rt, split;
+  tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
+  if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
+  const int row_nom = rt * TBN;
+  const int row0 = min(row_nom, n_rows - TBN);
+  const int t0 = (int)((long long)split * n_vtiles / splits);
+  const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
+  const int nk = d / BK;  // even
+  const uint32_t rowb = (uint32_t)d * 2;
+  const __amdgpu_buffer_rsrc_t rH = rsrc_of(H, (uint32_t)n_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
+  const uint32_t hrow = (uint32_t)row0 * rowb;
+  const int dr = wid * RPD + lane / CH;
+  const uint32_t dvoff = (uint32_t)dr * rowb + (uint32_t)(((lane % CH) ^ swz<CH>(dr)) * 16);
+  const uint32_t m0_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds +
+                           (uint32_t)wid * 1024u;
+  // fragment slot of k-step ks (0, 1) for block row 0 of this wave's half: row r16 of the
+  // block, chunk 4 ks + q; blocks are 16 rows (128 slots) apart
+  int fslot[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) fslot[ks] = r16 * CH + ((4 * ks + q) ^ swz<CH>(r16));
+  const int a_off = wm * 128 * CH, b_off_h = ASZ + wn * 128 * CH;
+
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) runs[wid][nt][lane] = make_float2(-INFINITY, 0.f);
+
+  const int G = (t1 - t0) * nk;
+  int lt = t0, lk = 0, lg = 0;  // load cursor
+  uint32_t l_ws = 0, l_hs = 0;
+#define JET_CURSOR()                                                                         \
+  {                                                                                          \
+    const uint32_t ko = (uint32_t)lk * (BK * 2);                                             \
+    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)min(lt * TBM, V - TBM) * rowb + ko);     \
+    l_hs = __builtin_amdgcn_readfirstlane(hrow + ko);                                        \
+    if (lg + 1 < G) {                                                                        \
+      ++lg;                                                                                  \
+      if (++lk == nk) {                                                                      \
+        lk = 0;                                                                              \
+        ++lt;                                                                                \
+      }                                                                                      \
+    }                                                                                        \
+  }
+  // load instruction Q (0 .. 2 NDO - 1): head rows first, then hidden-state rows
+#define JET_DMA1(BI, Q)                                                                      \
+  {                                                                                          \
+    const int op_ = (Q) / NDO, jj_ = (Q) % NDO;                                              \
+    dma16(op_ ? rH : rW, dvoff, (op_ ? l_hs : l_ws) + (uint32_t)(jj_ * 4 * RPD) * rowb,        \
+          m0_base + (uint32_t)(((BI) * BUFSZ + op_ * ASZ + jj_ * 256) * 16));                \
+  }
+  bf16x8 fa[2][8], fb[2][8];
+  // fragment read JR (0 .. 15) of k-step KS_ into set F, in order of first use:
+  // a0, b0..b7, a1..a7
+#define JET_FRAG1(F, BOFF, KS_, JR)                                                          \
+  {                                                                                          \
+    if ((JR) >= 1 && (JR) <= 8) {                                                            \
+      fb[F][(JR) - 1] = __builtin_bit_cast(                                                  \
+          bf16x8, lds[(BOFF) + b_off_h + fslot[KS_] + ((JR) - 1) * 16 * CH]);                 \
+    } else {                                                                                 \
+      const int ta_ = (JR) == 0 ? 0 : (JR) - 8;                                              \
+      fa[F][ta_] = __builtin_bit_cast(bf16x8, lds[(BOFF) + a_off + fslot[KS_] + ta_ * 16 * CH]); \
+    }                                                                                        \
+  }
+  int bc = 0;
+  // One stage g (buffer bc; the k-step 0 fragments of stage g already in set 0): two
+  // k-steps of 64 MFMAs (block (i / 8, i % 8)).  k-step 0 reads the k-step 1 fragments at
+  // every fourth slot.  Then every wave is done with buffer bc and stage g + 1 is awaited
+  // (its loads were issued during the previous stage's k-step 1) behind the one barrier
+  // of the stage.  k-step 1 reads the k-step 0 fragments of stage g + 1 (even slots
+  // 0..30) and loads stage g + 2 into buffer bc (slots 1, 5, .., 61), so loads get half a
+  // stage to a stage to land and no stage starts by waiting for LDS.
+#define JET_MSTAGE(FIRST)                                                                    \
+  {                                                                                          \
+    const int b_nx = bc ^ 1;                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    _Pragma("unroll") for (int i = 0; i < 64; ++i) {                                         \
+      acc[i / 8][i % 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                           \
+          fa[0][i / 8], fb[0][i % 8], (FIRST) ? f32x4{} : acc[i / 8][i % 8], 0, 0, 0);       \
+      if (i % 4 == 0) JET_FRAG1(1, bc * BUFSZ, 1, i / 4);                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+    }                                                                                        \
+    vm_wait<0>();                                                                            \
+    __syncthreads();                                                                         \
+    JET_CURSOR();                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    _Pragma("unroll") for (int i = 0; i < 64; ++i) {                                         \
+      acc[i / 8][i % 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                           \
+          fa[1][i / 8], fb[1][i % 8], acc[i / 8][i % 8], 0, 0, 0);                           \
+      if (i < 32 && i % 2 == 0) {                                                            \
+        JET_FRAG1(0, b_nx * BUFSZ, 0, i / 2);                                                \
+      } else if (i % 4 == 1) {                                                               \
+        JET_DMA1(bc, i / 4);                                                                 \
+      }                                                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+    }                                                                                        \
+    bc = b_nx;                                                                               \
+  }
+
+  // prologue: stage 0 into buffer 0, stage 1 into buffer 1; stage 0 complete; its k-step 0
+  // fragments into set 0
+  JET_CURSOR();
+#pragma unroll
+  for (int qq = 0; qq < 2 * NDO; ++qq) JET_DMA1(0, qq);
+  JET_CURSOR();
+#pragma unroll
+  for (int qq = 0; qq < 2 * NDO; ++qq) JET_DMA1(1, qq);
+  vm_wait<2 * NDO>();
+  __syncthreads();
+#pragma unroll
+  for (int jr = 0; jr < 16; ++jr) JET_FRAG1(0, 0, 0, jr);
+
+  for (int vt = t0; vt < t1; ++vt) {
+    f32x4 acc[8][8];
+    JET_MSTAGE(true);
+    JET_MSTAGE(false);
+    for (int kb = 2; kb < nk; kb += 2) {
+      JET_MSTAGE(false);
+      JET_MSTAGE(false);
+    }
+    {
+      // lane-derived values recomputed here (from the exec mask, in a form the compiler
+      // cannot hoist) instead of being kept live across the stage loop: a spill reload
+      // would make the epilogue wait for the loads in flight
+      int lane_e;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+      float m_run[8], s_run[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const float2 r = runs[wid][nt][lane_e];
+        m_run[nt] = r.x;
+        s_run[nt] = r.y;
+      }
+      tile_epilogue16(acc, m_run, s_run, vt, V, wm, wn, lane_e & 15, lane_e >> 4, rt, n_vtiles, row0,
+                      b_off, b_tok, tok_row, tok_target, z_tgt);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) runs[wid][nt][lane_e] = make_float2(m_run[nt], s_run[nt]);
+    }
+  }
+  vm_wait<0>();  // no load may land in LDS after the workgroup ends
+#undef JET_CURSOR
+#undef JET_DMA1
+#undef JET_FRAG1
+#undef JET_MSTAGE
+  // merge the four lanes of each row (q = 0..3), then the two vocabulary halves (wm)
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    float m = runs[wid][nt][lane].x, sm = runs[wid][nt][lane].y;
+    float m2 = __shfl_xor(m, 16), s2 = __shfl_xor(sm, 16);
+    lse_merge(m, sm, m2, s2);
+    m2 = __shfl_xor(m, 32);
+    s2 = __shfl_xor(sm, 32);
+    lse_merge(m, sm, m2, s2);
+    if (q == 0) red[wm][wn * 128 + nt * 16 + r16] = make_float2(m, sm);
+  }
+  __syncthreads();
+  {
+    const int r = tid;  // 256 threads, 256 rows
+    float m = red[0][r].x, sm = red[0][r].y;
+    lse_merge(m, sm, red[1][r].x, red[1][r].y);
+    const int row = row0 + r;
+    if (row >= row_nom) part[(size_t)split * n_rows + row] = make_float2(m, sm);
+  }
+}
+
 }  // namespace
 
 // d must be a multiple of two stages (the stage loop is unrolled by two)
@@ -731,6 +995,7 @@ int tiled_bk(bool hilo) {
 }
 
 const char* tiled_kernel_name(bool hilo) {
+  if (!hilo && JET_TILED_M16) return "k_project_tiled_m16";
   return (hilo ? JET_TILED_DTL2 : JET_TILED_DTL) ? "k_project_tiled_dtl" : "k_project_tiled_bf16";
 }
 
@@ -762,9 +1027,14 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
                        hlo, p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target,
                        z_tgt, part, R, S, sr, ss, remap);
   } else {
-    hipLaunchKernelGGL((JET_TILED_DTL ? k_project_tiled_dtl<1> : k_project_tiled_bf16<1>), grid, block, 0, a.stream, W, p->V, p->d,
-                       static_cast<const uint16_t*>(p->H), nullptr, p->n_rows, pl.n_vgroups,
-                       b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
+    if (JET_TILED_M16)
+      hipLaunchKernelGGL(k_project_tiled_m16, grid, block, 0, a.stream, W, p->V, p->d,
+                         static_cast<const uint16_t*>(p->H), p->n_rows, pl.n_vgroups, b_off,
+                         b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
+    else
+      hipLaunchKernelGGL((JET_TILED_DTL ? k_project_tiled_dtl<1> : k_project_tiled_bf16<1>), grid, block, 0, a.stream, W, p->V, p->d,
+                         static_cast<const uint16_t*>(p->H), nullptr, p->n_rows, pl.n_vgroups,
+                         b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
   }
   return hipGetLastError();
 }
