@@ -5,49 +5,30 @@
 // Sec. 3.3): z[r, v] = <H[r], W[v]> with fp32 accumulation, folded into a running
 // (max, sum of exp) per row, plus the logit of every scored (row, target) pair.
 //
-// Tiling (gfx950): a workgroup of 4 waves owns a 256-row tile of H and sweeps a contiguous
-// range of 256-entry vocabulary tiles.  Each wave computes a 128 x 128 quadrant (vocabulary
-// x rows) as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, i.e. 256 fp32 accumulators per lane
-// (all AGPRs; one wave per SIMD).
-//
-// Pipeline: K advances in 32-wide stages; the stages of all the split's vocabulary tiles
-// form one stream, so the next tile's first stages are in flight during an epilogue.
-//  * global -> registers: lane-contiguous 16-byte buffer loads (4 lanes cover one 64-byte
-//    row segment), issued three stages ahead into two register sets;
-//  * registers -> LDS: a ring of three buffers; stage g + 2 is written while stage g
-//    computes, so the buffer of stage g + 1 was completed before the previous barrier and
-//    its first fragments are read before this stage's barrier (no read-after-barrier
-//    bubble); one barrier per stage;
-//  * every MFMA is followed by one memory instruction (fragment read, LDS write or global
-//    load), so with one wave per SIMD the memory traffic overlaps the matrix core instead
-//    of stalling its issue in bursts.
-// The last vocabulary tile (and row tile) is shifted back to end exactly at V (n_rows), so
-// every load is in bounds; the overlap is masked in the epilogue and only the tile's own
-// rows are reported.  LDS chunk (row r, 16-byte chunk c) lives at r * CH + (c ^ f(r)),
-// which keeps the row-wise writes and the 32-row fragment reads conflict-free.
+// Tiling (gfx950): a workgroup of 4 waves (one per SIMD) owns a 256-row tile of H and
+// sweeps a contiguous range of 256-entry vocabulary tiles; each wave computes a 128 x 128
+// quadrant (vocabulary x rows), 256 fp32 accumulators per lane (all AGPRs).  The stages of
+// all the range's vocabulary tiles form one stream, so the next tile's first stages are in
+// flight during an epilogue.  Two kernels:
+//  * k_project_tiled_m16 (bf16 H): 8 x 8 blocks of v_mfma_f32_16x16x32_bf16 per wave;
+//    64-wide stages loaded by the buffer unit straight into two LDS buffers; one barrier
+//    per stage, at its midpoint (see the kernel);
+//  * k_project_tiled_bf16 (fp32 H as two bf16 planes, hi + lo, each product accumulated
+//    twice): 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 per wave; 32-wide stages staged
+//    through two register sets into a ring of three LDS buffers.
+// In both, every MFMA is followed by at most one memory instruction (fragment read, LDS
+// write or global load), so with one wave per SIMD the memory traffic overlaps the matrix
+// core instead of stalling its issue in bursts.  The last vocabulary tile (and row tile) is
+// shifted back to end exactly at V (n_rows), so every load is in bounds; the overlap is
+// masked in the epilogue and only the tile's own rows are reported.  LDS chunk (row r,
+// 16-byte chunk c) lives at r * CH + (c ^ f(r)), which keeps the row-wise writes and the
+// fragment reads conflict-free.
 //
 // Workgroup placement: workgroup L runs on XCD L % 8, and each XCD runs about 32 at a time
 // (one per CU).  Launch index L is remapped so that those 32 form an SR x SS block of
 // (row tile, vocabulary split) pairs: the SR row tiles' H tiles are shared SS ways and the
-// SS splits' head tiles SR ways inside that XCD's L2.  Fragment k layout: lane half h,
-// sub-step kk reads chunk 2 kk + h of its row for both operands (any k permutation shared
-// by A and B gives the same dot product).
-//
-// H in one bf16 plane (bf16 hidden states) or two (fp32 hidden states split into hi + lo,
-// each product accumulated twice).
+// SS splits' head tiles SR ways inside that XCD's L2.
 #include "jet_internal.h"
-
-// Per plane count: 1 = stages are loaded straight into LDS, 0 = staged through registers
-#ifndef JET_TILED_DTL
-#define JET_TILED_DTL 1
-#endif
-#ifndef JET_TILED_DTL2
-#define JET_TILED_DTL2 0
-#endif
-// bf16 hidden states: 1 = k_project_tiled_m16 (16 x 16 x 32 MFMAs)
-#ifndef JET_TILED_M16
-#define JET_TILED_M16 1
-#endif
 
 namespace jet {
 namespace {
@@ -112,11 +93,9 @@ __device__ __forceinline__ void tile_assign(int n_rtiles, int sr, int ss, int sp
 }
 
 // Fold the finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
-// this lane's rows and capture the logits of the tile's scored targets.  The shifted last
-// vocabulary tile skips the entries before v_nom, which the previous tile counted: with
-// MASK_MFMA by adding -inf to them through the matrix core (the accumulators stay in
-// place and the fold has one path), otherwise with a masked copy of the fold.
-template <bool MASK_MFMA>
+// this lane's rows and capture the logits of the tile's scored targets (fp32-H kernel,
+// 4 x 4 blocks of 32 x 32).  The shifted last vocabulary tile skips the entries before
+// v_nom, which the previous tile counted, with a masked copy of the fold.
 __device__ __forceinline__ void tile_epilogue(
     f32x16 (&acc)[4][4], float (&m_run)[4], float (&s_run)[4], int vt, int V, int wm, int wn,
     int n, int h, int rt, int n_vtiles, int row0, const int* __restrict__ b_off,
@@ -124,8 +103,7 @@ __device__ __forceinline__ void tile_epilogue(
     const int* __restrict__ tok_target, float* __restrict__ z_tgt) {
   const int v_nom = vt * TBM;
   const int v0 = min(v_nom, V - TBM);
-  if (!MASK_MFMA && v0 != v_nom) {
-    // shifted last tile, masked per entry: skip the entries below v_nom
+  if (v0 != v_nom) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float gm = -INFINITY;
@@ -149,37 +127,13 @@ __device__ __forceinline__ void tile_epilogue(
       }
     }
   } else {
-    if (MASK_MFMA && v0 != v_nom) {
-      // Shifted last tile: entries below v_nom were counted by the previous tile.  One MFMA
-      // per 32 x 32 tile adds -inf to exactly those entries: A holds -inf at k = 0 for a
-      // dropped vocabulary entry (0 elsewhere), B holds 1 at k = 0 (0 elsewhere), so no
-      // 0 * inf is formed.  The tile's scored targets are all >= v_nom: capture is unaffected.
-      const int thr = v_nom - v0 - wm * 128;  // local entries below thr are dropped
-      bf16x8 bone = {};
-      if (h == 0) bone[0] = (__bf16)1.0f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        bf16x8 amask = {};
-        if (h == 0 && mt * 32 + n < thr) amask[0] = (__bf16)(-INFINITY);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(amask, bone, acc[mt][nt], 0, 0, 0);
-      }
-    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      // (direct-to-LDS kernel) the accumulators of row tile nt are read only from here on:
-      // one group of 64 values in VGPRs at a time instead of all 256
-      if (MASK_MFMA) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
-      }
       float gm = m_run[nt];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
-      // gm is -inf only when this half tile is entirely dropped and nothing came before
       const float mb = gm == -INFINITY ? 0.f : gm * kLog2e;
       // four partial sums, so that consecutive exponentials do not wait on one another
       float ps[4] = {0.f, 0.f, 0.f, 0.f};
@@ -187,8 +141,7 @@ __device__ __forceinline__ void tile_epilogue(
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) ps[i & 3] += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
-      const float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + sum;
+      s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
       m_run[nt] = gm;
     }
   }
@@ -241,21 +194,11 @@ __device__ __forceinline__ void tile_finish(float (&m_run)[4], float (&s_run)[4]
   }
 }
 
-// Stage shapes.  A stage is BK columns of K for the 256-row head tile and the 256-row
-// hidden-state tile (each of NP planes): CH = BK / 8 16-byte chunks per row, so one load
-// round of 256 threads covers RPI = 256 / CH rows with CH lanes per contiguous row segment.
-// Loads per CU per stage are limited by the number of L1 requests in flight, not bytes, so
-// the bf16 path uses BK = 64 (128-byte row segments, one full line per 8 lanes) with two
-// LDS buffers; the two-plane path keeps BK = 32 and a three-buffer ring, which is what the
-// 160 KB of LDS holds.
-#ifndef JET_TILED_BK1
-#define JET_TILED_BK1 64
-#endif
-#ifndef JET_TILED_NBUF1
-#define JET_TILED_NBUF1 2
-#endif
+// Stage shape of the fp32-H kernel: a stage is BK = 32 columns of K for the 256-row head
+// tile and the two 256-row hidden-state planes: CH = BK / 8 16-byte chunks per row, so one
+// load round of 256 threads covers RPI = 256 / CH rows with CH lanes per contiguous row
+// segment.  Three 48 KB buffers fill the LDS ring.
 template <int NP> struct TiledShape;
-template <> struct TiledShape<1> { static constexpr int BK = JET_TILED_BK1, NBUF = JET_TILED_NBUF1; };
 template <> struct TiledShape<2> { static constexpr int BK = 32, NBUF = 3; };
 
 template <int NP>
@@ -461,7 +404,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       JET_STAGE((NBUF - 1) & 1, NBUF & 1, false);
     }
 
-    tile_epilogue<false>(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
+    tile_epilogue(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
                          tok_row, tok_target, z_tgt);
   }
 #undef JET_LOAD
@@ -475,262 +418,14 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   tile_finish(m_run, s_run, red, tid, wm, wn, n, h, row0, row_nom, split, n_rows, part);
 }
 
-// ---------------------------------------------------------------------------------------
-// Direct-to-LDS variant: the same block tile, epilogue and placement, but every stage is
-// loaded by the buffer unit straight into its LDS buffer (no register staging, no LDS
-// store instructions).  Each load instruction fills 1 KB of a buffer: 64 / CH rows x CH
-// chunks; lane l fetches the chunk that the swizzled layout puts in slot l, i.e. logical
-// chunk (l % CH) ^ f(row).  Stage g + NBUF - 1 is fetched during stage g into buffer
-// (g - 1) % NBUF, which every wave finished reading before the previous barrier.  With PF
-// the first fragments of stage g + 1 are read before the barrier at the end of stage g,
-// so stage g + 1 must be complete one barrier earlier.
-#ifndef JET_DTL_BK1
-#define JET_DTL_BK1 64
-#endif
-#ifndef JET_DTL_NBUF1
-#define JET_DTL_NBUF1 2
-#endif
-#ifndef JET_DTL_PF1
-#define JET_DTL_PF1 0
-#endif
-template <int NP> struct DtlShape;
-template <> struct DtlShape<1> {
-  static constexpr int BK = JET_DTL_BK1, NBUF = JET_DTL_NBUF1, PF = JET_DTL_PF1;
-};
-#ifndef JET_DTL_PF2
-#define JET_DTL_PF2 1
-#endif
-template <> struct DtlShape<2> { static constexpr int BK = 32, NBUF = 3, PF = JET_DTL_PF2; };
-
-// loads issued in sub-step kk of a stage: as many as the slots left by its fragment reads
-// allow, but at most JET_DTL_MAXD (or the even share, if that is larger), earliest sub-steps
-// first.  Six per sub-step (6, 6, 4, 0 for the bf16 stage) measured faster than packing
-// them into the first two sub-steps (8, 8, 0, 0), which stalls issue on the memory path,
-// and than an even spread (4, 4, 4, 4), which leaves the last loads too little lead.
-#ifndef JET_DTL_MAXD
-#define JET_DTL_MAXD 6
-#endif
-constexpr int dtl_cap(int k, int KK, int ndma, int slots, int nrd, int nrd_last) {
-  const int c = slots - (k + 1 < KK ? nrd : nrd_last);
-  const int even = (ndma + KK - 1) / KK;
-  const int m = JET_DTL_MAXD > even ? JET_DTL_MAXD : even;
-  return c < m ? c : m;
-}
-constexpr int dtl_nd(int kk, int KK, int ndma, int slots, int nrd, int nrd_last) {
-  int before = 0;
-  for (int k = 0; k < kk; ++k) {
-    const int cap = dtl_cap(k, KK, ndma, slots, nrd, nrd_last);
-    const int left = ndma - before;
-    before += cap < left ? cap : left;
-  }
-  const int cap = dtl_cap(kk, KK, ndma, slots, nrd, nrd_last);
-  const int left = ndma - before;
-  return cap < left ? cap : left;
-}
-constexpr int dtl_before(int kk, int KK, int ndma, int slots, int nrd, int nrd_last) {
-  int before = 0;
-  for (int k = 0; k < kk; ++k) before += dtl_nd(k, KK, ndma, slots, nrd, nrd_last);
-  return before;
-}
-
-template <int NP>
-__global__ __launch_bounds__(256, 1) void k_project_tiled_dtl(
-    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
-    const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
-    int n_rtiles, int splits, int sr, int ss, int remap) {
-  constexpr int BK = DtlShape<NP>::BK, NBUF = DtlShape<NP>::NBUF, PF = DtlShape<NP>::PF;
-  constexpr int D = NBUF - 1;         // stages fetched ahead
-  constexpr int CH = BK / 8;          // 16-byte chunks per row per stage
-  constexpr int KK = BK / 16;         // MFMA k sub-steps per stage
-  constexpr int RPD = 64 / CH;        // rows per load instruction
-  constexpr int ASZ = TBM * CH;       // 16-byte slots per operand plane per buffer
-  constexpr int BUFSZ = ASZ * (1 + NP);
-  constexpr int NDO = CH;             // load instructions per wave per operand plane per stage
-  constexpr int NDMA = (1 + NP) * NDO;
-  constexpr int NRD = 4 + 4 * NP;     // fragment reads per sub-step
-  constexpr int SLOTS = 16 * NP;      // MFMAs (memory slots) per sub-step
-  constexpr int NRD_LAST = PF ? NRD : 0;
-  static_assert(KK % 2 == 0 && NBUF >= 2 && NBUF <= 4 && (PF == 0 || NBUF >= 3), "stage layout");
-  static_assert(dtl_before(KK, KK, NDMA, SLOTS, NRD, NRD_LAST) == NDMA, "every load needs a slot");
-  static_assert(D - 1 - PF >= 0, "ring depth");
-  __shared__ u32x4 lds[NBUF * BUFSZ];
-  __shared__ float2 red[2][TBN];
-  // running (max, sum of exp) per wave, row tile and lane; kept in LDS between vocabulary
-  // tiles so that no registers stay live across the stage loop for them
-  __shared__ float2 runs[4][4][64];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid & 1, wn = wid >> 1;
-  const int n = lane & 31, h = lane >> 5;
-  int rt, split;
-  tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
-  if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
-  const int row_nom = rt * TBN;
-  const int row0 = min(row_nom, n_rows - TBN);
-  const int t0 = (int)((long long)split * n_vtiles / splits);
-  const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
-  const int nk = d / BK;                           // even
-  const uint32_t rowb = (uint32_t)d * 2;
-
-  const __amdgpu_buffer_rsrc_t rH0 = rsrc_of(H0, (uint32_t)n_rows * rowb);
-  const __amdgpu_buffer_rsrc_t rH1 = rsrc_of(NP == 2 ? H1 : H0, (uint32_t)n_rows * rowb);
-  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
-  const uint32_t hrow = (uint32_t)row0 * rowb;
-  // load instruction jj of this wave (per plane) covers tile rows (jj * 4 + wid) * RPD + [0, RPD):
-  // lane l takes row (jj * 4 + wid) * RPD + l / CH, LDS slot (jj * 4 + wid) * 64 + l, which
-  // holds logical chunk (l % CH) ^ f(row); f depends on row & 15, the same for every jj
-  const int dr = wid * RPD + lane / CH;
-  const uint32_t dvoff = (uint32_t)dr * rowb + (uint32_t)(((lane % CH) ^ swz<CH>(dr)) * 16);
-  const uint32_t m0_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds +
-                           (uint32_t)wid * 1024u;
-  int ra_slot[KK], rb_slot[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    ra_slot[kk] = (wm * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
-    rb_slot[kk] = ASZ + (wn * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
-  }
-
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) runs[wid][nt][lane] = make_float2(-INFINITY, 0.f);
-
-  const int G = (t1 - t0) * nk;
-  int lt = t0, lk = 0, lg = 0;  // load cursor
-  uint32_t l_ws = 0, l_hs = 0;
-#define JET_CURSOR()                                                                         \
-  {                                                                                          \
-    const uint32_t ko = (uint32_t)lk * (BK * 2);                                             \
-    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)min(lt * TBM, V - TBM) * rowb + ko);     \
-    l_hs = __builtin_amdgcn_readfirstlane(hrow + ko);                                        \
-    if (lg + 1 < G) {                                                                        \
-      ++lg;                                                                                  \
-      if (++lk == nk) {                                                                      \
-        lk = 0;                                                                              \
-        ++lt;                                                                                \
-      }                                                                                      \
-    }                                                                                        \
-  }
-  // load instruction q (0 .. NDMA - 1) of the stage at the cursor into buffer BI
-#define JET_DMA1(BI, Q)                                                                      \
-  {                                                                                          \
-    const int op_ = (Q) / NDO, jj_ = (Q) % NDO;                                              \
-    const uint32_t m0_ = m0_base + (uint32_t)(((BI) * BUFSZ + op_ * ASZ + jj_ * 256) * 16);   \
-    const uint32_t so_ = (op_ == 0 ? l_ws : l_hs) + (uint32_t)(jj_ * 4 * RPD) * rowb;         \
-    dma16(op_ == 0 ? rW : (op_ == 1 ? rH0 : rH1), dvoff, so_, m0_);                          \
-  }
-  bf16x8 fa[2][4], fb[2][NP][4];
-#define JET_FRAG1(F, BOFF, KK_, JR)                                                          \
-  {                                                                                          \
-    if ((JR) == 0) {                                                                         \
-      fa[F][0] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_]]);                     \
-    } else if ((JR) <= 4 * NP) {                                                             \
-      const int pb = ((JR) - 1) % NP, tb = ((JR) - 1) / NP;                                  \
-      fb[F][pb][tb] =                                                                        \
-          __builtin_bit_cast(bf16x8, lds[(BOFF) + pb * ASZ + rb_slot[KK_] + tb * 32 * CH]);  \
-    } else {                                                                                 \
-      const int ta = (JR) - 4 * NP;                                                          \
-      fa[F][ta] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_] + ta * 32 * CH]);     \
-    }                                                                                        \
-  }
-#define JET_FRAGS(F, BOFF, KK_)                                                              \
-  {                                                                                          \
-    _Pragma("unroll") for (int jr_ = 0; jr_ < NRD; ++jr_) JET_FRAG1(F, BOFF, KK_, jr_);      \
-  }
-  int bc = 0;  // buffer index of stage g
-#define JET_DSTAGE(FIRST)                                                                    \
-  {                                                                                          \
-    const int b_nx = bc + 1 == NBUF ? 0 : bc + 1;       /* stage g + 1 */                    \
-    const int b_ld = bc == 0 ? NBUF - 1 : bc - 1;       /* stage g + NBUF - 1 */             \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
-    if (!PF) JET_FRAGS(0, bc * BUFSZ, 0);                                                    \
-    JET_CURSOR();                                                                            \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
-    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                      \
-      const int nrd = kk + 1 < KK ? NRD : NRD_LAST;                                          \
-      const int nd = dtl_nd(kk, KK, NDMA, SLOTS, NRD, NRD_LAST);                             \
-      const int q0 = dtl_before(kk, KK, NDMA, SLOTS, NRD, NRD_LAST);                         \
-      const int nls = nrd + nd;                                                              \
-      _Pragma("unroll") for (int i = 0; i < SLOTS; ++i) {                                    \
-        acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(            \
-            fa[kk & 1][i / (4 * NP)], fb[kk & 1][i % NP][(i / NP) % 4],                      \
-            (FIRST) && kk == 0 && i % NP == 0 ? f32x16{} : acc[i / (4 * NP)][(i / NP) % 4], 0, \
-            0, 0);                                                                           \
-        if (i < nls) {                                                                       \
-          const int ndb = nd ? (i * nd) / nls : 0;                                           \
-          if (nd && ((i + 1) * nd) / nls > ndb) {                                            \
-            JET_DMA1(b_ld, q0 + ndb);                                                        \
-          } else if (kk + 1 < KK) {                                                          \
-            JET_FRAG1((kk + 1) & 1, bc * BUFSZ, kk + 1, i - ndb);                            \
-          } else {                                                                           \
-            JET_FRAG1(0, b_nx * BUFSZ, 0, i - ndb);                                          \
-          }                                                                                  \
-        }                                                                                    \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
-      }                                                                                      \
-    }                                                                                        \
-    vm_wait<(D - 1 - PF) * NDMA>();                                                          \
-    __syncthreads();                                                                         \
-    bc = b_nx;                                                                               \
-  }
-
-  // prologue: stages 0 .. D - 1 into buffers 0 .. D - 1; stages 0 (and 1 with PF) complete
-#pragma unroll
-  for (int st = 0; st < D; ++st) {
-    JET_CURSOR();
-#pragma unroll
-    for (int q = 0; q < NDMA; ++q) JET_DMA1(st, q);
-  }
-  vm_wait<(D - 1 - PF) * NDMA>();
-  __syncthreads();
-  if (PF) JET_FRAGS(0, 0, 0);
-
-  for (int vt = t0; vt < t1; ++vt) {
-    f32x16 acc[4][4];
-    // the tile's first stage is peeled: the first MFMA of every accumulator block starts
-    // from an inline-constant zero, so the 256 accumulators are never cleared
-    JET_DSTAGE(true);
-    JET_DSTAGE(false);
-    for (int kb = 2; kb < nk; kb += 2) {
-      JET_DSTAGE(false);
-      JET_DSTAGE(false);
-    }
-    {
-      float m_run[4], s_run[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float2 r = runs[wid][nt][lane];
-        m_run[nt] = r.x;
-        s_run[nt] = r.y;
-      }
-      tile_epilogue<true>(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
-                          tok_row, tok_target, z_tgt);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) runs[wid][nt][lane] = make_float2(m_run[nt], s_run[nt]);
-    }
-  }
-  vm_wait<0>();  // no load may land in LDS after the workgroup ends
-#undef JET_CURSOR
-#undef JET_DMA1
-#undef JET_FRAG1
-#undef JET_FRAGS
-#undef JET_DSTAGE
-  float m_run[4], s_run[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const float2 r = runs[wid][nt][lane];
-    m_run[nt] = r.x;
-    s_run[nt] = r.y;
-  }
-  tile_finish(m_run, s_run, red, tid, wm, wn, n, h, row0, row_nom, split, n_rows, part);
-}
-
-
 // ------------------------------------------------------------------------------------
-// bf16 hidden states on v_mfma_f32_16x16x32_bf16.  Same block tile, stage width (64), LDS
-// buffers, swizzle, load discipline and placement as k_project_tiled_dtl; each wave's
-// 128 x 128 quadrant is 8 x 8 blocks of 16 x 16 (4 accumulators per lane each).  Operand
+// bf16 hidden states on v_mfma_f32_16x16x32_bf16.  A stage is 64 columns of K for the
+// 256-row head tile and the 256-row hidden-state tile (8 chunks of 16 bytes per row), two
+// 64 KB buffers.  Every load instruction is issued by the buffer unit straight into LDS
+// (1 KB: 8 rows x 8 chunks; lane l fetches the chunk that the swizzled layout puts in slot
+// l).  Each wave's 128 x 128 quadrant is 8 x 8 blocks of 16 x 16 (4 accumulators per lane
+// each).  On this matrix-core shape the chip sustains a higher clock under its power limit
+// than with 32 x 32 blocks, which more than pays for the extra instructions.  Operand
 // layout: lane l supplies row (A) or column (B) l % 16 and k = 8 (l / 16) + j, so a stage's
 // k-step ks (32 wide) reads chunk 4 ks + l / 16; the swizzle depends on row & 15 = l % 16,
 // so the 16 lanes of a quarter-wave hit 16 different bank groups.  Output register i of
@@ -989,14 +684,10 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
 }  // namespace
 
 // d must be a multiple of two stages (the stage loop is unrolled by two)
-int tiled_bk(bool hilo) {
-  if (hilo) return 2 * (JET_TILED_DTL2 ? DtlShape<2>::BK : TiledShape<2>::BK);
-  return 2 * (JET_TILED_DTL ? DtlShape<1>::BK : TiledShape<1>::BK);
-}
+int tiled_bk(bool hilo) { return hilo ? 2 * TiledShape<2>::BK : 128; }
 
 const char* tiled_kernel_name(bool hilo) {
-  if (!hilo && JET_TILED_M16) return "k_project_tiled_m16";
-  return (hilo ? JET_TILED_DTL2 : JET_TILED_DTL) ? "k_project_tiled_dtl" : "k_project_tiled_bf16";
+  return hilo ? "k_project_tiled_bf16" : "k_project_tiled_m16";
 }
 
 hipError_t launch_project_tiled(const ScoreArgs& a) {
@@ -1023,18 +714,13 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
-    hipLaunchKernelGGL((JET_TILED_DTL2 ? k_project_tiled_dtl<2> : k_project_tiled_bf16<2>), grid, block, 0, a.stream, W, p->V, p->d, hhi,
-                       hlo, p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target,
-                       z_tgt, part, R, S, sr, ss, remap);
+    hipLaunchKernelGGL(k_project_tiled_bf16<2>, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
+                       p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
+                       part, R, S, sr, ss, remap);
   } else {
-    if (JET_TILED_M16)
-      hipLaunchKernelGGL(k_project_tiled_m16, grid, block, 0, a.stream, W, p->V, p->d,
-                         static_cast<const uint16_t*>(p->H), p->n_rows, pl.n_vgroups, b_off,
-                         b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
-    else
-      hipLaunchKernelGGL((JET_TILED_DTL ? k_project_tiled_dtl<1> : k_project_tiled_bf16<1>), grid, block, 0, a.stream, W, p->V, p->d,
-                         static_cast<const uint16_t*>(p->H), nullptr, p->n_rows, pl.n_vgroups,
-                         b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
+    hipLaunchKernelGGL(k_project_tiled_m16, grid, block, 0, a.stream, W, p->V, p->d,
+                       static_cast<const uint16_t*>(p->H), p->n_rows, pl.n_vgroups, b_off, b_tok,
+                       p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
   }
   return hipGetLastError();
 }
