@@ -585,8 +585,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
   // k-steps of 64 MFMAs (block (i / 8, i % 8)).  k-step 0 reads the k-step 1 fragments at
   // every fourth slot.  Then every wave is done with buffer bc and stage g + 1 is awaited
   // (its loads were issued during the previous stage's k-step 1) behind the one barrier
-  // of the stage.  k-step 1 reads the k-step 0 fragments of stage g + 1 (even slots
-  // 0..30) and loads stage g + 2 into buffer bc (slots 1, 5, .., 61), so loads get half a
+  // of the stage.  k-step 1 reads the k-step 0 fragments of stage g + 1 (slots 0, 4, ..,
+  // 60) and loads stage g + 2 into buffer bc (slots 2, 6, .., 62), so loads get half a
   // stage to a stage to land and no stage starts by waiting for LDS.
 #define JET_MSTAGE(FIRST)                                                                    \
   {                                                                                          \
@@ -605,9 +605,9 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
     _Pragma("unroll") for (int i = 0; i < 64; ++i) {                                         \
       acc[i / 8][i % 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                           \
           fa[1][i / 8], fb[1][i % 8], acc[i / 8][i % 8], 0, 0, 0);                           \
-      if (i < 32 && i % 2 == 0) {                                                            \
-        JET_FRAG1(0, b_nx * BUFSZ, 0, i / 2);                                                \
-      } else if (i % 4 == 1) {                                                               \
+      if (i % 4 == 0) {                                                                      \
+        JET_FRAG1(0, b_nx * BUFSZ, 0, i / 4);                                                \
+      } else if (i % 4 == 2) {                                                               \
         JET_DMA1(bc, i / 4);                                                                 \
       }                                                                                      \
       __builtin_amdgcn_sched_barrier(0);                                                     \
