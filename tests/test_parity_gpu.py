@@ -123,6 +123,35 @@ def test_tiled_stream(jet, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, 'tiled_stream', sampled=True)} on {len(rows)} rows")
 
 
+@pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
+def test_tiled_grid_bucketing(jet, h_dtype):
+    """More (row tile, vocabulary tile) buckets than one workgroup sorts in LDS, so the
+    targets are bucketed by the grid-wide launches; an out-of-range target and an
+    out-of-range row raise their flags there and leave only their own tokens NaN."""
+    p = wl.make_problem(V=262147, d=128, n_q=40, K=(2, 6), lengths=(1, 4), layout="prefix",
+                        seed=67, h_dtype=h_dtype, n_extra_rows=3000)
+    n_buckets = -(-p["n_rows"] // 256) * -(-p["V"] // 256)
+    log(f"[gpu] grid bucketing {h_dtype} rows={p['n_rows']} V={p['V']} buckets={n_buckets}")
+    assert n_buckets > 12288
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    rows = np.unique(np.asarray(p["tok_row"]))
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] errs {compare(p, out, ref, 'grid_bucketing', sampled=True)} on {len(rows)} rows")
+    q = dict(p)
+    q["tok_target"] = p["tok_target"].copy()
+    q["tok_row"] = p["tok_row"].copy()
+    q["tok_target"][3] = p["V"] + 5
+    q["tok_row"][7] = p["n_rows"] + 9
+    bad = _run(jet, q)
+    assert int(bad["dev_flags"][0]) & 1 and int(bad["dev_flags"][0]) & 2
+    assert np.isnan(bad["tok_logp"][3]) and np.isnan(bad["tok_logp"][7])
+    good = np.ones(len(p["tok_target"]), bool)
+    good[[3, 7]] = False
+    assert np.array_equal(bad["tok_logp"][good], out["tok_logp"][good])
+    assert np.array_equal(bad["row_lse"], out["row_lse"])
+
+
 @pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
 def test_deduplicated_rows(jet, h_dtype):
     """Predictor-row deduplication (history trie built by the library on the host): scoring
