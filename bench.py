@@ -81,6 +81,38 @@ def _timed_runs(fn, min_s: float = 10.0, max_runs: int = 100):
     return runs, total
 
 
+def _stream_read_gbs(buf, stream, reps: int = 20) -> float:
+    """GB/s of jet_stream_read (every byte read once, nothing else) over buf, timed with
+    events on the bench's stream: the achievable read rate next to the 8 TB/s spec."""
+    import torch
+
+    from candidate_likelihood_scoring_amd import api
+    out = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            api.stream_read(buf, out, stream)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            api.stream_read(buf, out, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return buf.numel() * buf.element_size() * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def _cpu_model() -> str:
+    """', on <model name>' of the host CPU, from /proc/cpuinfo (empty if unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return ", on " + line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 30.0) -> dict:
     """The fp64 oracle on the host's cores, on a bounded sample of the same workload: whole
     questions (all of them if they fit about budget_s), repeated until about 10 s of work."""
@@ -96,7 +128,8 @@ def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 30.0) -> dict:
         n = int(p["field_off"][-1])
         runs, dt = _timed_runs(lambda: oracle.score_restricted(p))
         return dict(value=n * runs / dt, unit="scored candidate tokens/s", cores=int(cores), kind="oracle",
-                    sample=f"the whole batch ({n} allowed-token slots), {runs} runs, {dt:.2f} s")
+                    sample=f"the whole batch ({n} allowed-token slots), {runs} runs, {dt:.2f} s"
+                           f"{_cpu_model()}")
     n_tok = len(p["tok_target"])
     tok_row = np.arange(n_tok) if p.get("tok_row") is None else np.asarray(p["tok_row"])
     # Time one question first; then as many whole questions as fit the budget.
@@ -121,7 +154,8 @@ def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 30.0) -> dict:
     what = ("the whole batch" if sample_q == n_q else f"the first {sample_q} of {n_q} questions")
     n_r = n_rows if rows is None else len(rows)
     return dict(value=toks * runs / dt, unit="scored candidate tokens/s", cores=int(cores), kind="oracle",
-                sample=f"{what}: {toks} tokens on {n_r} predictor rows, {runs} runs, {dt:.2f} s")
+                sample=f"{what}: {toks} tokens on {n_r} predictor rows, {runs} runs, {dt:.2f} s"
+                       f"{_cpu_model()}")
 
 
 def main(argv=None) -> int:
@@ -274,6 +308,10 @@ def main(argv=None) -> int:
         traffic = None if args.dedup else _traffic_from_profiles(kernel, args.workload)
         if intensity < 300.0:
             achieved = alg_bytes / k_avg_s / 1e9
+            # the device's plain-read rate over the same head bytes, on the same stream
+            ceiling = _stream_read_gbs(pd["W"], stream)
+            extra["stream_read_gbs"] = round(ceiling, 1)
+            extra["projection_frac_of_stream_read"] = round(achieved / ceiling, 4)
             roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                             frac=round(achieved / HBM_PEAK_GBS, 4),
                             traffic=traffic)

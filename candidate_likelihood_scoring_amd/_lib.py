@@ -67,6 +67,7 @@ EXPORTS = {
     "jet_score_profiled": (c_int, [POINTER(JetProblem), POINTER(JetOutputs), c_void_p, c_size_t,
                                    c_void_p, c_void_p, c_void_p]),
     "jet_projection_kernel": (c_char_p, [POINTER(JetProblem)]),
+    "jet_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "jet_fit_temperature_workspace_size": (c_size_t, [c_int32]),
     "jet_fit_temperature": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                     c_float, c_float, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -176,6 +176,16 @@ def projection_kernel(prob: JetProblem) -> str | None:
     return r.decode() if r else None
 
 
+def stream_read(buf, out, stream=None) -> None:
+    """Read every byte of the device tensor buf once (jet_stream_read); XOR a checksum of its
+    words into out (a one-element int32 device tensor).  Measurement helper."""
+    nbytes = buf.numel() * buf.element_size()
+    st = _stream_handle(stream)
+    rc = _lib.load().jet_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), st)
+    if rc != 0:
+        raise JetError(rc, "jet_stream_read")
+
+
 def score_workspace_size(prob: JetProblem) -> int:
     return int(_lib.load().jet_score_workspace_size(ctypes.byref(prob)))
 

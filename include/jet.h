@@ -141,11 +141,19 @@ JET_API jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o
                               void* ev_after);
 
 /* Name of the projection kernel jet_score launches for this problem (the plan depends
- * only on the problem's scalars), as profilers report it: "k_project_tiled_dtl",
+ * only on the problem's scalars), as profilers report it: "k_project_tiled_m16",
  * "k_project_tiled_bf16", "k_project_wg_bf16", "k_project_small_bf16" or
  * "k_project_small_f32".  NULL when the problem is invalid.  Host only; the string is
  * static. */
 JET_API const char* jet_projection_kernel(const jet_problem* p);
+
+/* Measurement helper, not part of scoring: reads every byte of buf (device memory, 16-byte
+ * aligned, bytes a multiple of 16) once with plain coalesced loads and XORs a checksum of
+ * the words into *out (device memory; not cleared).  Timed around the same bytes the
+ * projection streams, it gives the device's achievable read rate next to the HBM spec.
+ * Enqueued on stream; JET_E_NULL / JET_E_SHAPE on bad arguments, JET_E_HIP on a failed
+ * launch. */
+JET_API jet_status jet_stream_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
 
 /* Host-side validation of a problem whose index arrays (tok_row, tok_target,
  * cand_tok_off, q_cand_off, q_true_idx) are HOST pointers; H and W are not read.

@@ -303,3 +303,14 @@ def test_fit_temperature_host_checks(lib):
     assert call(wsp=None) == -6 and call(wsp=w + 1) == -6 and call(wsb=16) == -6
     assert lib.jet_fit_temperature_workspace_size(0) == 0
     assert 0 < lib.jet_fit_temperature_workspace_size(10) <= lib.jet_fit_temperature_workspace_size(10 ** 6)
+
+
+def test_stream_read_host_checks(lib):
+    """The measurement helper rejects bad arguments before anything is enqueued."""
+    E_NULL, E_SHAPE = -1, -2
+    out = ctypes.c_uint32(0)
+    assert lib.jet_stream_read(None, 1024, ctypes.addressof(out), None) == E_NULL
+    assert lib.jet_stream_read(16, 1024, None, None) == E_NULL
+    assert lib.jet_stream_read(17, 1024, ctypes.addressof(out), None) == E_SHAPE  # misaligned
+    assert lib.jet_stream_read(16, 1000, ctypes.addressof(out), None) == E_SHAPE  # not 16 B whole
+    assert lib.jet_stream_read(16, 0, ctypes.addressof(out), None) == 0            # nothing to read

@@ -326,6 +326,19 @@ def test_true_index_and_gold(jet):
     assert np.isinf(out["q_gold_nll"][0])
 
 
+def test_stream_read_checksum(jet):
+    """The plain-read helper the bench times reads every word once: its XOR checksum
+    matches the host's, for a buffer that is not a multiple of the grid's stride."""
+    from candidate_likelihood_scoring_amd import api
+    rng = np.random.default_rng(12)
+    host = rng.integers(0, 2**32, size=(1 << 22) + 12, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to("cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.stream_read(buf, out)
+    torch.cuda.synchronize()
+    assert int(out.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
+
+
 def test_empty_problem(jet):
     p = wl.make_problem(V=100, d=32, n_q=0, seed=2, n_extra_rows=3)
     out = _run(jet, p)
