@@ -202,7 +202,8 @@ jet_status jet_fit_temperature(const float* cand_s, const int32_t* q_cand_off, i
 jet_status jet_build_predictor_trie(const int32_t* tok_target, const int32_t* cand_tok_off,
                                     int32_t n_cand, const int32_t* q_cand_off, int32_t n_q,
                                     int32_t* tok_node, int32_t* node_tok, int32_t* n_nodes) {
-  if (!cand_tok_off || !q_cand_off || !n_nodes || n_cand < 0 || n_q < 0) return JET_E_NULL;
+  if (!cand_tok_off || !q_cand_off || !n_nodes) return JET_E_NULL;
+  if (n_cand < 0 || n_q < 0) return JET_E_SHAPE;
   if (cand_tok_off[0] != 0 || q_cand_off[0] != 0 || q_cand_off[n_q] != n_cand) return JET_E_SHAPE;
   for (int32_t g = 0; g < n_q; ++g)
     if (q_cand_off[g + 1] <= q_cand_off[g]) return JET_E_SHAPE;

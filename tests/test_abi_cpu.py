@@ -265,6 +265,12 @@ def test_predictor_trie_rejects_malformed_input():
     with pytest.raises(_lib.JetError) as e:
         api.build_predictor_trie([1, -2], [0, 2], [0, 1])     # negative target
     assert e.value.status == -4
+    lib = _lib.load()
+    off = (ctypes.c_int32 * 2)(0, 0)
+    n = ctypes.c_int32(0)
+    assert lib.jet_build_predictor_trie(None, off, -1, off, 0, None, None, ctypes.byref(n)) == -2
+    assert lib.jet_build_predictor_trie(None, off, 0, off, -1, None, None, ctypes.byref(n)) == -2
+    assert lib.jet_build_predictor_trie(None, None, 0, off, 0, None, None, ctypes.byref(n)) == -1
 
 
 def test_decision_sensitivity_host_checks(lib):
