@@ -44,6 +44,27 @@ def _stream_handle(stream) -> int | None:
     return h or None
 
 
+def _enter_stream(stream, *tensors) -> None:
+    """Before enqueueing library work on `stream` (a torch stream or a raw hipStream_t):
+    when it is not the current stream, order it after the current stream's work (where the
+    tensors handed to the library were allocated and initialised) and record the tensors'
+    use on it, so that torch neither overwrites them early nor frees them before it ends."""
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream()
+    if not isinstance(stream, torch.cuda.Stream):
+        h = int(stream)
+        if h == 0 or h == cur.cuda_stream:
+            return
+        stream = torch.cuda.ExternalStream(h)
+    elif stream == cur:
+        return
+    stream.wait_stream(cur)
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            t.record_stream(stream)
+
+
 class Workspace:
     """A reusable device workspace (grown on demand, 256-byte aligned)."""
 
@@ -131,6 +152,7 @@ def decision_sensitivity(z: torch.Tensor, z_skip: torch.Tensor, seg_off: torch.T
                J=torch.empty(L, dtype=torch.float32, device=dev),
                selected=torch.empty(max(k, 1), dtype=torch.int32, device=dev),
                dev_flags=torch.zeros(1, dtype=torch.int32, device=dev))
+    _enter_stream(stream, z, z_skip, seg_off, *out.values())
     sh = _stream_handle(stream)
     st = _lib.load().jet_decision_sensitivity(
         _ptr(z), _ptr(z_skip), _ptr(seg_off), n_in, int(z.numel()), L, float(eps), int(k),
@@ -160,6 +182,7 @@ def fit_temperature(cand_s: torch.Tensor, q_cand_off: torch.Tensor, cand_text_id
     need = int(lib.jet_fit_temperature_workspace_size(max(n_q, 1)))
     ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
     base = (ws.data_ptr() + 255) & ~255
+    _enter_stream(stream, cand_s, q_cand_off, cand_text_id, q_gold_text_id, ws, *out.values())
     st = lib.jet_fit_temperature(
         _ptr(cand_s), _ptr(q_cand_off), n_q, int(cand_s.numel()),
         _ptr(cand_text_id), _ptr(q_gold_text_id), float(T_min), float(T_max), _ptr(out["T"]),
@@ -180,6 +203,7 @@ def stream_read(buf, out, stream=None) -> None:
     """Read every byte of the device tensor buf once (jet_stream_read); XOR a checksum of its
     words into out (a one-element int32 device tensor).  Measurement helper."""
     nbytes = buf.numel() * buf.element_size()
+    _enter_stream(stream, buf, out)
     st = _stream_handle(stream)
     rc = _lib.load().jet_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), st)
     if rc != 0:
@@ -226,6 +250,8 @@ def score(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None, cand_
         raise JetError(lib.jet_score(ctypes.byref(prob), ctypes.byref(o), None, 0, sh), "jet_score")
     ws = _workspace(workspace, W.device)
     base, size = ws.get(need)
+    _enter_stream(stream, H, W, tok_target, cand_tok_off, q_cand_off, tok_row, cand_text_id,
+                  q_gold_text_id, q_true_idx, ws.buf, *out.values())
     if events is None:
         st = lib.jet_score(ctypes.byref(prob), ctypes.byref(o), base, size, sh)
     else:
@@ -313,7 +339,10 @@ def score_restricted(H, W, union_ids, field_row, field_slot_off, slot_uidx, T=1.
     if need == 0:  # invalid scalars: the entry point reports which check failed
         raise JetError(lib.jet_score_restricted(ctypes.byref(prob), ctypes.byref(o), None, 0,
                                                 _stream_handle(stream)), "jet_score_restricted")
-    base, size = _workspace(workspace, dev).get(need)
+    ws = _workspace(workspace, dev)
+    base, size = ws.get(need)
+    _enter_stream(stream, H, W, union_ids, field_row, field_slot_off, slot_uidx, ws.buf,
+                  *out.values())
     st = lib.jet_score_restricted(ctypes.byref(prob), ctypes.byref(o), base, size,
                                   _stream_handle(stream))
     if st != 0:

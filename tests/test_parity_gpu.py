@@ -326,6 +326,21 @@ def test_true_index_and_gold(jet):
     assert np.isinf(out["q_gold_nll"][0])
 
 
+def test_side_stream_matches_current_stream(jet):
+    """Scoring on a stream other than the current one (outputs and workspace allocated, and
+    the flag word zeroed, on the current stream) gives the same bits as on the current one."""
+    from candidate_likelihood_scoring_amd import api
+    p = wl.make_problem(V=6151, d=128, n_q=12, K=(2, 6), lengths=(1, 4), layout="prefix", seed=71)
+    dp = jet.to_device(p, "cuda")
+    ref = api.score(**dp)
+    side = torch.cuda.Stream()
+    got = api.score(**dp, workspace=api.Workspace("cuda"), stream=side)
+    torch.cuda.synchronize()
+    for k in ref:  # bit patterns: q_true is NaN for non-binary questions
+        assert torch.equal(ref[k].view(torch.int32), got[k].view(torch.int32)), k
+    assert int(got["dev_flags"][0]) == 0
+
+
 def test_stream_read_checksum(jet):
     """The plain-read helper the bench times reads every word once: its XOR checksum
     matches the host's, for a buffer that is not a multiple of the grid's stride."""
