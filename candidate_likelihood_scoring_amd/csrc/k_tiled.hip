@@ -427,11 +427,21 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 // each).  On this matrix-core shape the chip sustains a higher clock under its power limit
 // than with 32 x 32 blocks, which more than pays for the extra instructions.  Operand
 // layout: lane l supplies row (A) or column (B) l % 16 and k = 8 (l / 16) + j, so a stage's
-// k-step ks (32 wide) reads chunk 4 ks + l / 16; the swizzle depends on row & 15 = l % 16,
-// so the 16 lanes of a quarter-wave hit 16 different bank groups.  Output register i of
+// k-step ks (32 wide) reads chunk 4 ks + l / 16 (swizzled by swz16).  Output register i of
 // lane l holds vocabulary entry 4 (l / 16) + i and row l % 16 of its block.
 // ------------------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// Chunk swizzle of the 16 x 16 kernel, a function of row & 15: logical chunk c of row r
+// sits in slot c ^ swz16(r).  A quarter-wave reads 16 consecutive rows at one chunk, and
+// lanes l and l + 32 are served together (the same 8 rows at chunks c and c + 2, c with
+// bit 1 clear).  Both are conflict-free when the rows of one parity get distinct values
+// and no two rows of one parity within an aligned group of 8 differ by 2 (XOR): value
+// 4 b2 + 2 b3 + b1 of the row's bits.  A plain XOR with row & 7 doubled the LDS time of the
+// fragment reads.
+__device__ inline int swz16(int r) {
+  return (((r >> 2) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 1) & 1);
+}
 
 // Fold a finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
 // this lane's eight rows and capture the tile's scored targets (see tile_epilogue).
@@ -531,14 +541,14 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
   const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
   const uint32_t hrow = (uint32_t)row0 * rowb;
   const int dr = wid * RPD + lane / CH;
-  const uint32_t dvoff = (uint32_t)dr * rowb + (uint32_t)(((lane % CH) ^ swz<CH>(dr)) * 16);
+  const uint32_t dvoff = (uint32_t)dr * rowb + (uint32_t)(((lane % CH) ^ swz16(dr)) * 16);
   const uint32_t m0_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds +
                            (uint32_t)wid * 1024u;
   // fragment slot of k-step ks (0, 1) for block row 0 of this wave's half: row r16 of the
   // block, chunk 4 ks + q; blocks are 16 rows (128 slots) apart
   int fslot[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) fslot[ks] = r16 * CH + ((4 * ks + q) ^ swz<CH>(r16));
+  for (int ks = 0; ks < 2; ++ks) fslot[ks] = r16 * CH + ((4 * ks + q) ^ swz16(r16));
   const int a_off = wm * 128 * CH, b_off_h = ASZ + wn * 128 * CH;
 
 #pragma unroll
