@@ -113,8 +113,9 @@ hipError_t launch_merge(const ScoreArgs& a);
 hipError_t launch_decide(const ScoreArgs& a);
 
 struct RestrictedPlan {
-  bool hilo;
-  size_t off_wu, off_hhi, off_hlo, off_z, off_flags, total;
+  bool fused;  // bf16 head: gather and split inside the projection, k-split partials of Z
+  int n_kg;    // partial sums of Z (k groups)
+  size_t off_wu, off_z, off_flags, total;
 };
 bool make_restricted_plan(const jet_restricted_problem* p, RestrictedPlan* plan);
 hipError_t launch_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
@@ -125,11 +126,8 @@ hipError_t launch_restricted(const jet_restricted_problem* p, const jet_restrict
 hipError_t launch_split(const float* H, long long n_elems, uint16_t* hi, uint16_t* lo,
                         hipStream_t stream);
 
-// Projection core used by the restricted path: Z[row][u] = <H[row], Wu[u]> for all rows and
-// union entries (bf16 head rows; H bf16 or split fp32).
-hipError_t launch_project_store_bf16(const uint16_t* Wu, int U, int d, const uint16_t* Hhi,
-                                     const uint16_t* Hlo, int n_rows, float* Z,
-                                     hipStream_t stream);
+// Projection core of the restricted path with an fp32 head: Z[row][u] = <H[row], Wu[u]>
+// for all rows and gathered union entries.
 hipError_t launch_project_store_f32(const float* Wu, int U, int d, const float* H, int n_rows,
                                     float* Z, hipStream_t stream);
 

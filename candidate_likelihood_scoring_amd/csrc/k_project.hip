@@ -114,7 +114,8 @@ __device__ inline void store_partial(float m_run, float s_run, int n, int half, 
   }
 }
 
-// Store epilogue (restricted path): Z[row][v] for valid rows and vocabulary entries.
+// Store epilogue (restricted path with an fp32 head): Z[row][v] for valid rows and
+// vocabulary entries.
 template <int NT>
 __device__ inline void epilogue_store(const Acc<NT>& acc, int v0, int V, int n, int half,
                                       int row0, int n_rows, float* __restrict__ Z) {
@@ -153,13 +154,12 @@ __device__ inline FragK<KB> ldk(const uint16_t* p) {
 // ------------------------------------------------------------------------------------
 // bf16 head
 // ------------------------------------------------------------------------------------
-template <int NT, int KB, int S, bool HILO, bool STORE>
+template <int NT, int KB, int S, bool HILO>
 __global__ __launch_bounds__(256) void k_project_small_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ Hhi,
     const uint16_t* __restrict__ Hlo, int n_rows, int n_groups, const int* __restrict__ b_off,
     const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
-    float* __restrict__ Z) {
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part) {
   static_assert(KB % 32 == 0 && S >= 2, "stage shape");
   __shared__ float2 red[kWpb][32];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -221,13 +221,10 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
         }
       }
     }
-    if (STORE)
-      epilogue_store<NT>(acc, v0, V, n, half, row0, n_rows, Z);
-    else
-      epilogue_lse<NT>(acc, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
-                       tok_target, z_tgt, m_run, s_run);
+    epilogue_lse<NT>(acc, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
+                     tok_target, z_tgt, m_run, s_run);
   }
-  if (!STORE) store_partial(m_run, s_run, n, half, wid, row0, n_rows, part, red);
+  store_partial(m_run, s_run, n, half, wid, row0, n_rows, part, red);
 }
 
 // ------------------------------------------------------------------------------------
@@ -492,14 +489,14 @@ hipError_t launch_project(const ScoreArgs& a) {
     if (pl.hilo) {
       const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
       const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
-      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, true, false>), grid, block, 0, a.stream,
+      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, true>), grid, block, 0, a.stream,
                          W, p->V, p->d, hhi, hlo, p->n_rows, pl.n_vgroups, b_off, b_tok,
-                         p->tok_row, p->tok_target, z_tgt, part, nullptr);
+                         p->tok_row, p->tok_target, z_tgt, part);
     } else {
       const uint16_t* h = static_cast<const uint16_t*>(p->H);
-      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, false, false>), grid, block, 0,
+      hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, false>), grid, block, 0,
                          a.stream, W, p->V, p->d, h, nullptr, p->n_rows, pl.n_vgroups, b_off,
-                         b_tok, p->tok_row, p->tok_target, z_tgt, part, nullptr);
+                         b_tok, p->tok_row, p->tok_target, z_tgt, part);
     }
   } else if (pl.variant == VAR_SMALL_F32) {
     hipLaunchKernelGGL((k_project_small_f32<kSmallNTf32, false>), grid, block, 0, a.stream,
@@ -531,22 +528,6 @@ int small_grid(int variant, int d, int n_groups, int max_waves) {
 static int store_grid(int n_groups) {
   int g = (n_groups + kWpb - 1) / kWpb;
   return g < 1 ? 1 : g;
-}
-
-hipError_t launch_project_store_bf16(const uint16_t* Wu, int U, int d, const uint16_t* Hhi,
-                                     const uint16_t* Hlo, int n_rows, float* Z,
-                                     hipStream_t stream) {
-  const int n_groups = (U + 31) / 32;
-  dim3 grid(store_grid(n_groups), (n_rows + 31) / 32), block(256);
-  if (Hlo)
-    hipLaunchKernelGGL((k_project_small_bf16<1, 32, 2, true, true>), grid, block, 0, stream, Wu, U, d,
-                       Hhi, Hlo, n_rows, n_groups, nullptr, nullptr, nullptr, nullptr, nullptr,
-                       nullptr, Z);
-  else
-    hipLaunchKernelGGL((k_project_small_bf16<1, 32, 2, false, true>), grid, block, 0, stream, Wu, U, d,
-                       Hhi, nullptr, n_rows, n_groups, nullptr, nullptr, nullptr, nullptr,
-                       nullptr, nullptr, Z);
-  return hipGetLastError();
 }
 
 hipError_t launch_project_store_f32(const float* Wu, int U, int d, const float* H, int n_rows,

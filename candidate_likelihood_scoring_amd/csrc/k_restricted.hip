@@ -2,13 +2,16 @@
 // steps 5-6): gather only the allowed head rows, project the hidden states onto their
 // union, and let each field take a softmax over its own allowed ids at temperature T.
 //
-//   k_gather_rows : Wu[j, :] = W[union_ids[j], :], a bit-exact copy of each row with
-//                   16-byte coalesced loads/stores (one workgroup per union row).
-//   projection    : Z[r, j] = <H[r], Wu[j]> with the small-row matrix-core kernel's store
-//                   epilogue (fp32 accumulation; fp32 H split into bf16 hi + lo).
-//   k_field_softmax: one wave per field: slot_logit = Z[field_row, slot_uidx], a = logit/T,
-//                   q = softmax(a) over the field's slots, argmax = lowest index among the
-//                   exact maxima of a.
+// bf16 head (two launches):
+//   k_restricted_project: Z[r, j] = <H[r], W[union_ids[j]]> on the matrix cores, fp32
+//                   accumulation, with the row gather and the fp32 split (H = hi + lo, both
+//                   bf16) done in the operand loads, so the gathered rows never exist in
+//                   memory; k is split over workgroups, which store fp32 partial sums.
+//   k_field_softmax: one wave per field: slot_logit = the sum of the partials (in a fixed
+//                   order) at (field_row, slot_uidx), a = logit/T, q = softmax(a) over the
+//                   field's slots, argmax = lowest index among the exact maxima of a.
+// fp32 head: k_gather_rows (Wu[j, :] = W[union_ids[j], :], 16-byte coalesced copies), the
+// small-row fp32 kernel's store epilogue, then k_field_softmax.
 #include "jet_internal.h"
 
 namespace jet {
@@ -32,11 +35,122 @@ __global__ void k_clear_flag(int32_t* __restrict__ flags) {
   if (threadIdx.x == 0) flags[0] = 0;
 }
 
+// Projection onto the union for a bf16 head.  Tile (ut, rt, kg) covers union entries
+// [32 ut, 32 ut + 32), rows [32 rt, 32 rt + 32) and k in [512 kg, 512 kg + 512); wave w of
+// the workgroup takes the 128-wide k slice at 512 kg + 128 w and issues all of its loads
+// before its first matrix op, so a tile costs one memory round trip.  Lane l supplies
+// union entry l % 32 (A operand, read straight from the head row union_ids[.]) and row
+// l % 32 (B operand); in each 32-wide block kb its half h = l / 32 covers k in
+// [kb + 16 h, kb + 16 h + 16): 32 contiguous bytes of the head row and 32 (bf16 H) or 64
+// (fp32 H) of the hidden row, consumed by two v_mfma_f32_32x32x16_bf16 (A and B use the
+// same k order, so the sum is unchanged).  fp32 H is split on the fly, hi = bf16(x) and
+// lo = bf16(x - hi), two products per step.  The four waves' 32x32 tiles are added in wave
+// order through LDS and stored as the partial Zp[kg][u][row] (rows contiguous, so each
+// store instruction writes two 128-byte runs).  An id outside [0, V) reads as a zero row;
+// k_field_softmax reports it.  Workgroup 0 clears the flag word first: this kernel sets no
+// flags, and the next launch on the stream does.
+constexpr int kRkWave = 128, kRWaves = 4, kRkTile = kRkWave * kRWaves;
+
+template <bool HF32>
+__global__ __launch_bounds__(256) void k_restricted_project(
+    const uint16_t* __restrict__ W, int V, int d, const int* __restrict__ ids, int n_union,
+    const void* __restrict__ H, int n_rows, int n_ut, int n_rt, int n_kg,
+    float* __restrict__ Zp, int32_t* __restrict__ flags) {
+  __shared__ f32x16 red[kRWaves - 1][kWave];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int m = lane & 31, h = lane >> 5;
+  if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0;
+  const long long n_tiles = (long long)n_ut * n_rt * n_kg;
+  for (long long tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int kg = (int)(tile % n_kg);
+    const int rt = (int)((tile / n_kg) % n_rt);
+    const int ut = (int)(tile / ((long long)n_kg * n_rt));
+    const int u0 = ut * 32, row0 = rt * 32;
+    const int id = ids[min(u0 + m, n_union - 1)];
+    const bool id_ok = id >= 0 && id < V;
+    const uint16_t* wrow = W + (size_t)(id_ok ? id : 0) * d;
+    const int hr = min(row0 + m, n_rows - 1);
+    const int k0 = kg * kRkTile + wid * kRkWave;
+    // 32-wide blocks of this wave's slice inside [0, d) (d is a multiple of 32); blocks
+    // past the end load the last block again (in bounds) and are not used
+    const int nb = min(kRkWave, max(0, d - k0)) / 32;
+    uint4 a[4][2], b[4][HF32 ? 4 : 2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = min(k0 + 32 * t, d - 32) + 16 * h;
+      const uint4* wp = reinterpret_cast<const uint4*>(wrow + kb);
+      a[t][0] = wp[0];
+      a[t][1] = wp[1];
+      if constexpr (HF32) {
+        const uint4* hp = reinterpret_cast<const uint4*>(static_cast<const float*>(H) + (size_t)hr * d + kb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[t][j] = hp[j];
+      } else {
+        const uint4* hp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(H) + (size_t)hr * d + kb);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[t][j] = hp[j];
+      }
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < nb) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint4 av = id_ok ? a[t][j] : make_uint4(0, 0, 0, 0);
+          if constexpr (HF32) {
+            const uint4 x0 = b[t][2 * j], x1 = b[t][2 * j + 1];
+            uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+            split_pair(__uint_as_float(x0.x), __uint_as_float(x0.y), h0, l0);
+            split_pair(__uint_as_float(x0.z), __uint_as_float(x0.w), h1, l1);
+            split_pair(__uint_as_float(x1.x), __uint_as_float(x1.y), h2, l2);
+            split_pair(__uint_as_float(x1.z), __uint_as_float(x1.w), h3, l3);
+            const u32x4 hi = {h0, h1, h2, h3}, lo = {l0, l1, l2, l3};
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, hi), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, lo), acc, 0, 0, 0);
+          } else {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, b[t][j]), acc, 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (wid > 0) red[wid - 1][lane] = acc;
+    __syncthreads();
+    if (wid == 0) {
+#pragma unroll
+      for (int w = 0; w < kRWaves - 1; ++w) acc += red[w][lane];
+      // output (union entry, row) of register i: entry 8 (i / 4) + 4 h + i % 4, row lane % 32
+      const int row = row0 + m;
+      if (row < n_rows) {
+        float* zp = Zp + (size_t)kg * n_union * n_rows;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int u = u0 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (u < n_union) zp[(size_t)u * n_rows + row] = acc[i];
+        }
+      }
+    }
+    __syncthreads();  // red is rewritten by the next tile
+  }
+}
+
+// Z holds n_part partial sums of the logits: z(r, u) = sum over p in order 0, 1, ... of
+// Z[p * part_stride + u * u_stride + r * r_stride].  Every workgroup also checks a strided
+// share of the union ids (an id outside [0, V) raises JET_FLAG_BAD_UNION).
 __global__ __launch_bounds__(256) void k_field_softmax(
-    const float* __restrict__ Z, int n_rows, int n_union, const int* __restrict__ field_row,
-    const int* __restrict__ slot_off, const int* __restrict__ slot_uidx, int n_fields, int n_slots,
-    float T, float* __restrict__ slot_logit, float* __restrict__ slot_q, int* __restrict__ f_argmax,
+    const float* __restrict__ Z, int n_part, size_t part_stride, int u_stride, int r_stride,
+    int n_rows, int n_union, const int* __restrict__ ids, int V,
+    const int* __restrict__ field_row, const int* __restrict__ slot_off,
+    const int* __restrict__ slot_uidx, int n_fields, int n_slots, float T,
+    float* __restrict__ slot_logit, float* __restrict__ slot_q, int* __restrict__ f_argmax,
     int32_t* __restrict__ flags) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n_union; j += gridDim.x * blockDim.x) {
+    const int id = ids[j];
+    if (id < 0 || id >= V) flag_or(flags, JET_FLAG_BAD_UNION);
+  }
   const int lane = threadIdx.x & 63;
   const int f = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (f >= n_fields) return;
@@ -58,8 +172,13 @@ __global__ __launch_bounds__(256) void k_field_softmax(
   for (int j = j0 + lane; j < j1; j += 64) {
     const int u = slot_uidx[j];
     float z = NaN;
-    if (row_ok && u >= 0 && u < n_union) z = Z[(size_t)r * n_union + u];
-    else bad = true;
+    if (row_ok && u >= 0 && u < n_union) {
+      const float* zp = Z + (size_t)u * u_stride + (size_t)r * r_stride;
+      z = zp[0];
+      for (int q = 1; q < n_part; ++q) z += zp[q * part_stride];
+    } else {
+      bad = true;
+    }
     slot_logit[j] = z;
     const float a = z / T;
     if (a > best) {
@@ -90,67 +209,76 @@ __global__ __launch_bounds__(256) void k_field_softmax(
 bool make_restricted_plan(const jet_restricted_problem* p, RestrictedPlan* pl) {
   const size_t elt = p->w_dtype == JET_BF16 ? 2 : 4;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
+  // bf16 head: k-split partials of Z, no gathered copy; fp32 head: the gathered rows and Z
+  pl->fused = p->w_dtype == JET_BF16;
+  pl->n_kg = pl->fused ? (p->d + kRkTile - 1) / kRkTile : 1;
   size_t off = 0;
   pl->off_wu = off;
-  off += al((size_t)p->n_union * p->d * elt);
-  pl->off_hhi = off;
-  if (pl->hilo) off += al((size_t)p->n_rows * p->d * 2);
-  pl->off_hlo = off;
-  if (pl->hilo) off += al((size_t)p->n_rows * p->d * 2);
+  if (!pl->fused) off += al((size_t)p->n_union * p->d * elt);
   pl->off_z = off;
-  off += al((size_t)p->n_rows * p->n_union * 4);
+  off += al((size_t)pl->n_kg * p->n_rows * p->n_union * 4);
   pl->off_flags = off;
   off += 256;
   pl->total = off;
   return true;
 }
 
-hipError_t launch_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
-                             const RestrictedPlan* pl, char* ws, int32_t* flags,
-                             hipStream_t stream) {
-  const size_t elt = p->w_dtype == JET_BF16 ? 2 : 4;
-  const int row_vec = (int)((size_t)p->d * elt / 16);
-  // flags: cleared by a one-thread kernel (no memset, so the sequence stays capturable)
+// fp32 head: clear the flags, gather the union rows, project them with the small-row fp32
+// kernel's store epilogue into Z[row][u].
+static hipError_t launch_restricted_f32(const jet_restricted_problem* p, const RestrictedPlan* pl,
+                                        char* ws, int32_t* flags, float* Z, hipStream_t stream) {
+  const int row_vec = (int)((size_t)p->d * 4 / 16);
   hipError_t e;
   hipLaunchKernelGGL(k_clear_flag, dim3(1), dim3(64), 0, stream, flags);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p->n_union > 0) {
-    int grid = p->n_union < 4096 ? p->n_union : 4096;
+    const int grid = p->n_union < 4096 ? p->n_union : 4096;
     hipLaunchKernelGGL(k_gather_rows, dim3(grid), dim3(256), 0, stream,
                        static_cast<const uint4*>(p->W), p->V, row_vec, p->union_ids, p->n_union,
                        reinterpret_cast<uint4*>(ws + pl->off_wu), flags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if (p->n_union > 0 && p->n_rows > 0)
+    return launch_project_store_f32(reinterpret_cast<const float*>(ws + pl->off_wu), p->n_union,
+                                    p->d, static_cast<const float*>(p->H), p->n_rows, Z, stream);
+  return hipSuccess;
+}
+
+hipError_t launch_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
+                             const RestrictedPlan* pl, char* ws, int32_t* flags,
+                             hipStream_t stream) {
+  // the flag word is cleared by the first kernel (no memset, so the sequence stays
+  // capturable) and set only by kernels after it
+  hipError_t e;
   float* Z = reinterpret_cast<float*>(ws + pl->off_z);
-  if (p->n_union > 0 && p->n_rows > 0) {
-    if (p->w_dtype == JET_BF16) {
-      const uint16_t* hhi;
-      const uint16_t* hlo = nullptr;
-      if (pl->hilo) {
-        uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl->off_hhi);
-        uint16_t* lo = reinterpret_cast<uint16_t*>(ws + pl->off_hlo);
-        if ((e = launch_split(static_cast<const float*>(p->H), (long long)p->n_rows * p->d, hi, lo,
-                              stream)) != hipSuccess)
-          return e;
-        hhi = hi;
-        hlo = lo;
-      } else {
-        hhi = static_cast<const uint16_t*>(p->H);
-      }
-      e = launch_project_store_bf16(reinterpret_cast<const uint16_t*>(ws + pl->off_wu), p->n_union,
-                                    p->d, hhi, hlo, p->n_rows, Z, stream);
-    } else {
-      e = launch_project_store_f32(reinterpret_cast<const float*>(ws + pl->off_wu), p->n_union,
-                                   p->d, static_cast<const float*>(p->H), p->n_rows, Z, stream);
-    }
-    if (e != hipSuccess) return e;
+  size_t part_stride = 0;
+  int u_stride = 1, r_stride = p->n_union;
+  if (pl->fused) {
+    // one launch whatever the sizes: its workgroup 0 clears the flag word
+    const int n_ut = (p->n_union + 31) / 32, n_rt = (p->n_rows + 31) / 32;
+    const long long n_tiles = (long long)n_ut * n_rt * pl->n_kg;
+    const int grid = n_tiles < 1 ? 1 : (n_tiles > 65536 ? 65536 : (int)n_tiles);
+    if (p->h_dtype == JET_F32)
+      hipLaunchKernelGGL(k_restricted_project<true>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(p->W), p->V, p->d, p->union_ids, p->n_union,
+                         p->H, p->n_rows, n_ut, n_rt, pl->n_kg, Z, flags);
+    else
+      hipLaunchKernelGGL(k_restricted_project<false>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(p->W), p->V, p->d, p->union_ids, p->n_union,
+                         p->H, p->n_rows, n_ut, n_rt, pl->n_kg, Z, flags);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    part_stride = (size_t)p->n_union * p->n_rows;
+    u_stride = p->n_rows;
+    r_stride = 1;
+  } else {
+    if ((e = launch_restricted_f32(p, pl, ws, flags, Z, stream)) != hipSuccess) return e;
   }
-  if (p->n_fields > 0) {
-    hipLaunchKernelGGL(k_field_softmax, dim3((p->n_fields + 3) / 4), dim3(256), 0, stream, Z,
-                       p->n_rows, p->n_union, p->field_row, p->field_slot_off, p->slot_uidx,
-                       p->n_fields, p->n_slots, p->T, o->slot_logit, o->slot_q, o->field_argmax,
-                       flags);
+  if (p->n_fields > 0 || p->n_union > 0) {
+    const int grid = p->n_fields > 0 ? (p->n_fields + 3) / 4 : 1;
+    hipLaunchKernelGGL(k_field_softmax, dim3(grid), dim3(256), 0, stream, Z, pl->n_kg,
+                       part_stride, u_stride, r_stride, p->n_rows, p->n_union, p->union_ids, p->V,
+                       p->field_row, p->field_slot_off, p->slot_uidx, p->n_fields, p->n_slots,
+                       p->T, o->slot_logit, o->slot_q, o->field_argmax, flags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

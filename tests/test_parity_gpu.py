@@ -501,6 +501,9 @@ def test_restricted(jet, max_variant):
     dict(n_fields=70, V=30011, d=256, K=(1, 26), seed=4, shared_rows=True, n_rows=9),
     dict(n_fields=3, V=500, d=32, K=(2, 4), seed=5, h_dtype="bf16"),
     dict(n_fields=4, V=700, d=64, K=(1, 5), seed=6, w_dtype="f32"),
+    # several union tiles, two row tiles with a ragged tail, d = 512 + 96 (a partial k group)
+    dict(n_fields=45, V=20000, d=608, K=(1, 26), seed=7),
+    dict(n_fields=40, V=3000, d=1056, K=(1, 26), seed=8, h_dtype="bf16", n_rows=33),
 ])
 def test_restricted_ragged(jet, case):
     rp = wl.make_restricted(T=1.7, **case)
@@ -514,3 +517,24 @@ def test_restricted_ragged(jet, case):
     assert np.max(np.abs(out["slot_q"] - ref["slot_q"])) <= Q_TOL
     dec = ref["field_gap"] > Q_TOL
     assert np.array_equal(out["field_argmax"][dec], ref["field_argmax"][dec])
+
+
+def test_restricted_bad_union_id(jet):
+    """A union id outside [0, V) on the device reads as a zero head row and raises
+    JET_FLAG_BAD_UNION; fields that do not use it are scored as usual."""
+    rp = wl.make_restricted(n_fields=12, V=4000, d=256, K=(2, 6), seed=9)
+    rd = jet.restricted_to_device(rp, "cuda")
+    bad = len(rd["host_union"]) - 1
+    rd["union_ids"][bad] = rp["V"] + 7
+    out = jet.to_numpy(jet.score_restricted_problem(rd))
+    torch.cuda.synchronize()
+    assert out["dev_flags"][0] & 16
+    ref = jo.score_restricted(rp)
+    fo = rp["field_off"]
+    uses = np.array([bad in rd["host_slot_uidx"][fo[f]:fo[f + 1]] for f in range(len(fo) - 1)])
+    assert uses.any() and not uses.all()
+    slot_bad = rd["host_slot_uidx"] == bad
+    assert np.all(out["slot_logit"][slot_bad] == 0.0)
+    keep = np.repeat(~uses, np.diff(fo))
+    assert np.max(np.abs(out["slot_logit"][keep] - ref["slot_logit"][keep])) <= 2e-3
+    assert np.max(np.abs(out["slot_q"][keep] - ref["slot_q"][keep])) <= Q_TOL
