@@ -101,6 +101,47 @@ def _stream_read_gbs(buf, stream, reps: int = 20) -> float:
     return buf.numel() * buf.element_size() * reps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
+def _per_call_ms(fn, stream, n: int):
+    """Median and minimum of n single-call durations, each bracketed by its own events on
+    the bench's stream (the warm per-call latency of a launch-bound workload)."""
+    import torch
+
+    pairs = []
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in pairs)
+    return ms[len(ms) // 2], ms[0]
+
+
+def _full_path_step(p: dict, dev, lib, stream):
+    """A jet_score step over the restricted problem's fields posed as single-token
+    candidates of a full-vocabulary problem (same H, head, ids and T), for the restricted
+    path's speedup; returns the step function and what it holds alive."""
+    import workloads as wl
+    from candidate_likelihood_scoring_amd import _lib, api, problem
+
+    pd = problem.to_device(wl.restricted_as_full(p), dev)
+    prob = api.make_problem(**pd)
+    ws = api.Workspace(dev)
+    base, size = ws.get(api.score_workspace_size(prob))
+    out = api.alloc_outputs(prob, dev, optional=True)
+    o = api._outputs_struct(out)
+    sh = stream.cuda_stream or None
+
+    def step():
+        st = lib.jet_score(ctypes.byref(prob), ctypes.byref(o), base, size, sh)
+        if st:
+            raise _lib.JetError(st, "jet_score")
+
+    return step, (pd, prob, ws, out, o)
+
+
 def _cpu_model() -> str:
     """', on <model name>' of the host CPU, from /proc/cpuinfo (empty if unavailable)."""
     try:
@@ -289,15 +330,32 @@ def main(argv=None) -> int:
     value = n_tokens * args.steps / wall
 
     V, d = int(p["V"]), int(p["d"])
+    extra = {}
+    if restricted or args.workload == "tiny":
+        # launch-bound workloads: warm per-call latency, median and minimum
+        med, mn = _per_call_ms(step, stream, args.steps)
+        extra["call_ms_median"] = round(med, 5)
+        extra["call_ms_min"] = round(mn, 5)
+    if restricted:
+        # the same fields through the full-vocabulary path (one jet_score call)
+        _log("[bench] timing the full-vocabulary path on the same fields")
+        full_step, _keep = _full_path_step(p, dev, lib, stream)
+        for _ in range(args.warmup):
+            full_step()
+        med_f, mn_f = _per_call_ms(full_step, stream, args.steps)
+        extra["full_path_call_ms_median"] = round(med_f, 5)
+        extra["full_path_call_ms_min"] = round(mn_f, 5)
+        extra["speedup_over_full_path"] = round(med_f / extra["call_ms_median"], 2)
+        del _keep
     w_elt = 4 if p["w_dtype"] == "f32" else 2
     rows = int(p["n_rows"])
     roofline = None
-    extra = {}
     if events:
         kms = np.array([a.elapsed_time(b) for a, b in events])
         k_avg_s = float(kms.mean()) * 1e-3
         extra["projection_kernel_ms_mean"] = round(float(kms.mean()), 5)
         extra["projection_kernel_ms_min"] = round(float(kms.min()), 5)
+        extra["projection_kernel_ms_median"] = round(float(np.median(kms)), 5)
         flops = 2.0 * rows * d * V
         h_bytes = rows * d * (4 if p["h_dtype"] == "f32" else 2)
         alg_bytes = V * d * w_elt + h_bytes
@@ -321,6 +379,9 @@ def main(argv=None) -> int:
             roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                             frac=round(achieved / peak, 4),
                             traffic=traffic)
+            if p["h_dtype"] == "f32" and p["w_dtype"] == "bf16":
+                # fp32 H runs as two bf16 planes (hi and lo): twice the algorithmic MFMA work
+                extra["executed_mfma_frac"] = round(2.0 * achieved / peak, 4)
         extra["kernel"] = kernel
         extra["algorithmic_bytes_per_launch"] = int(alg_bytes)
         extra["algorithmic_flop_per_launch"] = int(flops)
