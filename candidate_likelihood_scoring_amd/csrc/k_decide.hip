@@ -35,15 +35,26 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
+// Lane i folds partials i, i + 64, ... in order; eight of them are loaded before any is
+// folded, so the loads of a row overlap instead of waiting one after another.
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, int n_parts,
                                                int n_rows, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;
   float m = -INFINITY, s = 0.f;
-  for (int j = lane; j < n_parts; j += 64) {
-    const float2 v = part[(size_t)j * n_rows + row];
-    lse_merge(m, s, v.x, v.y);
+  for (int j0 = lane; j0 < n_parts; j0 += 64 * kMergeBatch) {
+    float2 v[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int j = j0 + 64 * u;
+      v[u] = j < n_parts ? part[(size_t)j * n_rows + row] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (j0 + 64 * u < n_parts) lse_merge(m, s, v[u].x, v[u].y);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -84,6 +95,8 @@ __global__ __launch_bounds__(256) void k_decide(
   float best = -INFINITY, smax = -INFINITY;
   int best_c = c1;  // sentinel: no finite candidate seen
   bool bad_off = false;
+  // with at most 64 candidates a lane holds one: its sum stays in a register for passes 2-3
+  float s_mine = 0.f;
   for (int c = c0 + lane; c < c1; c += 64) {
     int t0 = cand_tok_off[c], t1 = cand_tok_off[c + 1];
     float s = 0.f;
@@ -99,6 +112,7 @@ __global__ __launch_bounds__(256) void k_decide(
       }
     }
     cand_s[c] = s;
+    s_mine = s;
     smax = fmaxf(smax, s);
     const float a = s / T;
     if (a > best || (a == best && c < best_c)) {
@@ -120,10 +134,11 @@ __global__ __launch_bounds__(256) void k_decide(
   const float Ms = wave_max(smax);  // shift of the mass sum
   const bool have_text = cand_text_id && q_gold_text_id;
   const int gold = have_text ? q_gold_text_id[q] : 0;
+  const bool one_each = K <= 64;
   // pass 2: normalisers (all candidates; gold-text candidates)
   float z_part = 0.f, mg = -INFINITY;
   for (int c = c0 + lane; c < c1; c += 64) {
-    const float a = cand_s[c] / T;
+    const float a = (one_each ? s_mine : cand_s[c]) / T;
     z_part += expf(a - M);
     if (have_text && cand_text_id[c] == gold) mg = fmaxf(mg, a);
   }
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(256) void k_decide(
   // pass 3: q, expectation, entropy, mass, gold sum
   float e_part = 0.f, h_part = 0.f, mass_part = 0.f, zg_part = 0.f;
   for (int c = c0 + lane; c < c1; c += 64) {
-    const float s = cand_s[c];
+    const float s = one_each ? s_mine : cand_s[c];
     const float a = s / T;
     const float qc = expf(a - M) / Z;
     cand_q[c] = qc;

@@ -63,6 +63,11 @@ RAGGED = [
     dict(V=64, d=32, n_q=1, K=1, lengths=1, layout="field", seed=19),
     dict(V=4096, d=256, n_q=8, K=(2, 5), lengths=(1, 3), layout="own", seed=20, w_dtype="f32",
          n_extra_rows=0, w_std=0.5),
+    # streaming kernel, 1,843 single-token candidates scored from 100 field rows
+    dict(V=5003, d=128, n_q=100, K=(10, 26), layout="field", seed=21),
+    # streaming kernel, 200 rows in 7 row tiles
+    dict(V=65536, d=128, n_q=100, K=(2, 6), lengths=1, layout="prefix", seed=22,
+         n_extra_rows=100),
 ]
 
 
@@ -362,9 +367,11 @@ def test_empty_problem(jet):
     assert np.max(np.abs(out["row_lse"] - ref["lse"])) < 2e-3
 
 
-def test_bad_indices_set_flags_without_faulting(jet):
-    """Out-of-range rows/targets and malformed offsets are bounds-checked on the device."""
-    p = wl.make_problem(V=500, d=32, n_q=4, K=(2, 4), lengths=(1, 3), layout="prefix", seed=41)
+@pytest.mark.parametrize("d", [32, 128])
+def test_bad_indices_set_flags_without_faulting(jet, d):
+    """Out-of-range rows/targets and malformed offsets are bounds-checked on the device
+    (d = 32: the register-staged kernel; d = 128: the streaming kernel)."""
+    p = wl.make_problem(V=500, d=d, n_q=4, K=(2, 4), lengths=(1, 3), layout="prefix", seed=41)
     q = dict(p)
     q["tok_target"] = p["tok_target"].copy()
     q["tok_target"][0] = p["V"] + 7
