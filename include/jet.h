@@ -217,7 +217,18 @@ typedef struct {
   int32_t* dev_flags;     /* [1] optional                                                   */
 } jet_restricted_outputs;
 
+/* Bytes of device workspace jet_score_restricted needs (from the scalars only; 0 when the
+ * problem is invalid): with a bf16 head, the fp32 partial sums of the projection over
+ * ceil(d / 512) groups of k, [groups][n_union][n_rows]; with an fp32 head, the gathered
+ * rows [n_union][d] and the logits [n_rows][n_union]; and a flag word. */
 JET_API size_t jet_restricted_workspace_size(const jet_restricted_problem* p);
+/* Enqueue the restricted path: project the rows onto the union (a bf16 head is read
+ * through union_ids directly; an fp32 head is gathered first), then each field's softmax
+ * and argmax over its slots.  workspace: at least jet_restricted_workspace_size(p) bytes,
+ * 256-byte aligned, not shared with a concurrent call.  Host checks return JET_E_NULL,
+ * JET_E_SHAPE, JET_E_DTYPE, JET_E_TEMP or JET_E_WORKSPACE and enqueue nothing.  On the
+ * device an id outside [0, V) reads as a zero row and a slot index, field row or field
+ * offset out of range yields NaN / -1 in that field; each raises its JET_FLAG_* bit. */
 JET_API jet_status jet_score_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
                                 void* workspace, size_t workspace_bytes, void* stream);
 /* Host-side validation of a restricted problem whose index arrays are HOST pointers. */
