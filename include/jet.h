@@ -54,7 +54,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status and dtype values cross the ABI as 32-bit ints and may come from any caller; in
+ * C++ the enums take int32_t as their underlying type so that every such value is a valid
+ * enumerator-typed value (C enums are int already). */
+#ifdef __cplusplus
+#define JET_ENUM_INT : int32_t
+#else
+#define JET_ENUM_INT
+#endif
+
+typedef enum JET_ENUM_INT {
   JET_OK = 0,
   JET_E_NULL = -1,      /* a required pointer is NULL                                  */
   JET_E_SHAPE = -2,     /* a size is out of range (negative count, d % 32 != 0, ...)    */
@@ -65,7 +74,7 @@ typedef enum {
   JET_E_HIP = -7,       /* a HIP runtime call (launch, event record) failed             */
 } jet_status;
 
-typedef enum { JET_F32 = 0, JET_BF16 = 1 } jet_dtype;
+typedef enum JET_ENUM_INT { JET_F32 = 0, JET_BF16 = 1 } jet_dtype;
 
 /* Device flag bits written to *dev_flags (OR-ed; the buffer is cleared by each call). */
 #define JET_FLAG_BAD_ROW 1u      /* tok_row[k] outside [0, n_rows)                        */

@@ -13,6 +13,7 @@ import workloads as wl
 from tests.parity import Q_TOL, compare, log, tol_logp
 
 torch = pytest.importorskip("torch")
+from candidate_likelihood_scoring_amd import api  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
@@ -545,3 +546,95 @@ def test_restricted_bad_union_id(jet):
     keep = np.repeat(~uses, np.diff(fo))
     assert np.max(np.abs(out["slot_logit"][keep] - ref["slot_logit"][keep])) <= 2e-3
     assert np.max(np.abs(out["slot_q"][keep] - ref["slot_q"][keep])) <= Q_TOL
+
+
+# ----------------------------------------------------------------------------------------
+# no stray writes: outputs and workspace padded with a canary that must survive the call
+# ----------------------------------------------------------------------------------------
+
+_CANARY = 0x7FA5A5A5  # a NaN bit pattern that no kernel writes
+_PAD = 64
+
+
+def _padded_outputs(names_sizes, dev):
+    full, views = {}, {}
+    for name, (n, dtype) in names_sizes.items():
+        buf = torch.full((n + _PAD,), _CANARY, dtype=torch.int32, device=dev)
+        full[name] = buf
+        views[name] = buf[:n] if dtype == torch.int32 else buf[:n].view(torch.float32)
+    return full, views
+
+
+def _tails_intact(full, names_sizes):
+    return {name: bool((full[name][n:] == _CANARY).all()) for name, (n, _) in names_sizes.items()}
+
+
+class _CanaryWorkspace(api.Workspace):
+    """A workspace of exactly the requested size followed by 4 KB of canary bytes."""
+
+    def get(self, nbytes):
+        if nbytes > self.size or self.buf is None:
+            self.buf = torch.full((nbytes + 256 + 4096,), 0xA5, dtype=torch.uint8, device=self.device)
+            self.base = (self.buf.data_ptr() + 255) & ~255
+            self.size = nbytes
+        return self.base, self.size
+
+    def tail_intact(self):
+        start = self.base - self.buf.data_ptr() + self.size
+        return bool((self.buf[start:] == 0xA5).all())
+
+
+_CANARY_CASES = [
+    dict(V=4099, d=32, n_q=5, K=(1, 9), lengths=(1, 4), layout="prefix", seed=71),
+    dict(V=5003, d=128, n_q=7, K=(1, 12), lengths=(1, 5), layout="prefix", seed=72),
+    dict(V=3001, d=64, n_q=4, K=(1, 6), lengths=(1, 4), layout="own", seed=73, w_dtype="f32"),
+    dict(V=1283, d=256, n_q=25, K=(1, 12), lengths=(1, 5), layout="prefix", seed=74,
+         h_dtype="bf16", n_extra_rows=211),
+    dict(V=2500, d=64, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=75, n_extra_rows=250),
+]
+
+
+@pytest.mark.parametrize("case", _CANARY_CASES, ids=[f"canary{i}" for i in range(len(_CANARY_CASES))])
+def test_no_writes_past_outputs_or_workspace(jet, case):
+    p = wl.make_problem(**case)
+    pd = jet.to_device(p, "cuda")
+    prob = api.make_problem(**pd)
+    log(f"[gpu] canary {case} kernel={api.projection_kernel(prob)}")
+    f, i = torch.float32, torch.int32
+    sizes = dict(tok_logp=(prob.n_tok, f), row_lse=(prob.n_rows, f), cand_s=(prob.n_cand, f),
+                 cand_q=(prob.n_cand, f), q_argmax=(prob.n_q, i), q_true=(prob.n_q, f),
+                 q_expect=(prob.n_q, f), q_gold_nll=(prob.n_q, f), q_confidence=(prob.n_q, f),
+                 q_mass=(prob.n_q, f), dev_flags=(1, i))
+    full, views = _padded_outputs(sizes, "cuda")
+    views["dev_flags"].zero_()
+    ws = _CanaryWorkspace("cuda")
+    jet.score_problem(pd, out=views, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(views["dev_flags"][0]) == 0
+    assert all(_tails_intact(full, sizes).values()), _tails_intact(full, sizes)
+    assert ws.tail_intact()
+    ref = jo.score(p)
+    out = {k: v.cpu().numpy() for k, v in views.items()}
+    compare(p, out, ref, f"canary {case}")
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
+def test_restricted_no_writes_past_outputs_or_workspace(jet, w_dtype):
+    rp = wl.make_restricted(n_fields=45, V=20000, d=608 if w_dtype == "bf16" else 96,
+                            K=(1, 26), seed=76, w_dtype=w_dtype)
+    rd = jet.restricted_to_device(rp, "cuda")
+    n_slots, n_f = int(rp["field_off"][-1]), len(rp["field_off"]) - 1
+    f, i = torch.float32, torch.int32
+    sizes = dict(slot_logit=(n_slots, f), slot_q=(n_slots, f), field_argmax=(n_f, i),
+                 dev_flags=(1, i))
+    full, views = _padded_outputs(sizes, "cuda")
+    views["dev_flags"].zero_()
+    ws = _CanaryWorkspace("cuda")
+    jet.score_restricted_problem(rd, out=views, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(views["dev_flags"][0]) == 0
+    assert all(_tails_intact(full, sizes).values()), _tails_intact(full, sizes)
+    assert ws.tail_intact()
+    ref = jo.score_restricted(rp)
+    tl = 1e-4 if w_dtype == "f32" else 2e-3
+    assert np.max(np.abs(views["slot_logit"].cpu().numpy() - ref["slot_logit"])) <= tl
