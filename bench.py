@@ -374,10 +374,12 @@ def main(argv=None) -> int:
         traffic = None if args.dedup else _traffic_from_profiles(kernel, args.workload)
         if intensity < 300.0:
             achieved = alg_bytes / k_avg_s / 1e9
-            # the device's plain-read rate over the same head bytes, on the same stream
-            ceiling = _stream_read_gbs(pd["W"], stream)
-            extra["stream_read_gbs"] = round(ceiling, 1)
-            extra["projection_frac_of_stream_read"] = round(achieved / ceiling, 4)
+            if alg_bytes >= (256 << 20):
+                # the device's plain-read rate over the same head bytes, on the same stream
+                # (a head that fits the last-level cache is read at launch latency instead)
+                ceiling = _stream_read_gbs(pd["W"], stream)
+                extra["stream_read_gbs"] = round(ceiling, 1)
+                extra["projection_frac_of_stream_read"] = round(achieved / ceiling, 4)
             roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                             frac=round(achieved / HBM_PEAK_GBS, 4),
                             traffic=traffic)

@@ -362,10 +362,15 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
 
 // ------------------------------------------------------------------------------------
 // fp32 head and fp32 hidden states: v_mfma_f32_32x32x2_f32 takes one k per lane half.
-// A stage is a 16-wide block: lane half h loads 8 consecutive k (two float4) of its row,
-// k = kb + 8 h + 4 q + c for float4 q and component c; each component is one MFMA step.
+// A workgroup takes one 32-entry vocabulary group at a time and its four waves split the
+// k range: wave w takes the 16-wide blocks w, w + 4, ...; in a block, lane half h loads 8
+// consecutive k (two float4) of its row, k = kb + 8 h + 4 q + c for float4 q and component
+// c, each component one MFMA step.  (One wave over the whole row would make a 32 x 32 tile
+// a chain of d / 2 dependent matrix ops; split four ways the chain is a quarter as long and
+// four times as many waves are in flight.)  The waves' tiles are added in wave order
+// through LDS, and wave 0 runs the epilogue.
 // ------------------------------------------------------------------------------------
-template <int NT, bool STORE>
+template <bool STORE>
 __global__ __launch_bounds__(256) void k_project_small_f32(
     const float* __restrict__ W, int V, int d, const float* __restrict__ H, int n_rows,
     int n_groups, const int* __restrict__ b_off, const int* __restrict__ b_tok,
@@ -373,68 +378,70 @@ __global__ __launch_bounds__(256) void k_project_small_f32(
     float* __restrict__ z_tgt, float2* __restrict__ part, float* __restrict__ Z) {
   constexpr int KB = 16, S = 2;
   __shared__ float2 red[kWpb][32];
+  __shared__ f32x16 tiles[kWpb - 1][kWave];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n = lane & 31, half = lane >> 5;
   const int rt = blockIdx.y, row0 = rt * 32;
   const int hrow = min(row0 + n, n_rows - 1);
   const float* hp = H + (size_t)hrow * d + half * (KB / 2);
-  const long long nw = (long long)gridDim.x * kWpb;
-  const long long w = (long long)blockIdx.x * kWpb + wid;
-  const int g0 = (int)(w * n_groups / nw), g1 = (int)((w + 1) * n_groups / nw);
-  const int nkb = d / KB;
+  const int g0 = (int)((long long)blockIdx.x * n_groups / gridDim.x);
+  const int g1 = (int)((long long)(blockIdx.x + 1) * n_groups / gridDim.x);
+  const int nkb = d / KB;  // >= 2 (d is a multiple of 32)
+  // this wave's blocks wid, wid + kWpb, ...: nmy of them (none when nkb <= wid)
+  const int nmy = nkb > wid ? (nkb - wid + kWpb - 1) / kWpb : 0;
+  // k offset of the wave's block j; past its last block (or with no block) the load
+  // re-reads a valid block and is not used
+  auto koff = [&](int j) { return min(wid + kWpb * j, nkb - 1) * KB; };
   float m_run = -INFINITY, s_run = 0.f;
   for (int g = g0; g < g1; ++g) {
-    const int v0 = g * (32 * NT);
-    const float* wp[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      wp[t] = W + (size_t)min(v0 + 32 * t + n, V - 1) * d + half * (KB / 2);
-    Acc<NT> acc;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc.t[t] = f32x16{};
-    float4 A[S][NT][2], B[S][2];
+    const int v0 = g * 32;
+    const float* wp = W + (size_t)min(v0 + n, V - 1) * d + half * (KB / 2);
+    f32x16 acc = {};
+    float4 A[S][2], B[S][2];
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) {
-      const int off = min(s, nkb - 1) * KB;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        A[s][t][0] = *reinterpret_cast<const float4*>(wp[t] + off);
-        A[s][t][1] = *reinterpret_cast<const float4*>(wp[t] + off + 4);
-      }
+      const int off = koff(s);
+      A[s][0] = *reinterpret_cast<const float4*>(wp + off);
+      A[s][1] = *reinterpret_cast<const float4*>(wp + off + 4);
       B[s][0] = *reinterpret_cast<const float4*>(hp + off);
       B[s][1] = *reinterpret_cast<const float4*>(hp + off + 4);
     }
-    for (int i = 0; i < nkb; i += S) {
+    for (int i = 0; i < nmy; i += S) {  // nmy is uniform over the wave
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         const int ls = (s + S - 1) % S;
-        const int off = min(i + s + S - 1, nkb - 1) * KB;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          A[ls][t][0] = *reinterpret_cast<const float4*>(wp[t] + off);
-          A[ls][t][1] = *reinterpret_cast<const float4*>(wp[t] + off + 4);
-        }
+        const int off = koff(i + s + S - 1);
+        A[ls][0] = *reinterpret_cast<const float4*>(wp + off);
+        A[ls][1] = *reinterpret_cast<const float4*>(wp + off + 4);
         B[ls][0] = *reinterpret_cast<const float4*>(hp + off);
         B[ls][1] = *reinterpret_cast<const float4*>(hp + off + 4);
-        if (i + s < nkb) {
+        if (i + s < nmy) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].x, B[s][q].x, acc.t[t], 0, 0, 0);
-              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].y, B[s][q].y, acc.t[t], 0, 0, 0);
-              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].z, B[s][q].z, acc.t[t], 0, 0, 0);
-              acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][t][q].w, B[s][q].w, acc.t[t], 0, 0, 0);
-            }
+          for (int q = 0; q < 2; ++q) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][q].x, B[s][q].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][q].y, B[s][q].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][q].z, B[s][q].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[s][q].w, B[s][q].w, acc, 0, 0, 0);
+          }
         }
       }
     }
-    if (STORE)
-      epilogue_store<NT>(acc, v0, V, n, half, row0, n_rows, Z);
-    else
-      epilogue_lse<NT>(acc, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
-                       tok_target, z_tgt, m_run, s_run);
+    if (wid > 0) tiles[wid - 1][lane] = acc;
+    __syncthreads();
+    if (wid == 0) {
+      Acc<1> sum;
+      sum.t[0] = acc;
+#pragma unroll
+      for (int w = 0; w < kWpb - 1; ++w) sum.t[0] += tiles[w][lane];
+      if (STORE)
+        epilogue_store<1>(sum, v0, V, n, half, row0, n_rows, Z);
+      else
+        epilogue_lse<1>(sum, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
+                        tok_target, z_tgt, m_run, s_run);
+    }
+    __syncthreads();  // tiles is rewritten for the next group
   }
+  // waves 1.. hold (-inf, 0), which the wave-order merge leaves unchanged
   if (!STORE) store_partial(m_run, s_run, n, half, wid, row0, n_rows, part, red);
 }
 
@@ -462,7 +469,6 @@ constexpr int kStreamS = JET_STREAM_S;
 constexpr int kSmallNT = JET_SMALL_NT;
 constexpr int kSmallKB = JET_SMALL_KB;
 constexpr int kSmallS = JET_SMALL_S;
-constexpr int kSmallNTf32 = 2;
 
 hipError_t launch_project(const ScoreArgs& a) {
   const jet_problem* p = a.p;
@@ -499,7 +505,7 @@ hipError_t launch_project(const ScoreArgs& a) {
                          b_tok, p->tok_row, p->tok_target, z_tgt, part);
     }
   } else if (pl.variant == VAR_SMALL_F32) {
-    hipLaunchKernelGGL((k_project_small_f32<kSmallNTf32, false>), grid, block, 0, a.stream,
+    hipLaunchKernelGGL((k_project_small_f32<false>), grid, block, 0, a.stream,
                        static_cast<const float*>(p->W), p->V, p->d,
                        static_cast<const float*>(p->H), p->n_rows, pl.n_vgroups, b_off, b_tok,
                        p->tok_row, p->tok_target, z_tgt, part, nullptr);
@@ -511,7 +517,7 @@ hipError_t launch_project(const ScoreArgs& a) {
 
 // Vocabulary entries per group (the bucketing unit) and workgroups of the small-row path.
 int small_group_size(int variant, int d) {
-  if (variant == VAR_SMALL_F32) return 32 * kSmallNTf32;
+  if (variant == VAR_SMALL_F32) return 32;
   return d % 128 == 0 ? 32 * kStreamWPB : 32 * kSmallNT;
 }
 
@@ -520,21 +526,23 @@ int small_grid(int variant, int d, int n_groups, int max_waves) {
     int wg = max_waves / kStreamWPB;
     return n_groups < wg ? n_groups : wg;
   }
+  if (variant == VAR_SMALL_F32) {  // one group at a time per workgroup
+    const int cap = max_waves / kWpb;
+    return n_groups < 1 ? 1 : (n_groups > cap ? cap : n_groups);
+  }
   int gx = (n_groups + kWpb - 1) / kWpb;
   const int cap = max_waves / kWpb;
   return gx < 1 ? 1 : (gx > cap ? cap : gx);
 }
 
-static int store_grid(int n_groups) {
-  int g = (n_groups + kWpb - 1) / kWpb;
-  return g < 1 ? 1 : g;
-}
 
 hipError_t launch_project_store_f32(const float* Wu, int U, int d, const float* H, int n_rows,
                                     float* Z, hipStream_t stream) {
   const int n_groups = (U + 31) / 32;
-  dim3 grid(store_grid(n_groups), (n_rows + 31) / 32), block(256);
-  hipLaunchKernelGGL((k_project_small_f32<1, true>), grid, block, 0, stream, Wu, U, d, H, n_rows,
+  // one group at a time per workgroup, at most two workgroups per CU
+  const int gx = n_groups < 1 ? 1 : (n_groups < 512 ? n_groups : 512);
+  dim3 grid(gx, (n_rows + 31) / 32), block(256);
+  hipLaunchKernelGGL((k_project_small_f32<true>), grid, block, 0, stream, Wu, U, d, H, n_rows,
                      n_groups, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, Z);
   return hipGetLastError();
 }
