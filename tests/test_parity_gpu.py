@@ -638,3 +638,92 @@ def test_restricted_no_writes_past_outputs_or_workspace(jet, w_dtype):
     ref = jo.score_restricted(rp)
     tl = 1e-4 if w_dtype == "f32" else 2e-3
     assert np.max(np.abs(views["slot_logit"].cpu().numpy() - ref["slot_logit"])) <= tl
+
+
+# ----------------------------------------------------------------------------------------
+# concurrency and graph capture
+# ----------------------------------------------------------------------------------------
+
+_GRAPH_CASES = {
+    "stream": dict(V=5003, d=128, n_q=9, K=(1, 12), lengths=(1, 6), layout="prefix", seed=81),
+    "tiled": dict(V=3001, d=128, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=82,
+                  h_dtype="bf16", n_extra_rows=300),
+    "tiled_f32": dict(V=2500, d=64, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=83,
+                      n_extra_rows=250),
+}
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
+def test_concurrent_streams_with_own_workspaces(jet):
+    """Calls on different streams with different workspaces may overlap; each gives the
+    bits it gives alone."""
+    probs = [jet.to_device(wl.make_problem(**c), "cuda") for c in _GRAPH_CASES.values()]
+    alone = [api.score(**dp) for dp in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in probs]
+    wss = [api.Workspace("cuda") for _ in probs]
+    outs = []
+    for _ in range(3):  # enqueue every problem on its own stream, several times, no syncs
+        outs = [api.score(**dp, workspace=ws, stream=st) for dp, ws, st in zip(probs, wss, streams)]
+    torch.cuda.synchronize()
+    for a, b in zip(alone, outs):
+        for k in a:
+            assert torch.equal(_bits(a[k]), _bits(b[k])), k
+
+
+@pytest.mark.parametrize("name", list(_GRAPH_CASES))
+def test_graph_capture_replays_match_eager(jet, name):
+    """The whole jet_score sequence (no memsets, no allocation, no host synchronisation) can
+    be captured in a HIP graph; every replay, with other device work and synchronisations
+    between replays, gives the eager bits."""
+    dp = jet.to_device(wl.make_problem(**_GRAPH_CASES[name]), "cuda")
+    eager = api.score(**dp)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    ws = api.Workspace("cuda")
+    out = {k: torch.empty_like(v) for k, v in eager.items()}
+    with torch.cuda.stream(side):
+        api.score(**dp, out=out, workspace=ws, stream=side)  # sizes the workspace first
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        api.score(**dp, out=out, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for v in out.values():
+            v.fill_(-7)  # eager work between replays: scribble over the outputs
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(_bits(eager[k]), _bits(out[k])), (rep, k)
+    del g
+
+
+def test_restricted_graph_capture_replays_match_eager(jet):
+    rp = wl.make_restricted(n_fields=45, V=20000, d=608, K=(1, 26), seed=84)
+    rd = {k: v for k, v in jet.restricted_to_device(rp, "cuda").items() if not k.startswith("host_")}
+    eager = api.score_restricted(**rd)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    ws = api.Workspace("cuda")
+    out = {k: torch.empty_like(v) for k, v in eager.items()}
+    with torch.cuda.stream(side):
+        api.score_restricted(**rd, out=out, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        api.score_restricted(**rd, out=out, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for v in out.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(_bits(eager[k]), _bits(out[k])), (rep, k)
+    del g
