@@ -231,7 +231,42 @@ def _fit_grid_only(s, q_cand_off, cand_text_id, q_gold_text_id, T_min=1e-2, T_ma
     return math.exp(grid[i]), float(vals[i])
 
 
+def _restricted_variant(kind):
+    """score_restricted with one planted mistake: 'field_as_row' scores field f from row f
+    (ignoring field_row), 'no_temperature' drops T, 'union_softmax' normalises each field
+    over the whole union of allowed ids instead of its own slots."""
+    def fn(rp):
+        fo = np.asarray(rp["field_off"])
+        ids = np.asarray(rp["field_ids"], dtype=np.int64)
+        rows = np.asarray(rp["field_row"], dtype=np.int64)
+        H64 = jom.widen(rp["H"], rp["h_dtype"])
+        W64 = jom.widen(np.asarray(rp["W"])[ids], rp["w_dtype"])
+        n_f = len(fo) - 1
+        logit, qv = np.empty(len(ids)), np.empty(len(ids))
+        am, gap = np.empty(n_f, dtype=np.int64), np.empty(n_f)
+        uni = np.unique(ids)
+        for f in range(n_f):
+            a0, a1 = int(fo[f]), int(fo[f + 1])
+            r_f = f % H64.shape[0] if kind == "field_as_row" else rows[f]
+            b = W64[a0:a1] @ H64[r_f]
+            logit[a0:a1] = b
+            T = 1.0 if kind == "no_temperature" else rp["T"]
+            r = jom.decide_question(b, T)
+            q = r["q"]
+            if kind == "union_softmax":
+                allz = jom.widen(np.asarray(rp["W"])[uni], rp["w_dtype"]) @ H64[r_f] / T
+                q = np.exp(b / T - allz.max()) / np.exp(allz - allz.max()).sum()
+            qv[a0:a1] = q
+            am[f] = r["argmax"]
+            gap[f] = r["gap"]
+        return dict(slot_logit=logit, slot_q=qv, field_argmax=am, field_gap=gap)
+    return fn
+
+
 MUTANTS = {
+    "restricted_field_index_as_row": ("score_restricted", _restricted_variant("field_as_row")),
+    "restricted_temperature_dropped": ("score_restricted", _restricted_variant("no_temperature")),
+    "restricted_softmax_over_union": ("score_restricted", _restricted_variant("union_softmax")),
     "lse_without_max_shift": ("logsumexp_rows", _lse_no_shift),
     "lse_sign_error": ("logsumexp_rows", _lse_sign),
     "lse_dropped_max_term": ("logsumexp_rows", _lse_drop_max),
