@@ -481,6 +481,23 @@ def test_large_batch_full_sampled(jet):
     log(f"[gpu] large_batch errs {compare(p, out, ref, 'large_batch', sampled=True)}")
 
 
+def test_large_batch_deduplicated_full_sampled(jet):
+    """The large workload with one row per predictor node of the history trie (the layout
+    the bench's --dedup line times): 22,962 rows instead of 26,546, a different ragged
+    last row tile; parity on sampled questions."""
+    p = wl.large_batch()
+    tok_node, node_tok = api.build_predictor_trie(p["tok_target"], p["cand_tok_off"], p["q_cand_off"])
+    tok_row = np.arange(len(p["tok_target"])) if p.get("tok_row") is None else np.asarray(p["tok_row"])
+    q = dict(p, H=np.ascontiguousarray(p["H"][tok_row[node_tok]]), n_rows=len(node_tok),
+             tok_row=tok_node.astype(np.int32))
+    log(f"[gpu] large_batch dedup rows={q['n_rows']}")
+    out = _run(jet, q)
+    _full_size_properties(q, out)
+    rows = _rows_of_questions(q, [3, 200, 511])
+    ref = jo.score(q, rows=rows)
+    log(f"[gpu] large_batch dedup errs {compare(q, out, ref, 'large_batch_dedup', sampled=True)}")
+
+
 @pytest.mark.parametrize("max_variant", [False, True])
 def test_restricted(jet, max_variant):
     rp = wl.restricted(max_variant=max_variant)
