@@ -81,8 +81,8 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     pl->variant = VAR_TILED_BF16;
   pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
   if (pl->variant == VAR_TILED_BF16) {
-    pl->row_tile = 256;
-    pl->n_rtiles = (p->n_rows + 255) / 256;
+    pl->row_tile = tiled_row_tile(pl->hilo, p->d);
+    pl->n_rtiles = (p->n_rows + pl->row_tile - 1) / pl->row_tile;
     pl->vgroup = 256;
     pl->n_vgroups = (p->V + 255) / 256;
     // Split count S (vocabulary ranges per row tile), from a makespan estimate: R * S
@@ -249,7 +249,7 @@ const char* jet_projection_kernel(const jet_problem* p) {
   Plan pl;
   make_plan(p, true, &pl);
   switch (pl.variant) {
-    case VAR_TILED_BF16: return tiled_kernel_name(pl.hilo);
+    case VAR_TILED_BF16: return tiled_kernel_name(pl.hilo, p->d);
     case VAR_SMALL_F32: return "k_project_small_f32";
     default: return pl.stream ? "k_project_wg_bf16" : "k_project_small_bf16";
   }

@@ -98,7 +98,8 @@ hipError_t launch_prep(const ScoreArgs& a);
 hipError_t launch_project(const ScoreArgs& a);
 hipError_t launch_project_tiled(const ScoreArgs& a);
 int tiled_bk(bool hilo);
-const char* tiled_kernel_name(bool hilo);
+int tiled_row_tile(bool hilo, int d);
+const char* tiled_kernel_name(bool hilo, int d);
 int sensitivity_max_layers();
 size_t fit_temperature_workspace(int n_q);
 hipError_t launch_fit_temperature(const float* s, const int* q_cand_off, int n_q, int n_cand,

@@ -9,14 +9,17 @@
 // sweeps a contiguous range of 256-entry vocabulary tiles; each wave computes a 128 x 128
 // quadrant (vocabulary x rows), 256 fp32 accumulators per lane (all AGPRs).  The stages of
 // all the range's vocabulary tiles form one stream, so the next tile's first stages are in
-// flight during an epilogue.  Two kernels:
+// flight during an epilogue.  Three kernels:
 //  * k_project_tiled_m16 (bf16 H): 8 x 8 blocks of v_mfma_f32_16x16x32_bf16 per wave;
 //    64-wide stages loaded by the buffer unit straight into two LDS buffers; one barrier
 //    per stage, at its midpoint (see the kernel);
-//  * k_project_tiled_bf16 (fp32 H as two bf16 planes, hi + lo, each product accumulated
-//    twice): 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 per wave; 32-wide stages staged
-//    through two register sets into a ring of three LDS buffers.
-// In both, every MFMA is followed by at most one memory instruction (fragment read, LDS
+//  * k_project_tiled_m16x2 (fp32 H as two bf16 planes, hi + lo, d a multiple of 128): the
+//    same kernel with the hi and lo rows of 128 rows as its 256 B-operand rows, both
+//    products of a row accumulated into one accumulator;
+//  * k_project_tiled_bf16 (fp32 H as two planes, d a multiple of 64 only): 4 x 4 blocks of
+//    v_mfma_f32_32x32x16_bf16 per wave, each product issued for hi and lo; 32-wide stages
+//    staged through two register sets into a ring of three LDS buffers.
+// In all, every MFMA is followed by at most one memory instruction (fragment read, LDS
 // write or global load), so with one wave per SIMD the memory traffic overlaps the matrix
 // core instead of stalling its issue in bursts.  The last vocabulary tile (and row tile) is
 // shifted back to end exactly at V (n_rows), so every load is in bounds; the overlap is
@@ -444,12 +447,18 @@ __device__ inline int swz16(int r) {
 }
 
 // Fold a finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
-// this lane's eight rows and capture the tile's scored targets (see tile_epilogue).
+// this lane's rows and capture the tile's scored targets (see tile_epilogue).  TWO (fp32 H
+// as two planes): both planes' products of a row are in one accumulator, four block
+// columns per wave (64 rows).
+template <bool TWO>
 __device__ __forceinline__ void tile_epilogue16(
-    f32x4 (&acc)[8][8], float (&m_run)[8], float (&s_run)[8], int vt, int V, int wm, int wn,
+    f32x4 (&acc)[8][TWO ? 4 : 8], float (&m_run)[8], float (&s_run)[8], int vt, int V, int wm, int wn,
     int r16, int q, int rt, int n_vtiles, int row0, const int* __restrict__ b_off,
     const int* __restrict__ b_tok, const int* __restrict__ tok_row,
     const int* __restrict__ tok_target, float* __restrict__ z_tgt) {
+  constexpr int NR = TWO ? 4 : 8;          // block columns of distinct rows
+  constexpr int WROWS = 16 * NR;           // rows per wave
+  constexpr int TROWS = 2 * WROWS;         // rows per block tile
   const int v_nom = vt * TBM;
   const int v0 = min(v_nom, V - TBM);
   if (v0 != v_nom) {
@@ -463,12 +472,12 @@ __device__ __forceinline__ void tile_epilogue16(
       bf16x8 amask = {};
       if (q == 0 && mt * 16 + r16 < thr) amask[0] = (__bf16)(-INFINITY);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < NR; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(amask, bone, acc[mt][nt], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
+  for (int nt = 0; nt < NR; ++nt) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
     float gm = m_run[nt];
@@ -491,15 +500,15 @@ __device__ __forceinline__ void tile_epilogue16(
     const int k = b_tok[e];
     const int lr = (tok_row ? tok_row[k] : k) - row0;
     const int lv = tok_target[k] - v0;
-    if (lv < 0 || lv >= TBM || lr < 0 || lr >= TBN) continue;
-    if ((lv >> 7) != wm || (lr >> 7) != wn) continue;  // wave-uniform
-    const int tmt = (lv >> 4) & 7, tnt = (lr >> 4) & 7, ti = lv & 3;
+    if (lv < 0 || lv >= TBM || lr < 0 || lr >= TROWS) continue;
+    if ((lv >> 7) != wm || lr / WROWS != wn) continue;  // wave-uniform
+    const int tmt = (lv >> 4) & 7, tnt = (lr % WROWS) >> 4, ti = lv & 3;
     if (r16 == (lr & 15) && q == ((lv >> 2) & 3)) {
       float val = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int nt = 0; nt < NR; ++nt)
           if (mt == tmt && nt == tnt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -510,13 +519,22 @@ __device__ __forceinline__ void tile_epilogue16(
   }
 }
 
-__global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
-    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H, int n_rows,
-    int n_vtiles, const int* __restrict__ b_off, const int* __restrict__ b_tok,
-    const int* __restrict__ tok_row, const int* __restrict__ tok_target,
-    float* __restrict__ z_tgt, float2* __restrict__ part, int n_rtiles, int splits, int sr,
-    int ss, int remap) {
+// TWO (fp32 H as bf16 planes hi and lo, H = hi + lo): the B tile's 256 rows are, per
+// 64-row quarter j, plane j & 1 of real rows 64 (j >> 1) .. + 63, so wave column wn holds
+// the hi rows of its 64 real rows as fragments 0..3 and their lo rows as 4..7.  A k-step
+// issues the 32 hi products (block (i / 4, i % 4)) and then the 32 lo products into the
+// same 32 accumulators, 32 matrix ops apart.  A block tile covers 128 real rows with the
+// matrix work of a 256-row bf16 tile and half its accumulators.
+template <bool TWO>
+__device__ __forceinline__ void project_m16(
+    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H,
+    const uint16_t* __restrict__ Hlo, int n_rows, int n_vtiles, const int* __restrict__ b_off,
+    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
+    int n_rtiles, int splits, int sr, int ss, int remap) {
   constexpr int BK = 64, CH = 8, RPD = 64 / CH;
+  constexpr int NR = TWO ? 4 : 8;       // block columns of distinct rows per wave
+  constexpr int RT = TWO ? 128 : TBN;   // real rows per block tile
   constexpr int ASZ = TBM * CH;  // 16-byte slots per operand half per buffer (32 KB)
   constexpr int BUFSZ = 2 * ASZ;
   constexpr int NDO = CH;        // load instructions per wave per operand per stage
@@ -531,13 +549,14 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
   int rt, split;
   tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
   if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
-  const int row_nom = rt * TBN;
-  const int row0 = min(row_nom, n_rows - TBN);
+  const int row_nom = rt * RT;
+  const int row0 = min(row_nom, n_rows - RT);
   const int t0 = (int)((long long)split * n_vtiles / splits);
   const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
   const int nk = d / BK;  // even
   const uint32_t rowb = (uint32_t)d * 2;
   const __amdgpu_buffer_rsrc_t rH = rsrc_of(H, (uint32_t)n_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rL = TWO ? rsrc_of(Hlo, (uint32_t)n_rows * rowb) : rH;
   const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
   const uint32_t hrow = (uint32_t)row0 * rowb;
   const int dr = wid * RPD + lane / CH;
@@ -570,11 +589,16 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
       }                                                                                      \
     }                                                                                        \
   }
-  // load instruction Q (0 .. 2 NDO - 1): head rows first, then hidden-state rows
+  // load instruction Q (0 .. 2 NDO - 1): head rows first, then hidden-state rows.
+  // Instruction jj of an operand fills B-tile rows 32 jj .. 32 jj + 31; with TWO those are
+  // plane (jj >> 1) & 1 of real rows 64 (jj >> 2) + 32 (jj & 1) + 0 .. 31.
 #define JET_DMA1(BI, Q)                                                                      \
   {                                                                                          \
     const int op_ = (Q) / NDO, jj_ = (Q) % NDO;                                              \
-    dma16(op_ ? rH : rW, dvoff, (op_ ? l_hs : l_ws) + (uint32_t)(jj_ * 4 * RPD) * rowb,        \
+    const int hr_ = TWO ? 64 * (jj_ >> 2) + 32 * (jj_ & 1) : jj_ * 4 * RPD;                  \
+    const __amdgpu_buffer_rsrc_t rb_ = (TWO && ((jj_ >> 1) & 1)) ? rL : rH;                  \
+    dma16(op_ ? rb_ : rW, dvoff,                                                             \
+          op_ ? l_hs + (uint32_t)hr_ * rowb : l_ws + (uint32_t)(jj_ * 4 * RPD) * rowb,         \
           m0_base + (uint32_t)(((BI) * BUFSZ + op_ * ASZ + jj_ * 256) * 16));                \
   }
   bf16x8 fa[2][8], fb[2][8];
@@ -598,13 +622,18 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
   // of the stage.  k-step 1 reads the k-step 0 fragments of stage g + 1 (slots 0, 4, ..,
   // 60) and loads stage g + 2 into buffer bc (slots 2, 6, .., 62), so loads get half a
   // stage to a stage to land and no stage starts by waiting for LDS.
+  // matrix op i of a k-step: A fragment MT_(i), B fragment FB_(i), accumulator (MT_, NT_)
+#define MT_(i) (TWO ? ((i) % 32) / 4 : (i) / 8)
+#define FB_(i) (TWO ? (i) % 4 + 4 * ((i) / 32) : (i) % 8)
+#define NT_(i) (TWO ? (i) % 4 : (i) % 8)
 #define JET_MSTAGE(FIRST)                                                                    \
   {                                                                                          \
     const int b_nx = bc ^ 1;                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     _Pragma("unroll") for (int i = 0; i < 64; ++i) {                                         \
-      acc[i / 8][i % 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                           \
-          fa[0][i / 8], fb[0][i % 8], (FIRST) ? f32x4{} : acc[i / 8][i % 8], 0, 0, 0);       \
+      acc[MT_(i)][NT_(i)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                         \
+          fa[0][MT_(i)], fb[0][FB_(i)],                                                      \
+          ((FIRST) && (!TWO || i < 32)) ? f32x4{} : acc[MT_(i)][NT_(i)], 0, 0, 0);           \
       if (i % 4 == 0) JET_FRAG1(1, bc * BUFSZ, 1, i / 4);                                    \
       __builtin_amdgcn_sched_barrier(0);                                                     \
     }                                                                                        \
@@ -613,8 +642,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
     JET_CURSOR();                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     _Pragma("unroll") for (int i = 0; i < 64; ++i) {                                         \
-      acc[i / 8][i % 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                           \
-          fa[1][i / 8], fb[1][i % 8], acc[i / 8][i % 8], 0, 0, 0);                           \
+      acc[MT_(i)][NT_(i)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                         \
+          fa[1][MT_(i)], fb[1][FB_(i)], acc[MT_(i)][NT_(i)], 0, 0, 0);                       \
       if (i % 4 == 0) {                                                                      \
         JET_FRAG1(0, b_nx * BUFSZ, 0, i / 4);                                                \
       } else if (i % 4 == 2) {                                                               \
@@ -639,7 +668,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
   for (int jr = 0; jr < 16; ++jr) JET_FRAG1(0, 0, 0, jr);
 
   for (int vt = t0; vt < t1; ++vt) {
-    f32x4 acc[8][8];
+    f32x4 acc[8][NR];
     JET_MSTAGE(true);
     JET_MSTAGE(false);
     for (int kb = 2; kb < nk; kb += 2) {
@@ -654,15 +683,15 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
       float m_run[8], s_run[8];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
+      for (int nt = 0; nt < NR; ++nt) {
         const float2 r = runs[wid][nt][lane_e];
         m_run[nt] = r.x;
         s_run[nt] = r.y;
       }
-      tile_epilogue16(acc, m_run, s_run, vt, V, wm, wn, lane_e & 15, lane_e >> 4, rt, n_vtiles, row0,
-                      b_off, b_tok, tok_row, tok_target, z_tgt);
+      tile_epilogue16<TWO>(acc, m_run, s_run, vt, V, wm, wn, lane_e & 15, lane_e >> 4, rt,
+                           n_vtiles, row0, b_off, b_tok, tok_row, tok_target, z_tgt);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) runs[wid][nt][lane_e] = make_float2(m_run[nt], s_run[nt]);
+      for (int nt = 0; nt < NR; ++nt) runs[wid][nt][lane_e] = make_float2(m_run[nt], s_run[nt]);
     }
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
@@ -670,20 +699,23 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
 #undef JET_DMA1
 #undef JET_FRAG1
 #undef JET_MSTAGE
+#undef MT_
+#undef FB_
+#undef NT_
   // merge the four lanes of each row (q = 0..3), then the two vocabulary halves (wm)
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
+  for (int nt = 0; nt < NR; ++nt) {
     float m = runs[wid][nt][lane].x, sm = runs[wid][nt][lane].y;
     float m2 = __shfl_xor(m, 16), s2 = __shfl_xor(sm, 16);
     lse_merge(m, sm, m2, s2);
     m2 = __shfl_xor(m, 32);
     s2 = __shfl_xor(sm, 32);
     lse_merge(m, sm, m2, s2);
-    if (q == 0) red[wm][wn * 128 + nt * 16 + r16] = make_float2(m, sm);
+    if (q == 0) red[wm][wn * (16 * NR) + nt * 16 + r16] = make_float2(m, sm);
   }
   __syncthreads();
-  {
-    const int r = tid;  // 256 threads, 256 rows
+  if (tid < RT) {
+    const int r = tid;
     float m = red[0][r].x, sm = red[0][r].y;
     lse_merge(m, sm, red[1][r].x, red[1][r].y);
     const int row = row0 + r;
@@ -691,12 +723,38 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
   }
 }
 
+__global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
+    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H, int n_rows,
+    int n_vtiles, const int* __restrict__ b_off, const int* __restrict__ b_tok,
+    const int* __restrict__ tok_row, const int* __restrict__ tok_target,
+    float* __restrict__ z_tgt, float2* __restrict__ part, int n_rtiles, int splits, int sr,
+    int ss, int remap) {
+  project_m16<false>(W, V, d, H, nullptr, n_rows, n_vtiles, b_off, b_tok, tok_row, tok_target,
+                     z_tgt, part, n_rtiles, splits, sr, ss, remap);
+}
+
+__global__ __launch_bounds__(256, 1) void k_project_tiled_m16x2(
+    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ Hhi,
+    const uint16_t* __restrict__ Hlo, int n_rows, int n_vtiles, const int* __restrict__ b_off,
+    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
+    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
+    int n_rtiles, int splits, int sr, int ss, int remap) {
+  project_m16<true>(W, V, d, Hhi, Hlo, n_rows, n_vtiles, b_off, b_tok, tok_row, tok_target,
+                    z_tgt, part, n_rtiles, splits, sr, ss, remap);
+}
+
 }  // namespace
 
 // d must be a multiple of two stages (the stage loop is unrolled by two)
 int tiled_bk(bool hilo) { return hilo ? 2 * TiledShape<2>::BK : 128; }
 
-const char* tiled_kernel_name(bool hilo) {
+// fp32 H runs on the 16 x 16 kernel's two-plane form when d allows its 64-wide stages
+static bool tiled_two_plane_m16(bool hilo, int d) { return hilo && d % 128 == 0; }
+
+int tiled_row_tile(bool hilo, int d) { return tiled_two_plane_m16(hilo, d) ? 128 : TBN; }
+
+const char* tiled_kernel_name(bool hilo, int d) {
+  if (tiled_two_plane_m16(hilo, d)) return "k_project_tiled_m16x2";
   return hilo ? "k_project_tiled_bf16" : "k_project_tiled_m16";
 }
 
@@ -721,7 +779,13 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   }
   dim3 grid(total), block(256);
   const uint16_t* W = static_cast<const uint16_t*>(p->W);
-  if (pl.hilo) {
+  if (pl.hilo && tiled_two_plane_m16(pl.hilo, p->d)) {
+    const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
+    const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
+    hipLaunchKernelGGL(k_project_tiled_m16x2, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
+                       p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
+                       part, R, S, sr, ss, remap);
+  } else if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
     hipLaunchKernelGGL(k_project_tiled_bf16<2>, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,

@@ -220,7 +220,8 @@ def test_projection_kernel_choice(lib):
 
     F32, BF16 = 0, 1
     assert pick(26546, 248320, 2560, BF16, BF16) == "k_project_tiled_m16"
-    assert pick(3330, 262144, 1536, F32, BF16) == "k_project_tiled_bf16"
+    assert pick(3330, 262144, 1536, F32, BF16) == "k_project_tiled_m16x2"
+    assert pick(3330, 262144, 192, F32, BF16) == "k_project_tiled_bf16"  # d % 128 != 0
     assert pick(32, 248320, 2560, F32, BF16) == "k_project_wg_bf16"
     assert pick(1000, 5000, 192, BF16, BF16) == "k_project_small_bf16"  # d not whole tiled stages
     assert pick(255, 5000, 256, BF16, BF16) == "k_project_wg_bf16"      # too few rows to tile

@@ -95,6 +95,11 @@ TILED = [
     dict(V=2500, d=64, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=63, n_extra_rows=250),
     dict(V=4099, d=192, n_q=20, K=(1, 10), lengths=(1, 4), layout="field", seed=64,
          n_extra_rows=400, T=1.7),
+    # fp32 H with d a multiple of 128: the 16 x 16 kernel's two-plane form, 128-row tiles
+    dict(V=3001, d=128, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=68, n_extra_rows=300),
+    dict(V=1283, d=256, n_q=25, K=(1, 12), lengths=(1, 5), layout="prefix", seed=69,
+         n_extra_rows=211),
+    dict(V=256, d=128, n_q=10, K=(2, 4), lengths=(1, 3), layout="own", seed=70, n_extra_rows=256),
 ]
 
 
@@ -123,7 +128,7 @@ def test_tiled_stream(jet, h_dtype):
     _full_size_properties(p, out)
     # oracle on every referenced row plus the rows at each 256-row tile boundary and the tail
     n = p["n_rows"]
-    edges = [r for b in range(0, n, 256) for r in (b, b + 1, b + 255) if r < n]
+    edges = [r for b in range(0, n, 128) for r in (b, b + 1, b + 127) if r < n]
     rows = np.unique(np.concatenate([np.asarray(p["tok_row"]), edges, np.arange(n - 3, n)]))
     ref = jo.score(p, rows=rows)
     log(f"[gpu] errs {compare(p, out, ref, 'tiled_stream', sampled=True)} on {len(rows)} rows")
