@@ -219,7 +219,7 @@ def main(argv=None) -> int:
                     help="run a device copy of this many MiB first (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         return 2
 

@@ -28,7 +28,7 @@ What it computes, in the pages' order (citations name the page and its equation/
   restricted: softmax over a field's allowed-token logits divided by T
                                                          (nimble page, Execution steps 5-6)
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * T scales candidate scores only, once, before the candidate softmax; token
     log-probabilities are never tempered (JET says tokens are scored without temperature;
     the gemma-e2b doc and the nimble page apply T to candidate scores).
