@@ -158,9 +158,9 @@ __global__ __launch_bounds__(256) void k_bk_scatter(
   b_tok[b_off[(long long)(r / row_tile) * n_groups + tok_target[k] / vgroup] + pos] = k;
 }
 
-// Counting sort in LDS when the buckets fit (one workgroup): counts, exclusive scan and
-// offsets never leave LDS until the final offsets are stored.
-constexpr int kLdsBuckets = 12288;
+// Counting sort in LDS when the buckets fit (one workgroup, 128 KB of counts): counts,
+// exclusive scan and offsets never leave LDS until the final offsets are stored.
+constexpr int kLdsBuckets = 32768;
 
 __global__ __launch_bounds__(kPrepThreads) void k_bucket_lds(
     const int* __restrict__ tok_row, const int* __restrict__ tok_target, int n_tok, int n_rows,

@@ -140,10 +140,10 @@ def test_tiled_grid_bucketing(jet, h_dtype):
     targets are bucketed by the grid-wide launches; an out-of-range target and an
     out-of-range row raise their flags there and leave only their own tokens NaN."""
     p = wl.make_problem(V=262147, d=128, n_q=40, K=(2, 6), lengths=(1, 4), layout="prefix",
-                        seed=67, h_dtype=h_dtype, n_extra_rows=3000)
-    n_buckets = -(-p["n_rows"] // 256) * -(-p["V"] // 256)
+                        seed=67, h_dtype=h_dtype, n_extra_rows=9000)
+    n_buckets = -(-p["n_rows"] // 256) * -(-p["V"] // 256)  # (128-row tiles for fp32 H: twice)
     log(f"[gpu] grid bucketing {h_dtype} rows={p['n_rows']} V={p['V']} buckets={n_buckets}")
-    assert n_buckets > 12288
+    assert n_buckets > 32768
     out = _run(jet, p)
     _full_size_properties(p, out)
     rows = np.unique(np.asarray(p["tok_row"]))
