@@ -448,6 +448,26 @@ def test_stress_tiled(jet, h_dtype):
     log(f"[gpu] stress tiled {h_dtype} ({kern}) errs {compare(p, out, ref, 'stress_tiled')}")
 
 
+@pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
+def test_many_rows(jet, h_dtype):
+    """300,050 rows (2,345 tiles of 128 or 1,173 of 256) of which most score no token: the
+    full-vocabulary LSE of every row (row_lse) on sampled rows across the whole range,
+    including the shifted last row tile, against the oracle."""
+    p = wl.make_problem(V=4099, d=128, n_q=50, K=(2, 6), layout="field", seed=91,
+                        h_dtype=h_dtype, n_extra_rows=300000)
+    n = p["n_rows"]
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] many rows {h_dtype} rows={n} ({kern})")
+    assert kern.startswith("k_project_tiled"), kern
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.asarray(p["tok_row"]), rng.choice(n, 200, replace=False),
+                                     np.arange(n - 300, n), np.arange(0, 40)]))
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] many rows errs {compare(p, out, ref, 'many_rows', sampled=True)}")
+
+
 def _rows_of_questions(p, qs):
     co, qo = p["cand_tok_off"], p["q_cand_off"]
     tok_row = np.arange(len(p["tok_target"])) if p["tok_row"] is None else p["tok_row"]
