@@ -85,21 +85,20 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     pl->n_rtiles = (p->n_rows + pl->row_tile - 1) / pl->row_tile;
     pl->vgroup = 256;
     pl->n_vgroups = (p->V + 255) / 256;
-    // Split count S (vocabulary ranges per row tile), from a makespan estimate: R * S
-    // workgroups run in ceil(R S / 256) rounds on the 256 CUs, each taking ceil(n_vt / S)
-    // tiles plus about a quarter tile of per-workgroup overhead.  S a multiple of 8 lets
-    // the launch use the XCD-aware 4 x 8 placement (others pay an estimated 5%).
+    // Split count S (vocabulary ranges per row tile).  Every workgroup takes the same
+    // number L of consecutive vocabulary tiles (the last range of a row tile may be shorter
+    // or empty), about 8 when there is work for many workgroups: workgroups of equal
+    // length finish together, so each XCD's next 32 again form one 4 x 8 block sharing
+    // its L2, and short ones keep the eight XCDs on nearby head tiles.  (Measured on both
+    // tiled kernels: 8 tiles 3.5-7% faster than ranges of 16 or ~31, and than ranges of
+    // unequal length.)  Fewer tiles per workgroup when 8 would leave CUs idle.  S is
+    // rounded up to a multiple of 8 (XCD-aware placement) when that adds few empty ranges.
     const int R = pl->n_rtiles, nvt = pl->n_vgroups;
-    int splits = 1;
-    double best = 1e300;
-    for (int S = 1; S <= std::min(nvt, 1024); ++S) {
-      const double rounds = std::ceil((double)R * S / 256.0);
-      const double t = rounds * ((nvt + S - 1) / S + 0.25) * (S % 8 ? 1.05 : 1.0);
-      if (t < best - 1e-9) {
-        best = t;
-        splits = S;
-      }
-    }
+    const long long work = (long long)R * nvt;
+    int L = (int)std::min<long long>(8, std::max<long long>(1, work / 256));
+    L = std::min(L, nvt);
+    int splits = (nvt + L - 1) / L;
+    if (splits >= 32) splits = (splits + 7) / 8 * 8;
     pl->grid_x = splits;
   } else {
     pl->row_tile = 32;

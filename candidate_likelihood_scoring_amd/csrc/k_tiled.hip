@@ -234,8 +234,10 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
   const int row_nom = rt * TBN;                    // first row this tile reports
   const int row0 = min(row_nom, n_rows - TBN);     // rows loaded: [row0, row0 + 256), all valid
-  const int t0 = (int)((long long)split * n_vtiles / splits);
-  const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
+  // consecutive ranges of L tiles (see the split choice); trailing ranges may be empty
+  const int L = (n_vtiles + splits - 1) / splits;
+  const int t0 = min(split * L, n_vtiles);
+  const int t1 = min(t0 + L, n_vtiles);
   const int nk = d / BK;                           // even
   const uint32_t rowb = (uint32_t)d * 2;           // bytes per row (head and H planes)
 
@@ -551,8 +553,10 @@ __device__ __forceinline__ void project_m16(
   if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
   const int row_nom = rt * RT;
   const int row0 = min(row_nom, n_rows - RT);
-  const int t0 = (int)((long long)split * n_vtiles / splits);
-  const int t1 = (int)((long long)(split + 1) * n_vtiles / splits);
+  // consecutive ranges of L tiles (see the split choice); trailing ranges may be empty
+  const int L = (n_vtiles + splits - 1) / splits;
+  const int t0 = min(split * L, n_vtiles);
+  const int t1 = min(t0 + L, n_vtiles);
   const int nk = d / BK;  // even
   const uint32_t rowb = (uint32_t)d * 2;
   const __amdgpu_buffer_rsrc_t rH = rsrc_of(H, (uint32_t)n_rows * rowb);
