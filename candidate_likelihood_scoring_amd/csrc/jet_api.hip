@@ -87,15 +87,16 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     pl->n_vgroups = (p->V + 255) / 256;
     // Split count S (vocabulary ranges per row tile).  Every workgroup takes the same
     // number L of consecutive vocabulary tiles (the last range of a row tile may be shorter
-    // or empty), about 8 when there is work for many workgroups: workgroups of equal
-    // length finish together, so each XCD's next 32 again form one 4 x 8 block sharing
-    // its L2, and short ones keep the eight XCDs on nearby head tiles.  (Measured on both
-    // tiled kernels: 8 tiles 3.5-7% faster than ranges of 16 or ~31, and than ranges of
-    // unequal length.)  Fewer tiles per workgroup when 8 would leave CUs idle.  S is
-    // rounded up to a multiple of 8 (XCD-aware placement) when that adds few empty ranges.
+    // or empty), 4 when there is work for many workgroups: workgroups of equal length
+    // finish together, so each XCD's next 32 again form one 4 x 8 block sharing its L2,
+    // and short ones keep the eight XCDs on nearby head tiles.  (Measured on both tiled
+    // kernels: runs of 4 tiles 1-3% faster than 8, 6-10% faster than balanced ranges of
+    // unequal length; single tiles 2-3% slower.)  Fewer tiles per workgroup when 4 would
+    // leave CUs idle.  S is rounded up to a multiple of 8 (XCD-aware placement) when that
+    // adds few empty ranges.
     const int R = pl->n_rtiles, nvt = pl->n_vgroups;
     const long long work = (long long)R * nvt;
-    int L = (int)std::min<long long>(8, std::max<long long>(1, work / 256));
+    int L = (int)std::min<long long>(4, std::max<long long>(1, work / 256));
     L = std::min(L, nvt);
     int splits = (nvt + L - 1) / L;
     if (splits >= 32) splits = (splits + 7) / 8 * 8;
