@@ -42,20 +42,29 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines, so a comment edit keeps the digest."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def _source_digest(files):
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
-# Sources that determine each projection kernel's code; a traffic figure measured with
-# hardware counters is reported only while these are unchanged.
+# Sources that determine each projection kernel's code and launch plan; a traffic figure
+# measured with hardware counters is reported only while their code is unchanged.
 _SMALL_SRC = ["candidate_likelihood_scoring_amd/csrc/k_project.hip",
-              "candidate_likelihood_scoring_amd/csrc/jet_internal.h"]
+              "candidate_likelihood_scoring_amd/csrc/jet_internal.h",
+              "candidate_likelihood_scoring_amd/csrc/jet_api.hip"]
 _TILED_SRC = ["candidate_likelihood_scoring_amd/csrc/k_tiled.hip",
-              "candidate_likelihood_scoring_amd/csrc/jet_internal.h"]
+              "candidate_likelihood_scoring_amd/csrc/jet_internal.h",
+              "candidate_likelihood_scoring_amd/csrc/jet_api.hip"]
 KERNEL_SOURCES = {"k_project_wg_bf16": _SMALL_SRC, "k_project_small_bf16": _SMALL_SRC,
                   "k_project_small_f32": _SMALL_SRC, "k_project_tiled_bf16": _TILED_SRC,
                   "k_project_tiled_m16": _TILED_SRC, "k_project_tiled_m16x2": _TILED_SRC}

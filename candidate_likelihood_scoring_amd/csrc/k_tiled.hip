@@ -774,8 +774,8 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   // 256; padding workgroups (row tile >= R) exit at once.  Otherwise the plain order
   // P = rt * S + split.  bf16 H takes 8 x 4 blocks (each head tile shared 8 ways; 2%
   // faster than 4 x 8 on large_batch) when that pads at most 1/16 of the row tiles; the
-  // two-plane kernels, whose H tiles hold two planes, take 4 x 8 (8 x 4 was 20% slower on
-  // multi_token).
+  // two-plane kernels, whose H tiles hold two planes, take 4 x 8 (with 8 x 4 they were no
+  // faster at 32 row tiles and 7% slower at 64).
   const int S = pl.grid_x, R = pl.n_rtiles;
   int sr = 1, ss = S, remap = 0, total = S * R;
   if (S % 8 == 0) {

@@ -321,3 +321,13 @@ def test_stream_read_host_checks(lib):
     assert lib.jet_stream_read(17, 1024, ctypes.addressof(out), None) == E_SHAPE  # misaligned
     assert lib.jet_stream_read(16, 1000, ctypes.addressof(out), None) == E_SHAPE  # not 16 B whole
     assert lib.jet_stream_read(16, 0, ctypes.addressof(out), None) == 0            # nothing to read
+
+
+def test_profile_digest_ignores_comments_only():
+    """The counter-traffic digest changes with the kernel code, not with its comments."""
+    import bench
+    code = "int f(int a) {\n  return a + 1;  // one\n}\n"
+    assert bench._code_only(code) == bench._code_only("/* header\n note */\n" + code.replace("// one", "// two") + "\n\n")
+    assert bench._code_only(code) != bench._code_only(code.replace("a + 1", "a + 2"))
+    for files in bench.KERNEL_SOURCES.values():
+        assert "candidate_likelihood_scoring_amd/csrc/jet_api.hip" in files
