@@ -134,6 +134,24 @@ def test_tiled_stream(jet, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, 'tiled_stream', sampled=True)} on {len(rows)} rows")
 
 
+def test_tiled_padded_row_groups(jet):
+    """bf16 H in 31 row tiles of 256 over 513 vocabulary tiles (136 splits): the launch
+    places 8 row tiles x 4 splits per XCD and pads the last row group with one empty row
+    tile, whose workgroups exit at once.  Every row of the last two row groups and the
+    tile boundaries are checked."""
+    p = wl.make_problem(V=131101, d=128, n_q=40, K=(2, 6), lengths=(1, 4), layout="prefix",
+                        seed=71, h_dtype="bf16", n_extra_rows=7611)
+    n = p["n_rows"]
+    log(f"[gpu] padded row groups rows={n} V={p['V']}")
+    assert 30 * 256 < n <= 31 * 256
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    edges = [r for b in range(0, n, 256) for r in (b, b + 255) if r < n]
+    rows = np.unique(np.concatenate([np.asarray(p["tok_row"]), edges, np.arange(16 * 256, n)]))
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] errs {compare(p, out, ref, 'padded_row_groups', sampled=True)} on {len(rows)} rows")
+
+
 @pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
 def test_tiled_grid_bucketing(jet, h_dtype):
     """More (row tile, vocabulary tile) buckets than one workgroup sorts in LDS, so the
