@@ -35,7 +35,9 @@ MFMA_F32_PEAK_TFS = 157.3
 # kernel's average duration.
 EVENT_EVERY = 4
 
-WORKLOADS = ("binary_enum", "multi_token", "large_batch", "restricted", "restricted_max", "tiny")
+WORKLOADS = ("binary_enum", "multi_token", "large_batch", "restricted", "restricted_max", "tiny",
+             "sensitivity", "temperature_fit")
+FIT_ROUNDS = 6  # the device fit evaluates 64 grid temperatures per round, six rounds
 
 
 def _log(msg):
@@ -169,17 +171,22 @@ def _cpu_model() -> str:
     return ""
 
 
+def _oracle_threads() -> int:
+    """Threads the oracle's numpy BLAS uses on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 30.0) -> dict:
     """The fp64 oracle on the host's cores, on a bounded sample of the same workload: whole
     questions (all of them if they fit about budget_s), repeated until about 10 s of work."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    cores = _oracle_threads()
     if restricted:
         n = int(p["field_off"][-1])
         runs, dt = _timed_runs(lambda: oracle.score_restricted(p))
@@ -214,6 +221,88 @@ def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 30.0) -> dict:
                        f"{_cpu_model()}")
 
 
+def _bench_calibration(args) -> int:
+    """Per-call latency of the two calibration entry points on the pages' sizes: layer-skip
+    sensitivity over 32 inputs of 2-65 logits and 28 layers (k = 4 selected), and the
+    temperature fit over 4096 labelled questions of 2-26 candidates.  Both are launch-bound;
+    the roofline line prices their input bytes (once per round for the fit) against HBM."""
+    import numpy as np
+    import torch
+
+    import oracle as jo
+    import workloads as wl
+    from candidate_likelihood_scoring_amd import api
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    if args.workload == "sensitivity":
+        c = wl.calibration_logits()
+        z, zs = torch.from_numpy(c["z"]).to(dev), torch.from_numpy(c["z_skip"]).to(dev)
+        off = torch.from_numpy(c["seg_off"]).to(dev)
+        k = 4
+
+        def step():
+            return api.decision_sensitivity(z, zs, off, k)
+
+        def oracle_call():
+            return jo.decision_sensitivity(c["z"], c["z_skip"], c["seg_off"])
+
+        n_in, L, n = int(c["n_inputs"]), int(c["n_layers"]), int(c["z"].size)
+        alg_bytes = 4 * (n * (L + 1) + n_in + 1) + 4 * (L * n_in + L + k)
+        config = dict(workload="sensitivity", inputs=n_in, layers=L, logits=n, k=k)
+        unit, metric = "passes/s", "decision-sensitivity passes/s"
+        note = "launch latency: four launches of a few microseconds"
+    else:
+        q = wl.labelled_questions()
+        t = {key: torch.from_numpy(q[key]).to(dev)
+             for key in ("cand_s", "q_cand_off", "cand_text_id", "q_gold_text_id")}
+
+        def step():
+            return api.fit_temperature(t["cand_s"], t["q_cand_off"], t["cand_text_id"],
+                                       t["q_gold_text_id"])
+
+        def oracle_call():
+            return jo.fit_temperature(q["cand_s"].astype(np.float64), q["q_cand_off"],
+                                      q["cand_text_id"], q["q_gold_text_id"])
+
+        n_q, n_c = len(q["q_cand_off"]) - 1, len(q["cand_s"])
+        alg_bytes = FIT_ROUNDS * 4 * (2 * n_c + 2 * n_q + 1) + 8
+        config = dict(workload="temperature_fit", questions=n_q, candidates=n_c,
+                      grid_per_round=64, rounds=FIT_ROUNDS)
+        unit, metric = "fits/s", "temperature fits/s"
+        note = ("six rounds of two dependent launches; a wave takes its question's candidates "
+                "one after another")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(res["dev_flags"][0].item()) == 0
+    med, mn = _per_call_ms(step, stream, args.steps)
+    achieved = alg_bytes / (med * 1e-3) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 3), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 6), traffic=None)
+    cpu = None
+    if not args.no_cpu_baseline:
+        runs, total = _timed_runs(oracle_call, min_s=10.0, max_runs=2000)
+        cpu = dict(value=round(runs / total, 3), unit=unit, cores=_oracle_threads(), kind="oracle",
+                   sample=f"the whole input, {runs} runs, {total:.2f} s{_cpu_model()}")
+    line = dict(metric=metric, value=round(args.steps / wall, 1), unit=unit, n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=round(wall * 1e3 / args.steps, 5),
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                data="synthetic", config=config, roofline=roofline, cpu_baseline=cpu,
+                extra=dict(call_ms_median=round(med, 5), call_ms_min=round(mn, 5),
+                           algorithmic_bytes_per_call=int(alg_bytes),
+                           bound_note=note))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +320,8 @@ def main(argv=None) -> int:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         return 2
+    if args.workload in ("sensitivity", "temperature_fit"):
+        return _bench_calibration(args)
 
     import numpy as np
     import torch

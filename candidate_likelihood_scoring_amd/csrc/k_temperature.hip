@@ -6,10 +6,13 @@
 // Each round evaluates 64 temperatures spaced evenly in log T over the current interval,
 // one per lane.  k_fit_partial: wave w of the launch takes questions w, w + W, ... (W waves
 // in all) and every lane accumulates its temperature's NLL over them in question order; a
-// workgroup adds its 4 waves in order into one partial per temperature.  k_fit_reduce (one
-// wave): adds the workgroups' partials in order, takes the argmin (lowest index on ties, NaN
-// last) and narrows the interval to the two neighbouring grid points, kept in the
-// workspace for the next round.  Six rounds shrink the spacing from ln(T_max / T_min) / 63
+// workgroup adds its 4 waves in order into one partial per temperature.  There are up to
+// 1024 workgroups, one wave per question up to 4096 questions: a wave's questions run one
+// after another, so the question count per wave sets the kernel's length.  k_fit_reduce (16
+// waves): wave w adds the partials of the w-th contiguous slice of workgroups in order, wave
+// 0 adds the 16 slice sums in order, takes the argmin (lowest index on ties, NaN last) and
+// narrows the interval to the two neighbouring grid points, kept in the workspace for the
+// next round.  Six rounds shrink the spacing from ln(T_max / T_min) / 63
 // by (2/63)^5, below fp32 resolution of ln T.  Questions with no label (gold id < 0) or no
 // candidate of the gold text are not counted.  The result is bitwise reproducible.
 #include <algorithm>
@@ -19,7 +22,7 @@
 namespace jet {
 namespace {
 
-constexpr int kGrid = 64, kRounds = 6, kMaxBlocks = 256;
+constexpr int kGrid = 64, kRounds = 6, kMaxBlocks = 1024, kReduceWaves = 16;
 
 __device__ inline float grid_point(float lo, float hi, int g) {
   return lo + (hi - lo) * (float)g / (float)(kGrid - 1);
@@ -47,18 +50,31 @@ __global__ __launch_bounds__(256) void k_fit_partial(
     }
     const int gt = gold[q];
     if (gt < 0) continue;
+    // The question's scores and text ids arrive 64 at a time, one per lane, in one coalesced
+    // load; each candidate is then broadcast from its lane, so the loops below wait on one
+    // load per 64 candidates instead of one per candidate.  Candidates are visited in order.
     float M = -INFINITY, Mg = -INFINITY;
-    for (int c = c0; c < c1; ++c) {
-      const float a = s[c] * inv_t;
-      M = fmaxf(M, a);
-      if (text[c] == gt) Mg = fmaxf(Mg, a);
+    for (int b = c0; b < c1; b += kGrid) {
+      const int n = min(kGrid, c1 - b);
+      const float sv = g < n ? s[b + g] : 0.f;
+      const int tv = g < n ? text[b + g] : 0;
+      for (int j = 0; j < n; ++j) {
+        const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), j)) * inv_t;
+        M = fmaxf(M, a);
+        if (__builtin_amdgcn_readlane(tv, j) == gt) Mg = fmaxf(Mg, a);
+      }
     }
     if (Mg == -INFINITY) continue;  // no candidate of the gold text
     float Z = 0.f, Zg = 0.f;
-    for (int c = c0; c < c1; ++c) {
-      const float a = s[c] * inv_t;
-      Z += expf(a - M);
-      if (text[c] == gt) Zg += expf(a - Mg);
+    for (int b = c0; b < c1; b += kGrid) {
+      const int n = min(kGrid, c1 - b);
+      const float sv = g < n ? s[b + g] : 0.f;
+      const int tv = g < n ? text[b + g] : 0;
+      for (int j = 0; j < n; ++j) {
+        const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), j)) * inv_t;
+        Z += expf(a - M);
+        if (__builtin_amdgcn_readlane(tv, j) == gt) Zg += expf(a - Mg);
+      }
     }
     acc += (M + logf(Z)) - (Mg + logf(Zg));
     ++used;
@@ -73,21 +89,34 @@ __global__ __launch_bounds__(256) void k_fit_partial(
   }
 }
 
-__global__ __launch_bounds__(64) void k_fit_reduce(const float* __restrict__ part,
-                                                   const int* __restrict__ cnt, int nb,
-                                                   float* __restrict__ iv, float lo0, float hi0,
-                                                   int first, int last, float* __restrict__ T_out,
-                                                   float* __restrict__ nll_out) {
-  const int g = threadIdx.x;
-  const float lo = first ? lo0 : iv[0], hi = first ? hi0 : iv[1];
-  const float u = grid_point(lo, hi, g);
+__global__ __launch_bounds__(kReduceWaves * 64) void k_fit_reduce(
+    const float* __restrict__ part, const int* __restrict__ cnt, int nb, float* __restrict__ iv,
+    float lo0, float hi0, int first, int last, float* __restrict__ T_out,
+    float* __restrict__ nll_out) {
+  __shared__ float wsum[kReduceWaves][kGrid];
+  __shared__ int wn[kReduceWaves];
+  const int g = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int per = (nb + kReduceWaves - 1) / kReduceWaves;
+  const int b0 = min(nb, w * per), b1 = min(nb, b0 + per);
   float tot = 0.f;
   int n = 0;
 #pragma unroll 8
-  for (int b = 0; b < nb; ++b) {
+  for (int b = b0; b < b1; ++b) {
     tot += part[(size_t)b * kGrid + g];
     n += cnt[b];
   }
+  wsum[w][g] = tot;
+  if (g == 0) wn[w] = n;
+  __syncthreads();
+  if (w != 0) return;
+  tot = 0.f;
+  n = 0;
+  for (int v = 0; v < kReduceWaves; ++v) {
+    tot += wsum[v][g];
+    n += wn[v];
+  }
+  const float lo = first ? lo0 : iv[0], hi = first ? hi0 : iv[1];
+  const float u = grid_point(lo, hi, g);
   const float f = n ? tot / (float)n : __builtin_nanf("");
   float bv = f != f ? INFINITY : f;
   int bi = g;
@@ -116,7 +145,7 @@ __global__ void k_temp_clear(int32_t* __restrict__ flags) {
   if (threadIdx.x == 0) flags[0] = 0;
 }
 
-int fit_blocks(int n_q) { return std::max(1, std::min(kMaxBlocks, (n_q + 31) / 32)); }
+int fit_blocks(int n_q) { return std::max(1, std::min(kMaxBlocks, (n_q + 3) / 4)); }
 
 }  // namespace
 
@@ -143,7 +172,7 @@ hipError_t launch_fit_temperature(const float* s, const int* q_cand_off, int n_q
     hipLaunchKernelGGL(k_fit_partial, dim3(nb), dim3(256), 0, stream, s, q_cand_off, n_q, n_cand,
                        text, gold, round ? iv : nullptr, lo0, hi0, part, cnt, flags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_fit_reduce, dim3(1), dim3(64), 0, stream, part, cnt, nb, iv, lo0, hi0,
+    hipLaunchKernelGGL(k_fit_reduce, dim3(1), dim3(kReduceWaves * 64), 0, stream, part, cnt, nb, iv, lo0, hi0,
                        round == 0 ? 1 : 0, round + 1 == kRounds ? 1 : 0, T_out, nll_out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
