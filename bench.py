@@ -253,7 +253,7 @@ def _bench_calibration(args) -> int:
         alg_bytes = 4 * (n * (L + 1) + n_in + 1) + 4 * (L * n_in + L + k)
         config = dict(workload="sensitivity", inputs=n_in, layers=L, logits=n, k=k)
         unit, metric = "passes/s", "decision-sensitivity passes/s"
-        note = "launch latency: four launches of a few microseconds"
+        note = "launch latency: three launches of a few microseconds"
     else:
         q = wl.labelled_questions()
         t = {key: torch.from_numpy(q[key]).to(dev)

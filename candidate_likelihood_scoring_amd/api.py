@@ -151,7 +151,7 @@ def decision_sensitivity(z: torch.Tensor, z_skip: torch.Tensor, seg_off: torch.T
     out = dict(d=torch.empty(L, max(n_in, 0), dtype=torch.float32, device=dev),
                J=torch.empty(L, dtype=torch.float32, device=dev),
                selected=torch.empty(max(k, 1), dtype=torch.int32, device=dev),
-               dev_flags=torch.zeros(1, dtype=torch.int32, device=dev))
+               dev_flags=torch.empty(1, dtype=torch.int32, device=dev))
     _enter_stream(stream, z, z_skip, seg_off, *out.values())
     sh = _stream_handle(stream)
     st = _lib.load().jet_decision_sensitivity(
@@ -176,7 +176,7 @@ def fit_temperature(cand_s: torch.Tensor, q_cand_off: torch.Tensor, cand_text_id
         _check_i32(name, t, dev)
     out = dict(T=torch.empty(1, dtype=torch.float32, device=dev),
                nll=torch.empty(1, dtype=torch.float32, device=dev),
-               dev_flags=torch.zeros(1, dtype=torch.int32, device=dev))
+               dev_flags=torch.empty(1, dtype=torch.int32, device=dev))
     lib = _lib.load()
     n_q = int(q_cand_off.numel()) - 1
     need = int(lib.jet_fit_temperature_workspace_size(max(n_q, 1)))
