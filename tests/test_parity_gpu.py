@@ -301,7 +301,7 @@ def _check_fit(s, qo, text, gold, out, T_min=1e-2, T_max=1e2, what="", ds=0.0):
         f"(tol {2 * tol:.1e})")
 
 
-@pytest.mark.parametrize("case", ["planted", "closed_form", "partly_unlabelled", "wide"])
+@pytest.mark.parametrize("case", ["planted", "closed_form", "partly_unlabelled", "wide", "many"])
 def test_fit_temperature(jet, case):
     """Temperature fitting against the oracle's minimiser, compared by the NLL it attains."""
     from candidate_likelihood_scoring_amd import api
@@ -313,6 +313,10 @@ def test_fit_temperature(jet, case):
         s = np.array([0.0, -2.0, 0.0, 1.0], np.float32)
         qo, text, gold = (np.array([0, 2, 4], np.int32), np.array([0, 1, 0, 1], np.int32),
                           np.array([0, 0], np.int32))
+    elif case == "many":
+        # more questions than the 4096 waves of a full launch: waves take one or two each
+        c = wl.labelled_questions(n_q=5001, K=(2, 8), seed=811)
+        s, qo, text, gold = c["cand_s"], c["q_cand_off"], c["cand_text_id"], c["q_gold_text_id"]
     elif case == "wide":
         # 60-150 candidates per question: scores arrive in chunks of 64 (one per lane)
         c = wl.labelled_questions(n_q=200, K=(60, 150), seed=810)
