@@ -88,7 +88,7 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     // Split count S (vocabulary ranges per row tile).  Every workgroup takes the same
     // number L of consecutive vocabulary tiles (the last range of a row tile may be shorter
     // or empty), 4 when there is work for many workgroups: workgroups of equal length
-    // finish together, so each XCD's next 32 again form one 4 x 8 block sharing its L2,
+    // finish together, so each XCD's next 32 again form one block sharing its L2,
     // and short ones keep the eight XCDs on nearby head tiles.  (Measured on both tiled
     // kernels: runs of 4 tiles 1-3% faster than 8, 6-10% faster than balanced ranges of
     // unequal length; single tiles 2-3% slower.)  Fewer tiles per workgroup when 4 would
