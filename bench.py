@@ -457,6 +457,21 @@ def main(argv=None) -> int:
     w_elt = 4 if p["w_dtype"] == "f32" else 2
     rows = int(p["n_rows"])
     roofline = None
+    if restricted:
+        # Input bytes read once (the union's head rows, each field's H row, the index arrays)
+        # plus the outputs, over the warm per-call duration of the whole call (a gather, the
+        # fused projection and the per-field softmax): a lower bound on the dominant kernel's
+        # own bandwidth.
+        h_elt = 4 if p["h_dtype"] == "f32" else 2
+        n_h = len(np.unique(np.asarray(p["field_row"])))
+        alg_bytes = (prob.n_union * d * w_elt + n_h * d * h_elt + 4 * prob.n_union
+                     + 4 * (2 * prob.n_fields + 1) + 4 * prob.n_slots
+                     + 8 * prob.n_slots + 4 * prob.n_fields)
+        achieved = alg_bytes / (extra["call_ms_median"] * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+        extra["algorithmic_bytes_per_call"] = int(alg_bytes)
+        extra["roofline_timing"] = "whole call (three launches), warm median"
     if events:
         kms = np.array([a.elapsed_time(b) for a, b in events])
         k_avg_s = float(kms.mean()) * 1e-3
