@@ -153,6 +153,27 @@ def test_tiled_padded_row_groups(jet):
 
 
 @pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("R", [8, 9, 15, 16, 17, 24, 31, 33, 40])
+def test_tiled_placement_sweep(jet, h_dtype, R):
+    """Row-tile counts on both sides of the XCD block-shape rule (8 x 4 blocks for bf16 H
+    when padding to a multiple of 8 costs at most R/16 row tiles, else 4 x 8, padded), over
+    129 vocabulary tiles (40 splits): the sampled rows cover every tile boundary and the
+    last two row tiles."""
+    tile = 256 if h_dtype == "bf16" else 128
+    p = wl.make_problem(V=33001, d=128, n_q=40, K=(2, 6), lengths=(1, 4), layout="prefix",
+                        seed=71, h_dtype=h_dtype, n_extra_rows=R * tile - 7 - 289)
+    n = p["n_rows"]
+    log(f"[gpu] placement sweep {h_dtype} R={R} rows={n}")
+    assert -(-n // tile) == R
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    edges = [r for b in range(0, n, tile) for r in (b, b + tile - 1) if r < n]
+    rows = np.unique(np.concatenate([np.asarray(p["tok_row"]), edges, np.arange(n - 2 * tile, n)]))
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] errs {compare(p, out, ref, f'placement_{h_dtype}_{R}', sampled=True)}")
+
+
+@pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
 def test_tiled_grid_bucketing(jet, h_dtype):
     """More (row tile, vocabulary tile) buckets than one workgroup sorts in LDS, so the
     targets are bucketed by the grid-wide launches; an out-of-range target and an
