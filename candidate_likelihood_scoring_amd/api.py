@@ -83,13 +83,16 @@ class Workspace:
         return self.base, self.size
 
 
+# Default workspaces, one per (device, stream): the library's calls on one stream run in
+# order and may share scratch memory, while calls on different streams may overlap, so
+# each stream gets its own.
 _default_ws: dict = {}
 
 
-def _workspace(ws, device) -> Workspace:
+def _workspace(ws, device, stream=None) -> Workspace:
     if ws is not None:
         return ws
-    key = str(device)
+    key = (str(torch.device(device)), _stream_handle(stream) or 0)
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
@@ -237,7 +240,9 @@ def score(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None, cand_
           events=None, optional=True) -> dict:
     """jet_score on device tensors.  Returns a dict of output tensors (allocated unless
     `out` is given).  events: optional (before, after) raw hipEvent_t handles recorded
-    around the projection kernel."""
+    around the projection kernel.  Without `workspace` the call uses this module's
+    workspace for its (device, stream): calls on different streams never share scratch
+    memory; a caller-supplied workspace must not be used by two streams at once."""
     prob = make_problem(H, W, tok_target, cand_tok_off, q_cand_off, T, tok_row, cand_text_id,
                         q_gold_text_id, q_true_idx)
     lib = _lib.load()
@@ -248,7 +253,7 @@ def score(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None, cand_
     sh = _stream_handle(stream)
     if need == 0:  # invalid scalars: jet_score reports which check failed, enqueuing nothing
         raise JetError(lib.jet_score(ctypes.byref(prob), ctypes.byref(o), None, 0, sh), "jet_score")
-    ws = _workspace(workspace, W.device)
+    ws = _workspace(workspace, W.device, stream)
     base, size = ws.get(need)
     _enter_stream(stream, H, W, tok_target, cand_tok_off, q_cand_off, tok_row, cand_text_id,
                   q_gold_text_id, q_true_idx, ws.buf, *out.values())
@@ -323,7 +328,8 @@ def make_restricted_problem(H, W, union_ids, field_row, field_slot_off, slot_uid
 
 def score_restricted(H, W, union_ids, field_row, field_slot_off, slot_uidx, T=1.0, *, out=None,
                      workspace=None, stream=None) -> dict:
-    """jet_score_restricted on device tensors: slot_logit, slot_q, field_argmax, dev_flags."""
+    """jet_score_restricted on device tensors: slot_logit, slot_q, field_argmax, dev_flags.
+    Without `workspace` the call uses this module's workspace for its (device, stream)."""
     prob = make_restricted_problem(H, W, union_ids, field_row, field_slot_off, slot_uidx, T)
     lib = _lib.load()
     need = int(lib.jet_restricted_workspace_size(ctypes.byref(prob)))
@@ -339,7 +345,7 @@ def score_restricted(H, W, union_ids, field_row, field_slot_off, slot_uidx, T=1.
     if need == 0:  # invalid scalars: the entry point reports which check failed
         raise JetError(lib.jet_score_restricted(ctypes.byref(prob), ctypes.byref(o), None, 0,
                                                 _stream_handle(stream)), "jet_score_restricted")
-    ws = _workspace(workspace, dev)
+    ws = _workspace(workspace, dev, stream)
     base, size = ws.get(need)
     _enter_stream(stream, H, W, union_ids, field_row, field_slot_off, slot_uidx, ws.buf,
                   *out.values())

@@ -1,6 +1,8 @@
 // C ABI of libjet: host-side validation, execution planning and launch sequencing.
-// Every check here runs on the host before anything is enqueued; a failing call
-// enqueues nothing.  The device kernels bounds-check every index themselves.
+// Every check here runs on the host before anything is enqueued, so a call rejected by a
+// check enqueues nothing.  JET_E_HIP alone comes after enqueueing may have begun: it
+// reports a failed launch or event record, and the launches before it stay enqueued.  The
+// device kernels bounds-check every index themselves.
 #include <algorithm>
 #include <cmath>
 #include <unordered_map>

@@ -355,6 +355,12 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
 #undef JET_STAGE_LOAD
     epilogue_lse<1>(acc, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
                     tok_target, z_tgt, m_run, s_run);
+    // The H stage buffer is hb[stage & 1] and the stage count restarts with every group.
+    // With an odd count the group's last stage and the next group's first share buffer 0,
+    // so no wave may write the next group's stage 0 before every wave has read the last
+    // stage: one barrier per group (uniform; an even count alternates across the boundary
+    // and needs none).
+    if (nst & 1) __syncthreads();
   }
   store_partial<WPB>(m_run, s_run, n, half, wid, row0, n_rows, part, red);
 

@@ -29,9 +29,14 @@
  *    into two bf16 terms so the product keeps about 16 significant bits of H), and
  *    (W fp32, H fp32).  Anything else returns JET_E_DTYPE.
  *  - d must be a positive multiple of 32 (at most 65536); V >= 1; counts >= 0.
- *  - Errors: functions return a negative jet_status and enqueue nothing.  Only scalars
- *    and pointers are checked on the host, since index arrays live on the device; use
- *    jet_validate_host (host copies) to check indices.  On the device every index is
+ *  - Errors: functions return a negative jet_status.  Every status except JET_E_HIP
+ *    comes from a check made on the host before anything is enqueued, so such a call
+ *    enqueues nothing.  JET_E_HIP reports a HIP runtime call (a kernel launch or an event
+ *    record) that failed: the launches the same call enqueued before it stay enqueued
+ *    (they read and write only the call's own buffers), and the outputs, the workspace and
+ *    *dev_flags are then undefined.  Only scalars and pointers are checked on the host,
+ *    since index arrays live on the device; use jet_validate_host (host copies) to check
+ *    indices.  On the device every index is
  *    bounds-checked: an out-of-range row, target or offset never causes an out-of-bounds
  *    access; it sets a bit in *dev_flags (when given) and yields NaN in the affected
  *    outputs.  Outputs are defined only when the status is JET_OK and *dev_flags is 0.
@@ -71,7 +76,8 @@ typedef enum JET_ENUM_INT {
   JET_E_INDEX = -4,     /* host validation: index out of range or offsets not monotone  */
   JET_E_TEMP = -5,      /* T is not finite or not > 0                                   */
   JET_E_WORKSPACE = -6, /* workspace NULL, smaller than the size query, or misaligned   */
-  JET_E_HIP = -7,       /* a HIP runtime call (launch, event record) failed             */
+  JET_E_HIP = -7,       /* a HIP runtime call (launch, event record) failed; earlier
+                           launches of the same call may already be enqueued            */
 } jet_status;
 
 typedef enum JET_ENUM_INT { JET_F32 = 0, JET_BF16 = 1 } jet_dtype;

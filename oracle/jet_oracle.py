@@ -33,8 +33,9 @@ Readings taken where the pages are silent:
     log-probabilities are never tempered (JET says tokens are scored without temperature;
     the gemma-e2b doc and the nimble page apply T to candidate scores).
   * "Fixed ordering" for ties = supplied candidate order, lowest index wins.  The decision
-    is taken on float32-rounded a = s/T, the precision the GPU kernel decides in, so both
-    sides see the same exact ties; top-two gaps are reported in fp64.
+    is taken on the exact fp64 a = s/T (a tie is exact equality there, as for candidates
+    with identical inputs); top-two gaps in q are reported so that a comparison can tell
+    a clear decision from a near tie.
   * Binary "true" index: per-question index if given, else 1 for K == 2 ([false, true]),
     else none (NaN).
   * Gold NLL uses the same q as the decision (so T is included), natural log; +inf when
@@ -126,8 +127,7 @@ def decide_question(s: np.ndarray, T: float, text_id=None, gold_text=None, true_
     e = np.exp(a - M)
     Z = float(np.sum(e))
     q = e / Z
-    a32 = a.astype(np.float32)
-    argmax = int(np.flatnonzero(a32 == a32.max())[0])
+    argmax = int(np.flatnonzero(a == M)[0])
     qs = np.sort(q)[::-1]
     gap = float(qs[0] - qs[1]) if K >= 2 else math.inf
     if true_idx is None:
@@ -196,13 +196,15 @@ def decide(s: np.ndarray, q_cand_off: np.ndarray, T: float, cand_text_id=None,
 # full problem
 # ----------------------------------------------------------------------------------------
 
-def score(p: dict, rows=None) -> dict:
+def score(p: dict, rows=None, W64=None) -> dict:
     """Score a whole problem (a dict as built by the workloads package).
 
     rows: None for every row, or an index array of the predictor rows to compute (sampled
     parity at full size); tokens on other rows get NaN, and so does everything built on
-    them.  Returns fp64 arrays: lse (per row, NaN if not computed), tok_logp, cand_s,
-    cand_q, q_argmax, q_gap, q_true, q_expect, q_nll, q_confidence, q_mass.
+    them.  W64: the head already widened to fp64 by widen() (so that repeated calls, e.g.
+    when timing the scoring alone, widen it once); None widens p["W"] here.  Returns fp64
+    arrays: lse (per row, NaN if not computed), tok_logp, cand_s, cand_q, q_argmax, q_gap,
+    q_true, q_expect, q_nll, q_confidence, q_mass.
     """
     n_rows = int(p["n_rows"])
     tok_target = np.asarray(p["tok_target"], dtype=np.int64)
@@ -210,7 +212,8 @@ def score(p: dict, rows=None) -> dict:
     tok_row = (np.arange(n_tok, dtype=np.int64) if p.get("tok_row") is None
                else np.asarray(p["tok_row"], dtype=np.int64))
     rows = np.arange(n_rows) if rows is None else np.unique(np.asarray(rows, dtype=np.int64))
-    W64 = widen(p["W"], p["w_dtype"])
+    if W64 is None:
+        W64 = widen(p["W"], p["w_dtype"])
     H64 = widen(np.asarray(p["H"])[rows], p["h_dtype"])
     lse = np.full(n_rows, np.nan)
     z_tgt = np.full(n_tok, np.nan)
@@ -250,8 +253,8 @@ def build_union(field_ids: np.ndarray, field_off: np.ndarray, V: int):
 
 def score_restricted(rp: dict) -> dict:
     """Per field f with row r and allowed ids j: b_j = z[r, j]; q = softmax(b / T) over the
-    field's allowed ids; argmax with the lowest index winning ties, decided on
-    float32-rounded b / T (nimble page, Execution step 6; scaling applied once before the
+    field's allowed ids; argmax with the lowest index winning ties, decided on the
+    exact fp64 b / T (nimble page, Execution step 6; scaling applied once before the
     softmax, "V2 probability default").  No full-vocabulary normaliser is involved
     ("Correctness and limits": full-vocabulary probabilities are not part of this path)."""
     fo = np.asarray(rp["field_off"])

@@ -8,7 +8,14 @@ evaluated by the oracle on the same bf16 bits; q: 1e-4) and the ones derived fro
   gold NLL  2 * m_max * tol_l / T  (difference of two log-sum-exps of s / T)
   mass      relative m_max * tol_l (sum_c exp s(c))
   confidence  2 m_max tol_l / T + 1e-5 (first-order bound through the entropy)
-Decisions must match wherever the oracle's top-two gap in q exceeds 1e-4.
+Decisions (check_decisions), for every question:
+  * the kernel's own tie rule: its decision is the lowest index among the exact maxima of
+    its own a = float32(s) / T (the kernel divides with correct rounding, as numpy does),
+    so candidates with bitwise-equal scores always go to the first;
+  * outside the near-tie band (the oracle's top-two gap in q above 1e-4) the decision
+    equals the oracle's, which is taken on the exact fp64 scores;
+  * inside the band the decision is one of the oracle's near-maximal candidates: its
+    oracle q is within 1e-4 of the largest.
 """
 from __future__ import annotations
 
@@ -40,6 +47,31 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+def check_decisions(argmax, s_out, off, T, ref_argmax, ref_gap, ref_q, name="", qmask=None) -> dict:
+    """Assert the decision rules above for the groups [off[g], off[g+1]) (questions, or
+    fields of the restricted path).  s_out: the kernel's fp32 scores (cand_s, or the
+    restricted slot logits); qmask: groups the oracle computed (None: all).  Returns the
+    number of groups decided outside the band and inside it."""
+    a = np.asarray(s_out, np.float32) / np.float32(T)
+    off = np.asarray(off)
+    n_clear = n_band = 0
+    for g in range(len(off) - 1):
+        c0, c1 = int(off[g]), int(off[g + 1])
+        ag = a[c0:c1]
+        top = np.flatnonzero(ag == ag.max())
+        assert top.size and int(argmax[g]) == int(top[0]), (name, "own tie rule", g, int(argmax[g]), top[:8])
+        if qmask is not None and not qmask[g]:
+            continue
+        if ref_gap[g] > Q_TOL:
+            n_clear += 1
+            assert int(argmax[g]) == int(ref_argmax[g]), (name, "argmax", g, int(argmax[g]), int(ref_argmax[g]))
+        else:
+            n_band += 1
+            qg = np.asarray(ref_q[c0:c1], np.float64)
+            assert qg[int(argmax[g])] >= qg.max() - Q_TOL, (name, "near-tie decision", g, int(argmax[g]))
+    return dict(argmax_checked=n_clear, argmax_in_band=n_band)
+
+
 def compare(p: dict, out: dict, ref: dict, name: str = "", sampled: bool = False) -> dict:
     """Assert every output of `out` (numpy) against the oracle `ref`; return observed errors.
 
@@ -67,10 +99,8 @@ def compare(p: dict, out: dict, ref: dict, name: str = "", sampled: bool = False
     errs["cand_q"] = _maxerr(out["cand_q"], ref["cand_q"], cmask)
     assert errs["cand_q"] <= Q_TOL, (name, "cand_q", errs["cand_q"])
     qmask = ~np.isnan(ref["q_expect"]) if sampled else np.ones(len(K), bool)
-    decided = qmask & (ref["q_gap"] > Q_TOL)
-    mism = np.flatnonzero(decided & (out["q_argmax"] != ref["q_argmax"]))
-    assert mism.size == 0, (name, "argmax mismatch", mism[:10])
-    errs["argmax_checked"] = int(decided.sum())
+    errs.update(check_decisions(out["q_argmax"], out["cand_s"], qo, T, ref["q_argmax"],
+                                ref["q_gap"], ref["cand_q"], name, qmask))
     if "q_true" in out:
         errs["q_true"] = _maxerr(out["q_true"], ref["q_true"], qmask)
         assert errs["q_true"] <= Q_TOL, (name, "q_true", errs["q_true"])

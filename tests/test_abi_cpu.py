@@ -193,6 +193,44 @@ def test_score_rejects_invalid_scalars_without_a_device(lib):
     assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), mis, 1 << 19, None) == -6
 
 
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="launches on fake pointers only where no GPU exists")
+def test_failed_launch_returns_hip_status(lib):
+    """A problem that passes every host check reaches its first launch; with no GPU present
+    that launch fails, and each device entry point reports JET_E_HIP (the status that may
+    follow work the same call already enqueued) rather than crashing."""
+    h = np.zeros(64, np.float32)
+    p = _lib.JetProblem()
+    p.H, p.h_dtype, p.n_rows = h.ctypes.data, 0, 1
+    p.W, p.w_dtype, p.V, p.d = h.ctypes.data, 1, 2, 32
+    tgt = np.zeros(1, np.int32)
+    off = np.array([0, 1], np.int32)
+    p.tok_target, p.n_tok = tgt.ctypes.data, 1
+    p.cand_tok_off, p.n_cand = off.ctypes.data, 1
+    p.q_cand_off, p.n_q = off.ctypes.data, 1
+    p.T = 1.0
+    o = _lib.JetOutputs()
+    f = np.zeros(4, np.float32)
+    o.tok_logp = o.cand_s = o.cand_q = o.q_argmax = f.ctypes.data
+    need = lib.jet_score_workspace_size(ctypes.byref(p))
+    ws = np.zeros(need + 512, np.uint8)
+    base = (ws.ctypes.data + 255) & ~255
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), base, need, None) == -7
+    assert lib.jet_score_profiled(ctypes.byref(p), ctypes.byref(o), base, need, None, None, None) == -7
+    rp = _lib.JetRestrictedProblem()
+    rp.H, rp.h_dtype, rp.n_rows = h.ctypes.data, 0, 1
+    rp.W, rp.w_dtype, rp.V, rp.d = h.ctypes.data, 1, 2, 32
+    uid = np.zeros(1, np.int32)
+    rp.union_ids, rp.n_union = uid.ctypes.data, 1
+    rp.field_row, rp.field_slot_off, rp.slot_uidx = uid.ctypes.data, off.ctypes.data, uid.ctypes.data
+    rp.n_fields, rp.n_slots, rp.T = 1, 1, 1.0
+    ro = _lib.JetRestrictedOutputs()
+    ro.slot_logit = ro.slot_q = ro.field_argmax = f.ctypes.data
+    rneed = lib.jet_restricted_workspace_size(ctypes.byref(rp))
+    rws = np.zeros(rneed + 512, np.uint8)
+    rbase = (rws.ctypes.data + 255) & ~255
+    assert lib.jet_score_restricted(ctypes.byref(rp), ctypes.byref(ro), rbase, rneed, None) == -7
+
+
 def test_workspace_size_is_monotone_in_problem_size(lib):
     sizes = []
     for n_rows in (1, 32, 33, 1000):

@@ -66,8 +66,15 @@ def _decide_T_times(s, T, *a, **k):
 
 def _decide_last_tie(s, T, *a, **k):
     r = _orig_decide_question(s, T, *a, **k)
+    a = np.asarray(s, np.float64) / T
+    r["argmax"] = int(np.flatnonzero(a == a.max())[-1])
+    return r
+
+
+def _decide_on_float32(s, T, *a, **k):
+    r = _orig_decide_question(s, T, *a, **k)
     a32 = (np.asarray(s, np.float64) / T).astype(np.float32)
-    r["argmax"] = int(np.flatnonzero(a32 == a32.max())[-1])
+    r["argmax"] = int(np.flatnonzero(a32 == a32.max())[0])
     return r
 
 
@@ -279,6 +286,7 @@ MUTANTS = {
     "temperature_multiplies": ("decide_question", _decide_T_times),
     "temperature_ignored": ("decide_question", _decide_no_temperature),
     "tie_goes_to_last": ("decide_question", _decide_last_tie),
+    "decision_on_float32_scores": ("decide_question", _decide_on_float32),
     "ordinal_levels_from_one": ("decide_question", _decide_levels_from_one),
     "gold_nll_not_summed": ("decide_question", _decide_gold_first_only),
     "binary_true_is_first": ("decide_question", _decide_true_first),

@@ -23,10 +23,6 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 # helpers independent of the oracle
 # ----------------------------------------------------------------------------------------
 
-def _f32_round(x: float) -> float:
-    return struct.unpack("<f", struct.pack("<f", x))[0]
-
-
 def _bf16_to_float(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
 
@@ -61,9 +57,8 @@ def brute_force(p: dict) -> dict:
         Z = math.fsum(e)
         q = [x / Z for x in e]
         out["cand_q"] += q
-        a32 = [_f32_round(x) for x in a]
-        best = max(a32)
-        out["q_argmax"].append(a32.index(best))
+        best = max(a)
+        out["q_argmax"].append(a.index(best))  # list.index: the first (lowest) maximum
         K = len(a)
         t = (1 if K == 2 else -1) if p.get("q_true_idx") is None else int(p["q_true_idx"][g])
         out["q_true"].append(q[t] if 0 <= t < K else math.nan)
@@ -319,6 +314,20 @@ def pin_temperature():
     _close(jo.decide_question(s, 1.0)["q"], L / L.sum(), 1e-15, "ratio")
     q2 = jo.decide_question(s, 2.0)["q"]
     _close(q2, np.sqrt(L) / np.sqrt(L).sum(), 1e-15, "T=2 is the square root")
+
+
+def pin_exact_decision():
+    """The decision is the lowest index among the exact maxima of a = s / T (JET Eq. 5 with
+    ties resolved by a fixed ordering).  Scores 1e-12 apart are distinct: the larger wins
+    even though both round to the same fp32 value; bitwise-equal scores tie and go to the
+    first; a near tie after scaling is still decided by the exact values."""
+    s = np.array([-1.0 - 1e-12, -1.0, -3.0])
+    assert np.float32(s[0]) == np.float32(s[1])
+    assert jo.decide_question(s, 1.0)["argmax"] == 1
+    assert jo.decide_question(s, 0.3)["argmax"] == 1
+    s = np.array([-2.0, -0.5, -0.5, -0.5 - 2.0 ** -40])
+    assert jo.decide_question(s, 1.0)["argmax"] == 1
+    assert jo.decide_question(s[::-1].copy(), 1.0)["argmax"] == 1  # now -0.5 at 1 and 2
 
 
 def pin_gold_nll():
