@@ -18,6 +18,7 @@ STATUS = {
     0: "JET_OK", -1: "JET_E_NULL", -2: "JET_E_SHAPE", -3: "JET_E_DTYPE", -4: "JET_E_INDEX",
     -5: "JET_E_TEMP", -6: "JET_E_WORKSPACE", -7: "JET_E_HIP",
 }
+NOALLOC_MAX_WORKSPACE = 64 << 20  # JET_NOALLOC_MAX_WORKSPACE
 FLAG_BAD_ROW = 1
 FLAG_BAD_TARGET = 2
 FLAG_BAD_OFFSETS = 4
@@ -66,6 +67,7 @@ EXPORTS = {
     "jet_score": (c_int, [POINTER(JetProblem), POINTER(JetOutputs), c_void_p, c_size_t, c_void_p]),
     "jet_score_profiled": (c_int, [POINTER(JetProblem), POINTER(JetOutputs), c_void_p, c_size_t,
                                    c_void_p, c_void_p, c_void_p]),
+    "jet_score_noalloc": (c_int, [POINTER(JetProblem), POINTER(JetOutputs), c_void_p]),
     "jet_projection_kernel": (c_char_p, [POINTER(JetProblem)]),
     "jet_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "jet_fit_temperature_workspace_size": (c_size_t, [c_int32]),

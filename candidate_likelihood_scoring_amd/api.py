@@ -14,7 +14,7 @@ import torch
 from . import _lib
 from ._lib import JetError, JetOutputs, JetProblem, JetRestrictedOutputs, JetRestrictedProblem
 
-__all__ = ["score", "score_restricted", "build_union", "validate", "validate_restricted",
+__all__ = ["score", "score_noalloc", "score_restricted", "build_union", "validate", "validate_restricted",
            "score_workspace_size", "restricted_workspace_size", "Workspace"]
 
 
@@ -264,6 +264,24 @@ def score(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None, cand_
                                     events[0], events[1])
     if st != 0:
         raise JetError(st, "jet_score")
+    return out
+
+
+def score_noalloc(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None,
+                  cand_text_id=None, q_gold_text_id=None, q_true_idx=None, *, out,
+                  stream=None) -> dict:
+    """jet_score_noalloc on device tensors: jet_score with the library's static workspace
+    (no workspace argument; nothing allocated here either, so `out` must be given, e.g.
+    from alloc_outputs ahead of time).  Calls that overlap on one GPU race on that
+    workspace; calls ordered on one stream do not."""
+    prob = make_problem(H, W, tok_target, cand_tok_off, q_cand_off, T, tok_row, cand_text_id,
+                        q_gold_text_id, q_true_idx)
+    o = _outputs_struct(out)
+    _enter_stream(stream, H, W, tok_target, cand_tok_off, q_cand_off, tok_row, cand_text_id,
+                  q_gold_text_id, q_true_idx, *out.values())
+    st = _lib.load().jet_score_noalloc(ctypes.byref(prob), ctypes.byref(o), _stream_handle(stream))
+    if st != 0:
+        raise JetError(st, "jet_score_noalloc")
     return out
 
 

@@ -5,10 +5,18 @@
 // device kernels bounds-check every index themselves.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <unordered_map>
 #include <vector>
 
 #include "jet_internal.h"
+
+// Workspace of jet_score_noalloc: static device memory, one copy per GPU the library runs
+// on, held until the process ends.  Host code never passes this name to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static constexpr size_t kNoallocScratchBytes = JET_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace jet {
 
@@ -297,6 +305,42 @@ jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o, void* 
 jet_status jet_score(const jet_problem* p, const jet_outputs* o, void* workspace,
                      size_t workspace_bytes, void* stream) {
   return jet_score_profiled(p, o, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+constexpr int kNoallocMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kNoallocMaxDevices];  // device address of scratch, per device ordinal
+
+// Device address of the static scratch array on the current device, looked up once per
+// device (with that device current) and kept; NULL if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_dev[dev] = ptr;
+  }
+  return g_scratch_dev[dev];
+}
+}  // namespace
+
+extern "C" {
+
+jet_status jet_score_noalloc(const jet_problem* p, const jet_outputs* o, void* stream) {
+  jet_status st = check_problem(p);
+  if (st != JET_OK) return st;
+  if ((st = check_outputs(p, o)) != JET_OK) return st;
+  Plan pl;
+  make_plan(p, true, &pl);
+  if (pl.total > kNoallocScratchBytes) return JET_E_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return JET_E_HIP;
+  return jet_score_profiled(p, o, ws, kNoallocScratchBytes, stream, nullptr, nullptr);
 }
 
 jet_status jet_validate_host(const jet_problem* p) {

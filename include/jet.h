@@ -155,6 +155,24 @@ JET_API jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o
                               size_t workspace_bytes, void* stream, void* ev_before,
                               void* ev_after);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): jet_score with the workspace taken from
+ * a static device array of JET_NOALLOC_MAX_WORKSPACE bytes inside the library, so neither
+ * the caller nor the library allocates.  The caller still owns H, W, the index arrays and
+ * the outputs, and passes a stream of the current device.
+ *  - Each GPU holds one copy of the array from the library's first use on it until the
+ *    process ends.  The first call on a device looks up the array's device address with
+ *    that device current (a runtime query, no allocation) and keeps it.
+ *  - Every call on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ *    streams, other threads) race on it and give undefined results; calls ordered on one
+ *    stream are safe.  The array keeps the last call's contents; every call clears what
+ *    must start at zero itself, with kernels (no memsets).
+ *  - A problem whose workspace (jet_score_workspace_size) exceeds the array returns
+ *    JET_E_WORKSPACE with nothing enqueued; JET_E_HIP also when the address lookup fails.
+ *    Otherwise as jet_score: same checks, same kernels, same bits. */
+#define JET_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+JET_API jet_status jet_score_noalloc(const jet_problem* p, const jet_outputs* o, void* stream);
+
 /* Name of the projection kernel jet_score launches for this problem (the plan depends
  * only on the problem's scalars), as profilers report it: "k_project_tiled_m16",
  * "k_project_tiled_m16x2", "k_project_tiled_bf16", "k_project_wg_bf16",
