@@ -82,12 +82,10 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   *pl = Plan{};
   pl->variant = p->w_dtype == JET_F32 ? VAR_SMALL_F32 : VAR_SMALL_BF16;
   pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
-  // tiled path: enough rows, whole stages, at least one full 256 x 256 tile, and operands
-  // addressable with 32-bit buffer offsets
+  // tiled path: enough rows, whole stages, at least one full 256 x 256 tile (its buffer
+  // offsets are local to a workgroup's tiles, so operands of any size take it)
   if (pl->variant == VAR_SMALL_BF16 && p->n_rows >= kTiledMinRows && p->n_rows >= 256 &&
-      p->V >= 256 && p->d % tiled_bk(pl->hilo) == 0 &&
-      (unsigned long long)p->V * p->d * 2 < 0xffffffffull &&
-      (unsigned long long)p->n_rows * p->d * 2 < 0xffffffffull)
+      p->V >= 256 && p->d % tiled_bk(pl->hilo) == 0)
     pl->variant = VAR_TILED_BF16;
   pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
   if (pl->variant == VAR_TILED_BF16) {

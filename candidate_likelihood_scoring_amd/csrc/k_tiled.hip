@@ -244,10 +244,17 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   // load-side mapping: thread tid loads chunk tid % CH of tile rows tid / CH + i * RPI
   const int lr0 = tid / CH, lc = tid % CH;
   const uint32_t lvoff = (uint32_t)lr0 * rowb + lc * 16;
-  const __amdgpu_buffer_rsrc_t rH0 = rsrc_of(H0, (uint32_t)n_rows * rowb);
-  const __amdgpu_buffer_rsrc_t rH1 = rsrc_of(NP == 2 ? H1 : H0, (uint32_t)n_rows * rowb);
-  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
-  const uint32_t hrow = (uint32_t)row0 * rowb;
+  // Buffer resources based at this workgroup's first H row and first head row, so that
+  // every offset is local to its own tiles (32 bits suffice whatever the operand sizes):
+  // H rows [row0, row0 + 256), head rows [vbase, vend) covering every tile of the range
+  // (a tile starts at min(t * 256, V - 256); an empty range still loads one tile).
+  const int vbase = min(t0 * TBM, V - TBM);
+  const int vend = max(min(t1 * TBM, V), vbase + TBM);
+  const __amdgpu_buffer_rsrc_t rH0 = rsrc_of(H0 + (size_t)row0 * d, (uint32_t)TBN * rowb);
+  const __amdgpu_buffer_rsrc_t rH1 =
+      rsrc_of((NP == 2 ? H1 : H0) + (size_t)row0 * d, (uint32_t)TBN * rowb);
+  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W + (size_t)vbase * d, (uint32_t)(vend - vbase) * rowb);
+  const uint32_t hrow = 0;
   // LDS write slot: rows lr0 + i * RPI share row & 15, hence one swizzle
   const int wslot = lr0 * CH + (lc ^ swz<CH>(lr0));
   // fragment read slots of sub-step kk: row (wm|wn)*128 + t*32 + n, chunk 2 kk + h
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
 #define JET_CURSOR()                                                                         \
   {                                                                                          \
     const uint32_t ko = (uint32_t)lk * (BK * 2);                                             \
-    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)min(lt * TBM, V - TBM) * rowb + ko);     \
+    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)(min(lt * TBM, V - TBM) - vbase) * rowb + ko); \
     l_hs = __builtin_amdgcn_readfirstlane(hrow + ko);                                        \
     if (lg + 1 < G) {                                                                        \
       ++lg;                                                                                  \
@@ -559,10 +566,16 @@ __device__ __forceinline__ void project_m16(
   const int t1 = min(t0 + L, n_vtiles);
   const int nk = d / BK;  // even
   const uint32_t rowb = (uint32_t)d * 2;
-  const __amdgpu_buffer_rsrc_t rH = rsrc_of(H, (uint32_t)n_rows * rowb);
-  const __amdgpu_buffer_rsrc_t rL = TWO ? rsrc_of(Hlo, (uint32_t)n_rows * rowb) : rH;
-  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W, (uint32_t)min((long long)V * rowb, 0xffffffffll));
-  const uint32_t hrow = (uint32_t)row0 * rowb;
+  // Buffer resources based at this workgroup's first H row and first head row, so that
+  // every offset is local to its own tiles (32 bits suffice whatever the operand sizes):
+  // H rows [row0, row0 + RT), head rows [vbase, vend) covering every tile of the range
+  // (a tile starts at min(t * 256, V - 256); an empty range still loads one tile).
+  const int vbase = min(t0 * TBM, V - TBM);
+  const int vend = max(min(t1 * TBM, V), vbase + TBM);
+  const __amdgpu_buffer_rsrc_t rH = rsrc_of(H + (size_t)row0 * d, (uint32_t)RT * rowb);
+  const __amdgpu_buffer_rsrc_t rL = TWO ? rsrc_of(Hlo + (size_t)row0 * d, (uint32_t)RT * rowb) : rH;
+  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W + (size_t)vbase * d, (uint32_t)(vend - vbase) * rowb);
+  const uint32_t hrow = 0;
   const int dr = wid * RPD + lane / CH;
   const uint32_t dvoff = (uint32_t)dr * rowb + (uint32_t)(((lane % CH) ^ swz16(dr)) * 16);
   const uint32_t m0_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds +
@@ -583,7 +596,7 @@ __device__ __forceinline__ void project_m16(
 #define JET_CURSOR()                                                                         \
   {                                                                                          \
     const uint32_t ko = (uint32_t)lk * (BK * 2);                                             \
-    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)min(lt * TBM, V - TBM) * rowb + ko);     \
+    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)(min(lt * TBM, V - TBM) - vbase) * rowb + ko); \
     l_hs = __builtin_amdgcn_readfirstlane(hrow + ko);                                        \
     if (lg + 1 < G) {                                                                        \
       ++lg;                                                                                  \

@@ -265,6 +265,12 @@ def test_projection_kernel_choice(lib):
     assert pick(255, 5000, 256, BF16, BF16) == "k_project_wg_bf16"      # too few rows to tile
     assert pick(300, 255, 256, BF16, BF16) == "k_project_wg_bf16"       # vocabulary below one tile
     assert pick(32, 1000, 64, F32, F32) == "k_project_small_f32"
+    # operands past 4 GiB keep the matrix-core kernels (offsets local to each workgroup)
+    assert pick(300, 262144, 8192, BF16, BF16) == "k_project_tiled_m16"   # head of 4 GiB
+    assert pick(300, 300007, 8192, BF16, BF16) == "k_project_tiled_m16"   # 4.9 GB head
+    assert pick(300, 262144, 8192, F32, BF16) == "k_project_tiled_m16x2"
+    assert pick(270000, 4099, 8192, BF16, BF16) == "k_project_tiled_m16"  # 4.4 GB of H
+    assert pick(2 ** 21, 262144, 8192, F32, BF16) == "k_project_tiled_m16x2"
     assert pick(32, 1000, 64, F32, BF16, T=-1.0) is None
 
 

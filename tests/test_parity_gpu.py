@@ -152,6 +152,39 @@ def test_tiled_stream(jet, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, 'tiled_stream', sampled=True)} on {len(rows)} rows")
 
 
+@pytest.mark.parametrize("operand", ["head", "hidden"])
+def test_tiled_operands_past_4gib(jet, operand):
+    """Operands larger than 4 GiB stay on the matrix-core kernel, whose buffer offsets are
+    local to each workgroup's tiles: a 4.9 GB head (V = 300,007, d = 8192: 37,863 head rows
+    lie past 4 GiB, and targets are planted there) or 4.4 GB of hidden states (270,000
+    rows of d = 8192; rows past 4 GiB sampled).  Sampled rows against the oracle."""
+    if operand == "head":
+        p = wl.make_problem(V=300007, d=8192, n_q=12, K=(2, 5), lengths=(1, 3), layout="own",
+                            seed=96, h_dtype="bf16", n_extra_rows=230)
+        edge = (1 << 32) // (8192 * 2)  # first head row past 4 GiB
+        tg = p["tok_target"].copy()
+        tg[:6] = [edge, edge + 1, p["V"] - 1, p["V"] - 2, p["V"] - 300, edge - 1]
+        p["tok_target"] = tg
+    else:
+        p = wl.make_problem(V=4099, d=8192, n_q=12, K=(2, 5), lengths=(1, 3), layout="prefix",
+                            seed=97, h_dtype="bf16", n_extra_rows=270000)
+    n = p["n_rows"]
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] past 4 GiB ({operand}): V={p['V']} rows={n} head={p['V'] * p['d'] * 2} "
+        f"H={n * p['d'] * 2} bytes ({kern})")
+    assert kern == "k_project_tiled_m16"
+    assert max(p["V"], n) * p["d"] * 2 > (1 << 32)
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    tok_row = np.arange(len(p["tok_target"])) if p["tok_row"] is None else np.asarray(p["tok_row"])
+    edge_r = (1 << 32) // (p["d"] * 2)
+    rows = np.unique(np.concatenate([tok_row, np.arange(0, 8), np.arange(n - 300, n),
+                                     [r for r in (edge_r - 1, edge_r, edge_r + 1) if r < n]]))
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] past 4 GiB ({operand}) errs {compare(p, out, ref, f'past4g_{operand}', sampled=True)}"
+        f" on {len(rows)} rows")
+
+
 def test_tiled_padded_row_groups(jet):
     """bf16 H in 31 row tiles of 256 over 513 vocabulary tiles (136 splits): the launch
     places 8 row tiles x 4 splits per XCD and pads the last row group with one empty row
@@ -564,24 +597,47 @@ def test_multi_token_full_sampled(jet):
     # duplicates: bitwise-equal log-probs for bitwise-equal rows at other positions
     for dst, src in p["dup_row_pairs"]:
         assert np.array_equal(out["row_lse"][dst], out["row_lse"][src])
-    # sampled parity: main questions 0 and 5 and their ordinal/binary subsets (same rows)
-    rows = _rows_of_questions(p, [0, 5])
-    log(f"[gpu] multi_token oracle on {len(rows)} rows")
-    ref = jo.score(p, rows=rows)
-    errs = compare(p, out, ref, "multi_token", sampled=True)
+    # full parity: every row, so every main question and every ordinal/binary subset
+    log(f"[gpu] multi_token oracle on all {p['n_rows']} rows")
+    ref = jo.score(p)
+    errs = compare(p, out, ref, "multi_token")
     log(f"[gpu] multi_token errs {errs}")
-    assert errs["argmax_checked"] >= 2
+    n_q = len(p["q_cand_off"]) - 1
+    assert errs["argmax_checked"] + errs["argmax_in_band"] == n_q
+
+
+def _one_question_per_row_tile(p, tile):
+    """Questions whose rows cover, for every row tile, a row inside it (rows follow tokens,
+    so each question owns a contiguous run of rows): the question holding the row 100 rows
+    into each tile, plus the last question (the shifted last tile)."""
+    co, qo = np.asarray(p["cand_tok_off"]), np.asarray(p["q_cand_off"])
+    tok_row = np.arange(len(p["tok_target"])) if p["tok_row"] is None else np.asarray(p["tok_row"])
+    first_row = tok_row[co[qo[:-1]]]
+    n = p["n_rows"]
+    qs = {len(qo) - 2}
+    for t0 in range(0, n, tile):
+        r = min(t0 + 100, n - 1)
+        qs.add(int(np.searchsorted(first_row, r, side="right") - 1))
+    return sorted(qs)
 
 
 def test_large_batch_full_sampled(jet):
+    """The headline workload in the benchmark's launch configuration; the oracle computes
+    one question in every 256-row tile of the matrix-core kernel (104 of 512 questions),
+    so every row tile's partials and captured targets are checked."""
     p = wl.large_batch()
     log(f"[gpu] large_batch rows={p['n_rows']}")
     out = _run(jet, p)
     _full_size_properties(p, out)
-    rows = _rows_of_questions(p, [0, 101, 257, 511])
-    log(f"[gpu] large_batch oracle on {len(rows)} rows")
+    qs = _one_question_per_row_tile(p, 256)
+    rows = _rows_of_questions(p, qs)
+    tiles = np.unique(rows // 256)
+    log(f"[gpu] large_batch oracle on {len(qs)} questions, {len(rows)} rows, {len(tiles)} row tiles")
+    assert len(tiles) == -(-p["n_rows"] // 256)
     ref = jo.score(p, rows=rows)
-    log(f"[gpu] large_batch errs {compare(p, out, ref, 'large_batch', sampled=True)}")
+    errs = compare(p, out, ref, "large_batch", sampled=True)
+    log(f"[gpu] large_batch errs {errs}")
+    assert errs["argmax_checked"] + errs["argmax_in_band"] == len(qs)
 
 
 def test_large_batch_deduplicated_full_sampled(jet):
@@ -596,7 +652,10 @@ def test_large_batch_deduplicated_full_sampled(jet):
     log(f"[gpu] large_batch dedup rows={q['n_rows']}")
     out = _run(jet, q)
     _full_size_properties(q, out)
-    rows = _rows_of_questions(q, [3, 200, 511])
+    qs = _one_question_per_row_tile(q, 256)
+    rows = _rows_of_questions(q, qs)
+    log(f"[gpu] large_batch dedup oracle on {len(qs)} questions, {len(rows)} rows")
+    assert len(np.unique(rows // 256)) == -(-q["n_rows"] // 256)
     ref = jo.score(q, rows=rows)
     log(f"[gpu] large_batch dedup errs {compare(q, out, ref, 'large_batch_dedup', sampled=True)}")
 
