@@ -93,8 +93,10 @@ __device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int n, in
 }
 
 // Merge the two lane halves, then the workgroup's waves in wave order; store one partial
-// per row of the tile.
-template <int NW = kWpb>
+// per row of the tile: at part[blockIdx.x * n_rows + row], or, ROW_MAJOR (the streaming
+// kernel, whose merge reads a row's partials as one contiguous run), at
+// part[row * gridDim.x + blockIdx.x].
+template <int NW = kWpb, bool ROW_MAJOR = false>
 __device__ inline void store_partial(float m_run, float s_run, int n, int half, int wid,
                                      int row0, int n_rows, float2* __restrict__ part,
                                      float2 (*red)[32]) {
@@ -110,7 +112,9 @@ __device__ inline void store_partial(float m_run, float s_run, int n, int half, 
 #pragma unroll
     for (int w = 1; w < NW; ++w) lse_merge(m, s, red[w][n].x, red[w][n].y);
     const int row = row0 + n;
-    if (row < n_rows) part[(size_t)blockIdx.x * n_rows + row] = make_float2(m, s);
+    if (row < n_rows)
+      part[ROW_MAJOR ? (size_t)row * gridDim.x + blockIdx.x : (size_t)blockIdx.x * n_rows + row] =
+          make_float2(m, s);
   }
 }
 
@@ -362,8 +366,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     // and needs none).
     if (nst & 1) __syncthreads();
   }
-  store_partial<WPB>(m_run, s_run, n, half, wid, row0, n_rows, part, red);
-
+  store_partial<WPB, true>(m_run, s_run, n, half, wid, row0, n_rows, part, red);
 }
 
 // ------------------------------------------------------------------------------------

@@ -12,7 +12,7 @@
 //                   field's slots, argmax = lowest index among the exact maxima of a.
 // fp32 head: k_gather_rows (Wu[j, :] = W[union_ids[j], :], 16-byte coalesced copies), the
 // small-row fp32 kernel's store epilogue, then k_field_softmax.
-#include "jet_internal.h"
+#include "jet_tail.h"
 
 namespace jet {
 namespace {
@@ -204,12 +204,162 @@ __global__ __launch_bounds__(256) void k_field_softmax(
   if (lane == 0) f_argmax[f] = best_j < j1 ? best_j - j0 : -1;
 }
 
+// One launch for a bf16 head (the common case: d <= 2560, at most 4096 slots): workgroup
+// f scores field f alone.  Its 16 waves take the field's slots in turn; for a slot, lane l
+// multiplies head row union_ids[slot_uidx[j]] by the field's hidden row at k = 512 c + 8 l
+// .. + 7 for each 512-wide chunk c (fp32 products, accumulated in k order per lane, then
+// the wave's fixed lane tree), so the logit is a full-length fp32 dot product; the hidden
+// row stays in registers for all the field's slots, and the next slot's head row is loaded
+// while the current one is summed.  Then wave 0 takes the field's softmax at T and argmax
+// (lowest index among the exact maxima).  No workgroup needs another's results.
+// Index checks: workgroup 0 checks every union id, field offset, field row and slot index
+// and stores the flag word (a plain store of the whole word: no other workgroup writes it,
+// so it needs no clearing first); each field treats its own bad indices as k_field_softmax
+// does (an id outside [0, V) reads as a zero row; a bad slot index or row gives NaN; bad
+// offsets give argmax -1).
+constexpr int kFieldWaves = 16, kFieldMaxSlots = 4096;
+
+template <bool HF32, int NC>  // NC: 512-wide chunks of k in registers (d <= 512 NC)
+__global__ __launch_bounds__(kFieldWaves * 64) void k_restricted_fields(
+    const uint16_t* __restrict__ W, int V, int d, const int* __restrict__ ids, int n_union,
+    const void* __restrict__ H, int n_rows, const int* __restrict__ field_row,
+    const int* __restrict__ slot_off, const int* __restrict__ slot_uidx, int n_fields,
+    int n_slots, float T, float* __restrict__ slot_logit, float* __restrict__ slot_q,
+    int* __restrict__ f_argmax, int32_t* __restrict__ flags) {
+  constexpr int NT = kFieldWaves * 64;
+  __shared__ float s_logit[kFieldMaxSlots];
+  __shared__ uint32_t s_bits;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int f = blockIdx.x;
+  if (f == 0) {
+    if (tid == 0) s_bits = 0u;
+    __syncthreads();
+    uint32_t bits = 0u;
+    for (int j = tid; j < n_union; j += NT)
+      if (ids[j] < 0 || ids[j] >= V) bits |= JET_FLAG_BAD_UNION;
+    for (int g = tid; g < n_fields; g += NT) {
+      const int a = slot_off[g], b = slot_off[g + 1], r = field_row[g];
+      if (a < 0 || b > n_slots || b <= a) bits |= JET_FLAG_BAD_OFFSETS;
+      else if (r < 0 || r >= n_rows) bits |= JET_FLAG_BAD_UNION;
+    }
+    for (int j = tid; j < n_slots; j += NT)
+      if (slot_uidx[j] < 0 || slot_uidx[j] >= n_union) bits |= JET_FLAG_BAD_UNION;
+    if (bits) atomicOr(&s_bits, bits);
+    __syncthreads();
+    if (tid == 0) flags[0] = (int32_t)s_bits;
+  }
+  if (f >= n_fields) return;
+  const int j0 = slot_off[f], j1 = slot_off[f + 1];
+  if (j0 < 0 || j1 > n_slots || j1 <= j0) {
+    if (tid == 0) f_argmax[f] = -1;
+    return;
+  }
+  const int r = field_row[f];
+  const bool row_ok = r >= 0 && r < n_rows;
+  const int K = j1 - j0;  // <= n_slots <= kFieldMaxSlots (host check)
+  // the field's hidden row: lane l's 8 values of each chunk (zero past d)
+  float hv[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int k = 512 * c + 8 * lane;
+    if (row_ok && k < d) {
+      if constexpr (HF32) {
+        const float4* hp = reinterpret_cast<const float4*>(static_cast<const float*>(H) + (size_t)r * d + k);
+        const float4 x0 = hp[0], x1 = hp[1];
+        hv[c][0] = x0.x; hv[c][1] = x0.y; hv[c][2] = x0.z; hv[c][3] = x0.w;
+        hv[c][4] = x1.x; hv[c][5] = x1.y; hv[c][6] = x1.z; hv[c][7] = x1.w;
+      } else {
+        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(H) + (size_t)r * d + k);
+        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hv[c][2 * e] = __uint_as_float(w4[e] << 16);
+          hv[c][2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[c][e] = 0.f;
+    }
+  }
+  // head row of slot j: its chunks (zero for an id outside [0, V), or past d)
+  auto load_w = [&](int j, uint4 (&wv)[NC], bool& use) {
+    const int u = slot_uidx[j];
+    const bool u_ok = u >= 0 && u < n_union;
+    const int id = u_ok ? ids[u] : 0;
+    const bool id_ok = u_ok && id >= 0 && id < V;
+    use = u_ok;
+    const uint16_t* wr = W + (size_t)(id_ok ? id : 0) * d;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int k = 512 * c + 8 * lane;
+      wv[c] = (id_ok && k < d) ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 wv[NC], wn[NC];
+  bool use = false, use_n = false;
+  int j = j0 + wid;
+  if (j < j1) load_w(j, wv, use);
+  for (; j < j1; j += kFieldWaves) {
+    const int jn = j + kFieldWaves;
+    if (jn < j1) load_w(jn, wn, use_n);
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t w4[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(__uint_as_float(w4[e] << 16), hv[c][2 * e], acc);
+        acc = fmaf(__uint_as_float(w4[e] & 0xffff0000u), hv[c][2 * e + 1], acc);
+      }
+    }
+    acc = wave_sum(acc);
+    const float z = (use && row_ok) ? acc : __builtin_nanf("");
+    if (lane == 0) {
+      s_logit[j - j0] = z;
+      slot_logit[j] = z;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) wv[c] = wn[c];
+    use = use_n;
+  }
+  __syncthreads();
+  if (wid != 0) return;
+  float best = -INFINITY;
+  int bi = K;
+  for (int i = lane; i < K; i += 64) {
+    const float av = s_logit[i] / T;
+    if (av > best) {  // increasing i: a lane keeps its lowest index among equal values
+      best = av;
+      bi = i;
+    }
+  }
+  wave_argmax(best, bi);
+  float zs = 0.f;
+  for (int i = lane; i < K; i += 64) zs += expf(s_logit[i] / T - best);
+  zs = wave_sum(zs);
+  for (int i = lane; i < K; i += 64) slot_q[j0 + i] = expf(s_logit[i] / T - best) / zs;
+  if (lane == 0) f_argmax[f] = bi < K ? bi : -1;
+}
+
 }  // namespace
 
 bool make_restricted_plan(const jet_restricted_problem* p, RestrictedPlan* pl) {
   const size_t elt = p->w_dtype == JET_BF16 ? 2 : 4;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  // bf16 head: k-split partials of Z, no gathered copy; fp32 head: the gathered rows and Z
+  // bf16 head, d <= 2560 (the hidden row in registers without spills), at most 4096
+  // slots: one launch, a workgroup per field, no workspace but the flag word
+  pl->per_field = p->w_dtype == JET_BF16 && p->d <= 2560 && p->n_slots <= kFieldMaxSlots;
+  if (pl->per_field) {
+    pl->fused = false;
+    pl->n_kg = 0;
+    pl->off_wu = pl->off_z = 0;
+    pl->off_flags = 0;
+    pl->total = 256;
+    return true;
+  }
+  // otherwise, bf16 head: k-split partials of Z, no gathered copy; fp32 head: the gathered
+  // rows and Z
   pl->fused = p->w_dtype == JET_BF16;
   pl->n_kg = pl->fused ? (p->d + kRkTile - 1) / kRkTile : 1;
   size_t off = 0;
@@ -244,9 +394,30 @@ static hipError_t launch_restricted_f32(const jet_restricted_problem* p, const R
   return hipSuccess;
 }
 
+template <bool HF32>
+static hipError_t launch_fields(const jet_restricted_problem* p, const jet_restricted_outputs* o,
+                                int32_t* flags, hipStream_t stream) {
+  const dim3 grid(p->n_fields > 0 ? p->n_fields : 1), block(kFieldWaves * 64);
+#define JET_FIELDS(NC)                                                                       \
+  hipLaunchKernelGGL((k_restricted_fields<HF32, NC>), grid, block, 0, stream,                 \
+                     static_cast<const uint16_t*>(p->W), p->V, p->d, p->union_ids, p->n_union, \
+                     p->H, p->n_rows, p->field_row, p->field_slot_off, p->slot_uidx,           \
+                     p->n_fields, p->n_slots, p->T, o->slot_logit, o->slot_q, o->field_argmax, \
+                     flags)
+  if (p->d <= 1024)
+    JET_FIELDS(2);
+  else
+    JET_FIELDS(5);
+#undef JET_FIELDS
+  return hipGetLastError();
+}
+
 hipError_t launch_restricted(const jet_restricted_problem* p, const jet_restricted_outputs* o,
                              const RestrictedPlan* pl, char* ws, int32_t* flags,
                              hipStream_t stream) {
+  if (pl->per_field)
+    return p->h_dtype == JET_F32 ? launch_fields<true>(p, o, flags, stream)
+                                 : launch_fields<false>(p, o, flags, stream);
   // the flag word is cleared by the first kernel (no memset, so the sequence stays
   // capturable) and set only by kernels after it
   hipError_t e;

@@ -99,6 +99,25 @@ def test_stream_odd_stage_count(jet, d, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, f'odd_stages_{d}_{h_dtype}')}")
 
 
+@pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
+def test_extra_row_tile_keeps_every_bit(jet, h_dtype):
+    """The same questions in a problem with one more, unreferenced row (64 rows in two
+    32-row tiles, then 65 in three): the streaming kernel's partials, the merge and the
+    decisions do not depend on how many rows or row tiles the problem has, so every output
+    keeps its bits; both against the oracle."""
+    p = wl.make_problem(V=20011, d=256, n_q=12, K=(2, 5), lengths=(1, 3), layout="prefix",
+                        seed=98, h_dtype=h_dtype, n_extra_rows=4)
+    q = wl.make_problem(V=20011, d=256, n_q=12, K=(2, 5), lengths=(1, 3), layout="prefix",
+                        seed=98, h_dtype=h_dtype, n_extra_rows=5)
+    assert p["n_rows"] == 64 and q["n_rows"] == 65
+    assert np.array_equal(p["H"], q["H"][:64]) and np.array_equal(p["tok_target"], q["tok_target"])
+    a, b = _run(jet, p), _run(jet, q)
+    log(f"[gpu] extra row tile {h_dtype}: errs {compare(p, a, jo.score(p), 'row_tiles')}")
+    for k in a:
+        x, y = (a[k], b[k][:64]) if k == "row_lse" else (a[k], b[k])
+        assert np.array_equal(x.view(np.int32), y.view(np.int32)), k
+
+
 # Large-row (matrix-core) path: at least 256 rows and 256 entries, d a multiple of two
 # K stages (128 for bf16 hidden states, 64 for fp32).  Ragged row and vocabulary tails
 # exercise the shifted last tiles; the medium case gives every workgroup several
@@ -693,6 +712,11 @@ def test_restricted(jet, max_variant):
     # several union tiles, two row tiles with a ragged tail, d = 512 + 96 (a partial k group)
     dict(n_fields=45, V=20000, d=608, K=(1, 26), seed=7),
     dict(n_fields=40, V=3000, d=1056, K=(1, 26), seed=8, h_dtype="bf16", n_rows=33),
+    # the one-launch path at its widest (five 512-wide chunks), bf16 hidden states
+    dict(n_fields=8, V=9000, d=2560, K=(2, 26), seed=12, h_dtype="bf16"),
+    # past its limits, the two-launch path: d above 2560, and more than 4096 slots
+    dict(n_fields=6, V=5000, d=2592, K=(1, 26), seed=10),
+    dict(n_fields=200, V=30011, d=128, K=(20, 26), seed=11),
 ])
 def test_restricted_ragged(jet, case):
     rp = wl.make_restricted(T=1.7, **case)
