@@ -463,9 +463,9 @@ def main(argv=None) -> int:
     roofline = None
     if restricted:
         # Input bytes read once (the union's head rows, each field's H row, the index arrays)
-        # plus the outputs, over the warm per-call duration of the whole call (a gather, the
-        # fused projection and the per-field softmax): a lower bound on the dominant kernel's
-        # own bandwidth.
+        # plus the outputs, over the warm per-call duration of the whole call (one launch
+        # for a bf16 head up to d = 2560, else the projection and the per-field softmax): a
+        # lower bound on the kernels' own bandwidth.
         h_elt = 4 if p["h_dtype"] == "f32" else 2
         n_h = len(np.unique(np.asarray(p["field_row"])))
         alg_bytes = (prob.n_union * d * w_elt + n_h * d * h_elt + 4 * prob.n_union
@@ -475,7 +475,7 @@ def main(argv=None) -> int:
         roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
         extra["algorithmic_bytes_per_call"] = int(alg_bytes)
-        extra["roofline_timing"] = "whole call (three launches), warm median"
+        extra["roofline_timing"] = "whole call, warm median"
     if events:
         kms = np.array([a.elapsed_time(b) for a, b in events])
         k_avg_s = float(kms.mean()) * 1e-3
