@@ -7,6 +7,7 @@ jet_score_restricted, build_union -> jet_build_union, validate -> jet_validate_h
 from __future__ import annotations
 
 import ctypes
+import os
 
 import numpy as np
 import torch
@@ -35,6 +36,33 @@ def _check_i32(name: str, t, dev) -> None:
 
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+def debug_validate() -> bool:
+    """True when JET_DEBUG_VALIDATE=1: before each scoring call the index arrays are copied
+    to the host and checked with jet_validate_host / jet_validate_restricted_host, and a
+    failure raises JetError (JET_E_INDEX) with nothing enqueued.  The copies synchronise
+    with the device, so this is a debugging mode; without it out-of-range indices are only
+    reported through the device flag word."""
+    return os.environ.get("JET_DEBUG_VALIDATE", "") == "1"
+
+
+def _host_i32(t):
+    return None if t is None else np.ascontiguousarray(t.detach().cpu().numpy(), dtype=np.int32)
+
+
+def _validate_score_on_host(prob: JetProblem, tok_row, tok_target, cand_tok_off, q_cand_off,
+                            q_true_idx, where: str) -> None:
+    h = {k: _host_i32(v) for k, v in dict(tok_row=tok_row, tok_target=tok_target,
+                                         cand_tok_off=cand_tok_off, q_cand_off=q_cand_off,
+                                         q_true_idx=q_true_idx).items()}
+    st = validate(h["tok_target"] if h["tok_target"] is not None else np.zeros(0, np.int32),
+                  h["cand_tok_off"] if h["cand_tok_off"] is not None else np.zeros(1, np.int32),
+                  h["q_cand_off"] if h["q_cand_off"] is not None else np.zeros(1, np.int32),
+                  prob.n_rows, prob.V, prob.d, prob.T, tok_row=h["tok_row"],
+                  q_true_idx=h["q_true_idx"], h_dtype=prob.h_dtype, w_dtype=prob.w_dtype)
+    if st != 0:
+        raise JetError(st, f"{where} (JET_DEBUG_VALIDATE)")
 
 
 def _stream_handle(stream) -> int | None:
@@ -253,6 +281,9 @@ def score(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=None, cand_
     sh = _stream_handle(stream)
     if need == 0:  # invalid scalars: jet_score reports which check failed, enqueuing nothing
         raise JetError(lib.jet_score(ctypes.byref(prob), ctypes.byref(o), None, 0, sh), "jet_score")
+    if debug_validate():
+        _validate_score_on_host(prob, tok_row, tok_target, cand_tok_off, q_cand_off, q_true_idx,
+                                "jet_score")
     ws = _workspace(workspace, W.device, stream)
     base, size = ws.get(need)
     _enter_stream(stream, H, W, tok_target, cand_tok_off, q_cand_off, tok_row, cand_text_id,
@@ -277,6 +308,9 @@ def score_noalloc(H, W, tok_target, cand_tok_off, q_cand_off, T=1.0, tok_row=Non
     prob = make_problem(H, W, tok_target, cand_tok_off, q_cand_off, T, tok_row, cand_text_id,
                         q_gold_text_id, q_true_idx)
     o = _outputs_struct(out)
+    if debug_validate():
+        _validate_score_on_host(prob, tok_row, tok_target, cand_tok_off, q_cand_off, q_true_idx,
+                                "jet_score_noalloc")
     _enter_stream(stream, H, W, tok_target, cand_tok_off, q_cand_off, tok_row, cand_text_id,
                   q_gold_text_id, q_true_idx, *out.values())
     st = _lib.load().jet_score_noalloc(ctypes.byref(prob), ctypes.byref(o), _stream_handle(stream))
@@ -363,6 +397,12 @@ def score_restricted(H, W, union_ids, field_row, field_slot_off, slot_uidx, T=1.
     if need == 0:  # invalid scalars: the entry point reports which check failed
         raise JetError(lib.jet_score_restricted(ctypes.byref(prob), ctypes.byref(o), None, 0,
                                                 _stream_handle(stream)), "jet_score_restricted")
+    if debug_validate():
+        hv = [_host_i32(t) for t in (union_ids, field_row, field_slot_off, slot_uidx)]
+        st = validate_restricted(*hv, n_rows=prob.n_rows, V=prob.V, d=prob.d, T=prob.T,
+                                 h_dtype=prob.h_dtype, w_dtype=prob.w_dtype)
+        if st != 0:
+            raise JetError(st, "jet_score_restricted (JET_DEBUG_VALIDATE)")
     ws = _workspace(workspace, dev, stream)
     base, size = ws.get(need)
     _enter_stream(stream, H, W, union_ids, field_row, field_slot_off, slot_uidx, ws.buf,

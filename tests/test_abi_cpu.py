@@ -231,6 +231,37 @@ def test_failed_launch_returns_hip_status(lib):
     assert lib.jet_score_restricted(ctypes.byref(rp), ctypes.byref(ro), rbase, rneed, None) == -7
 
 
+def test_debug_validate_checks_host_copies(monkeypatch):
+    """JET_DEBUG_VALIDATE=1 copies the index arrays to the host and validates them before
+    a call (here on CPU tensors, nothing is launched): a good problem passes, an
+    out-of-range target, row or true index raises JetError with JET_E_INDEX."""
+    import torch
+
+    p = wl.make_problem(V=300, d=32, n_q=5, K=(2, 4), lengths=(1, 3), layout="prefix", seed=44)
+    t = {k: torch.from_numpy(np.asarray(p[k])) for k in ("tok_target", "cand_tok_off", "q_cand_off", "tok_row")}
+    H = torch.zeros(p["n_rows"], 32, dtype=torch.float32)
+    W = torch.zeros(300, 32, dtype=torch.bfloat16)
+    monkeypatch.setenv("JET_DEBUG_VALIDATE", "1")
+    assert api.debug_validate()
+    prob = api.make_problem(H, W, t["tok_target"], t["cand_tok_off"], t["q_cand_off"], tok_row=t["tok_row"])
+    api._validate_score_on_host(prob, t["tok_row"], t["tok_target"], t["cand_tok_off"], t["q_cand_off"],
+                                None, "test")
+    for name, idx, val in (("tok_target", 2, 300), ("tok_row", 1, p["n_rows"])):
+        bad = t[name].clone()
+        bad[idx] = val
+        args = dict(t, **{name: bad})
+        with pytest.raises(_lib.JetError) as e:
+            api._validate_score_on_host(prob, args["tok_row"], args["tok_target"], args["cand_tok_off"],
+                                        args["q_cand_off"], None, "test")
+        assert e.value.status == -4
+    K = np.diff(p["q_cand_off"])
+    with pytest.raises(_lib.JetError):
+        api._validate_score_on_host(prob, t["tok_row"], t["tok_target"], t["cand_tok_off"], t["q_cand_off"],
+                                    torch.from_numpy((K + 1).astype(np.int32)), "test")
+    monkeypatch.setenv("JET_DEBUG_VALIDATE", "0")
+    assert not api.debug_validate()
+
+
 def test_workspace_size_is_monotone_in_problem_size(lib):
     sizes = []
     for n_rows in (1, 32, 33, 1000):

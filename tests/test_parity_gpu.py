@@ -518,6 +518,33 @@ def test_bad_indices_set_flags_without_faulting(jet, d):
     assert out["dev_flags"][0] & 8
 
 
+def test_debug_validate_rejects_before_launch(jet, monkeypatch):
+    """With JET_DEBUG_VALIDATE=1 the binding validates host copies of the index arrays: a
+    bad target (jet_score) or union id (jet_score_restricted) raises JET_E_INDEX and the
+    outputs are left untouched; valid calls still score."""
+    from candidate_likelihood_scoring_amd import _lib
+    p = wl.make_problem(V=500, d=128, n_q=4, K=(2, 4), lengths=(1, 3), layout="prefix", seed=42)
+    monkeypatch.setenv("JET_DEBUG_VALIDATE", "1")
+    good = _run(jet, p)
+    assert int(good["dev_flags"][0]) == 0
+    q = dict(p, tok_target=p["tok_target"].copy())
+    q["tok_target"][0] = p["V"] + 7
+    dq = jet.to_device(q, "cuda")
+    out = {k: torch.full_like(v, -5) for k, v in api.score(**jet.to_device(p, "cuda")).items()}
+    torch.cuda.synchronize()
+    with pytest.raises(_lib.JetError) as e:
+        api.score(**dq, out=out)
+    assert e.value.status == -4
+    torch.cuda.synchronize()
+    assert all(bool((v == -5).all()) for v in out.values())
+    rp = wl.make_restricted(n_fields=5, V=1000, d=64, K=(1, 9), seed=3)
+    rd = {k: v for k, v in jet.restricted_to_device(rp, "cuda").items() if not k.startswith("host_")}
+    rd["union_ids"][0] = rp["V"] + 3
+    with pytest.raises(_lib.JetError) as e:
+        api.score_restricted(**rd)
+    assert e.value.status == -4
+
+
 def test_deterministic(jet):
     p = wl.make_problem(V=20011, d=256, n_q=20, K=(2, 10), lengths=(1, 5), layout="prefix", seed=51)
     a = _run(jet, p)
