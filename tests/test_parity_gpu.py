@@ -99,6 +99,20 @@ def test_stream_odd_stage_count(jet, d, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, f'odd_stages_{d}_{h_dtype}')}")
 
 
+def test_stream_large_head_several_row_tiles(jet):
+    """The streaming kernel on binary_enum's head shape (V = 248,320, d = 2560: 1.27 GB, past
+    the last-level cache, so its loads carry the non-temporal hint) with 207 rows in seven
+    row tiles, each of which streams the head again; every output against the oracle."""
+    p = wl.make_problem(V=248320, d=2560, n_q=40, K=(2, 6), lengths=(1, 3), layout="prefix",
+                        seed=99, n_extra_rows=0)
+    n = p["n_rows"]
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] large head, {n} rows ({kern})")
+    assert kern == "k_project_wg_bf16" and 96 < n < 256
+    out = _run(jet, p)
+    log(f"[gpu] large head errs {compare(p, out, jo.score(p), 'large_head_row_tiles')}")
+
+
 @pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
 def test_extra_row_tile_keeps_every_bit(jet, h_dtype):
     """The same questions in a problem with one more, unreferenced row (64 rows in two
