@@ -15,7 +15,7 @@
 namespace jet {
 namespace {
 
-constexpr int kPrepThreads = 1024;
+constexpr int kPrepThreads = 1024;  // = kScanThreads: k_bucket_lds uses block_exscan
 
 __device__ inline void split_range(const float* __restrict__ H, long long n, uint16_t* __restrict__ hi,
                                    uint16_t* __restrict__ lo, long long i0, long long stride) {
@@ -34,6 +34,7 @@ __device__ inline void split_range(const float* __restrict__ H, long long n, uin
 // offsets do not depend on scheduling; only the order of tokens inside a bucket does, which
 // nothing depends on.
 constexpr int kScanThreads = 1024, kScanPer = 8, kScanTile = kScanThreads * kScanPer;
+static_assert(kPrepThreads == kScanThreads, "k_bucket_lds scans with block_exscan");
 
 __global__ __launch_bounds__(256) void k_bk_clear(int* __restrict__ b_count, long long n,
                                                   int32_t* __restrict__ flags) {
@@ -196,22 +197,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_bucket_lds(
   const int lo = tid * per, hi = min(lo + per, n_buckets);
   int sum = 0;
   for (int i = lo; i < hi; ++i) sum += cnt[i];
-  sh[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kPrepThreads; off <<= 1) {
-    const int v = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += v;
-    __syncthreads();
-  }
-  int run = tid ? sh[tid - 1] : 0;
+  int total;
+  int run = block_exscan(sum, sh, &total);  // wave scans and one scan of the wave totals
   for (int i = lo; i < hi; ++i) {
     const int c = cnt[i];
     cnt[i] = run;
     b_off[i] = run;
     run += c;
   }
-  if (tid == kPrepThreads - 1) b_off[n_buckets] = sh[kPrepThreads - 1];
+  if (tid == kPrepThreads - 1) b_off[n_buckets] = total;
   __syncthreads();
   for (int k = tid; k < n_tok; k += kPrepThreads) {
     const int pos = b_pos[k];
