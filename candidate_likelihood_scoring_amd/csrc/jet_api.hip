@@ -88,6 +88,7 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
       p->V >= 256 && p->d % tiled_bk(pl->hilo) == 0)
     pl->variant = VAR_TILED_BF16;
   pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
+  pl->direct = pl->stream && p->n_rows > 0;
   if (pl->variant == VAR_TILED_BF16) {
     pl->row_tile = tiled_row_tile(pl->hilo, p->d);
     pl->n_rtiles = (p->n_rows + pl->row_tile - 1) / pl->row_tile;
@@ -118,9 +119,11 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   }
   const int gx = pl->grid_x;
   pl->n_parts = gx;
-  pl->n_buckets = (long long)pl->n_rtiles * pl->n_vgroups;
+  // a direct plan neither buckets nor captures: no bucket, position or logit buffers
+  pl->n_buckets = pl->direct ? 0 : (long long)pl->n_rtiles * pl->n_vgroups;
   size_t off = 0;
-  const size_t rows = (size_t)p->n_rows, d = (size_t)p->d, ntok = (size_t)p->n_tok;
+  const size_t rows = (size_t)p->n_rows, d = (size_t)p->d;
+  const size_t ntok = pl->direct ? 0 : (size_t)p->n_tok;
   const bool split_buffers = pl->hilo && !pl->stream;
   pl->off_hhi = off;
   if (split_buffers) off += al256(rows * d * 2);
@@ -289,13 +292,16 @@ jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o, void* 
   a.lse = o->row_lse ? o->row_lse : reinterpret_cast<float*>(ws + pl.off_lse);
   a.flags = o->dev_flags ? o->dev_flags : reinterpret_cast<int32_t*>(ws + pl.off_flags);
   a.stream = static_cast<hipStream_t>(stream);
-  if (launch_prep(a) != hipSuccess) return JET_E_HIP;
+  // Direct plans: projection (which clears the flag word), token log-probabilities with
+  // the row merges, decisions.  Others: bucketing (clears the flag word), projection with
+  // target capture, merge, decisions.
+  if (!pl.direct && launch_prep(a) != hipSuccess) return JET_E_HIP;
   if (ev_before && hipEventRecord(static_cast<hipEvent_t>(ev_before), a.stream) != hipSuccess)
     return JET_E_HIP;
   if (p->n_rows > 0 && launch_project(a) != hipSuccess) return JET_E_HIP;
   if (ev_after && hipEventRecord(static_cast<hipEvent_t>(ev_after), a.stream) != hipSuccess)
     return JET_E_HIP;
-  if (launch_merge(a) != hipSuccess) return JET_E_HIP;
+  if ((pl.direct ? launch_token_logp(a) : launch_merge(a)) != hipSuccess) return JET_E_HIP;
   if (launch_decide(a) != hipSuccess) return JET_E_HIP;
   return JET_OK;
 }

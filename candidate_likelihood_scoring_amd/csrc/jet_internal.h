@@ -66,6 +66,8 @@ struct Plan {
   int variant;
   bool hilo;          // fp32 H split into bf16 hi + lo
   bool stream;        // streaming kernel (d % 128 == 0): splits fp32 H itself
+  bool direct;        // streaming kernel with rows: no bucketing launch; k_token_logp computes
+                      // each target logit as a dot product and writes the log-probabilities
   int row_tile;       // rows per projection tile (bucketing granularity over rows)
   int n_rtiles;
   int vgroup;         // vocabulary entries per bucket (a multiple of the kernel's tile)
@@ -111,6 +113,7 @@ hipError_t launch_sensitivity(const float* z, const float* z_skip, const int* se
                               float* d, float* J, int32_t* selected, int32_t* flags,
                               hipStream_t stream);  // the tiled kernel launched for this plane count
 hipError_t launch_merge(const ScoreArgs& a);
+hipError_t launch_token_logp(const ScoreArgs& a);
 hipError_t launch_decide(const ScoreArgs& a);
 
 struct RestrictedPlan {

@@ -133,6 +133,31 @@ __device__ inline float merge_row(const float2* __restrict__ part, int n_parts, 
   return m + logf(s);
 }
 
+// merge_row in two halves, so a wave can put other loads in flight between them: the
+// row's partials (at most 64 * kMergeBatch, partial j at part[row * n_parts + j]) are loaded
+// into registers, later folded in merge_row's order (same bits).
+struct RowParts {
+  float2 v[kMergeBatch];
+};
+__device__ inline RowParts merge_issue(const float2* __restrict__ part, int n_parts, int row,
+                                       int lane) {
+  RowParts r;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const int j = lane + 64 * u;
+    r.v[u] = j < n_parts ? part[(size_t)row * n_parts + j] : make_float2(-INFINITY, 0.f);
+  }
+  return r;
+}
+__device__ inline float merge_finish(const RowParts& r, int n_parts, int lane) {
+  float m = -INFINITY, s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    if (lane + 64 * u < n_parts) lse_merge(m, s, r.v[u].x, r.v[u].y);
+  wave_lse_merge(m, s);
+  return m + logf(s);
+}
+
 // Everything decide_question reads and writes (device pointers; optional ones may be NULL).
 struct DecideArgs {
   const float* z_tgt;
@@ -157,6 +182,7 @@ struct DecideArgs {
   float* q_conf;
   float* q_mass;
   int32_t* flags;
+  bool logp_ready;  // tok_logp already holds every l_k (written by k_token_logp)
 };
 
 // All outputs of question q, computed by one wave (every lane calls it with the same q).
@@ -189,11 +215,15 @@ __device__ inline void decide_question(const DecideArgs& a, int q, int lane) {
       bad_off = true;
       s = NaN;
     } else {
-      for (int k = t0; k < t1; ++k) {
-        const int r = a.tok_row ? a.tok_row[k] : k;
-        const float l = (r >= 0 && r < a.n_rows) ? a.z_tgt[k] - a.lse[r] : NaN;
-        a.tok_logp[k] = l;
-        s += l;
+      if (a.logp_ready) {
+        for (int k = t0; k < t1; ++k) s += a.tok_logp[k];
+      } else {
+        for (int k = t0; k < t1; ++k) {
+          const int r = a.tok_row ? a.tok_row[k] : k;
+          const float l = (r >= 0 && r < a.n_rows) ? a.z_tgt[k] - a.lse[r] : NaN;
+          a.tok_logp[k] = l;
+          s += l;
+        }
       }
     }
     a.cand_s[c] = s;

@@ -40,9 +40,9 @@ struct Acc {
   f32x16 t[NT];
 };
 
-// Fold one group's logits into the lane's running (m, s) state; capture the targets in
-// the group.  Shared by the bf16 and fp32 kernels.
-template <int NT>
+// Fold one group's logits into the lane's running (m, s) state; with CAPTURE, also capture
+// the targets in the group.  Shared by the bf16 and fp32 kernels.
+template <int NT, bool CAPTURE = true>
 __device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int n, int half,
                                     int row0, const int* __restrict__ b_off,
                                     const int* __restrict__ b_tok, int bkey,
@@ -71,6 +71,7 @@ __device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int n, in
     s_run = s_run * exp2f((m_run - mn) * kLog2e) + sum;
     m_run = mn;
   }
+  if (!CAPTURE) return;
   // Target capture: the bucket lists the tokens whose (row tile, vocabulary group) is
   // this one; the lane holding (row, target) writes the raw logit.
   const int e0 = b_off[bkey], e1 = b_off[bkey + 1];
@@ -255,12 +256,13 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // the caches could serve: one row tile, or a head larger than the last-level cache).
 // Measured on binary_enum (1.27 GB head, one row tile): 220 -> 207 us per launch, the plain
 // read of the same bytes 6.34 -> 7.06 TB/s.
+// Targets are not captured here: the launch after this one computes each token's target
+// logit as one dot product (k_token_logp), so no bucketing launch precedes this kernel, and
+// its first workgroup clears the flag word instead.
 template <int WPB, int S, bool HF32, bool NT>
 __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     const uint16_t* __restrict__ W, int V, int d, const void* __restrict__ Hsrc, int n_rows,
-    int n_groups, const int* __restrict__ b_off, const int* __restrict__ b_tok,
-    const int* __restrict__ tok_row, const int* __restrict__ tok_target,
-    float* __restrict__ z_tgt, float2* __restrict__ part) {
+    int n_groups, int32_t* __restrict__ flags, float2* __restrict__ part) {
   constexpr int KC = 128;                 // k per stage
   constexpr int NP = HF32 ? 2 : 1;        // H planes in LDS (hi, lo)
   constexpr int HQ = (HF32 ? 16 : 8) / WPB;  // H load instructions per wave per stage
@@ -277,6 +279,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
   const int nst = d / KC;
   u32x4* my = wt[wid];
   float m_run = -INFINITY, s_run = 0.f;
+  if (flags && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flags[0] = 0;
 
   // H stage loads.  bf16 H: instruction hq reads stage rows 4 hq + lane / 16, 16-byte chunk
   // lane % 16.  fp32 H: instruction hq reads rows 2 hq + lane / 32, four values at
@@ -364,8 +367,8 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
       if (s < nst - nmain) JET_STAGE_MMA(s, nmain + s);  // uniform over the workgroup
 #undef JET_STAGE_MMA
 #undef JET_STAGE_LOAD
-    epilogue_lse<1>(acc, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
-                    tok_target, z_tgt, m_run, s_run);
+    epilogue_lse<1, false>(acc, v0, V, n, half, row0, nullptr, nullptr, 0, nullptr, nullptr,
+                           nullptr, m_run, s_run);
     // The H stage buffer is hb[stage & 1] and the stage count restarts with every group.
     // With an odd count the group's last stage and the next group's first share buffer 0,
     // so no wave may write the next group's stage 0 before every wave has read the last
@@ -506,8 +509,7 @@ hipError_t launch_project(const ScoreArgs& a) {
     const bool nt = pl.n_rtiles == 1 || (size_t)p->V * p->d * 2 >= kStreamNtBytes;
 #define JET_WG(HF, NTV)                                                                      \
   hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, kStreamS, HF, NTV>), grid, sblock, 0,     \
-                     a.stream, W, p->V, p->d, p->H, p->n_rows, pl.n_vgroups, b_off, b_tok,     \
-                     p->tok_row, p->tok_target, z_tgt, part)
+                     a.stream, W, p->V, p->d, p->H, p->n_rows, pl.n_vgroups, a.flags, part)
     if (pl.hilo) {
       if (nt) JET_WG(true, true);
       else JET_WG(true, false);

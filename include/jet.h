@@ -120,7 +120,7 @@ typedef struct {
 /* Outputs of jet_score (device buffers, fp32 unless noted).  Required: tok_logp, cand_s,
  * cand_q, q_argmax.  Optional outputs may be NULL. */
 typedef struct {
-  float* tok_logp;     /* [n_tok]  l_k                                                     */
+  float* tok_logp;     /* [n_tok]  l_k (<= 0; NaN for an out-of-range row or target)       */
   float* row_lse;      /* [n_rows] LSE_r (optional)                                        */
   float* cand_s;       /* [n_cand] s(c)                                                    */
   float* cand_q;       /* [n_cand] q(c)                                                    */
@@ -140,7 +140,9 @@ typedef struct {
 JET_API size_t jet_score_workspace_size(const jet_problem* p);
 
 /* Enqueue the whole path: operand staging, fused projection + online full-vocabulary
- * logsumexp + target capture (logits never stored), the deterministic merge of the
+ * logsumexp (logits never stored), the target logits (captured in the projection's
+ * epilogue; on the streaming kernel, which serves fewer than 256 rows with d % 128 == 0
+ * and a bf16 head, one dot product per token after it), the deterministic merge of the
  * per-chunk normalisers, token log-probabilities, candidate sums and per-question
  * decisions.  workspace: device memory of at least jet_score_workspace_size(p) bytes,
  * 256-byte aligned, not shared with a concurrent call.  Results are bitwise

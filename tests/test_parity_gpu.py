@@ -99,6 +99,38 @@ def test_stream_odd_stage_count(jet, d, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, f'odd_stages_{d}_{h_dtype}')}")
 
 
+@pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
+def test_stream_target_logit_dominates(jet, h_dtype):
+    """Streaming path, where each target logit is a dot product of its own, summed in
+    another order than the projection's: every row gets one planted vocabulary entry
+    (head row bf16(40 h / |h|^2), logit near +40, every other logit about N(0, 1)) and all
+    its tokens target it, so l_k is about -1e-14 and a rounding apart from 0.  l_k must stay
+    <= 0 and match the oracle, and no output may depend on whether row_lse is requested
+    (without it the launch has no row waves)."""
+    p = wl.make_problem(V=8192, d=256, n_q=10, K=(2, 5), lengths=(1, 4), layout="prefix",
+                        seed=71, h_dtype=h_dtype)
+    H = np.asarray(p["H"])
+    H64 = ((H.astype(np.uint32) << 16).view(np.float32) if h_dtype == "bf16" else H).astype(np.float64)
+    rng = np.random.default_rng(72)
+    planted = rng.choice(p["V"], size=p["n_rows"], replace=False).astype(np.int32)
+    W = np.array(p["W"], copy=True)
+    for r in range(p["n_rows"]):
+        W[planted[r]] = wl.bf16_bits((40.0 * H64[r] / np.dot(H64[r], H64[r])).astype(np.float32))
+    rows = np.arange(len(p["tok_target"])) if p["tok_row"] is None else np.asarray(p["tok_row"])
+    p = dict(p, W=W, tok_target=planted[rows])
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] stream dominant targets {h_dtype} rows={p['n_rows']} tokens={len(rows)} ({kern})")
+    assert kern == "k_project_wg_bf16"
+    out = _run(jet, p)
+    ref = jo.score(p)
+    assert np.max(ref["tok_logp"]) > -1e-6
+    log(f"[gpu] errs {compare(p, out, ref, f'dominant_{h_dtype}')}")
+    assert np.all(out["tok_logp"] <= 0)
+    lean = _run(jet, p, optional=False)
+    for k in lean:
+        assert np.array_equal(lean[k], out[k]), k
+
+
 def test_stream_large_head_several_row_tiles(jet):
     """The streaming kernel on binary_enum's head shape (V = 248,320, d = 2560: 1.27 GB, past
     the last-level cache, so its loads carry the non-temporal hint) with 207 rows in seven
@@ -496,8 +528,9 @@ def test_stream_read_checksum(jet):
     assert int(out.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
 
 
-def test_empty_problem(jet):
-    p = wl.make_problem(V=100, d=32, n_q=0, seed=2, n_extra_rows=3)
+@pytest.mark.parametrize("d", [32, 128])
+def test_empty_problem(jet, d):
+    p = wl.make_problem(V=100, d=d, n_q=0, seed=2, n_extra_rows=3)
     out = _run(jet, p)
     ref = jo.score(p)
     assert out["dev_flags"][0] == 0
@@ -515,6 +548,17 @@ def test_bad_indices_set_flags_without_faulting(jet, d):
     out = _run(jet, q)
     assert out["dev_flags"][0] & 2
     assert np.isnan(out["tok_logp"][0])
+    # the same output buffers again with valid indices: the call clears the flag word
+    # itself; the other tokens' values do not depend on the bad one
+    dq = jet.to_device(q, "cuda")
+    buf = api.alloc_outputs(api.make_problem(**dq), "cuda")
+    jet.score_problem(dq, out=buf)
+    torch.cuda.synchronize()
+    assert int(buf["dev_flags"][0]) & 2
+    clean = jet.to_numpy(jet.score_problem(jet.to_device(p, "cuda"), out=buf))
+    assert clean["dev_flags"][0] == 0
+    assert np.array_equal(out["tok_logp"][1:], clean["tok_logp"][1:])
+    assert np.array_equal(out["row_lse"], clean["row_lse"])
     q = dict(p)
     q["tok_row"] = p["tok_row"].copy()
     q["tok_row"][1] = p["n_rows"] + 100
