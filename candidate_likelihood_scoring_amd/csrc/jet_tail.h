@@ -188,6 +188,11 @@ struct DecideArgs {
 // All outputs of question q, computed by one wave (every lane calls it with the same q).
 __device__ inline void decide_question(const DecideArgs& a, int q, int lane) {
   const float NaN = __builtin_nanf("");
+  // question-level inputs are loaded with the question's offsets, and each lane's candidate
+  // text id with its token offsets, so that no load waits behind the token loop
+  const bool have_text = a.cand_text_id && a.q_gold_text_id;
+  const int gold = have_text ? a.q_gold_text_id[q] : 0;
+  const int t_given = a.q_true_idx ? a.q_true_idx[q] : 0;
   int c0 = a.q_cand_off[q], c1 = a.q_cand_off[q + 1];
   if (c0 < 0 || c1 > a.n_cand || c1 <= c0) {
     if (lane == 0) {
@@ -206,10 +211,13 @@ __device__ inline void decide_question(const DecideArgs& a, int q, int lane) {
   float best = -INFINITY, smax = -INFINITY;
   int best_c = c1;  // sentinel: no finite candidate seen
   bool bad_off = false;
-  // with at most 64 candidates a lane holds one: its sum stays in a register for passes 2-3
+  // with at most 64 candidates a lane holds one: its sum and text id stay in registers for
+  // passes 2-3
   float s_mine = 0.f;
+  int text_mine = 0;
   for (int c = c0 + lane; c < c1; c += 64) {
     int t0 = a.cand_tok_off[c], t1 = a.cand_tok_off[c + 1];
+    if (have_text) text_mine = a.cand_text_id[c];
     float s = 0.f;
     if (t0 < 0 || t1 > a.n_tok || t1 <= t0) {
       bad_off = true;
@@ -239,19 +247,17 @@ __device__ inline void decide_question(const DecideArgs& a, int q, int lane) {
   wave_argmax(best, best_c);
   const float M = best;
   const float Ms = wave_max(smax);  // shift of the mass sum
-  const bool have_text = a.cand_text_id && a.q_gold_text_id;
-  const int gold = have_text ? a.q_gold_text_id[q] : 0;
   const bool one_each = K <= 64;
   // pass 2: normalisers (all candidates; gold-text candidates)
   float z_part = 0.f, mg = -INFINITY;
   for (int c = c0 + lane; c < c1; c += 64) {
     const float av = (one_each ? s_mine : a.cand_s[c]) / a.T;
     z_part += expf(av - M);
-    if (have_text && a.cand_text_id[c] == gold) mg = fmaxf(mg, av);
+    if (have_text && (one_each ? text_mine : a.cand_text_id[c]) == gold) mg = fmaxf(mg, av);
   }
   const float Z = wave_sum(z_part);
   const float Mg = have_text ? wave_max(mg) : -INFINITY;
-  int t_idx = a.q_true_idx ? a.q_true_idx[q] : (K == 2 ? 1 : -1);
+  int t_idx = a.q_true_idx ? t_given : (K == 2 ? 1 : -1);
   if (t_idx < -1 || t_idx >= K) {
     if (lane == 0) flag_or(a.flags, JET_FLAG_BAD_TRUE_IDX);
     t_idx = -1;
@@ -266,7 +272,8 @@ __device__ inline void decide_question(const DecideArgs& a, int q, int lane) {
     e_part += (float)(c - c0) * qc;
     if (qc > 0.f) h_part -= qc * logf(qc);
     mass_part += expf(s - Ms);
-    if (have_text && a.cand_text_id[c] == gold && Mg != -INFINITY) zg_part += expf(av - Mg);
+    if (have_text && (one_each ? text_mine : a.cand_text_id[c]) == gold && Mg != -INFINITY)
+      zg_part += expf(av - Mg);
     if (a.q_true && c - c0 == t_idx) a.q_true[q] = qc;
   }
   const float E = wave_sum(e_part);
