@@ -31,9 +31,11 @@ constexpr int kMaxV = 1 << 30;
 #define JET_SMALL_WAVES 2048  // 256 CUs x 8 resident waves
 #endif
 constexpr int kSmallWaves = JET_SMALL_WAVES;
-// Row count above which the tiled (matrix-core bound) kernel replaces the streaming one.
+// Fewest rows for the tiled (matrix-core) kernel: more than one 32-row tile of the streaming
+// kernel, which reads the whole head once per row tile (measured at V = 248,320, d = 2560:
+// 194 us per 32-row tile, so 1.48 ms at 255 rows, against 350 us for one tiled row tile).
 #ifndef JET_TILED_MIN_ROWS
-#define JET_TILED_MIN_ROWS 256
+#define JET_TILED_MIN_ROWS 33
 #endif
 constexpr int kTiledMinRows = JET_TILED_MIN_ROWS;
 
@@ -82,16 +84,20 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   *pl = Plan{};
   pl->variant = p->w_dtype == JET_F32 ? VAR_SMALL_F32 : VAR_SMALL_BF16;
   pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
-  // tiled path: enough rows, whole stages, at least one full 256 x 256 tile (its buffer
-  // offsets are local to a workgroup's tiles, so operands of any size take it)
-  if (pl->variant == VAR_SMALL_BF16 && p->n_rows >= kTiledMinRows && p->n_rows >= 256 &&
-      p->V >= 256 && p->d % tiled_bk(pl->hilo) == 0)
+  // tiled path: enough rows, whole stages, at least one full vocabulary tile (its buffer
+  // offsets are local to a workgroup's tiles, so operands of any size take it); fewer rows
+  // than one row tile run as one tile with zero rows appended to H
+  if (pl->variant == VAR_SMALL_BF16 && p->n_rows >= kTiledMinRows && p->V >= 256 &&
+      p->d % tiled_bk(pl->hilo) == 0)
     pl->variant = VAR_TILED_BF16;
+  pl->rows_k = p->n_rows;
   pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
   pl->direct = pl->stream && p->n_rows > 0;
   if (pl->variant == VAR_TILED_BF16) {
     pl->row_tile = tiled_row_tile(pl->hilo, p->d);
-    pl->n_rtiles = (p->n_rows + pl->row_tile - 1) / pl->row_tile;
+    pl->rows_k = std::max(p->n_rows, pl->row_tile);
+    pl->pad_h = !pl->hilo && p->n_rows < pl->row_tile;  // fp32 H: its split planes are padded
+    pl->n_rtiles = (pl->rows_k + pl->row_tile - 1) / pl->row_tile;
     pl->vgroup = 256;
     pl->n_vgroups = (p->V + 255) / 256;
     // Split count S (vocabulary ranges per row tile).  Every workgroup takes the same
@@ -100,15 +106,16 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     // finish together, so each XCD's next 32 again form one block sharing its L2,
     // and short ones keep the eight XCDs on nearby head tiles.  (Measured on both tiled
     // kernels: runs of 4 tiles 1-3% faster than 8, 6-10% faster than balanced ranges of
-    // unequal length; single tiles 2-3% slower.)  Fewer tiles per workgroup when 4 would
-    // leave CUs idle.  S is rounded up to a multiple of 8 (XCD-aware placement) when that
-    // adds few empty ranges.
+    // unequal length; single tiles 2-3% slower.)  With less work than 4 tiles per CU, the
+    // fewest tiles per workgroup that still fit every workgroup into one round on the 256
+    // CUs.  S is rounded up to a multiple of 8 (XCD-aware placement, which needs at least 4
+    // row tiles) when that adds few empty ranges.
     const int R = pl->n_rtiles, nvt = pl->n_vgroups;
     const long long work = (long long)R * nvt;
-    int L = (int)std::min<long long>(4, std::max<long long>(1, work / 256));
+    int L = (int)std::min<long long>(4, std::max<long long>(1, (work + 255) / 256));
     L = std::min(L, nvt);
     int splits = (nvt + L - 1) / L;
-    if (splits >= 32) splits = (splits + 7) / 8 * 8;
+    if (splits >= 32 && R >= 2) splits = (splits + 7) / 8 * 8;
     pl->grid_x = splits;
   } else {
     pl->row_tile = 32;
@@ -122,17 +129,19 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   // a direct plan neither buckets nor captures: no bucket, position or logit buffers
   pl->n_buckets = pl->direct ? 0 : (long long)pl->n_rtiles * pl->n_vgroups;
   size_t off = 0;
-  const size_t rows = (size_t)p->n_rows, d = (size_t)p->d;
+  const size_t rows = (size_t)p->n_rows, rows_k = (size_t)pl->rows_k, d = (size_t)p->d;
   const size_t ntok = pl->direct ? 0 : (size_t)p->n_tok;
   const bool split_buffers = pl->hilo && !pl->stream;
   pl->off_hhi = off;
-  if (split_buffers) off += al256(rows * d * 2);
+  if (split_buffers) off += al256(rows_k * d * 2);
   pl->off_hlo = off;
-  if (split_buffers) off += al256(rows * d * 2);
+  if (split_buffers) off += al256(rows_k * d * 2);
+  pl->off_hpad = off;
+  if (pl->pad_h) off += al256(rows_k * d * 2);
   pl->off_ztgt = off;
   off += al256(ntok * 4);
   pl->off_part = off;
-  off += al256((size_t)pl->n_parts * rows * 8);
+  off += al256((size_t)pl->n_parts * rows_k * 8);
   pl->off_lse = off;
   off += al256(rows * 4);
   pl->off_bcount = off;

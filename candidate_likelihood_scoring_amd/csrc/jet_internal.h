@@ -69,6 +69,9 @@ struct Plan {
   bool direct;        // streaming kernel with rows: no bucketing launch; k_token_logp computes
                       // each target logit as a dot product and writes the log-probabilities
   int row_tile;       // rows per projection tile (bucketing granularity over rows)
+  int rows_k;         // rows the projection kernel sees: n_rows, or one whole row tile of the
+                      // tiled kernel when n_rows is smaller (H then padded with zero rows)
+  bool pad_h;         // bf16 H copied into the workspace with zero rows up to rows_k
   int n_rtiles;
   int vgroup;         // vocabulary entries per bucket (a multiple of the kernel's tile)
   int n_vgroups;
@@ -77,8 +80,8 @@ struct Plan {
   long long n_buckets;
   long long n_btiles; // bucket-count tiles of the grid-wide scan (kBucketScanTile buckets each)
   // workspace byte offsets
-  size_t off_hhi, off_hlo, off_ztgt, off_part, off_lse, off_bcount, off_btile, off_boff, off_btok,
-      off_bpos, off_flags, total;
+  size_t off_hhi, off_hlo, off_hpad, off_ztgt, off_part, off_lse, off_bcount, off_btile, off_boff,
+      off_btok, off_bpos, off_flags, total;
 };
 
 bool make_plan(const jet_problem* p, bool want_lse_buffer, Plan* plan);
@@ -127,9 +130,10 @@ hipError_t launch_restricted(const jet_restricted_problem* p, const jet_restrict
                              const RestrictedPlan* plan, char* ws, int32_t* flags,
                              hipStream_t stream);
 
-// H fp32 -> (hi, lo) bf16 split, shared by both paths.
-hipError_t launch_split(const float* H, long long n_elems, uint16_t* hi, uint16_t* lo,
-                        hipStream_t stream);
+// H fp32 -> (hi, lo) bf16 planes for the tiled and fallback kernels; elements n_elems ..
+// n_out - 1 of the planes are zero (padding rows).
+hipError_t launch_split(const float* H, long long n_elems, long long n_out, uint16_t* hi,
+                        uint16_t* lo, hipStream_t stream);
 
 // Projection core of the restricted path with an fp32 head: Z[row][u] = <H[row], Wu[u]>
 // for all rows and gathered union entries.

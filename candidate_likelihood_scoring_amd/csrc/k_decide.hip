@@ -158,8 +158,9 @@ hipError_t launch_merge(const ScoreArgs& a) {
   const jet_problem* p = a.p;
   const Plan& pl = *a.plan;
   if (p->n_rows == 0) return hipSuccess;
-  // row-major partials (streaming kernel): row r's partials contiguous
-  const long long rs = pl.stream ? pl.n_parts : 1, ps = pl.stream ? 1 : p->n_rows;
+  // row-major partials (streaming kernel): row r's partials contiguous; the others: one
+  // partial per row per workgroup, strided by the rows the projection kernel saw
+  const long long rs = pl.stream ? pl.n_parts : 1, ps = pl.stream ? 1 : pl.rows_k;
   hipLaunchKernelGGL(k_merge, dim3((p->n_rows + 3) / 4), dim3(256), 0, a.stream,
                      reinterpret_cast<const float2*>(a.ws + pl.off_part), pl.n_parts, p->n_rows,
                      rs, ps, a.lse);

@@ -782,16 +782,19 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   const int* b_tok = reinterpret_cast<const int*>(a.ws + pl.off_btok);
   float* z_tgt = reinterpret_cast<float*>(a.ws + pl.off_ztgt);
   float2* part = reinterpret_cast<float2*>(a.ws + pl.off_part);
-  // XCD-aware placement when the split count is a multiple of 8: blocks of sr row tiles x
-  // ss splits per XCD, row tiles padded to a multiple of sr and the launch to a multiple of
-  // 256; padding workgroups (row tile >= R) exit at once.  Otherwise the plain order
-  // P = rt * S + split.  bf16 H takes 8 x 4 blocks (each head tile shared 8 ways; 2%
+  // XCD-aware placement when the split count is a multiple of 8 and there are at least 2
+  // row tiles: blocks of sr row tiles x ss splits per XCD, row tiles padded to a multiple of
+  // sr and the launch to a multiple of 256; padding workgroups (row tile >= R) exit at once.
+  // Otherwise the plain order P = rt * S + split.  One row tile has no head tile for a block
+  // to share, and padding it to a block left 3 of 4 workgroups empty: 467 -> 352 us at
+  // 256 rows, V = 248,320, d = 2560.  With 2 or 3 row tiles the blocks' sharing of each head
+  // tile in L2 outweighs their padding (629 against 677 us at 384 rows).  bf16 H takes 8 x 4 blocks (each head tile shared 8 ways; 2%
   // faster than 4 x 8 on large_batch) when that pads at most 1/16 of the row tiles; the
   // two-plane kernels, whose H tiles hold two planes, take 4 x 8 (with 8 x 4 they were no
   // faster at 32 row tiles and 7% slower at 64).
   const int S = pl.grid_x, R = pl.n_rtiles;
   int sr = 1, ss = S, remap = 0, total = S * R;
-  if (S % 8 == 0) {
+  if (S % 8 == 0 && R >= 2) {
     sr = 4;
     ss = 8;
     if (!pl.hilo && R >= 8 && ((R + 7) / 8 * 8 - R) * 16 <= R) {
@@ -804,22 +807,27 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   }
   dim3 grid(total), block(256);
   const uint16_t* W = static_cast<const uint16_t*>(p->W);
+  // the kernels see rows_k rows (n_rows, or one whole row tile of zero-padded H); partials
+  // are strided by rows_k
+  const int rk = pl.rows_k;
   if (pl.hilo && tiled_two_plane_m16(pl.hilo, p->d)) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
     hipLaunchKernelGGL(k_project_tiled_m16x2, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
-                       p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
+                       rk, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
                        part, R, S, sr, ss, remap);
   } else if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
     hipLaunchKernelGGL(k_project_tiled_bf16<2>, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
-                       p->n_rows, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
+                       rk, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
                        part, R, S, sr, ss, remap);
   } else {
-    hipLaunchKernelGGL(k_project_tiled_m16, grid, block, 0, a.stream, W, p->V, p->d,
-                       static_cast<const uint16_t*>(p->H), p->n_rows, pl.n_vgroups, b_off, b_tok,
-                       p->tok_row, p->tok_target, z_tgt, part, R, S, sr, ss, remap);
+    const uint16_t* H = pl.pad_h ? reinterpret_cast<const uint16_t*>(a.ws + pl.off_hpad)
+                                 : static_cast<const uint16_t*>(p->H);
+    hipLaunchKernelGGL(k_project_tiled_m16, grid, block, 0, a.stream, W, p->V, p->d, H, rk,
+                       pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R,
+                       S, sr, ss, remap);
   }
   return hipGetLastError();
 }

@@ -88,12 +88,12 @@ def test_stream_odd_stage_count(jet, d, h_dtype):
     """The streaming kernel with an odd number of 128-wide stages (3 and 5): its H stage
     buffers alternate by stage, so the last stage of one vocabulary group and the first of
     the next share a buffer.  513 groups over 256 workgroups give every workgroup two or
-    three groups in a row; every output against the oracle."""
-    p = wl.make_problem(V=131101, d=d, n_q=30, K=(2, 6), lengths=(1, 4), layout="prefix",
-                        seed=95, h_dtype=h_dtype, n_extra_rows=12)
+    three groups in a row; every output against the oracle (30 field rows: one row tile)."""
+    p = wl.make_problem(V=131101, d=d, n_q=30, K=(2, 6), layout="field", seed=95,
+                        h_dtype=h_dtype)
     kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
     log(f"[gpu] stream odd stages d={d} {h_dtype} rows={p['n_rows']} ({kern})")
-    assert kern == "k_project_wg_bf16" and p["n_rows"] < 256
+    assert kern == "k_project_wg_bf16" and p["n_rows"] <= 32
     out = _run(jet, p)
     ref = jo.score(p)
     log(f"[gpu] errs {compare(p, out, ref, f'odd_stages_{d}_{h_dtype}')}")
@@ -107,7 +107,7 @@ def test_stream_target_logit_dominates(jet, h_dtype):
     its tokens target it, so l_k is about -1e-14 and a rounding apart from 0.  l_k must stay
     <= 0 and match the oracle, and no output may depend on whether row_lse is requested
     (without it the launch has no row waves)."""
-    p = wl.make_problem(V=8192, d=256, n_q=10, K=(2, 5), lengths=(1, 4), layout="prefix",
+    p = wl.make_problem(V=8192, d=256, n_q=5, K=(2, 5), lengths=(1, 2), layout="prefix",
                         seed=71, h_dtype=h_dtype)
     H = np.asarray(p["H"])
     H64 = ((H.astype(np.uint32) << 16).view(np.float32) if h_dtype == "bf16" else H).astype(np.float64)
@@ -131,36 +131,58 @@ def test_stream_target_logit_dominates(jet, h_dtype):
         assert np.array_equal(lean[k], out[k]), k
 
 
-def test_stream_large_head_several_row_tiles(jet):
-    """The streaming kernel on binary_enum's head shape (V = 248,320, d = 2560: 1.27 GB, past
-    the last-level cache, so its loads carry the non-temporal hint) with 207 rows in seven
-    row tiles, each of which streams the head again; every output against the oracle."""
+@pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
+def test_mid_rows_large_head(jet, h_dtype):
+    """Between one streaming row tile and one whole tiled row tile, on binary_enum's head
+    shape (V = 248,320, d = 2560): 207 rows run on the tiled kernel, with fp32 H as two
+    128-row tiles (XCD-aware blocks padded with empty row tiles) and with bf16 H as one
+    256-row tile of zero-padded H.  fp32 H against the full oracle, bf16 H on every row of
+    10 sampled questions."""
     p = wl.make_problem(V=248320, d=2560, n_q=40, K=(2, 6), lengths=(1, 3), layout="prefix",
-                        seed=99, n_extra_rows=0)
+                        seed=99, h_dtype=h_dtype, n_extra_rows=0)
     n = p["n_rows"]
     kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
-    log(f"[gpu] large head, {n} rows ({kern})")
-    assert kern == "k_project_wg_bf16" and 96 < n < 256
+    log(f"[gpu] mid rows, large head, {n} rows {h_dtype} ({kern})")
+    assert 128 < n < 256
+    assert kern == ("k_project_tiled_m16x2" if h_dtype == "f32" else "k_project_tiled_m16")
     out = _run(jet, p)
-    log(f"[gpu] large head errs {compare(p, out, jo.score(p), 'large_head_row_tiles')}")
+    _full_size_properties(p, out)
+    qs = np.random.default_rng(5).choice(len(p["q_cand_off"]) - 1, 10, replace=False)
+    rows = None if h_dtype == "f32" else _rows_of_questions(p, qs)
+    ref = jo.score(p, rows=rows)
+    log(f"[gpu] mid rows errs {compare(p, out, ref, 'mid_rows_' + h_dtype, sampled=rows is not None)}")
 
 
-@pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
-def test_extra_row_tile_keeps_every_bit(jet, h_dtype):
-    """The same questions in a problem with one more, unreferenced row (64 rows in two
-    32-row tiles, then 65 in three): the streaming kernel's partials, the merge and the
-    decisions do not depend on how many rows or row tiles the problem has, so every output
-    keeps its bits; both against the oracle."""
-    p = wl.make_problem(V=20011, d=256, n_q=12, K=(2, 5), lengths=(1, 3), layout="prefix",
-                        seed=98, h_dtype=h_dtype, n_extra_rows=4)
-    q = wl.make_problem(V=20011, d=256, n_q=12, K=(2, 5), lengths=(1, 3), layout="prefix",
-                        seed=98, h_dtype=h_dtype, n_extra_rows=5)
-    assert p["n_rows"] == 64 and q["n_rows"] == 65
-    assert np.array_equal(p["H"], q["H"][:64]) and np.array_equal(p["tok_target"], q["tok_target"])
+# (V, extra rows, rows before -> after): the streaming kernel (a vocabulary below one tiled
+# tile) going from two 32-row tiles to three; the tiled kernel from one zero-padded row tile
+# to one exact one (bf16 H: 256 rows) and from one to two (fp32 H: 128-row tiles)
+_ROW_TILE_STEPS = {
+    "stream_f32": (250, "f32", 4, 64), "stream_bf16": (250, "bf16", 4, 64),
+    "tiled_bf16": (20011, "bf16", 196, 256), "tiled_f32": (20011, "f32", 68, 128),
+}
+
+
+@pytest.mark.parametrize("case", list(_ROW_TILE_STEPS))
+def test_extra_row_tile_keeps_every_bit(jet, case):
+    """The same questions in a problem with one more, unreferenced row: a kernel's
+    partials, the merge and the decisions do not depend on how many rows or row tiles the
+    problem has (nor on zero padding rows), so every output keeps its bits; both against
+    the oracle."""
+    V, h_dtype, extra, n0 = _ROW_TILE_STEPS[case]
+    p = wl.make_problem(V=V, d=256, n_q=12, K=(2, 5), lengths=(1, 3), layout="prefix",
+                        seed=98, h_dtype=h_dtype, n_extra_rows=extra)
+    q = wl.make_problem(V=V, d=256, n_q=12, K=(2, 5), lengths=(1, 3), layout="prefix",
+                        seed=98, h_dtype=h_dtype, n_extra_rows=extra + 1)
+    assert p["n_rows"] == n0 and q["n_rows"] == n0 + 1
+    assert np.array_equal(p["H"], q["H"][:n0]) and np.array_equal(p["tok_target"], q["tok_target"])
+    kp = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    kq = api.projection_kernel(api.make_problem(**jet.to_device(q, "cuda")))
+    log(f"[gpu] extra row {case}: {n0} rows ({kp}) -> {n0 + 1} ({kq})")
+    assert kp == kq and (kp == "k_project_wg_bf16") == case.startswith("stream")
     a, b = _run(jet, p), _run(jet, q)
-    log(f"[gpu] extra row tile {h_dtype}: errs {compare(p, a, jo.score(p), 'row_tiles')}")
+    log(f"[gpu] extra row {case}: errs {compare(p, a, jo.score(p), 'row_tiles_' + case)}")
     for k in a:
-        x, y = (a[k], b[k][:64]) if k == "row_lse" else (a[k], b[k])
+        x, y = (a[k], b[k][:n0]) if k == "row_lse" else (a[k], b[k])
         assert np.array_equal(x.view(np.int32), y.view(np.int32)), k
 
 
@@ -935,7 +957,8 @@ def test_restricted_no_writes_past_outputs_or_workspace(jet, w_dtype):
 # ----------------------------------------------------------------------------------------
 
 _GRAPH_CASES = {
-    "stream": dict(V=5003, d=128, n_q=9, K=(1, 12), lengths=(1, 6), layout="prefix", seed=81),
+    "stream": dict(V=5003, d=128, n_q=9, K=(1, 12), layout="field", seed=81),
+    "tiled_padded": dict(V=5003, d=128, n_q=9, K=(1, 12), lengths=(1, 6), layout="prefix", seed=81),
     "tiled": dict(V=3001, d=128, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=82,
                   h_dtype="bf16", n_extra_rows=300),
     "tiled_f32": dict(V=2500, d=64, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=83,

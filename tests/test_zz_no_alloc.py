@@ -1,5 +1,5 @@
 """jet_score_noalloc (workspace in the library's static device array) against jet_score
-with a caller workspace: two calls in a row on one stream, the second on a smaller problem,
+with a caller workspace: three calls in a row on one stream, each on a smaller problem,
 each bitwise equal to jet_score's outputs and within the oracle's tolerances; a problem
 whose workspace exceeds the array is rejected before anything is enqueued."""
 import ctypes
@@ -20,8 +20,10 @@ CASES = [
     # matrix-core path (bf16 H, 11 row tiles, grid-bucketed targets): the larger call first
     dict(V=20011, d=256, n_q=60, K=(2, 8), lengths=(1, 6), layout="own", seed=901,
          h_dtype="bf16", n_extra_rows=2500),
-    # streaming path, fp32 H, shared prefix rows: smaller workspace, same array
-    dict(V=6151, d=128, n_q=9, K=(1, 12), lengths=(1, 5), layout="prefix", seed=902, dups=2),
+    # matrix-core path with fewer rows than one row tile (fp32 H planes zero-padded)
+    dict(V=6151, d=128, n_q=4, K=(1, 12), lengths=(1, 5), layout="prefix", seed=902, dups=2),
+    # streaming path, fp32 H, one row per field: smallest workspace, same array
+    dict(V=6151, d=128, n_q=9, K=(1, 12), layout="field", seed=903, dups=2),
 ]
 
 
