@@ -31,13 +31,14 @@ constexpr int kMaxV = 1 << 30;
 #define JET_SMALL_WAVES 2048  // 256 CUs x 8 resident waves
 #endif
 constexpr int kSmallWaves = JET_SMALL_WAVES;
-// Fewest rows for the tiled (matrix-core) kernel: more than one 32-row tile of the streaming
-// kernel, which reads the whole head once per row tile (measured at V = 248,320, d = 2560:
-// 194 us per 32-row tile, so 1.48 ms at 255 rows, against 350 us for one tiled row tile).
-#ifndef JET_TILED_MIN_ROWS
-#define JET_TILED_MIN_ROWS 33
-#endif
-constexpr int kTiledMinRows = JET_TILED_MIN_ROWS;
+// Rows the streaming kernel takes in one pass over the head: its workgroups carry up to 2
+// (fp32 H, split into two planes) or 4 (bf16 H) 32-row tiles of H, as many as the LDS
+// holds.  Past that the tiled (matrix-core) kernel takes the problem, and also past one
+// 32-row tile when d rules the streaming kernel out (the fallback reads the whole head once
+// per 32-row tile).  Measured at V = 248,320, d = 2560: the streaming kernel with one row
+// tile per workgroup 194 us per 32-row tile (1.48 ms at 255 rows), one tiled row tile about
+// 350 us.
+int stream_max_row_tiles(bool hilo) { return hilo ? 2 : 4; }
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -87,7 +88,9 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   // tiled path: enough rows, whole stages, at least one full vocabulary tile (its buffer
   // offsets are local to a workgroup's tiles, so operands of any size take it); fewer rows
   // than one row tile run as one tile with zero rows appended to H
-  if (pl->variant == VAR_SMALL_BF16 && p->n_rows >= kTiledMinRows && p->V >= 256 &&
+  const bool stream_d = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
+  const int one_pass_rows = stream_d ? 32 * stream_max_row_tiles(pl->hilo) : 32;
+  if (pl->variant == VAR_SMALL_BF16 && p->n_rows > one_pass_rows && p->V >= 256 &&
       p->d % tiled_bk(pl->hilo) == 0)
     pl->variant = VAR_TILED_BF16;
   pl->rows_k = p->n_rows;
@@ -118,8 +121,14 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     if (splits >= 32 && R >= 2) splits = (splits + 7) / 8 * 8;
     pl->grid_x = splits;
   } else {
-    pl->row_tile = 32;
-    pl->n_rtiles = (p->n_rows + 31) / 32;
+    // streaming kernel: the fewest row tiles per workgroup (1, 2, 4) that cover the rows,
+    // up to the LDS limit (more rows only with a vocabulary below one tiled tile)
+    int nr = 1;
+    if (pl->stream)
+      while (nr < stream_max_row_tiles(pl->hilo) && 32 * nr < p->n_rows) nr *= 2;
+    pl->stream_nr = nr;
+    pl->row_tile = 32 * nr;
+    pl->n_rtiles = (p->n_rows + pl->row_tile - 1) / pl->row_tile;
     pl->vgroup = small_group_size(pl->variant, p->d);
     pl->n_vgroups = (p->V + pl->vgroup - 1) / pl->vgroup;
     pl->grid_x = std::max(1, small_grid(pl->variant, p->d, pl->n_vgroups, kSmallWaves));

@@ -66,6 +66,7 @@ struct Plan {
   int variant;
   bool hilo;          // fp32 H split into bf16 hi + lo
   bool stream;        // streaming kernel (d % 128 == 0): splits fp32 H itself
+  int stream_nr;      // streaming kernel: 32-row tiles of H per workgroup (1, 2 or 4)
   bool direct;        // streaming kernel with rows: no bucketing launch; k_token_logp computes
                       // each target logit as a dot product and writes the log-probabilities
   int row_tile;       // rows per projection tile (bucketing granularity over rows)

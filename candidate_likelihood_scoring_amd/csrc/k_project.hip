@@ -259,26 +259,36 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // Targets are not captured here: the launch after this one computes each token's target
 // logit as one dot product (k_token_logp), so no bucketing launch precedes this kernel, and
 // its first workgroup clears the flag word instead.
-template <int WPB, int S, bool HF32, bool NT>
+// NR: 32-row tiles of H per workgroup (1, 2 or 4): each head fragment is multiplied into NR
+// accumulator tiles, so the head is read once for 32 NR rows.  The H stage holds NR x 32
+// rows (LDS: 64 KB of head tiles + 2 x NP x NR x 8 KB of H stages, at most 128 KB).
+template <int WPB, int S, bool HF32, bool NT, int NR>
 __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     const uint16_t* __restrict__ W, int V, int d, const void* __restrict__ Hsrc, int n_rows,
     int n_groups, int32_t* __restrict__ flags, float2* __restrict__ part) {
   constexpr int KC = 128;                 // k per stage
   constexpr int NP = HF32 ? 2 : 1;        // H planes in LDS (hi, lo)
-  constexpr int HQ = (HF32 ? 16 : 8) / WPB;  // H load instructions per wave per stage
-  static_assert(HQ >= 1 && (HF32 ? 16 : 8) % WPB == 0, "H stage split");
+  constexpr int HQ = (HF32 ? 16 : 8) * NR / WPB;  // H load instructions per wave per stage
+  static_assert(HQ >= 1 && ((HF32 ? 16 : 8) * NR) % WPB == 0, "H stage split");
+  static_assert(NP * NR <= 4, "H stages within the LDS budget");
+  constexpr int HP = NR * 512;            // 16-byte slots per H plane
   __shared__ u32x4 wt[WPB][512];          // per-wave 32-row head tile
-  __shared__ u32x4 hb[2][NP][512];        // H stage, double buffered
-  __shared__ float2 red[WPB][32];
+  __shared__ u32x4 hb[2][NP][HP];         // H stage, double buffered
+  __shared__ float2 red[NR][WPB][32];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n = lane & 31, half = lane >> 5;
   const int lrow = lane >> 4, lch = lane & 15;
-  const int rt = blockIdx.y, row0 = rt * 32;
+  const int rt = blockIdx.y, row0 = rt * 32 * NR;
   const int g0 = (int)((long long)blockIdx.x * n_groups / gridDim.x);
   const int g1 = (int)((long long)(blockIdx.x + 1) * n_groups / gridDim.x);
   const int nst = d / KC;
   u32x4* my = wt[wid];
-  float m_run = -INFINITY, s_run = 0.f;
+  float m_run[NR], s_run[NR];
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
+    m_run[t] = -INFINITY;
+    s_run[t] = 0.f;
+  }
   if (flags && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flags[0] = 0;
 
   // H stage loads.  bf16 H: instruction hq reads stage rows 4 hq + lane / 16, 16-byte chunk
@@ -299,8 +309,9 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
 
   for (int g = g0; g < g1; ++g) {
     const int v0 = g * (WPB * 32) + wid * 32;
-    Acc<1> acc;
-    acc.t[0] = f32x16{};
+    Acc<NR> acc;
+#pragma unroll
+    for (int t = 0; t < NR; ++t) acc.t[t] = f32x16{};
     u32x4 R[S][8], Hr[S][HQ];
 #define JET_STAGE_LOAD(SLOT, ST)                                                            \
   {                                                                                         \
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
         split_pair(__uint_as_float(x[0]), __uint_as_float(x[1]), h01, l01);                 \
         split_pair(__uint_as_float(x[2]), __uint_as_float(x[3]), h23, l23);                 \
         uint2* dh = reinterpret_cast<uint2*>(&hbuf[slot_]) + (lane & 1);                    \
-        uint2* dl = reinterpret_cast<uint2*>(&hbuf[512 + slot_]) + (lane & 1);              \
+        uint2* dl = reinterpret_cast<uint2*>(&hbuf[HP + slot_]) + (lane & 1);               \
         *dh = make_uint2(h01, h23);                                                         \
         *dl = make_uint2(l01, l23);                                                         \
       } else {                                                                              \
@@ -339,9 +350,11 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
       const int c = ((half * 8 + j) ^ (n & 15)) + n * 16;                                    \
       const bf16x8 a = as_bf16x8v(my[c]);                                                   \
-      acc.t[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[c]), acc.t[0], 0, 0, 0); \
-      if (HF32)                                                                             \
-        acc.t[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[512 + c]), acc.t[0], 0, 0, 0); \
+      _Pragma("unroll") for (int t = 0; t < NR; ++t) {                                       \
+        acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[t * 512 + c]), acc.t[t], 0, 0, 0); \
+        if (HF32)                                                                           \
+          acc.t[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8v(hbuf[HP + t * 512 + c]), acc.t[t], 0, 0, 0); \
+      }                                                                                     \
     }                                                                                       \
   }
 #pragma unroll
@@ -367,8 +380,13 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
       if (s < nst - nmain) JET_STAGE_MMA(s, nmain + s);  // uniform over the workgroup
 #undef JET_STAGE_MMA
 #undef JET_STAGE_LOAD
-    epilogue_lse<1, false>(acc, v0, V, n, half, row0, nullptr, nullptr, 0, nullptr, nullptr,
-                           nullptr, m_run, s_run);
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      Acc<1> one;
+      one.t[0] = acc.t[t];
+      epilogue_lse<1, false>(one, v0, V, n, half, row0, nullptr, nullptr, 0, nullptr, nullptr,
+                             nullptr, m_run[t], s_run[t]);
+    }
     // The H stage buffer is hb[stage & 1] and the stage count restarts with every group.
     // With an odd count the group's last stage and the next group's first share buffer 0,
     // so no wave may write the next group's stage 0 before every wave has read the last
@@ -376,7 +394,9 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     // and needs none).
     if (nst & 1) __syncthreads();
   }
-  store_partial<WPB, true>(m_run, s_run, n, half, wid, row0, n_rows, part, red);
+#pragma unroll
+  for (int t = 0; t < NR; ++t)
+    store_partial<WPB, true>(m_run[t], s_run[t], n, half, wid, row0 + 32 * t, n_rows, part, red[t]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -507,16 +527,23 @@ hipError_t launch_project(const ScoreArgs& a) {
     dim3 sblock(kStreamWPB * 64);
     // non-temporal head loads unless several row tiles could find a small head in a cache
     const bool nt = pl.n_rtiles == 1 || (size_t)p->V * p->d * 2 >= kStreamNtBytes;
-#define JET_WG(HF, NTV)                                                                      \
-  hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, kStreamS, HF, NTV>), grid, sblock, 0,     \
+#define JET_WG(HF, NTV, NRV)                                                                 \
+  hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, (NRV == 1 ? kStreamS : 2), HF, NTV, NRV>), \
+                     grid, sblock, 0,                                                           \
                      a.stream, W, p->V, p->d, p->H, p->n_rows, pl.n_vgroups, a.flags, part)
+#define JET_WG_NT(HF, NRV) \
+  if (nt) JET_WG(HF, true, NRV); else JET_WG(HF, false, NRV)
     if (pl.hilo) {
-      if (nt) JET_WG(true, true);
-      else JET_WG(true, false);
+      if (pl.stream_nr == 1) { JET_WG_NT(true, 1); }
+      else if (pl.stream_nr == 2) { JET_WG_NT(true, 2); }
+      else return hipErrorInvalidValue;
     } else {
-      if (nt) JET_WG(false, true);
-      else JET_WG(false, false);
+      if (pl.stream_nr == 1) { JET_WG_NT(false, 1); }
+      else if (pl.stream_nr == 2) { JET_WG_NT(false, 2); }
+      else if (pl.stream_nr == 4) { JET_WG_NT(false, 4); }
+      else return hipErrorInvalidValue;
     }
+#undef JET_WG_NT
 #undef JET_WG
   } else if (pl.variant == VAR_SMALL_BF16) {
     const uint16_t* W = static_cast<const uint16_t*>(p->W);

@@ -99,6 +99,45 @@ def test_stream_odd_stage_count(jet, d, h_dtype):
     log(f"[gpu] errs {compare(p, out, ref, f'odd_stages_{d}_{h_dtype}')}")
 
 
+# (d, H dtype, rows): the streaming kernel carrying 2 (fp32 H) or 4 (bf16 H) 32-row tiles
+# per workgroup, with full and ragged last tiles and odd stage counts (d = 384, 640)
+_STREAM_MULTI = [(256, "f32", 64), (384, "f32", 41), (256, "bf16", 128), (640, "bf16", 97),
+                 (128, "bf16", 70), (384, "bf16", 33)]
+
+
+@pytest.mark.parametrize("d,h_dtype,rows", _STREAM_MULTI,
+                         ids=[f"d{d}_{h}_{r}" for d, h, r in _STREAM_MULTI])
+def test_stream_row_tiles_per_workgroup(jet, d, h_dtype, rows):
+    """The streaming kernel with several 32-row tiles of H per workgroup: each head fragment
+    is multiplied into every row tile's accumulators, so the head is read once for up to 64
+    (fp32 H) or 128 (bf16 H) rows.  One question per row (single-token fields), so every
+    row carries tokens; every output against the oracle."""
+    p = wl.make_problem(V=131101, d=d, n_q=rows, K=(2, 8), layout="field", seed=300 + rows,
+                        h_dtype=h_dtype)
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] stream row tiles d={d} {h_dtype} rows={p['n_rows']} ({kern})")
+    assert kern == "k_project_wg_bf16" and p["n_rows"] == rows
+    out = _run(jet, p)
+    log(f"[gpu] errs {compare(p, out, jo.score(p), f'stream_multi_{d}_{h_dtype}_{rows}')}")
+
+
+@pytest.mark.parametrize("h_dtype,rows", [("f32", 64), ("bf16", 128)])
+def test_stream_row_tiles_large_head(jet, h_dtype, rows):
+    """The most rows one pass of the streaming kernel takes (64 of fp32 H, 128 of bf16 H) on
+    binary_enum's head shape (V = 248,320, d = 2560, non-temporal head loads): every output of
+    16 sampled questions (one row each) against the oracle, properties on all."""
+    p = wl.make_problem(V=248320, d=2560, n_q=rows, K=(2, 8), layout="field", seed=77,
+                        h_dtype=h_dtype)
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] stream row tiles, large head, {h_dtype} rows={p['n_rows']} ({kern})")
+    assert kern == "k_project_wg_bf16" and p["n_rows"] == rows
+    out = _run(jet, p)
+    _full_size_properties(p, out)
+    qs = np.random.default_rng(6).choice(rows, 16, replace=False)
+    ref = jo.score(p, rows=_rows_of_questions(p, qs))
+    log(f"[gpu] errs {compare(p, out, ref, 'stream_multi_large_' + h_dtype, sampled=True)}")
+
+
 @pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
 def test_stream_target_logit_dominates(jet, h_dtype):
     """Streaming path, where each target logit is a dot product of its own, summed in

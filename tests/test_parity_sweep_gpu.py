@@ -1,15 +1,15 @@
 """Seeded random sweep of problem shapes through every projection plan, against the fp64
 oracle (needs an MI355X).
 
-Thirty-six problems are drawn from one seed, six per plan family: the streaming kernel
-(bf16 head, d % 128 == 0, at most 32 rows, one row tile; target logits after the
-projection), the register-staged fallback (bf16 head, d a multiple of neither 64 nor 128),
-the fp32 head, the tiled kernels between 33 and about 255 rows (one zero-padded row tile,
-or two with fp32 H), and the tiled kernels with bf16 H and with fp32 H past 256 rows.  Each
-draws its vocabulary size, d, layout (prefix row, one row per field, a row per token),
-candidate counts and lengths, exact duplicates, temperature and H dtype.  Every output is
-compared element by element over every row a token references plus a sample of
-unreferenced rows.
+Forty-two problems are drawn from one seed, six per plan family: the streaming kernel
+(bf16 head, d % 128 == 0) with one 32-row tile and with 33 to 64 (fp32 H) or 128 (bf16
+H) rows in one pass; the register-staged fallback (bf16 head, d a multiple of neither 64
+nor 128); the fp32 head; the tiled kernels just past the streaming kernel's rows (one
+zero-padded row tile, or two with fp32 H); and the tiled kernels with bf16 H and with fp32
+H past 256 rows.  Each draws its vocabulary size, d, layout (prefix row, one row per
+field, a row per token), candidate counts and lengths, exact duplicates, temperature and H
+dtype, and asserts the kernel the plan's documented rule picks.  Every output is compared
+element by element over every row a token references plus a sample of unreferenced rows.
 """
 import numpy as np
 import pytest
@@ -22,16 +22,25 @@ torch = pytest.importorskip("torch")
 from candidate_likelihood_scoring_amd import api  # noqa: E402
 pytestmark = pytest.mark.gpu
 
-FAMILIES = ("stream", "fallback", "f32_head", "tiled_mid", "tiled_bf16h", "tiled_f32h")
-TILED_BY_H = {"bf16": ("k_project_tiled_m16",), "f32": ("k_project_tiled_m16x2", "k_project_tiled_bf16")}
+FAMILIES = ("stream", "stream_multi", "fallback", "f32_head", "tiled_mid", "tiled_bf16h",
+            "tiled_f32h")
 
 
-def expected(fam, h_dtype):
-    return {"stream": ("k_project_wg_bf16",), "fallback": ("k_project_small_bf16",),
-            "f32_head": ("k_project_small_f32",)}.get(fam) or TILED_BY_H[h_dtype]
+def plan_kernel(p):
+    """The projection kernel of the plan's rule, from the problem's scalars."""
+    rows, V, d, hf = p["n_rows"], p["V"], p["d"], p["h_dtype"] == "f32"
+    if p["w_dtype"] == "f32":
+        return "k_project_small_f32"
+    if d % 128 == 0:
+        if rows <= (64 if hf else 128) or V < 256:
+            return "k_project_wg_bf16"
+        return "k_project_tiled_m16x2" if hf else "k_project_tiled_m16"
+    if hf and d % 64 == 0 and rows > 32 and V >= 256:
+        return "k_project_tiled_bf16"
+    return "k_project_small_bf16"
 
 
-def _cases(n=36, seed=4711):
+def _cases(n=42, seed=4711):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -41,20 +50,24 @@ def _cases(n=36, seed=4711):
                  dups=int(rng.integers(0, 3)), seed=9000 + i, name=f"sweep{i}_{fam}",
                  K=(1, int(rng.integers(2, 13))), lengths=(1, int(rng.integers(1, 5))),
                  n_q=int(rng.integers(1, 6)), n_extra_rows=0)
+        hd = pick(["f32", "bf16"])
         if fam == "stream":  # at most 2 questions x 8 candidates x 2 tokens: 32 rows
             c.update(d=pick([128, 256, 384, 512, 640, 1024]), V=int(rng.integers(300, 120_000)),
-                     h_dtype=pick(["f32", "bf16"]), w_dtype="bf16", n_q=int(rng.integers(1, 3)),
+                     h_dtype=hd, w_dtype="bf16", n_q=int(rng.integers(1, 3)),
                      K=(1, int(rng.integers(2, 9))), lengths=(1, int(rng.integers(1, 3))))
+        elif fam in ("stream_multi", "tiled_mid"):  # one row per field, then unreferenced rows
+            top = 64 if hd == "f32" else 128
+            lo, hi = (33, top) if fam == "stream_multi" else (top + 1, 255)
+            rows = int(rng.integers(lo, hi + 1))
+            n_q = int(rng.integers(1, min(rows, 20) + 1))
+            c.update(d=pick([128, 256, 384, 512]), V=int(rng.integers(256, 60_000)), h_dtype=hd,
+                     w_dtype="bf16", layout="field", n_q=n_q, n_extra_rows=rows - n_q)
         elif fam == "fallback":  # never tiled: d is not a multiple of 64
             c.update(d=pick([32, 96, 160, 224, 288]), V=int(rng.integers(300, 60_000)),
-                     h_dtype=pick(["f32", "bf16"]), w_dtype="bf16")
+                     h_dtype=hd, w_dtype="bf16")
         elif fam == "f32_head":
             c.update(d=pick([32, 64, 128, 160]), V=int(rng.integers(100, 30_000)),
                      h_dtype="f32", w_dtype="f32")
-        elif fam == "tiled_mid":  # 34 rows and up, mostly under one 256-row tile
-            c.update(d=pick([128, 256, 384, 512]), V=int(rng.integers(256, 40_000)),
-                     h_dtype=pick(["f32", "bf16"]), w_dtype="bf16", n_q=int(rng.integers(1, 5)),
-                     n_extra_rows=int(rng.integers(33, 120)))
         elif fam == "tiled_bf16h":
             c.update(d=pick([128, 256, 384]), V=int(rng.integers(256, 30_000)), h_dtype="bf16",
                      w_dtype="bf16", n_q=int(rng.integers(6, 15)), n_extra_rows=int(rng.integers(256, 500)))
@@ -79,7 +92,7 @@ def test_sweep(fam, case):
     kern = api.projection_kernel(api.make_problem(**dev))
     log(f"[gpu] {case['name']}: V={p['V']} d={p['d']} rows={p['n_rows']} tokens={len(p['tok_target'])} "
         f"H {p['h_dtype']} W {p['w_dtype']} T={p['T']} layout={case['layout']} dups={case['dups']} ({kern})")
-    assert kern in expected(fam, p["h_dtype"]), (fam, kern)
+    assert kern == plan_kernel(p), (fam, kern, plan_kernel(p))
     out = problem.to_numpy(problem.score_problem(dev))
     torch.cuda.synchronize()
     tok_row = np.arange(len(p["tok_target"])) if p["tok_row"] is None else np.asarray(p["tok_row"])

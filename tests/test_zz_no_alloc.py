@@ -21,7 +21,7 @@ CASES = [
     dict(V=20011, d=256, n_q=60, K=(2, 8), lengths=(1, 6), layout="own", seed=901,
          h_dtype="bf16", n_extra_rows=2500),
     # matrix-core path with fewer rows than one row tile (fp32 H planes zero-padded)
-    dict(V=6151, d=128, n_q=4, K=(1, 12), lengths=(1, 5), layout="prefix", seed=902, dups=2),
+    dict(V=6151, d=128, n_q=4, K=(1, 12), layout="field", seed=902, dups=2, n_extra_rows=96),
     # streaming path, fp32 H, one row per field: smallest workspace, same array
     dict(V=6151, d=128, n_q=9, K=(1, 12), layout="field", seed=903, dups=2),
 ]
