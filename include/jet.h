@@ -141,9 +141,9 @@ JET_API size_t jet_score_workspace_size(const jet_problem* p);
 
 /* Enqueue the whole path: operand staging, fused projection + online full-vocabulary
  * logsumexp (logits never stored), the target logits (captured in the projection's
- * epilogue; on the streaming kernel, which serves up to 32 rows (more only with fewer
- * than 256 head rows) with d % 128 == 0 and a bf16 head, one dot product per token after
- * it), the deterministic merge of the
+ * epilogue; on the streaming kernel, which serves up to 64 rows of fp32 H or 128 of bf16
+ * H (more only with fewer than 256 head rows) with d % 128 == 0 and a bf16 head, one dot
+ * product per token after it), the deterministic merge of the
  * per-chunk normalisers, token log-probabilities, candidate sums and per-question
  * decisions.  workspace: device memory of at least jet_score_workspace_size(p) bytes,
  * 256-byte aligned, not shared with a concurrent call.  Results are bitwise
