@@ -203,14 +203,16 @@ __global__ __launch_bounds__(kPrepThreads) void k_bucket_lds(
   for (int i = lo; i < hi; ++i) sum += cnt[i];
   int total;
   int run = block_exscan(sum, sh, &total);  // wave scans and one scan of the wave totals
-  for (int i = lo; i < hi; ++i) {
+  for (int i = lo; i < hi; ++i) {  // each thread's contiguous range, in LDS only
     const int c = cnt[i];
     cnt[i] = run;
-    b_off[i] = run;
     run += c;
   }
-  if (tid == kPrepThreads - 1) b_off[n_buckets] = total;
+  if (tid == 0) cnt[n_buckets] = total;
   __syncthreads();
+  // offsets stored with consecutive threads on consecutive buckets (a store per bucket
+  // from each thread's own range touched a cache line per lane)
+  for (int i = tid; i <= n_buckets; i += kPrepThreads) b_off[i] = cnt[i];
   for (int k = tid; k < n_tok; k += kPrepThreads) {
     const int pos = b_pos[k];
     if (pos < 0) continue;
