@@ -111,7 +111,7 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     // kernels: runs of 4 tiles 1-3% faster than 8, 6-10% faster than balanced ranges of
     // unequal length; single tiles 2-3% slower.)  With less work than 4 tiles per CU, the
     // fewest tiles per workgroup that still fit every workgroup into one round on the 256
-    // CUs.  S is rounded up to a multiple of 8 (XCD-aware placement, which needs at least 4
+    // CUs.  S is rounded up to a multiple of 8 (XCD-aware placement, which needs at least 2
     // row tiles) when that adds few empty ranges.
     const int R = pl->n_rtiles, nvt = pl->n_vgroups;
     const long long work = (long long)R * nvt;

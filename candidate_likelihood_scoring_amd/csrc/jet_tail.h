@@ -1,4 +1,4 @@
-// Device code of the normaliser merge and the per-question decisions (k_merge, k_decide).
+// Device code of the normaliser merge and the per-question decisions (k_merge, k_token_logp, k_decide).
 //
 // merge_row: LSE_r = M + log sum_j s_j exp(m_j - M) over the row's (m_j, s_j) partials
 //   (JET paper, Eq. 2: the full-vocabulary denominator).  One wave per row: lane i folds
