@@ -121,6 +121,20 @@ def test_stream_row_tiles_per_workgroup(jet, d, h_dtype, rows):
     log(f"[gpu] errs {compare(p, out, jo.score(p), f'stream_multi_{d}_{h_dtype}_{rows}')}")
 
 
+@pytest.mark.parametrize("h_dtype,rows", [("f32", 150), ("bf16", 300)])
+def test_stream_small_vocab_many_rows(jet, h_dtype, rows):
+    """A vocabulary below one tiled tile (V = 200) keeps many rows on the streaming kernel:
+    several passes of 2 (fp32 H) or 4 (bf16 H) row tiles, the last one ragged; every
+    output against the oracle."""
+    p = wl.make_problem(V=200, d=256, n_q=rows, K=(2, 8), layout="field", seed=400 + rows,
+                        h_dtype=h_dtype)
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] stream small vocab {h_dtype} rows={p['n_rows']} ({kern})")
+    assert kern == "k_project_wg_bf16" and p["n_rows"] == rows
+    out = _run(jet, p)
+    log(f"[gpu] errs {compare(p, out, jo.score(p), f'stream_small_vocab_{h_dtype}')}")
+
+
 @pytest.mark.parametrize("h_dtype,rows", [("f32", 64), ("bf16", 128)])
 def test_stream_row_tiles_large_head(jet, h_dtype, rows):
     """The most rows one pass of the streaming kernel takes (64 of fp32 H, 128 of bf16 H) on
