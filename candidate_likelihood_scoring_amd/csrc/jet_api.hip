@@ -81,7 +81,7 @@ jet_status check_outputs(const jet_problem* p, const jet_outputs* o) {
 
 }  // namespace
 
-bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
+void make_plan(const jet_problem* p, Plan* pl) {
   *pl = Plan{};
   pl->variant = p->w_dtype == JET_F32 ? VAR_SMALL_F32 : VAR_SMALL_BF16;
   pl->hilo = p->w_dtype == JET_BF16 && p->h_dtype == JET_F32;
@@ -95,7 +95,6 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     pl->variant = VAR_TILED_BF16;
   pl->rows_k = p->n_rows;
   pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
-  pl->direct = pl->stream && p->n_rows > 0;
   if (pl->variant == VAR_TILED_BF16) {
     pl->row_tile = tiled_row_tile(pl->hilo, p->d);
     pl->rows_k = std::max(p->n_rows, pl->row_tile);
@@ -133,13 +132,11 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
     pl->n_vgroups = (p->V + pl->vgroup - 1) / pl->vgroup;
     pl->grid_x = std::max(1, small_grid(pl->variant, p->d, pl->n_vgroups, kSmallWaves));
   }
-  const int gx = pl->grid_x;
-  pl->n_parts = gx;
-  // a direct plan neither buckets nor captures: no bucket, position or logit buffers
-  pl->n_buckets = pl->direct ? 0 : (long long)pl->n_rtiles * pl->n_vgroups;
+  pl->n_parts = pl->grid_x;
+  // no target logit is captured by a projection kernel (k_token_logp computes them after
+  // it), so the workspace holds operands, partials and the flag word only
   size_t off = 0;
-  const size_t rows = (size_t)p->n_rows, rows_k = (size_t)pl->rows_k, d = (size_t)p->d;
-  const size_t ntok = pl->direct ? 0 : (size_t)p->n_tok;
+  const size_t rows_k = (size_t)pl->rows_k, d = (size_t)p->d;
   const bool split_buffers = pl->hilo && !pl->stream;
   pl->off_hhi = off;
   if (split_buffers) off += al256(rows_k * d * 2);
@@ -147,27 +144,11 @@ bool make_plan(const jet_problem* p, bool /*want_lse_buffer*/, Plan* pl) {
   if (split_buffers) off += al256(rows_k * d * 2);
   pl->off_hpad = off;
   if (pl->pad_h) off += al256(rows_k * d * 2);
-  pl->off_ztgt = off;
-  off += al256(ntok * 4);
   pl->off_part = off;
   off += al256((size_t)pl->n_parts * rows_k * 8);
-  pl->off_lse = off;
-  off += al256(rows * 4);
-  pl->off_bcount = off;
-  off += al256((size_t)(pl->n_buckets + 1) * 4);
-  pl->n_btiles = std::max(1LL, (pl->n_buckets + kBucketScanTile - 1) / kBucketScanTile);
-  pl->off_btile = off;
-  off += al256((size_t)pl->n_btiles * 4);
-  pl->off_boff = off;
-  off += al256((size_t)(pl->n_buckets + 1) * 4);
-  pl->off_btok = off;
-  off += al256(ntok * 4);
-  pl->off_bpos = off;
-  off += al256(ntok * 4);
   pl->off_flags = off;
   off += 256;
   pl->total = off;
-  return true;
 }
 
 }  // namespace jet
@@ -276,7 +257,7 @@ jet_status jet_build_predictor_trie(const int32_t* tok_target, const int32_t* ca
 const char* jet_projection_kernel(const jet_problem* p) {
   if (check_problem(p) != JET_OK) return nullptr;
   Plan pl;
-  make_plan(p, true, &pl);
+  make_plan(p, &pl);
   switch (pl.variant) {
     case VAR_TILED_BF16: return tiled_kernel_name(pl.hilo, p->d);
     case VAR_SMALL_F32: return "k_project_small_f32";
@@ -287,7 +268,7 @@ const char* jet_projection_kernel(const jet_problem* p) {
 size_t jet_score_workspace_size(const jet_problem* p) {
   if (check_problem(p) != JET_OK) return 0;
   Plan pl;
-  make_plan(p, true, &pl);
+  make_plan(p, &pl);
   return pl.total;
 }
 
@@ -298,8 +279,7 @@ jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o, void* 
   if (st != JET_OK) return st;
   if ((st = check_outputs(p, o)) != JET_OK) return st;
   Plan pl;
-  make_plan(p, true, &pl);
-  if (pl.n_btiles > kBucketMaxTiles) return JET_E_SHAPE;
+  make_plan(p, &pl);
   if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u)) return JET_E_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   ScoreArgs a;
@@ -307,19 +287,18 @@ jet_status jet_score_profiled(const jet_problem* p, const jet_outputs* o, void* 
   a.o = o;
   a.plan = &pl;
   a.ws = ws;
-  a.lse = o->row_lse ? o->row_lse : reinterpret_cast<float*>(ws + pl.off_lse);
   a.flags = o->dev_flags ? o->dev_flags : reinterpret_cast<int32_t*>(ws + pl.off_flags);
   a.stream = static_cast<hipStream_t>(stream);
-  // Direct plans: projection (which clears the flag word), token log-probabilities with
-  // the row merges, decisions.  Others: bucketing (clears the flag word), projection with
-  // target capture, merge, decisions.
-  if (!pl.direct && launch_prep(a) != hipSuccess) return JET_E_HIP;
+  // operand staging (fp32 H split into planes, zero-padded H; none for most plans), the
+  // projection (its first workgroup clears the flag word), token log-probabilities with the
+  // row merges (also the flag word's clear when there are no rows), decisions
+  if (launch_prep(a) != hipSuccess) return JET_E_HIP;
   if (ev_before && hipEventRecord(static_cast<hipEvent_t>(ev_before), a.stream) != hipSuccess)
     return JET_E_HIP;
   if (p->n_rows > 0 && launch_project(a) != hipSuccess) return JET_E_HIP;
   if (ev_after && hipEventRecord(static_cast<hipEvent_t>(ev_after), a.stream) != hipSuccess)
     return JET_E_HIP;
-  if ((pl.direct ? launch_token_logp(a) : launch_merge(a)) != hipSuccess) return JET_E_HIP;
+  if (launch_token_logp(a) != hipSuccess) return JET_E_HIP;
   if (launch_decide(a) != hipSuccess) return JET_E_HIP;
   return JET_OK;
 }
@@ -358,7 +337,7 @@ jet_status jet_score_noalloc(const jet_problem* p, const jet_outputs* o, void* s
   if (st != JET_OK) return st;
   if ((st = check_outputs(p, o)) != JET_OK) return st;
   Plan pl;
-  make_plan(p, true, &pl);
+  make_plan(p, &pl);
   if (pl.total > kNoallocScratchBytes) return JET_E_WORKSPACE;
   void* ws = scratch_on_current_device();
   if (!ws) return JET_E_HIP;

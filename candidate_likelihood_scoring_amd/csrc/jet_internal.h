@@ -58,34 +58,25 @@ __device__ inline void flag_or(int32_t* flags, uint32_t bit) {
 // ------------------------------------------------------------------------------------
 enum Variant { VAR_SMALL_BF16 = 0, VAR_SMALL_F32 = 1, VAR_TILED_BF16 = 2 };
 
-// buckets per tile of the grid-wide bucket scan, and the most tiles its one-workgroup
-// second level takes (so at most 2^26 buckets)
-constexpr long long kBucketScanTile = 8192, kBucketMaxTiles = 8192;
-
 struct Plan {
   int variant;
   bool hilo;          // fp32 H split into bf16 hi + lo
   bool stream;        // streaming kernel (d % 128 == 0): splits fp32 H itself
   int stream_nr;      // streaming kernel: 32-row tiles of H per workgroup (1, 2 or 4)
-  bool direct;        // streaming kernel with rows: no bucketing launch; k_token_logp computes
-                      // each target logit as a dot product and writes the log-probabilities
-  int row_tile;       // rows per projection tile (bucketing granularity over rows)
+  int row_tile;       // rows per projection tile
   int rows_k;         // rows the projection kernel sees: n_rows, or one whole row tile of the
                       // tiled kernel when n_rows is smaller (H then padded with zero rows)
   bool pad_h;         // bf16 H copied into the workspace with zero rows up to rows_k
   int n_rtiles;
-  int vgroup;         // vocabulary entries per bucket (a multiple of the kernel's tile)
+  int vgroup;         // vocabulary entries per group (a multiple of the kernel's tile)
   int n_vgroups;
   int grid_x;         // projection workgroups along the vocabulary
   int n_parts;        // (m, s) partials per row
-  long long n_buckets;
-  long long n_btiles; // bucket-count tiles of the grid-wide scan (kBucketScanTile buckets each)
   // workspace byte offsets
-  size_t off_hhi, off_hlo, off_hpad, off_ztgt, off_part, off_lse, off_bcount, off_btile, off_boff,
-      off_btok, off_bpos, off_flags, total;
+  size_t off_hhi, off_hlo, off_hpad, off_part, off_flags, total;
 };
 
-bool make_plan(const jet_problem* p, bool want_lse_buffer, Plan* plan);
+void make_plan(const jet_problem* p, Plan* plan);
 
 // ------------------------------------------------------------------------------------
 // Launchers (each returns hipSuccess or the launch error)
@@ -95,7 +86,6 @@ struct ScoreArgs {
   const jet_outputs* o;
   const Plan* plan;
   char* ws;
-  float* lse;        // row LSE buffer (caller's row_lse or workspace)
   int32_t* flags;    // device flag word (caller's or workspace)
   hipStream_t stream;
 };
@@ -116,8 +106,7 @@ hipError_t launch_sensitivity(const float* z, const float* z_skip, const int* se
                               int n_inputs, int n_values, int n_layers, float eps, int k,
                               float* d, float* J, int32_t* selected, int32_t* flags,
                               hipStream_t stream);  // the tiled kernel launched for this plane count
-hipError_t launch_merge(const ScoreArgs& a);
-hipError_t launch_token_logp(const ScoreArgs& a);
+hipError_t launch_token_logp(const ScoreArgs& a);  // also clears the flag word without rows
 hipError_t launch_decide(const ScoreArgs& a);
 
 struct RestrictedPlan {

@@ -1,13 +1,13 @@
-// Device code of the normaliser merge and the per-question decisions (k_merge, k_token_logp, k_decide).
+// Device code of the normaliser merge and the per-question decisions (k_token_logp, k_decide).
 //
-// merge_row: LSE_r = M + log sum_j s_j exp(m_j - M) over the row's (m_j, s_j) partials
-//   (JET paper, Eq. 2: the full-vocabulary denominator).  One wave per row: lane i folds
-//   partials i, i + 64, ... in order, then a fixed lane tree (wave_lse_merge) combines the
-//   lanes, so every lane ends with the same bits and the result does not depend on the
-//   row's position.
+// merge_issue / merge_finish: LSE_r = M + log sum_j s_j exp(m_j - M) over the row's
+//   (m_j, s_j) partials (JET paper, Eq. 2: the full-vocabulary denominator).  One wave per
+//   row: lane i folds partials i, i + 64, ... in order, then a fixed lane tree
+//   (wave_lse_merge) combines the lanes, so every lane ends with the same bits and the
+//   result does not depend on the row's position.
 // decide_question: one wave per question (JET Eq. 3-5 and the decision rules; gemma-e2b
-//   doc, "Candidate likelihoods" and "Output contracts"):
-//     l_k   = z[row_k, y_k] - LSE_{row_k}                (written to tok_logp)
+//   doc, "Candidate likelihoods" and "Output contracts"), from the token log-probabilities
+//   l_k = z[row_k, y_k] - LSE_{row_k} that k_token_logp stored in tok_logp:
 //     s(c)  = sum of l_k over the candidate's tokens, in token order
 //     a_c   = s(c) / T ;  q_c = exp(a_c - max a) / sum exp(a - max a)
 //     argmax: lowest index among the exact maxima of a (fixed order)
@@ -113,57 +113,44 @@ constexpr int kMergeBatch = 8;
 
 // Full-vocabulary LSE of one row from its n_parts partials, partial j of the row at
 // part[row * rs + j * ps] (the streaming kernel stores a row's partials contiguously, rs =
-// n_parts, ps = 1; the other kernels one partial per row per workgroup, rs = 1, ps =
-// n_rows); every lane of the wave returns the same value.
-__device__ inline float merge_row(const float2* __restrict__ part, int n_parts, size_t rs,
-                                  size_t ps, int row, int lane) {
-  float m = -INFINITY, s = 0.f;
-  for (int j0 = lane; j0 < n_parts; j0 += 64 * kMergeBatch) {
-    float2 v[kMergeBatch];
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int j = j0 + 64 * u;
-      v[u] = j < n_parts ? part[(size_t)row * rs + (size_t)j * ps] : make_float2(-INFINITY, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      if (j0 + 64 * u < n_parts) lse_merge(m, s, v[u].x, v[u].y);
-  }
-  wave_lse_merge(m, s);
-  return m + logf(s);
-}
-
-// merge_row in two halves, so a wave can put other loads in flight between them: the
-// row's partials (at most 64 * kMergeBatch, partial j at part[row * n_parts + j]) are loaded
-// into registers, later folded in merge_row's order (same bits).
+// n_parts, ps = 1; the other kernels one partial per row per workgroup, rs = 1, ps = the
+// kernel's row count).  Lane i folds partials i, i + 64, ... in order, then a fixed lane tree
+// (wave_lse_merge) combines the lanes, so every lane ends with the same bits and the result
+// does not depend on the row's position.  In two halves, so a wave can put other loads in
+// flight between them: merge_issue loads the first 64 * kMergeBatch partials into registers;
+// merge_finish folds them, then loads and folds the rest kMergeBatch per lane at a time.
 struct RowParts {
   float2 v[kMergeBatch];
 };
-__device__ inline RowParts merge_issue(const float2* __restrict__ part, int n_parts, int row,
-                                       int lane) {
+__device__ inline RowParts merge_issue(const float2* __restrict__ part, int n_parts, size_t rs,
+                                       size_t ps, int row, int lane) {
   RowParts r;
 #pragma unroll
   for (int u = 0; u < kMergeBatch; ++u) {
     const int j = lane + 64 * u;
-    r.v[u] = j < n_parts ? part[(size_t)row * n_parts + j] : make_float2(-INFINITY, 0.f);
+    r.v[u] = j < n_parts ? part[(size_t)row * rs + (size_t)j * ps] : make_float2(-INFINITY, 0.f);
   }
   return r;
 }
-__device__ inline float merge_finish(const RowParts& r, int n_parts, int lane) {
+__device__ inline float merge_finish(const RowParts& r, const float2* __restrict__ part,
+                                     int n_parts, size_t rs, size_t ps, int row, int lane) {
   float m = -INFINITY, s = 0.f;
 #pragma unroll
   for (int u = 0; u < kMergeBatch; ++u)
     if (lane + 64 * u < n_parts) lse_merge(m, s, r.v[u].x, r.v[u].y);
+  for (int j0 = lane + 64 * kMergeBatch; j0 < n_parts; j0 += 64 * kMergeBatch) {
+    const RowParts more = merge_issue(part + (size_t)(j0 - lane) * ps, n_parts - (j0 - lane), rs, ps, row, lane);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (j0 + 64 * u < n_parts) lse_merge(m, s, more.v[u].x, more.v[u].y);
+  }
   wave_lse_merge(m, s);
   return m + logf(s);
 }
 
 // Everything decide_question reads and writes (device pointers; optional ones may be NULL).
 struct DecideArgs {
-  const float* z_tgt;
-  const float* lse;
-  const int* tok_row;
-  int n_rows, n_tok;
+  int n_tok;
   const int* cand_tok_off;
   int n_cand;
   const int* q_cand_off;
@@ -172,7 +159,7 @@ struct DecideArgs {
   const int* q_gold_text_id;
   const int* q_true_idx;
   float T;
-  float* tok_logp;
+  const float* tok_logp;  // written by k_token_logp
   float* cand_s;
   float* cand_q;
   int* q_argmax;
@@ -182,7 +169,6 @@ struct DecideArgs {
   float* q_conf;
   float* q_mass;
   int32_t* flags;
-  bool logp_ready;  // tok_logp already holds every l_k (written by k_token_logp)
 };
 
 // All outputs of question q, computed by one wave (every lane calls it with the same q).
@@ -223,16 +209,7 @@ __device__ inline void decide_question(const DecideArgs& a, int q, int lane) {
       bad_off = true;
       s = NaN;
     } else {
-      if (a.logp_ready) {
-        for (int k = t0; k < t1; ++k) s += a.tok_logp[k];
-      } else {
-        for (int k = t0; k < t1; ++k) {
-          const int r = a.tok_row ? a.tok_row[k] : k;
-          const float l = (r >= 0 && r < a.n_rows) ? a.z_tgt[k] - a.lse[r] : NaN;
-          a.tok_logp[k] = l;
-          s += l;
-        }
-      }
+      for (int k = t0; k < t1; ++k) s += a.tok_logp[k];
     }
     a.cand_s[c] = s;
     s_mine = s;

@@ -40,15 +40,12 @@ struct Acc {
   f32x16 t[NT];
 };
 
-// Fold one group's logits into the lane's running (m, s) state; with CAPTURE, also capture
-// the targets in the group.  Shared by the bf16 and fp32 kernels.
-template <int NT, bool CAPTURE = true>
-__device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int n, int half,
-                                    int row0, const int* __restrict__ b_off,
-                                    const int* __restrict__ b_tok, int bkey,
-                                    const int* __restrict__ tok_row,
-                                    const int* __restrict__ tok_target,
-                                    float* __restrict__ z_tgt, float& m_run, float& s_run) {
+// Fold one group's logits into the lane's running (m, s) state.  Shared by the bf16 and fp32
+// kernels; no target logit is captured here (k_token_logp computes them after the
+// projection).
+template <int NT>
+__device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int half, float& m_run,
+                                    float& s_run) {
   float gm = -INFINITY;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -70,26 +67,6 @@ __device__ inline void epilogue_lse(const Acc<NT>& acc, int v0, int V, int n, in
       }
     s_run = s_run * exp2f((m_run - mn) * kLog2e) + sum;
     m_run = mn;
-  }
-  if (!CAPTURE) return;
-  // Target capture: the bucket lists the tokens whose (row tile, vocabulary group) is
-  // this one; the lane holding (row, target) writes the raw logit.
-  const int e0 = b_off[bkey], e1 = b_off[bkey + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int k = b_tok[e];
-    const int r = tok_row ? tok_row[k] : k;
-    const int lv = tok_target[k] - v0;
-    const int mm = lv & 31;
-    if (lv >= 0 && lv < 32 * NT && n == r - row0 && half == ((mm >> 2) & 1)) {
-      const int tt = lv >> 5, ii = ((mm >> 3) << 2) | (mm & 3);
-      float val = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (t == tt && i == ii) val = acc.t[t][i];
-      z_tgt[k] = val;
-    }
   }
 }
 
@@ -162,9 +139,8 @@ __device__ inline FragK<KB> ldk(const uint16_t* p) {
 template <int NT, int KB, int S, bool HILO>
 __global__ __launch_bounds__(256) void k_project_small_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ Hhi,
-    const uint16_t* __restrict__ Hlo, int n_rows, int n_groups, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part) {
+    const uint16_t* __restrict__ Hlo, int n_rows, int n_groups, int32_t* __restrict__ flags,
+    float2* __restrict__ part) {
   static_assert(KB % 32 == 0 && S >= 2, "stage shape");
   __shared__ float2 red[kWpb][32];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -178,6 +154,7 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
   const int g0 = (int)(w * n_groups / nw), g1 = (int)((w + 1) * n_groups / nw);
   const int nkb = d / KB;
   float m_run = -INFINITY, s_run = 0.f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flags[0] = 0;
 
   for (int g = g0; g < g1; ++g) {
     const int v0 = g * (32 * NT);
@@ -226,8 +203,7 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
         }
       }
     }
-    epilogue_lse<NT>(acc, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
-                     tok_target, z_tgt, m_run, s_run);
+    epilogue_lse<NT>(acc, v0, V, half, m_run, s_run);
   }
   store_partial(m_run, s_run, n, half, wid, row0, n_rows, part, red);
 }
@@ -256,9 +232,7 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // the caches could serve: one row tile, or a head larger than the last-level cache).
 // Measured on binary_enum (1.27 GB head, one row tile): 220 -> 207 us per launch, the plain
 // read of the same bytes 6.34 -> 7.06 TB/s.
-// Targets are not captured here: the launch after this one computes each token's target
-// logit as one dot product (k_token_logp), so no bucketing launch precedes this kernel, and
-// its first workgroup clears the flag word instead.
+// Its first workgroup clears the flag word (no launch before it does).
 // NR: 32-row tiles of H per workgroup (1, 2 or 4): each head fragment is multiplied into NR
 // accumulator tiles, so the head is read once for 32 NR rows.  The H stage holds NR x 32
 // rows (LDS: 64 KB of head tiles + 2 x NP x NR x 8 KB of H stages, at most 128 KB).
@@ -289,7 +263,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     m_run[t] = -INFINITY;
     s_run[t] = 0.f;
   }
-  if (flags && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flags[0] = 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flags[0] = 0;
 
   // H stage loads.  bf16 H: instruction hq reads stage rows 4 hq + lane / 16, 16-byte chunk
   // lane % 16.  fp32 H: instruction hq reads rows 2 hq + lane / 32, four values at
@@ -384,8 +358,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     for (int t = 0; t < NR; ++t) {
       Acc<1> one;
       one.t[0] = acc.t[t];
-      epilogue_lse<1, false>(one, v0, V, n, half, row0, nullptr, nullptr, 0, nullptr, nullptr,
-                             nullptr, m_run[t], s_run[t]);
+      epilogue_lse<1>(one, v0, V, half, m_run[t], s_run[t]);
     }
     // The H stage buffer is hb[stage & 1] and the stage count restarts with every group.
     // With an odd count the group's last stage and the next group's first share buffer 0,
@@ -412,9 +385,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
 template <bool STORE>
 __global__ __launch_bounds__(256) void k_project_small_f32(
     const float* __restrict__ W, int V, int d, const float* __restrict__ H, int n_rows,
-    int n_groups, const int* __restrict__ b_off, const int* __restrict__ b_tok,
-    const int* __restrict__ tok_row, const int* __restrict__ tok_target,
-    float* __restrict__ z_tgt, float2* __restrict__ part, float* __restrict__ Z) {
+    int n_groups, int32_t* __restrict__ flags, float2* __restrict__ part, float* __restrict__ Z) {
   constexpr int KB = 16, S = 2;
   __shared__ float2 red[kWpb][32];
   __shared__ f32x16 tiles[kWpb - 1][kWave];
@@ -432,6 +403,7 @@ __global__ __launch_bounds__(256) void k_project_small_f32(
   // re-reads a valid block and is not used
   auto koff = [&](int j) { return min(wid + kWpb * j, nkb - 1) * KB; };
   float m_run = -INFINITY, s_run = 0.f;
+  if (!STORE && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flags[0] = 0;
   for (int g = g0; g < g1; ++g) {
     const int v0 = g * 32;
     const float* wp = W + (size_t)min(v0 + n, V - 1) * d + half * (KB / 2);
@@ -475,8 +447,7 @@ __global__ __launch_bounds__(256) void k_project_small_f32(
       if (STORE)
         epilogue_store<1>(sum, v0, V, n, half, row0, n_rows, Z);
       else
-        epilogue_lse<1>(sum, v0, V, n, half, row0, b_off, b_tok, rt * n_groups + g, tok_row,
-                        tok_target, z_tgt, m_run, s_run);
+        epilogue_lse<1>(sum, v0, V, half, m_run, s_run);
     }
     __syncthreads();  // tiles is rewritten for the next group
   }
@@ -517,9 +488,6 @@ hipError_t launch_project(const ScoreArgs& a) {
   const jet_problem* p = a.p;
   const Plan& pl = *a.plan;
   if (pl.variant == VAR_TILED_BF16) return launch_project_tiled(a);
-  const int* b_off = reinterpret_cast<const int*>(a.ws + pl.off_boff);
-  const int* b_tok = reinterpret_cast<const int*>(a.ws + pl.off_btok);
-  float* z_tgt = reinterpret_cast<float*>(a.ws + pl.off_ztgt);
   float2* part = reinterpret_cast<float2*>(a.ws + pl.off_part);
   dim3 grid(pl.grid_x, pl.n_rtiles), block(256);
   if (pl.variant == VAR_SMALL_BF16 && p->d % 128 == 0) {
@@ -551,26 +519,25 @@ hipError_t launch_project(const ScoreArgs& a) {
       const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
       const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
       hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, true>), grid, block, 0, a.stream,
-                         W, p->V, p->d, hhi, hlo, p->n_rows, pl.n_vgroups, b_off, b_tok,
-                         p->tok_row, p->tok_target, z_tgt, part);
+                         W, p->V, p->d, hhi, hlo, p->n_rows, pl.n_vgroups, a.flags, part);
     } else {
       const uint16_t* h = static_cast<const uint16_t*>(p->H);
       hipLaunchKernelGGL((k_project_small_bf16<kSmallNT, kSmallKB, kSmallS, false>), grid, block, 0,
-                         a.stream, W, p->V, p->d, h, nullptr, p->n_rows, pl.n_vgroups, b_off,
-                         b_tok, p->tok_row, p->tok_target, z_tgt, part);
+                         a.stream, W, p->V, p->d, h, nullptr, p->n_rows, pl.n_vgroups, a.flags,
+                         part);
     }
   } else if (pl.variant == VAR_SMALL_F32) {
     hipLaunchKernelGGL((k_project_small_f32<false>), grid, block, 0, a.stream,
                        static_cast<const float*>(p->W), p->V, p->d,
-                       static_cast<const float*>(p->H), p->n_rows, pl.n_vgroups, b_off, b_tok,
-                       p->tok_row, p->tok_target, z_tgt, part, nullptr);
+                       static_cast<const float*>(p->H), p->n_rows, pl.n_vgroups, a.flags, part,
+                       nullptr);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// Vocabulary entries per group (the bucketing unit) and workgroups of the small-row path.
+// Vocabulary entries per group and workgroups of the small-row path.
 int small_group_size(int variant, int d) {
   if (variant == VAR_SMALL_F32) return 32;
   return d % 128 == 0 ? 32 * kStreamWPB : 32 * kSmallNT;
@@ -598,7 +565,7 @@ hipError_t launch_project_store_f32(const float* Wu, int U, int d, const float* 
   const int gx = n_groups < 1 ? 1 : (n_groups < 512 ? n_groups : 512);
   dim3 grid(gx, (n_rows + 31) / 32), block(256);
   hipLaunchKernelGGL((k_project_small_f32<true>), grid, block, 0, stream, Wu, U, d, H, n_rows,
-                     n_groups, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, Z);
+                     n_groups, nullptr, nullptr, Z);
   return hipGetLastError();
 }
 

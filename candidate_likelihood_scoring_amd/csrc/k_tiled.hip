@@ -1,9 +1,10 @@
-// Large-row fused projection + online full-vocabulary logsumexp + target capture
-// (matrix-core bound when rows >> 300: 2 * rows flop per head byte).
+// Large-row fused projection + online full-vocabulary logsumexp (matrix-core bound when
+// rows >> 300: 2 * rows flop per head byte).
 //
 // Computes the same quantities as the small-row kernels (JET paper, Eq. 1-2; FastJEV
 // Sec. 3.3): z[r, v] = <H[r], W[v]> with fp32 accumulation, folded into a running
-// (max, sum of exp) per row, plus the logit of every scored (row, target) pair.
+// (max, sum of exp) per row; the scored (row, target) logits are computed after it, one
+// dot product per token (k_token_logp).
 //
 // Tiling (gfx950): a workgroup of 4 waves (one per SIMD) owns a 256-row tile of H and
 // sweeps a contiguous range of 256-entry vocabulary tiles; each wave computes a 128 x 128
@@ -96,19 +97,20 @@ __device__ __forceinline__ void tile_assign(int n_rtiles, int sr, int ss, int sp
 }
 
 // Fold the finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
-// this lane's rows and capture the logits of the tile's scored targets (fp32-H kernel,
-// 4 x 4 blocks of 32 x 32).  The shifted last vocabulary tile skips the entries before
+// this lane's rows (fp32-H kernel, 4 x 4 blocks of 32 x 32); no target logit is captured
+// (k_token_logp computes them after the projection).  The shifted last vocabulary tile skips the entries before
 // v_nom, which the previous tile counted, with a masked copy of the fold.
 __device__ __forceinline__ void tile_epilogue(
-    f32x16 (&acc)[4][4], float (&m_run)[4], float (&s_run)[4], int vt, int V, int wm, int wn,
-    int n, int h, int rt, int n_vtiles, int row0, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt) {
+    f32x16 (&acc)[4][4], float (&m_run)[4], float (&s_run)[4], int vt, int V, int wm, int h) {
   const int v_nom = vt * TBM;
   const int v0 = min(v_nom, V - TBM);
+  // each block column's accumulators stay pinned in AGPRs until its fold reads them (left
+  // free, the compiler copied them out early and spilled the next stage's loaded operands)
   if (v0 != v_nom) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
       float gm = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -132,6 +134,8 @@ __device__ __forceinline__ void tile_epilogue(
   } else {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
       float gm = m_run[nt];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -146,31 +150,6 @@ __device__ __forceinline__ void tile_epilogue(
         for (int i = 0; i < 16; ++i) ps[i & 3] += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
       s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
       m_run[nt] = gm;
-    }
-  }
-  // target capture: tokens whose (row tile, vocabulary tile) is this block tile
-  const int bkey = rt * n_vtiles + vt;
-  const int e0 = b_off[bkey], e1 = b_off[bkey + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int k = b_tok[e];
-    const int lr = (tok_row ? tok_row[k] : k) - row0;
-    const int lv = tok_target[k] - v0;
-    if (lv < 0 || lv >= TBM || lr < 0 || lr >= TBN) continue;
-    if ((lv >> 7) != wm || (lr >> 7) != wn) continue;  // wave-uniform
-    const int tmt = (lv >> 5) & 3, tnt = (lr >> 5) & 3, mm = lv & 31;
-    if (n == (lr & 31) && h == ((mm >> 2) & 1)) {
-      const int ti = ((mm >> 3) << 2) | (mm & 3);
-      float val = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          if (mt == tmt && nt == tnt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (i == ti) val = acc[mt][nt][i];
-          }
-      z_tgt[k] = val;
     }
   }
 }
@@ -207,9 +186,8 @@ template <> struct TiledShape<2> { static constexpr int BK = 32, NBUF = 3; };
 template <int NP>
 __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
-    const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
+    const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, int32_t* __restrict__ flags,
+    float2* __restrict__ part,
     int n_rtiles, int splits, int sr, int ss, int remap) {
   constexpr int BK = TiledShape<NP>::BK, NBUF = TiledShape<NP>::NBUF;
   constexpr int CH = BK / 8;          // 16-byte chunks per row per stage
@@ -229,6 +207,8 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int wm = wid & 1, wn = wid >> 1;
   const int n = lane & 31, h = lane >> 5;
+  // the first launch index clears the flag word (no launch before this kernel does)
+  if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0;
   int rt, split;
   tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
   if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
@@ -416,8 +396,7 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
       JET_STAGE((NBUF - 1) & 1, NBUF & 1, false);
     }
 
-    tile_epilogue(acc, m_run, s_run, vt, V, wm, wn, n, h, rt, n_vtiles, row0, b_off, b_tok,
-                         tok_row, tok_target, z_tgt);
+    tile_epilogue(acc, m_run, s_run, vt, V, wm, h);
   }
 #undef JET_LOAD
 #undef JET_LOADU
@@ -456,18 +435,14 @@ __device__ inline int swz16(int r) {
 }
 
 // Fold a finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
-// this lane's rows and capture the tile's scored targets (see tile_epilogue).  TWO (fp32 H
+// this lane's rows (see tile_epilogue).  TWO (fp32 H
 // as two planes): both planes' products of a row are in one accumulator, four block
 // columns per wave (64 rows).
 template <bool TWO>
 __device__ __forceinline__ void tile_epilogue16(
-    f32x4 (&acc)[8][TWO ? 4 : 8], float (&m_run)[8], float (&s_run)[8], int vt, int V, int wm, int wn,
-    int r16, int q, int rt, int n_vtiles, int row0, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt) {
+    f32x4 (&acc)[8][TWO ? 4 : 8], float (&m_run)[8], float (&s_run)[8], int vt, int V, int wm,
+    int r16, int q) {
   constexpr int NR = TWO ? 4 : 8;          // block columns of distinct rows
-  constexpr int WROWS = 16 * NR;           // rows per wave
-  constexpr int TROWS = 2 * WROWS;         // rows per block tile
   const int v_nom = vt * TBM;
   const int v0 = min(v_nom, V - TBM);
   if (v0 != v_nom) {
@@ -503,29 +478,6 @@ __device__ __forceinline__ void tile_epilogue16(
     s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     m_run[nt] = gm;
   }
-  const int bkey = rt * n_vtiles + vt;
-  const int e0 = b_off[bkey], e1 = b_off[bkey + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int k = b_tok[e];
-    const int lr = (tok_row ? tok_row[k] : k) - row0;
-    const int lv = tok_target[k] - v0;
-    if (lv < 0 || lv >= TBM || lr < 0 || lr >= TROWS) continue;
-    if ((lv >> 7) != wm || lr / WROWS != wn) continue;  // wave-uniform
-    const int tmt = (lv >> 4) & 7, tnt = (lr % WROWS) >> 4, ti = lv & 3;
-    if (r16 == (lr & 15) && q == ((lv >> 2) & 3)) {
-      float val = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NR; ++nt)
-          if (mt == tmt && nt == tnt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (i == ti) val = acc[mt][nt][i];
-          }
-      z_tgt[k] = val;
-    }
-  }
 }
 
 // TWO (fp32 H as bf16 planes hi and lo, H = hi + lo): the B tile's 256 rows are, per
@@ -537,9 +489,8 @@ __device__ __forceinline__ void tile_epilogue16(
 template <bool TWO>
 __device__ __forceinline__ void project_m16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H,
-    const uint16_t* __restrict__ Hlo, int n_rows, int n_vtiles, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
+    const uint16_t* __restrict__ Hlo, int n_rows, int n_vtiles, int32_t* __restrict__ flags,
+    float2* __restrict__ part,
     int n_rtiles, int splits, int sr, int ss, int remap) {
   constexpr int BK = 64, CH = 8, RPD = 64 / CH;
   constexpr int NR = TWO ? 4 : 8;       // block columns of distinct rows per wave
@@ -555,6 +506,8 @@ __device__ __forceinline__ void project_m16(
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid & 1, wn = wid >> 1;
   const int r16 = lane & 15, q = lane >> 4;
+  // the first launch index clears the flag word (no launch before this kernel does)
+  if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0;
   int rt, split;
   tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
   if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
@@ -705,8 +658,7 @@ __device__ __forceinline__ void project_m16(
         m_run[nt] = r.x;
         s_run[nt] = r.y;
       }
-      tile_epilogue16<TWO>(acc, m_run, s_run, vt, V, wm, wn, lane_e & 15, lane_e >> 4, rt,
-                           n_vtiles, row0, b_off, b_tok, tok_row, tok_target, z_tgt);
+      tile_epilogue16<TWO>(acc, m_run, s_run, vt, V, wm, lane_e & 15, lane_e >> 4);
 #pragma unroll
       for (int nt = 0; nt < NR; ++nt) runs[wid][nt][lane_e] = make_float2(m_run[nt], s_run[nt]);
     }
@@ -742,22 +694,19 @@ __device__ __forceinline__ void project_m16(
 
 __global__ __launch_bounds__(256, 1) void k_project_tiled_m16(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H, int n_rows,
-    int n_vtiles, const int* __restrict__ b_off, const int* __restrict__ b_tok,
-    const int* __restrict__ tok_row, const int* __restrict__ tok_target,
-    float* __restrict__ z_tgt, float2* __restrict__ part, int n_rtiles, int splits, int sr,
-    int ss, int remap) {
-  project_m16<false>(W, V, d, H, nullptr, n_rows, n_vtiles, b_off, b_tok, tok_row, tok_target,
-                     z_tgt, part, n_rtiles, splits, sr, ss, remap);
+    int n_vtiles, int32_t* __restrict__ flags, float2* __restrict__ part, int n_rtiles,
+    int splits, int sr, int ss, int remap) {
+  project_m16<false>(W, V, d, H, nullptr, n_rows, n_vtiles, flags, part, n_rtiles, splits, sr,
+                     ss, remap);
 }
 
 __global__ __launch_bounds__(256, 1) void k_project_tiled_m16x2(
     const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ Hhi,
-    const uint16_t* __restrict__ Hlo, int n_rows, int n_vtiles, const int* __restrict__ b_off,
-    const int* __restrict__ b_tok, const int* __restrict__ tok_row,
-    const int* __restrict__ tok_target, float* __restrict__ z_tgt, float2* __restrict__ part,
+    const uint16_t* __restrict__ Hlo, int n_rows, int n_vtiles, int32_t* __restrict__ flags,
+    float2* __restrict__ part,
     int n_rtiles, int splits, int sr, int ss, int remap) {
-  project_m16<true>(W, V, d, Hhi, Hlo, n_rows, n_vtiles, b_off, b_tok, tok_row, tok_target,
-                    z_tgt, part, n_rtiles, splits, sr, ss, remap);
+  project_m16<true>(W, V, d, Hhi, Hlo, n_rows, n_vtiles, flags, part, n_rtiles, splits, sr, ss,
+                    remap);
 }
 
 }  // namespace
@@ -778,9 +727,6 @@ const char* tiled_kernel_name(bool hilo, int d) {
 hipError_t launch_project_tiled(const ScoreArgs& a) {
   const jet_problem* p = a.p;
   const Plan& pl = *a.plan;
-  const int* b_off = reinterpret_cast<const int*>(a.ws + pl.off_boff);
-  const int* b_tok = reinterpret_cast<const int*>(a.ws + pl.off_btok);
-  float* z_tgt = reinterpret_cast<float*>(a.ws + pl.off_ztgt);
   float2* part = reinterpret_cast<float2*>(a.ws + pl.off_part);
   // XCD-aware placement when the split count is a multiple of 8 and there are at least 2
   // row tiles: blocks of sr row tiles x ss splits per XCD, row tiles padded to a multiple of
@@ -814,20 +760,17 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
     hipLaunchKernelGGL(k_project_tiled_m16x2, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
-                       rk, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
-                       part, R, S, sr, ss, remap);
+                       rk, pl.n_vgroups, a.flags, part, R, S, sr, ss, remap);
   } else if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
     hipLaunchKernelGGL(k_project_tiled_bf16<2>, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
-                       rk, pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt,
-                       part, R, S, sr, ss, remap);
+                       rk, pl.n_vgroups, a.flags, part, R, S, sr, ss, remap);
   } else {
     const uint16_t* H = pl.pad_h ? reinterpret_cast<const uint16_t*>(a.ws + pl.off_hpad)
                                  : static_cast<const uint16_t*>(p->H);
     hipLaunchKernelGGL(k_project_tiled_m16, grid, block, 0, a.stream, W, p->V, p->d, H, rk,
-                       pl.n_vgroups, b_off, b_tok, p->tok_row, p->tok_target, z_tgt, part, R,
-                       S, sr, ss, remap);
+                       pl.n_vgroups, a.flags, part, R, S, sr, ss, remap);
   }
   return hipGetLastError();
 }

@@ -365,20 +365,21 @@ def test_tiled_placement_sweep(jet, h_dtype, R):
 
 
 @pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
-def test_tiled_grid_bucketing(jet, h_dtype):
-    """More (row tile, vocabulary tile) buckets than one workgroup sorts in LDS, so the
-    targets are bucketed by the grid-wide launches; an out-of-range target and an
-    out-of-range row raise their flags there and leave only their own tokens NaN."""
+def test_tiled_bad_indices_many_tiles(jet, h_dtype):
+    """The tiled kernel over many (row tile, vocabulary tile) pairs (about 36 x 1,025) with
+    its tokens spread over the row tiles; an out-of-range target and an out-of-range row
+    raise their flags and leave only their own tokens NaN, every other output bit and the
+    row LSEs unchanged."""
     p = wl.make_problem(V=262147, d=128, n_q=40, K=(2, 6), lengths=(1, 4), layout="prefix",
                         seed=67, h_dtype=h_dtype, n_extra_rows=9000)
-    n_buckets = -(-p["n_rows"] // 256) * -(-p["V"] // 256)  # (128-row tiles for fp32 H: twice)
-    log(f"[gpu] grid bucketing {h_dtype} rows={p['n_rows']} V={p['V']} buckets={n_buckets}")
-    assert n_buckets > 32768
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] tiled bad indices {h_dtype} rows={p['n_rows']} V={p['V']} ({kern})")
+    assert kern in ("k_project_tiled_m16", "k_project_tiled_m16x2")
     out = _run(jet, p)
     _full_size_properties(p, out)
     rows = np.unique(np.asarray(p["tok_row"]))
     ref = jo.score(p, rows=rows)
-    log(f"[gpu] errs {compare(p, out, ref, 'grid_bucketing', sampled=True)} on {len(rows)} rows")
+    log(f"[gpu] errs {compare(p, out, ref, 'tiled_bad_indices', sampled=True)} on {len(rows)} rows")
     q = dict(p)
     q["tok_target"] = p["tok_target"].copy()
     q["tok_row"] = p["tok_row"].copy()

@@ -17,7 +17,7 @@ from candidate_likelihood_scoring_amd import _lib, api, problem  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # matrix-core path (bf16 H, 11 row tiles, grid-bucketed targets): the larger call first
+    # matrix-core path (bf16 H, 15 row tiles): the larger call first
     dict(V=20011, d=256, n_q=60, K=(2, 8), lengths=(1, 6), layout="own", seed=901,
          h_dtype="bf16", n_extra_rows=2500),
     # matrix-core path with fewer rows than one row tile (fp32 H planes zero-padded)
