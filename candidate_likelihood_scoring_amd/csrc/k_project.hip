@@ -1,13 +1,14 @@
-// Fused LM-head projection + online full-vocabulary logsumexp + target-logit capture for
-// up to 32 predictor rows per row tile ("small-row" kernel, HBM-bound on the head).
+// Fused LM-head projection + online full-vocabulary logsumexp for few predictor rows
+// ("small-row" kernels, HBM-bound on the head).
 //
 // What it computes (JET paper, Eq. 1-2; FastJEV Sec. 3.3, candidate-preserving readout):
 // for each row r of a 32-row tile and every vocabulary entry v, z[r,v] = <H[r], W[v]>
-// with fp32 accumulation on the matrix cores; the logits stay in registers.  Each wave
-// folds its logits into a running (max, sum of exp) per row, and writes the logit of
-// every scored (row, target) pair that falls in its vocabulary range ("only candidate
-// log-probabilities leave the kernel", JET Sec. on GPU scoring).  A workgroup's waves
-// merge their running states in a fixed order and store one (m, s) partial per row.
+// with fp32 accumulation on the matrix cores; the logits stay in registers and never
+// reach memory (the JET paper's GPU scoring likewise hands back only the candidates'
+// log-probabilities).  Each wave folds its logits into a running (max, sum of exp) per row;
+// a workgroup's waves merge their running states in a fixed order and store one (m, s)
+// partial per row.  The scored (row, target) logits are computed after the projection,
+// one dot product per token (k_token_logp).
 //
 // Matrix-core mapping (gfx950, 64-lane waves): the head is the A operand (vocabulary as
 // M), the hidden states are the B operand (rows as N), both K(=d)-contiguous.  One

@@ -140,12 +140,9 @@ typedef struct {
 JET_API size_t jet_score_workspace_size(const jet_problem* p);
 
 /* Enqueue the whole path: operand staging, fused projection + online full-vocabulary
- * logsumexp (logits never stored), the target logits (captured in the projection's
- * epilogue; on the streaming kernel, which serves up to 64 rows of fp32 H or 128 of bf16
- * H (more only with fewer than 256 head rows) with d % 128 == 0 and a bf16 head, one dot
- * product per token after it), the deterministic merge of the
- * per-chunk normalisers, token log-probabilities, candidate sums and per-question
- * decisions.  workspace: device memory of at least jet_score_workspace_size(p) bytes,
+ * logsumexp (logits never stored), then per token its target logit (one dot product of the
+ * operands the projection multiplies), the deterministic merge of its row's per-chunk
+ * normalisers and its log-probability, then candidate sums and per-question decisions.  workspace: device memory of at least jet_score_workspace_size(p) bytes,
  * 256-byte aligned, not shared with a concurrent call.  Results are bitwise
  * reproducible for identical inputs and do not depend on a row's position. */
 JET_API jet_status jet_score(const jet_problem* p, const jet_outputs* o, void* workspace,
