@@ -613,6 +613,20 @@ def test_empty_problem(jet, d):
     assert np.max(np.abs(out["row_lse"] - ref["lse"])) < 2e-3
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
+def test_no_rows_clears_the_flag_word(jet, w_dtype):
+    """A problem without rows (hence without tokens, candidates or questions) runs no
+    projection; the call still clears a caller's stale flag word."""
+    p = wl.make_problem(V=300, d=128, n_q=0, seed=3, w_dtype=w_dtype)
+    assert p["n_rows"] == 0
+    dp = jet.to_device(p, "cuda")
+    buf = api.alloc_outputs(api.make_problem(**dp), "cuda")
+    buf["dev_flags"].fill_(7)
+    jet.score_problem(dp, out=buf)
+    torch.cuda.synchronize()
+    assert int(buf["dev_flags"][0]) == 0
+
+
 @pytest.mark.parametrize("d", [32, 128])
 def test_bad_indices_set_flags_without_faulting(jet, d):
     """Out-of-range rows/targets and malformed offsets are bounds-checked on the device
