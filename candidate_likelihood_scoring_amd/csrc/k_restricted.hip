@@ -204,79 +204,150 @@ __global__ __launch_bounds__(256) void k_field_softmax(
   if (lane == 0) f_argmax[f] = best_j < j1 ? best_j - j0 : -1;
 }
 
-// One launch for a bf16 head (the common case: d <= 2560, at most 4096 slots): workgroup
+// One launch for a bf16 head (the common case: d <= 16384, at most 4096 slots): workgroup
 // f scores field f alone.  Its 16 waves take the field's slots in turn; for a slot, lane l
 // multiplies head row union_ids[slot_uidx[j]] by the field's hidden row at k = 512 c + 8 l
 // .. + 7 for each 512-wide chunk c (fp32 products, accumulated in k order per lane, then
-// the wave's fixed lane tree), so the logit is a full-length fp32 dot product; the hidden
-// row stays in registers for all the field's slots, and the next slot's head row is loaded
-// while the current one is summed.  Then wave 0 takes the field's softmax at T and argmax
-// (lowest index among the exact maxima).  No workgroup needs another's results.
+// the wave's fixed lane tree), so the logit is a full-length fp32 dot product.  Up to
+// d = 2560 the hidden row stays in registers for all the field's slots and the next slot's
+// head row is loaded while the current one is summed (k_restricted_fields); past that the
+// row is staged once in LDS as fp32 and each slot's head row is loaded eight chunks at a
+// time (k_restricted_fields_lds), the same products summed in the same order.  Then wave
+// 0 takes the field's softmax at T and argmax (lowest index among the exact maxima).  No
+// workgroup needs another's results.
 // Index checks: workgroup 0 checks every union id, field offset, field row and slot index
 // and stores the flag word (a plain store of the whole word: no other workgroup writes it,
 // so it needs no clearing first); each field treats its own bad indices as k_field_softmax
 // does (an id outside [0, V) reads as a zero row; a bad slot index or row gives NaN; bad
 // offsets give argmax -1).
-constexpr int kFieldWaves = 16, kFieldMaxSlots = 4096;
+constexpr int kFieldWaves = 16, kFieldMaxSlots = 4096, kFieldMaxD = 16384;
+constexpr int kFieldThreads = kFieldWaves * 64;
+
+struct FieldArgs {
+  const uint16_t* W;
+  int V, d;
+  const int* ids;
+  int n_union;
+  const void* H;
+  int n_rows;
+  const int* field_row;
+  const int* slot_off;
+  const int* slot_uidx;
+  int n_fields, n_slots;
+  float T;
+  float* slot_logit;
+  float* slot_q;
+  int* f_argmax;
+  int32_t* flags;
+};
+
+// workgroup 0: every index array checked, the flag word stored whole
+__device__ inline void fields_check(const FieldArgs& a, uint32_t* s_bits, int tid) {
+  if (tid == 0) *s_bits = 0u;
+  __syncthreads();
+  uint32_t bits = 0u;
+  for (int j = tid; j < a.n_union; j += kFieldThreads)
+    if (a.ids[j] < 0 || a.ids[j] >= a.V) bits |= JET_FLAG_BAD_UNION;
+  for (int g = tid; g < a.n_fields; g += kFieldThreads) {
+    const int lo = a.slot_off[g], hi = a.slot_off[g + 1], r = a.field_row[g];
+    if (lo < 0 || hi > a.n_slots || hi <= lo) bits |= JET_FLAG_BAD_OFFSETS;
+    else if (r < 0 || r >= a.n_rows) bits |= JET_FLAG_BAD_UNION;
+  }
+  for (int j = tid; j < a.n_slots; j += kFieldThreads)
+    if (a.slot_uidx[j] < 0 || a.slot_uidx[j] >= a.n_union) bits |= JET_FLAG_BAD_UNION;
+  if (bits) atomicOr(s_bits, bits);
+  __syncthreads();
+  if (tid == 0) a.flags[0] = (int32_t)*s_bits;
+}
+
+// head row of slot j (its union entry valid or not, its id in range or not)
+struct SlotRow {
+  const uint16_t* row;  // row 0 for an id outside [0, V); not read then
+  bool use;             // the union index is valid (else the logit is NaN)
+  bool id_ok;           // the id is in [0, V) (else the row reads as zeros)
+};
+
+__device__ inline SlotRow slot_row(const FieldArgs& a, int j) {
+  const int u = a.slot_uidx[j];
+  const bool u_ok = u >= 0 && u < a.n_union;
+  const int id = u_ok ? a.ids[u] : 0;
+  const bool id_ok = u_ok && id >= 0 && id < a.V;
+  return SlotRow{a.W + (size_t)(id_ok ? id : 0) * a.d, u_ok, id_ok};
+}
+
+// lane's share of a chunk: 8 head values times 8 hidden values, in k order
+__device__ inline float chunk_dot(const uint4& w, const float (&h)[8], float acc) {
+  const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc = fmaf(__uint_as_float(w4[e] << 16), h[2 * e], acc);
+    acc = fmaf(__uint_as_float(w4[e] & 0xffff0000u), h[2 * e + 1], acc);
+  }
+  return acc;
+}
+
+// the hidden row's 8 values at k (fp32, or bf16 widened exactly)
+template <bool HF32>
+__device__ inline void load_h8(const void* H, size_t off, float (&h)[8]) {
+  if constexpr (HF32) {
+    const float4* hp = reinterpret_cast<const float4*>(static_cast<const float*>(H) + off);
+    const float4 x0 = hp[0], x1 = hp[1];
+    h[0] = x0.x; h[1] = x0.y; h[2] = x0.z; h[3] = x0.w;
+    h[4] = x1.x; h[5] = x1.y; h[6] = x1.z; h[7] = x1.w;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(H) + off);
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[2 * e] = __uint_as_float(w4[e] << 16);
+      h[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+    }
+  }
+}
+
+// wave 0: the field's softmax at T over its K logits in s_logit, and its argmax
+__device__ inline void fields_decide(const FieldArgs& a, const float* s_logit, int f, int j0,
+                                     int K, int lane) {
+  float best = -INFINITY;
+  int bi = K;
+  for (int i = lane; i < K; i += 64) {
+    const float av = s_logit[i] / a.T;
+    if (av > best) {  // increasing i: a lane keeps its lowest index among equal values
+      best = av;
+      bi = i;
+    }
+  }
+  wave_argmax(best, bi);
+  float zs = 0.f;
+  for (int i = lane; i < K; i += 64) zs += expf(s_logit[i] / a.T - best);
+  zs = wave_sum(zs);
+  for (int i = lane; i < K; i += 64) a.slot_q[j0 + i] = expf(s_logit[i] / a.T - best) / zs;
+  if (lane == 0) a.f_argmax[f] = bi < K ? bi : -1;
+}
 
 template <bool HF32, int NC>  // NC: 512-wide chunks of k in registers (d <= 512 NC)
-__global__ __launch_bounds__(kFieldWaves * 64) void k_restricted_fields(
-    const uint16_t* __restrict__ W, int V, int d, const int* __restrict__ ids, int n_union,
-    const void* __restrict__ H, int n_rows, const int* __restrict__ field_row,
-    const int* __restrict__ slot_off, const int* __restrict__ slot_uidx, int n_fields,
-    int n_slots, float T, float* __restrict__ slot_logit, float* __restrict__ slot_q,
-    int* __restrict__ f_argmax, int32_t* __restrict__ flags) {
-  constexpr int NT = kFieldWaves * 64;
+__global__ __launch_bounds__(kFieldThreads) void k_restricted_fields(FieldArgs a) {
   __shared__ float s_logit[kFieldMaxSlots];
   __shared__ uint32_t s_bits;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int f = blockIdx.x;
-  if (f == 0) {
-    if (tid == 0) s_bits = 0u;
-    __syncthreads();
-    uint32_t bits = 0u;
-    for (int j = tid; j < n_union; j += NT)
-      if (ids[j] < 0 || ids[j] >= V) bits |= JET_FLAG_BAD_UNION;
-    for (int g = tid; g < n_fields; g += NT) {
-      const int a = slot_off[g], b = slot_off[g + 1], r = field_row[g];
-      if (a < 0 || b > n_slots || b <= a) bits |= JET_FLAG_BAD_OFFSETS;
-      else if (r < 0 || r >= n_rows) bits |= JET_FLAG_BAD_UNION;
-    }
-    for (int j = tid; j < n_slots; j += NT)
-      if (slot_uidx[j] < 0 || slot_uidx[j] >= n_union) bits |= JET_FLAG_BAD_UNION;
-    if (bits) atomicOr(&s_bits, bits);
-    __syncthreads();
-    if (tid == 0) flags[0] = (int32_t)s_bits;
-  }
-  if (f >= n_fields) return;
-  const int j0 = slot_off[f], j1 = slot_off[f + 1];
-  if (j0 < 0 || j1 > n_slots || j1 <= j0) {
-    if (tid == 0) f_argmax[f] = -1;
+  if (f == 0) fields_check(a, &s_bits, tid);
+  if (f >= a.n_fields) return;
+  const int j0 = a.slot_off[f], j1 = a.slot_off[f + 1];
+  if (j0 < 0 || j1 > a.n_slots || j1 <= j0) {
+    if (tid == 0) a.f_argmax[f] = -1;
     return;
   }
-  const int r = field_row[f];
-  const bool row_ok = r >= 0 && r < n_rows;
+  const int r = a.field_row[f];
+  const bool row_ok = r >= 0 && r < a.n_rows;
   const int K = j1 - j0;  // <= n_slots <= kFieldMaxSlots (host check)
   // the field's hidden row: lane l's 8 values of each chunk (zero past d)
   float hv[NC][8];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int k = 512 * c + 8 * lane;
-    if (row_ok && k < d) {
-      if constexpr (HF32) {
-        const float4* hp = reinterpret_cast<const float4*>(static_cast<const float*>(H) + (size_t)r * d + k);
-        const float4 x0 = hp[0], x1 = hp[1];
-        hv[c][0] = x0.x; hv[c][1] = x0.y; hv[c][2] = x0.z; hv[c][3] = x0.w;
-        hv[c][4] = x1.x; hv[c][5] = x1.y; hv[c][6] = x1.z; hv[c][7] = x1.w;
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(H) + (size_t)r * d + k);
-        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hv[c][2 * e] = __uint_as_float(w4[e] << 16);
-          hv[c][2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
-        }
-      }
+    if (row_ok && k < a.d) {
+      load_h8<HF32>(a.H, (size_t)r * a.d + k, hv[c]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) hv[c][e] = 0.f;
@@ -284,16 +355,13 @@ __global__ __launch_bounds__(kFieldWaves * 64) void k_restricted_fields(
   }
   // head row of slot j: its chunks (zero for an id outside [0, V), or past d)
   auto load_w = [&](int j, uint4 (&wv)[NC], bool& use) {
-    const int u = slot_uidx[j];
-    const bool u_ok = u >= 0 && u < n_union;
-    const int id = u_ok ? ids[u] : 0;
-    const bool id_ok = u_ok && id >= 0 && id < V;
-    use = u_ok;
-    const uint16_t* wr = W + (size_t)(id_ok ? id : 0) * d;
+    const SlotRow s = slot_row(a, j);
+    use = s.use;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int k = 512 * c + 8 * lane;
-      wv[c] = (id_ok && k < d) ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0, 0, 0, 0);
+      wv[c] = (s.id_ok && k < a.d) ? *reinterpret_cast<const uint4*>(s.row + k)
+                                   : make_uint4(0, 0, 0, 0);
     }
   };
   uint4 wv[NC], wn[NC];
@@ -305,41 +373,79 @@ __global__ __launch_bounds__(kFieldWaves * 64) void k_restricted_fields(
     if (jn < j1) load_w(jn, wn, use_n);
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint32_t w4[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(__uint_as_float(w4[e] << 16), hv[c][2 * e], acc);
-        acc = fmaf(__uint_as_float(w4[e] & 0xffff0000u), hv[c][2 * e + 1], acc);
-      }
-    }
+    for (int c = 0; c < NC; ++c) acc = chunk_dot(wv[c], hv[c], acc);
     acc = wave_sum(acc);
     const float z = (use && row_ok) ? acc : __builtin_nanf("");
     if (lane == 0) {
       s_logit[j - j0] = z;
-      slot_logit[j] = z;
+      a.slot_logit[j] = z;
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) wv[c] = wn[c];
     use = use_n;
   }
   __syncthreads();
-  if (wid != 0) return;
-  float best = -INFINITY;
-  int bi = K;
-  for (int i = lane; i < K; i += 64) {
-    const float av = s_logit[i] / T;
-    if (av > best) {  // increasing i: a lane keeps its lowest index among equal values
-      best = av;
-      bi = i;
+  if (wid == 0) fields_decide(a, s_logit, f, j0, K, lane);
+}
+
+template <bool HF32>
+__global__ __launch_bounds__(kFieldThreads) void k_restricted_fields_lds(FieldArgs a) {
+  constexpr int NB = 8;  // 512-wide chunks of a head row in flight per wave
+  __shared__ float4 s_h[kFieldMaxD / 4];
+  __shared__ float s_logit[kFieldMaxSlots];
+  __shared__ uint32_t s_bits;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int f = blockIdx.x;
+  if (f == 0) fields_check(a, &s_bits, tid);
+  if (f >= a.n_fields) return;
+  const int j0 = a.slot_off[f], j1 = a.slot_off[f + 1];
+  if (j0 < 0 || j1 > a.n_slots || j1 <= j0) {
+    if (tid == 0) a.f_argmax[f] = -1;
+    return;
+  }
+  const int r = a.field_row[f];
+  const bool row_ok = r >= 0 && r < a.n_rows;
+  const int K = j1 - j0;  // <= n_slots <= kFieldMaxSlots (host check)
+  const int d = a.d;      // <= kFieldMaxD, a multiple of 32 (host checks)
+  // the field's hidden row in LDS as fp32 (zeros for a bad row, whose logits are NaN)
+  for (int k = 8 * tid; k < d; k += 8 * kFieldThreads) {
+    float h[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (row_ok) load_h8<HF32>(a.H, (size_t)r * d + k, h);
+    s_h[k / 4] = make_float4(h[0], h[1], h[2], h[3]);
+    s_h[k / 4 + 1] = make_float4(h[4], h[5], h[6], h[7]);
+  }
+  __syncthreads();
+  const int nch = (d + 511) / 512;
+  for (int j = j0 + wid; j < j1; j += kFieldWaves) {
+    const SlotRow s = slot_row(a, j);
+    float acc = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += NB) {
+      uint4 wv[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int k = 512 * (c0 + u) + 8 * lane;
+        wv[u] = (s.id_ok && k < d) ? *reinterpret_cast<const uint4*>(s.row + k)
+                                   : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int k = 512 * (c0 + u) + 8 * lane;
+        if (k < d) {
+          const float4 x0 = s_h[k / 4], x1 = s_h[k / 4 + 1];
+          const float h[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          acc = chunk_dot(wv[u], h, acc);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    const float z = (s.use && row_ok) ? acc : __builtin_nanf("");
+    if (lane == 0) {
+      s_logit[j - j0] = z;
+      a.slot_logit[j] = z;
     }
   }
-  wave_argmax(best, bi);
-  float zs = 0.f;
-  for (int i = lane; i < K; i += 64) zs += expf(s_logit[i] / T - best);
-  zs = wave_sum(zs);
-  for (int i = lane; i < K; i += 64) slot_q[j0 + i] = expf(s_logit[i] / T - best) / zs;
-  if (lane == 0) f_argmax[f] = bi < K ? bi : -1;
+  __syncthreads();
+  if (wid == 0) fields_decide(a, s_logit, f, j0, K, lane);
 }
 
 }  // namespace
@@ -347,9 +453,9 @@ __global__ __launch_bounds__(kFieldWaves * 64) void k_restricted_fields(
 bool make_restricted_plan(const jet_restricted_problem* p, RestrictedPlan* pl) {
   const size_t elt = p->w_dtype == JET_BF16 ? 2 : 4;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  // bf16 head, d <= 2560 (the hidden row in registers without spills), at most 4096
-  // slots: one launch, a workgroup per field, no workspace but the flag word
-  pl->per_field = p->w_dtype == JET_BF16 && p->d <= 2560 && p->n_slots <= kFieldMaxSlots;
+  // bf16 head, d <= 16384 (the hidden row in registers, or in LDS past d = 2560), at
+  // most 4096 slots: one launch, a workgroup per field, no workspace but the flag word
+  pl->per_field = p->w_dtype == JET_BF16 && p->d <= kFieldMaxD && p->n_slots <= kFieldMaxSlots;
   if (pl->per_field) {
     pl->fused = false;
     pl->n_kg = 0;
@@ -397,18 +503,31 @@ static hipError_t launch_restricted_f32(const jet_restricted_problem* p, const R
 template <bool HF32>
 static hipError_t launch_fields(const jet_restricted_problem* p, const jet_restricted_outputs* o,
                                 int32_t* flags, hipStream_t stream) {
-  const dim3 grid(p->n_fields > 0 ? p->n_fields : 1), block(kFieldWaves * 64);
-#define JET_FIELDS(NC)                                                                       \
-  hipLaunchKernelGGL((k_restricted_fields<HF32, NC>), grid, block, 0, stream,                 \
-                     static_cast<const uint16_t*>(p->W), p->V, p->d, p->union_ids, p->n_union, \
-                     p->H, p->n_rows, p->field_row, p->field_slot_off, p->slot_uidx,           \
-                     p->n_fields, p->n_slots, p->T, o->slot_logit, o->slot_q, o->field_argmax, \
-                     flags)
+  const dim3 grid(p->n_fields > 0 ? p->n_fields : 1), block(kFieldThreads);
+  FieldArgs a;
+  a.W = static_cast<const uint16_t*>(p->W);
+  a.V = p->V;
+  a.d = p->d;
+  a.ids = p->union_ids;
+  a.n_union = p->n_union;
+  a.H = p->H;
+  a.n_rows = p->n_rows;
+  a.field_row = p->field_row;
+  a.slot_off = p->field_slot_off;
+  a.slot_uidx = p->slot_uidx;
+  a.n_fields = p->n_fields;
+  a.n_slots = p->n_slots;
+  a.T = p->T;
+  a.slot_logit = o->slot_logit;
+  a.slot_q = o->slot_q;
+  a.f_argmax = o->field_argmax;
+  a.flags = flags;
   if (p->d <= 1024)
-    JET_FIELDS(2);
+    hipLaunchKernelGGL((k_restricted_fields<HF32, 2>), grid, block, 0, stream, a);
+  else if (p->d <= 2560)
+    hipLaunchKernelGGL((k_restricted_fields<HF32, 5>), grid, block, 0, stream, a);
   else
-    JET_FIELDS(5);
-#undef JET_FIELDS
+    hipLaunchKernelGGL(k_restricted_fields_lds<HF32>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -252,14 +252,14 @@ typedef struct {
 } jet_restricted_outputs;
 
 /* Bytes of device workspace jet_score_restricted needs (from the scalars only; 0 when the
- * problem is invalid): a flag word, and with a bf16 head and d > 2560 or more than 4096
+ * problem is invalid): a flag word, and with a bf16 head and d > 16384 or more than 4096
  * slots the fp32 partial sums of the projection over ceil(d / 512) groups of k,
  * [groups][n_union][n_rows]; with an fp32 head, the gathered rows [n_union][d] and the
  * logits [n_rows][n_union]. */
 JET_API size_t jet_restricted_workspace_size(const jet_restricted_problem* p);
 /* Enqueue the restricted path: project the rows onto the union (a bf16 head is read
  * through union_ids directly; an fp32 head is gathered first), then each field's softmax
- * and argmax over its slots.  A bf16 head with d <= 2560 and at most 4096 slots takes one
+ * and argmax over its slots.  A bf16 head with d <= 16384 and at most 4096 slots takes one
  * launch (a workgroup per field computes its slots' logits, softmax and argmax); other
  * problems take two or three.  workspace: at least jet_restricted_workspace_size(p) bytes,
  * 256-byte aligned, not shared with a concurrent call.  Host checks return JET_E_NULL,

@@ -274,6 +274,33 @@ def test_workspace_size_is_monotone_in_problem_size(lib):
     assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
 
 
+def test_restricted_one_launch_limits(lib):
+    """The restricted plan (host-only call): a bf16 head with d <= 16384 and at most 4096
+    slots takes the one-launch per-field kernel, whose only workspace is the flag word
+    (256 bytes); past either limit, or with an fp32 head, the projection keeps its partial
+    sums (bf16 head, one [n_union][n_rows] plane per 512-wide k group) or its gathered rows
+    and logits (fp32 head) in the workspace."""
+    h = np.zeros(16, np.float32)
+
+    def need(d, n_slots, w_dtype=1, n_union=100, n_rows=32):
+        rp = _lib.JetRestrictedProblem()
+        rp.H, rp.h_dtype, rp.n_rows = h.ctypes.data, 0, n_rows
+        rp.W, rp.w_dtype, rp.V, rp.d = h.ctypes.data, w_dtype, 248320, d
+        rp.union_ids, rp.n_union = h.ctypes.data, n_union
+        rp.field_row = rp.field_slot_off = rp.slot_uidx = h.ctypes.data
+        rp.n_fields, rp.n_slots, rp.T = 32, n_slots, 2.0
+        return lib.jet_restricted_workspace_size(ctypes.byref(rp))
+
+    for d in (32, 1024, 2560, 2592, 4096, 16384):
+        assert need(d, 832) == 256, d
+    assert need(16384, 4096) == 256
+    # past the limits: 256-byte aligned partial planes, then the flag word
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need(16416, 832) == al(33 * 100 * 32 * 4) + 256
+    assert need(2560, 4097) == al(5 * 100 * 32 * 4) + 256
+    assert need(2560, 832, w_dtype=0) == al(100 * 2560 * 4) + al(100 * 32 * 4) + 256
+
+
 def test_projection_kernel_choice(lib):
     """The plan's kernel choice depends only on the problem's scalars (host-only call)."""
     from candidate_likelihood_scoring_amd import api

@@ -887,14 +887,23 @@ def test_restricted(jet, max_variant):
     # several union tiles, two row tiles with a ragged tail, d = 512 + 96 (a partial k group)
     dict(n_fields=45, V=20000, d=608, K=(1, 26), seed=7),
     dict(n_fields=40, V=3000, d=1056, K=(1, 26), seed=8, h_dtype="bf16", n_rows=33),
-    # the one-launch path at its widest (five 512-wide chunks), bf16 hidden states
+    # the one-launch path with the hidden row in registers at its widest (five 512-wide
+    # chunks), bf16 hidden states
     dict(n_fields=8, V=9000, d=2560, K=(2, 26), seed=12, h_dtype="bf16"),
-    # past its limits, the two-launch path: d above 2560, and more than 4096 slots
+    # the one-launch path with the hidden row in LDS: just past the registers; nine chunks
+    # (a second batch of head loads with one chunk); at its widest
     dict(n_fields=6, V=5000, d=2592, K=(1, 26), seed=10),
+    dict(n_fields=9, V=4000, d=4608, K=(1, 26), seed=13, h_dtype="bf16"),
+    dict(n_fields=5, V=2000, d=16384, K=(2, 26), seed=14),
+    # past its limits, the two-launch path: d above 16384, and more than 4096 slots
+    dict(n_fields=4, V=1500, d=16416, K=(2, 26), seed=15),
     dict(n_fields=200, V=30011, d=128, K=(20, 26), seed=11),
 ])
 def test_restricted_ragged(jet, case):
     rp = wl.make_restricted(T=1.7, **case)
+    one_launch = rp["w_dtype"] == "bf16" and rp["d"] <= 16384 and len(rp["field_ids"]) <= 4096
+    log(f"[gpu] restricted d={rp['d']} slots={len(rp['field_ids'])} W {rp['w_dtype']} "
+        f"H {rp['h_dtype']} ({'one launch' if one_launch else 'projection + field softmax'})")
     rd = jet.restricted_to_device(rp, "cuda")
     out = jet.to_numpy(jet.score_restricted_problem(rd))
     torch.cuda.synchronize()
@@ -926,6 +935,64 @@ def test_restricted_bad_union_id(jet):
     keep = np.repeat(~uses, np.diff(fo))
     assert np.max(np.abs(out["slot_logit"][keep] - ref["slot_logit"][keep])) <= 2e-3
     assert np.max(np.abs(out["slot_q"][keep] - ref["slot_q"][keep])) <= Q_TOL
+
+
+@pytest.mark.parametrize("case", [
+    dict(n_fields=12, V=3000, d=256, K=(3, 6), seed=21),                   # one launch, registers
+    dict(n_fields=12, V=3000, d=2048, K=(3, 6), seed=22, h_dtype="bf16"),  # one launch, registers
+    dict(n_fields=12, V=3000, d=4096, K=(3, 6), seed=23),                  # one launch, LDS
+    dict(n_fields=170, V=9000, d=128, K=(25, 26), seed=24),                # > 4096 slots
+    dict(n_fields=12, V=3000, d=96, K=(3, 6), seed=25, w_dtype="f32"),     # fp32 head
+], ids=["fields_nc2", "fields_nc5", "fields_lds", "two_launch", "f32_head"])
+def test_restricted_bad_device_indices(jet, case):
+    """Malformed indices met on the device, the same on every restricted kernel: a field
+    row outside [0, n_rows) gives NaN logits and argmax -1 for its field; a slot index
+    outside [0, n_union) gives that slot a NaN logit (the field's softmax is then NaN, and
+    its argmax is taken over the other slots); an empty field (malformed offsets) gets
+    argmax -1.  Flags: JET_FLAG_BAD_UNION | JET_FLAG_BAD_OFFSETS.  Every other field is
+    scored as usual."""
+    rp = wl.make_restricted(T=1.3, **case)
+    rd = jet.restricted_to_device(rp, "cuda")
+    fo = np.asarray(rp["field_off"])
+    f_row, f_slot, f_empty = 2, 5, 8
+    rd["field_row"][f_row] = rp["n_rows"] + 5
+    bad_j = int(fo[f_slot]) + 1
+    rd["slot_uidx"][bad_j] = len(rd["host_union"]) + 3
+    rd["field_slot_off"][f_empty + 1] = int(fo[f_empty])  # field 8 empty, field 9 widened
+    out = jet.to_numpy(jet.score_restricted_problem(rd))
+    torch.cuda.synchronize()
+    log(f"[gpu] restricted bad indices d={rp['d']} slots={len(rp['field_ids'])} W {rp['w_dtype']}: "
+        f"flags {out['dev_flags'][0]}")
+    assert out["dev_flags"][0] == 16 | 4
+    ref = jo.score_restricted(rp)
+    tl = 1e-4 if rp["w_dtype"] == "f32" else 2e-3
+    # bad row: every logit and q NaN, no decision
+    sl = slice(fo[f_row], fo[f_row + 1])
+    assert np.all(np.isnan(out["slot_logit"][sl])) and np.all(np.isnan(out["slot_q"][sl]))
+    assert out["field_argmax"][f_row] == -1
+    # bad slot index: that logit NaN, the others exact; q NaN; argmax over the others
+    sl = slice(fo[f_slot], fo[f_slot + 1])
+    lg = out["slot_logit"][sl].copy()
+    good = np.arange(lg.size) != bad_j - fo[f_slot]
+    assert np.isnan(lg[~good]).all() and not np.isnan(lg[good]).any()
+    assert np.max(np.abs(lg[good] - ref["slot_logit"][sl][good])) <= tl
+    assert np.all(np.isnan(out["slot_q"][sl]))
+    b = ref["slot_logit"][sl] / rp["T"]
+    b[~good] = -np.inf
+    top = np.sort(b)[::-1]
+    if top[0] - top[1] > 1e-3:
+        assert out["field_argmax"][f_slot] == int(np.argmax(b))
+    # empty field: no decision
+    assert out["field_argmax"][f_empty] == -1
+    # every other field as the oracle has it
+    others = [f for f in range(len(fo) - 1) if f not in (f_row, f_slot, f_empty, f_empty + 1)]
+    keep = np.repeat(np.isin(np.arange(len(fo) - 1), others), np.diff(fo))
+    assert np.max(np.abs(out["slot_logit"][keep] - ref["slot_logit"][keep])) <= tl
+    assert np.max(np.abs(out["slot_q"][keep] - ref["slot_q"][keep])) <= Q_TOL
+    sub_off = np.concatenate([[0], np.cumsum(np.diff(fo)[others])])
+    check_decisions(out["field_argmax"][others], out["slot_logit"][keep], sub_off, rp["T"],
+                    ref["field_argmax"][others], ref["field_gap"][others], ref["slot_q"][keep],
+                    f"restricted bad indices {case}")
 
 
 # ----------------------------------------------------------------------------------------
