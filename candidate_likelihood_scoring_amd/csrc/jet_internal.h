@@ -110,7 +110,7 @@ hipError_t launch_token_logp(const ScoreArgs& a);  // also clears the flag word 
 hipError_t launch_decide(const ScoreArgs& a);
 
 struct RestrictedPlan {
-  bool per_field;  // bf16 head, d <= 16384, <= 4096 slots: one launch, a workgroup per field
+  bool per_field;  // d <= 16384, <= 4096 slots: one launch, a workgroup per field
   bool fused;  // bf16 head: gather and split inside the projection, k-split partials of Z
   int n_kg;    // partial sums of Z (k groups)
   size_t off_wu, off_z, off_flags, total;

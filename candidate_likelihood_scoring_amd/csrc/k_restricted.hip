@@ -2,6 +2,8 @@
 // steps 5-6): gather only the allowed head rows, project the hidden states onto their
 // union, and let each field take a softmax over its own allowed ids at temperature T.
 //
+// d <= 16384 and at most 4096 slots, either head dtype: one launch, a workgroup per field
+// (k_restricted_fields, k_restricted_fields_lds below).  Past those limits:
 // bf16 head (two launches):
 //   k_restricted_project: Z[r, j] = <H[r], W[union_ids[j]]> on the matrix cores, fp32
 //                   accumulation, with the row gather and the fp32 split (H = hi + lo, both
@@ -204,17 +206,18 @@ __global__ __launch_bounds__(256) void k_field_softmax(
   if (lane == 0) f_argmax[f] = best_j < j1 ? best_j - j0 : -1;
 }
 
-// One launch for a bf16 head (the common case: d <= 16384, at most 4096 slots): workgroup
-// f scores field f alone.  Its 16 waves take the field's slots in turn; for a slot, lane l
-// multiplies head row union_ids[slot_uidx[j]] by the field's hidden row at k = 512 c + 8 l
-// .. + 7 for each 512-wide chunk c (fp32 products, accumulated in k order per lane, then
-// the wave's fixed lane tree), so the logit is a full-length fp32 dot product.  Up to
-// d = 2560 the hidden row stays in registers for all the field's slots and the next slot's
-// head row is loaded while the current one is summed (k_restricted_fields); past that the
-// row is staged once in LDS as fp32 and each slot's head row is loaded eight chunks at a
-// time (k_restricted_fields_lds), the same products summed in the same order.  Then wave
-// 0 takes the field's softmax at T and argmax (lowest index among the exact maxima).  No
-// workgroup needs another's results.
+// One launch for d <= 16384 and at most 4096 slots (every problem of the common shapes):
+// workgroup f scores field f alone.  Its 16 waves take the field's slots in turn; for a
+// slot, lane l multiplies head row union_ids[slot_uidx[j]] by the field's hidden row at
+// k = 512 c + 8 l .. + 7 for each 512-wide chunk c (fp32 products, accumulated in k order
+// per lane, then the wave's fixed lane tree), so the logit is a full-length fp32 dot
+// product.  A bf16 head up to d = 2560: the hidden row stays in registers for all the
+// field's slots and the next slot's head row is loaded while the current one is summed
+// (k_restricted_fields).  Past that, and for an fp32 head at any d: the row is staged once
+// in LDS as fp32 and each slot's head row is loaded eight (bf16) or four (fp32) chunks at
+// a time (k_restricted_fields_lds), the same products summed in the same order.  Then
+// wave 0 takes the field's softmax at T and argmax (lowest index among the exact maxima).
+// No workgroup needs another's results.
 // Index checks: workgroup 0 checks every union id, field offset, field row and slot index
 // and stores the flag word (a plain store of the whole word: no other workgroup writes it,
 // so it needs no clearing first); each field treats its own bad indices as k_field_softmax
@@ -224,7 +227,7 @@ constexpr int kFieldWaves = 16, kFieldMaxSlots = 4096, kFieldMaxD = 16384;
 constexpr int kFieldThreads = kFieldWaves * 64;
 
 struct FieldArgs {
-  const uint16_t* W;
+  const void* W;
   int V, d;
   const int* ids;
   int n_union;
@@ -262,20 +265,22 @@ __device__ inline void fields_check(const FieldArgs& a, uint32_t* s_bits, int ti
 
 // head row of slot j (its union entry valid or not, its id in range or not)
 struct SlotRow {
-  const uint16_t* row;  // row 0 for an id outside [0, V); not read then
-  bool use;             // the union index is valid (else the logit is NaN)
-  bool id_ok;           // the id is in [0, V) (else the row reads as zeros)
+  const char* row;  // row 0 for an id outside [0, V); not read then
+  bool use;         // the union index is valid (else the logit is NaN)
+  bool id_ok;       // the id is in [0, V) (else the row reads as zeros)
 };
 
+template <bool WF32>
 __device__ inline SlotRow slot_row(const FieldArgs& a, int j) {
   const int u = a.slot_uidx[j];
   const bool u_ok = u >= 0 && u < a.n_union;
   const int id = u_ok ? a.ids[u] : 0;
   const bool id_ok = u_ok && id >= 0 && id < a.V;
-  return SlotRow{a.W + (size_t)(id_ok ? id : 0) * a.d, u_ok, id_ok};
+  return SlotRow{static_cast<const char*>(a.W) + (size_t)(id_ok ? id : 0) * a.d * (WF32 ? 4 : 2),
+                 u_ok, id_ok};
 }
 
-// lane's share of a chunk: 8 head values times 8 hidden values, in k order
+// lane's share of a chunk: 8 head values (bf16) times 8 hidden values, in k order
 __device__ inline float chunk_dot(const uint4& w, const float (&h)[8], float acc) {
   const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -283,6 +288,15 @@ __device__ inline float chunk_dot(const uint4& w, const float (&h)[8], float acc
     acc = fmaf(__uint_as_float(w4[e] << 16), h[2 * e], acc);
     acc = fmaf(__uint_as_float(w4[e] & 0xffff0000u), h[2 * e + 1], acc);
   }
+  return acc;
+}
+
+// the same for 8 fp32 head values (two 16-byte loads)
+__device__ inline float chunk_dot_f32(const uint4& w0, const uint4& w1, const float (&h)[8],
+                                      float acc) {
+  const uint32_t w8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf(__uint_as_float(w8[e]), h[e], acc);
   return acc;
 }
 
@@ -355,12 +369,12 @@ __global__ __launch_bounds__(kFieldThreads) void k_restricted_fields(FieldArgs a
   }
   // head row of slot j: its chunks (zero for an id outside [0, V), or past d)
   auto load_w = [&](int j, uint4 (&wv)[NC], bool& use) {
-    const SlotRow s = slot_row(a, j);
+    const SlotRow s = slot_row<false>(a, j);
     use = s.use;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int k = 512 * c + 8 * lane;
-      wv[c] = (s.id_ok && k < a.d) ? *reinterpret_cast<const uint4*>(s.row + k)
+      wv[c] = (s.id_ok && k < a.d) ? *reinterpret_cast<const uint4*>(s.row + (size_t)k * 2)
                                    : make_uint4(0, 0, 0, 0);
     }
   };
@@ -388,9 +402,10 @@ __global__ __launch_bounds__(kFieldThreads) void k_restricted_fields(FieldArgs a
   if (wid == 0) fields_decide(a, s_logit, f, j0, K, lane);
 }
 
-template <bool HF32>
+template <bool WF32, bool HF32>
 __global__ __launch_bounds__(kFieldThreads) void k_restricted_fields_lds(FieldArgs a) {
-  constexpr int NB = 8;  // 512-wide chunks of a head row in flight per wave
+  constexpr int NB = WF32 ? 4 : 8;  // 512-wide chunks of a head row in flight per wave
+  constexpr int WQ = WF32 ? 2 : 1;  // 16-byte loads per lane per chunk
   __shared__ float4 s_h[kFieldMaxD / 4];
   __shared__ float s_logit[kFieldMaxSlots];
   __shared__ uint32_t s_bits;
@@ -417,15 +432,16 @@ __global__ __launch_bounds__(kFieldThreads) void k_restricted_fields_lds(FieldAr
   __syncthreads();
   const int nch = (d + 511) / 512;
   for (int j = j0 + wid; j < j1; j += kFieldWaves) {
-    const SlotRow s = slot_row(a, j);
+    const SlotRow s = slot_row<WF32>(a, j);
     float acc = 0.f;
     for (int c0 = 0; c0 < nch; c0 += NB) {
-      uint4 wv[NB];
+      uint4 wv[NB][WQ];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int k = 512 * (c0 + u) + 8 * lane;
-        wv[u] = (s.id_ok && k < d) ? *reinterpret_cast<const uint4*>(s.row + k)
-                                   : make_uint4(0, 0, 0, 0);
+        const uint4* wp = reinterpret_cast<const uint4*>(s.row + (size_t)k * (WF32 ? 4 : 2));
+#pragma unroll
+        for (int q = 0; q < WQ; ++q) wv[u][q] = (s.id_ok && k < d) ? wp[q] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
@@ -433,7 +449,10 @@ __global__ __launch_bounds__(kFieldThreads) void k_restricted_fields_lds(FieldAr
         if (k < d) {
           const float4 x0 = s_h[k / 4], x1 = s_h[k / 4 + 1];
           const float h[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          acc = chunk_dot(wv[u], h, acc);
+          if constexpr (WF32)
+            acc = chunk_dot_f32(wv[u][0], wv[u][1], h, acc);
+          else
+            acc = chunk_dot(wv[u][0], h, acc);
         }
       }
     }
@@ -453,9 +472,9 @@ __global__ __launch_bounds__(kFieldThreads) void k_restricted_fields_lds(FieldAr
 bool make_restricted_plan(const jet_restricted_problem* p, RestrictedPlan* pl) {
   const size_t elt = p->w_dtype == JET_BF16 ? 2 : 4;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  // bf16 head, d <= 16384 (the hidden row in registers, or in LDS past d = 2560), at
-  // most 4096 slots: one launch, a workgroup per field, no workspace but the flag word
-  pl->per_field = p->w_dtype == JET_BF16 && p->d <= kFieldMaxD && p->n_slots <= kFieldMaxSlots;
+  // d <= 16384 (the hidden row in registers, or in LDS), at most 4096 slots: one launch,
+  // a workgroup per field, no workspace but the flag word
+  pl->per_field = p->d <= kFieldMaxD && p->n_slots <= kFieldMaxSlots;
   if (pl->per_field) {
     pl->fused = false;
     pl->n_kg = 0;
@@ -505,7 +524,7 @@ static hipError_t launch_fields(const jet_restricted_problem* p, const jet_restr
                                 int32_t* flags, hipStream_t stream) {
   const dim3 grid(p->n_fields > 0 ? p->n_fields : 1), block(kFieldThreads);
   FieldArgs a;
-  a.W = static_cast<const uint16_t*>(p->W);
+  a.W = p->W;
   a.V = p->V;
   a.d = p->d;
   a.ids = p->union_ids;
@@ -522,12 +541,18 @@ static hipError_t launch_fields(const jet_restricted_problem* p, const jet_restr
   a.slot_q = o->slot_q;
   a.f_argmax = o->field_argmax;
   a.flags = flags;
+  if constexpr (HF32) {  // an fp32 head comes with fp32 hidden states (host check)
+    if (p->w_dtype == JET_F32) {
+      hipLaunchKernelGGL((k_restricted_fields_lds<true, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (p->d <= 1024)
     hipLaunchKernelGGL((k_restricted_fields<HF32, 2>), grid, block, 0, stream, a);
   else if (p->d <= 2560)
     hipLaunchKernelGGL((k_restricted_fields<HF32, 5>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(k_restricted_fields_lds<HF32>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((k_restricted_fields_lds<false, HF32>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -252,16 +252,17 @@ typedef struct {
 } jet_restricted_outputs;
 
 /* Bytes of device workspace jet_score_restricted needs (from the scalars only; 0 when the
- * problem is invalid): a flag word, and with a bf16 head and d > 16384 or more than 4096
- * slots the fp32 partial sums of the projection over ceil(d / 512) groups of k,
- * [groups][n_union][n_rows]; with an fp32 head, the gathered rows [n_union][d] and the
+ * problem is invalid): a flag word, and with d > 16384 or more than 4096 slots also, for a
+ * bf16 head, the fp32 partial sums of the projection over ceil(d / 512) groups of k,
+ * [groups][n_union][n_rows], and for an fp32 head the gathered rows [n_union][d] and the
  * logits [n_rows][n_union]. */
 JET_API size_t jet_restricted_workspace_size(const jet_restricted_problem* p);
-/* Enqueue the restricted path: project the rows onto the union (a bf16 head is read
- * through union_ids directly; an fp32 head is gathered first), then each field's softmax
- * and argmax over its slots.  A bf16 head with d <= 16384 and at most 4096 slots takes one
- * launch (a workgroup per field computes its slots' logits, softmax and argmax); other
- * problems take two or three.  workspace: at least jet_restricted_workspace_size(p) bytes,
+/* Enqueue the restricted path: project the rows onto the union, then each field's softmax
+ * and argmax over its slots.  A problem with d <= 16384 and at most 4096 slots takes one
+ * launch (a workgroup per field computes its slots' logits, softmax and argmax, reading the
+ * head rows through union_ids).  Larger ones take two with a bf16 head (read through
+ * union_ids by the projection) and four with an fp32 head (its union rows gathered into the
+ * workspace first).  workspace: at least jet_restricted_workspace_size(p) bytes,
  * 256-byte aligned, not shared with a concurrent call.  Host checks return JET_E_NULL,
  * JET_E_SHAPE, JET_E_DTYPE, JET_E_TEMP or JET_E_WORKSPACE and enqueue nothing.  On the
  * device an id outside [0, V) reads as a zero row and a slot index, field row or field

@@ -275,11 +275,11 @@ def test_workspace_size_is_monotone_in_problem_size(lib):
 
 
 def test_restricted_one_launch_limits(lib):
-    """The restricted plan (host-only call): a bf16 head with d <= 16384 and at most 4096
-    slots takes the one-launch per-field kernel, whose only workspace is the flag word
-    (256 bytes); past either limit, or with an fp32 head, the projection keeps its partial
-    sums (bf16 head, one [n_union][n_rows] plane per 512-wide k group) or its gathered rows
-    and logits (fp32 head) in the workspace."""
+    """The restricted plan (host-only call): d <= 16384 and at most 4096 slots take the
+    one-launch per-field kernel, whose only workspace is the flag word (256 bytes), for
+    either head dtype; past either limit the projection keeps its partial sums (bf16 head,
+    one [n_union][n_rows] plane per 512-wide k group) or its gathered rows and logits (fp32
+    head) in the workspace."""
     h = np.zeros(16, np.float32)
 
     def need(d, n_slots, w_dtype=1, n_union=100, n_rows=32):
@@ -291,14 +291,17 @@ def test_restricted_one_launch_limits(lib):
         rp.n_fields, rp.n_slots, rp.T = 32, n_slots, 2.0
         return lib.jet_restricted_workspace_size(ctypes.byref(rp))
 
-    for d in (32, 1024, 2560, 2592, 4096, 16384):
-        assert need(d, 832) == 256, d
-    assert need(16384, 4096) == 256
-    # past the limits: 256-byte aligned partial planes, then the flag word
+    for w_dtype in (1, 0):
+        for d in (32, 1024, 2560, 2592, 4096, 16384):
+            assert need(d, 832, w_dtype) == 256, (d, w_dtype)
+        assert need(16384, 4096, w_dtype) == 256
+    # past the limits: 256-byte aligned partial planes (or gathered rows and logits), then
+    # the flag word
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert need(16416, 832) == al(33 * 100 * 32 * 4) + 256
     assert need(2560, 4097) == al(5 * 100 * 32 * 4) + 256
-    assert need(2560, 832, w_dtype=0) == al(100 * 2560 * 4) + al(100 * 32 * 4) + 256
+    assert need(16416, 832, w_dtype=0) == al(100 * 16416 * 4) + al(100 * 32 * 4) + 256
+    assert need(64, 4097, w_dtype=0) == al(100 * 64 * 4) + al(100 * 32 * 4) + 256
 
 
 def test_projection_kernel_choice(lib):

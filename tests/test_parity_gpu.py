@@ -884,6 +884,8 @@ def test_restricted(jet, max_variant):
     dict(n_fields=70, V=30011, d=256, K=(1, 26), seed=4, shared_rows=True, n_rows=9),
     dict(n_fields=3, V=500, d=32, K=(2, 4), seed=5, h_dtype="bf16"),
     dict(n_fields=4, V=700, d=64, K=(1, 5), seed=6, w_dtype="f32"),
+    # an fp32 head in one launch over two batches of four chunks
+    dict(n_fields=7, V=3000, d=2560, K=(1, 26), seed=16, w_dtype="f32"),
     # several union tiles, two row tiles with a ragged tail, d = 512 + 96 (a partial k group)
     dict(n_fields=45, V=20000, d=608, K=(1, 26), seed=7),
     dict(n_fields=40, V=3000, d=1056, K=(1, 26), seed=8, h_dtype="bf16", n_rows=33),
@@ -895,13 +897,15 @@ def test_restricted(jet, max_variant):
     dict(n_fields=6, V=5000, d=2592, K=(1, 26), seed=10),
     dict(n_fields=9, V=4000, d=4608, K=(1, 26), seed=13, h_dtype="bf16"),
     dict(n_fields=5, V=2000, d=16384, K=(2, 26), seed=14),
-    # past its limits, the two-launch path: d above 16384, and more than 4096 slots
+    # past its limits, the two-launch path: d above 16384, and more than 4096 slots; with
+    # an fp32 head, gather, projection and field softmax
     dict(n_fields=4, V=1500, d=16416, K=(2, 26), seed=15),
     dict(n_fields=200, V=30011, d=128, K=(20, 26), seed=11),
+    dict(n_fields=170, V=9000, d=64, K=(25, 26), seed=17, w_dtype="f32"),
 ])
 def test_restricted_ragged(jet, case):
     rp = wl.make_restricted(T=1.7, **case)
-    one_launch = rp["w_dtype"] == "bf16" and rp["d"] <= 16384 and len(rp["field_ids"]) <= 4096
+    one_launch = rp["d"] <= 16384 and len(rp["field_ids"]) <= 4096
     log(f"[gpu] restricted d={rp['d']} slots={len(rp['field_ids'])} W {rp['w_dtype']} "
         f"H {rp['h_dtype']} ({'one launch' if one_launch else 'projection + field softmax'})")
     rd = jet.restricted_to_device(rp, "cuda")
@@ -942,8 +946,9 @@ def test_restricted_bad_union_id(jet):
     dict(n_fields=12, V=3000, d=2048, K=(3, 6), seed=22, h_dtype="bf16"),  # one launch, registers
     dict(n_fields=12, V=3000, d=4096, K=(3, 6), seed=23),                  # one launch, LDS
     dict(n_fields=170, V=9000, d=128, K=(25, 26), seed=24),                # > 4096 slots
-    dict(n_fields=12, V=3000, d=96, K=(3, 6), seed=25, w_dtype="f32"),     # fp32 head
-], ids=["fields_nc2", "fields_nc5", "fields_lds", "two_launch", "f32_head"])
+    dict(n_fields=12, V=3000, d=96, K=(3, 6), seed=25, w_dtype="f32"),     # one launch, LDS
+    dict(n_fields=170, V=9000, d=64, K=(25, 26), seed=26, w_dtype="f32"),  # > 4096 slots
+], ids=["fields_nc2", "fields_nc5", "fields_lds", "two_launch", "f32_lds", "f32_gather"])
 def test_restricted_bad_device_indices(jet, case):
     """Malformed indices met on the device, the same on every restricted kernel: a field
     row outside [0, n_rows) gives NaN logits and argmax -1 for its field; a slot index
@@ -1065,10 +1070,12 @@ def test_no_writes_past_outputs_or_workspace(jet, case):
     compare(p, out, ref, f"canary {case}")
 
 
-@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
-def test_restricted_no_writes_past_outputs_or_workspace(jet, w_dtype):
-    rp = wl.make_restricted(n_fields=45, V=20000, d=608 if w_dtype == "bf16" else 96,
-                            K=(1, 26), seed=76, w_dtype=w_dtype)
+@pytest.mark.parametrize("w_dtype,d,n_fields,K", [
+    ("bf16", 608, 45, (1, 26)), ("f32", 96, 45, (1, 26)),         # one launch
+    ("bf16", 96, 170, (25, 26)), ("f32", 96, 170, (25, 26)),      # past 4096 slots
+], ids=["bf16_one_launch", "f32_one_launch", "bf16_two_launch", "f32_gather"])
+def test_restricted_no_writes_past_outputs_or_workspace(jet, w_dtype, d, n_fields, K):
+    rp = wl.make_restricted(n_fields=n_fields, V=20000, d=d, K=K, seed=76, w_dtype=w_dtype)
     rd = jet.restricted_to_device(rp, "cuda")
     n_slots, n_f = int(rp["field_off"][-1]), len(rp["field_off"]) - 1
     f, i = torch.float32, torch.int32
