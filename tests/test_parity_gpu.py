@@ -82,6 +82,41 @@ def test_ragged(jet, case):
     log(f"[gpu] errs {compare(p, out, ref, str(case))}")
 
 
+MANY_CANDIDATES = [
+    # one question of 20,000 single-token candidates, with exact duplicates
+    dict(V=30011, d=64, n_q=1, K=20000, layout="field", seed=31, T=1.3, dups=3),
+    # questions of 1 to 200 candidates side by side (64 and fewer on their own wave, the
+    # others on the whole workgroup)
+    dict(V=30011, d=64, n_q=30, K=(1, 200), layout="field", seed=32),
+    # multi-token candidates, 40 to 400 per question, bf16 H
+    dict(V=2053, d=32, n_q=6, K=(40, 400), lengths=(1, 3), layout="prefix", seed=33,
+         h_dtype="bf16", dups=2),
+    # 40 to 130 candidates (on either side of one wave's 64), fp32 head
+    dict(V=1000, d=32, n_q=20, K=(40, 130), lengths=(1, 2), layout="own", seed=34, w_dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("case", MANY_CANDIDATES, ids=["one_20000", "mixed_200", "multi_token_400",
+                                                       "around_64"])
+def test_many_candidates(jet, case):
+    """Questions with more than 64 candidates are decided by a whole workgroup (on problems
+    where one could have more than 1,024): every output against the oracle, the tie rule on
+    exact duplicates, and the same bits on a second call."""
+    p = wl.make_problem(**case)
+    Ks = np.diff(p["q_cand_off"])
+    assert int(p["q_cand_off"][-1]) - (len(Ks) - 1) > 1024 and Ks.max() > 64  # the case's premise
+    # a true index per question, last candidate or one past 64 (q_true of the thread that
+    # holds it)
+    p["q_true_idx"] = np.where(Ks > 70, 70, Ks - 1).astype(np.int32)
+    log(f"[gpu] many candidates {case}: K per question {Ks.tolist()[:12]}")
+    out = _run(jet, p)
+    ref = jo.score(p)
+    log(f"[gpu] errs {compare(p, out, ref, str(case))}")
+    again = _run(jet, p)
+    for k in out:
+        assert np.array_equal(out[k], again[k], equal_nan=True), k
+
+
 @pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [384, 640])
 def test_stream_odd_stage_count(jet, d, h_dtype):
