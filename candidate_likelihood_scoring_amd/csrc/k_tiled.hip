@@ -438,6 +438,22 @@ __device__ inline int swz16(int r) {
 // this lane's rows (see tile_epilogue).  TWO (fp32 H
 // as two planes): both planes' products of a row are in one accumulator, four block
 // columns per wave (64 rows).
+// Clear the accumulators of block column nt once the epilogue has folded them.  The zeros
+// are written to the accumulator registers and then made opaque to the compiler, so every
+// stage of a tile, the first included, runs one loop body that accumulates in place.
+// Seeding the first stage of each tile with an inline-constant zero instead (a peeled
+// first stage) made the register allocator permute all 256 accumulators through vector
+// registers in the stage after it, every tile: 344 register moves and stalled matrix ops
+// that waited on their predecessors, 0.6% of the large-row kernel's time.
+template <bool TWO>
+__device__ __forceinline__ void zero_column(f32x4 (&acc)[8][TWO ? 4 : 8], int nt) {
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    acc[mt][nt] = f32x4{};
+    asm volatile("" : "+a"(acc[mt][nt]));
+  }
+}
+
 template <bool TWO>
 __device__ __forceinline__ void tile_epilogue16(
     f32x4 (&acc)[8][TWO ? 4 : 8], float (&m_run)[8], float (&s_run)[8], int vt, int V, int wm,
@@ -477,6 +493,7 @@ __device__ __forceinline__ void tile_epilogue16(
       for (int i = 0; i < 4; ++i) ps[i] += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
     s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     m_run[nt] = gm;
+    zero_column<TWO>(acc, nt);  // folded: the next tile accumulates from zero
   }
 }
 
@@ -596,14 +613,13 @@ __device__ __forceinline__ void project_m16(
 #define MT_(i) (TWO ? ((i) % 32) / 4 : (i) / 8)
 #define FB_(i) (TWO ? (i) % 4 + 4 * ((i) / 32) : (i) % 8)
 #define NT_(i) (TWO ? (i) % 4 : (i) % 8)
-#define JET_MSTAGE(FIRST)                                                                    \
+#define JET_MSTAGE()                                                                         \
   {                                                                                          \
     const int b_nx = bc ^ 1;                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     _Pragma("unroll") for (int i = 0; i < 64; ++i) {                                         \
       acc[MT_(i)][NT_(i)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                         \
-          fa[0][MT_(i)], fb[0][FB_(i)],                                                      \
-          ((FIRST) && (!TWO || i < 32)) ? f32x4{} : acc[MT_(i)][NT_(i)], 0, 0, 0);           \
+          fa[0][MT_(i)], fb[0][FB_(i)], acc[MT_(i)][NT_(i)], 0, 0, 0);                       \
       if (i % 4 == 0) JET_FRAG1(1, bc * BUFSZ, 1, i / 4);                                    \
       __builtin_amdgcn_sched_barrier(0);                                                     \
     }                                                                                        \
@@ -637,13 +653,13 @@ __device__ __forceinline__ void project_m16(
 #pragma unroll
   for (int jr = 0; jr < 16; ++jr) JET_FRAG1(0, 0, 0, jr);
 
+  f32x4 acc[8][NR];
+#pragma unroll
+  for (int nt = 0; nt < NR; ++nt) zero_column<TWO>(acc, nt);
   for (int vt = t0; vt < t1; ++vt) {
-    f32x4 acc[8][NR];
-    JET_MSTAGE(true);
-    JET_MSTAGE(false);
-    for (int kb = 2; kb < nk; kb += 2) {
-      JET_MSTAGE(false);
-      JET_MSTAGE(false);
+    for (int kb = 0; kb < nk; kb += 2) {
+      JET_MSTAGE();
+      JET_MSTAGE();
     }
     {
       // lane-derived values recomputed here (from the exec mask, in a form the compiler
