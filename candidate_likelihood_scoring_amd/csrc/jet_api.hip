@@ -62,6 +62,9 @@ jet_status check_problem(const jet_problem* p) {
   if (st != JET_OK) return st;
   if (p->n_tok < 0 || p->n_cand < 0 || p->n_q < 0) return JET_E_SHAPE;
   if (p->n_cand < p->n_q || p->n_tok < p->n_cand) return JET_E_SHAPE;  // K >= 1, m_c >= 1
+  // the offset arrays end at n_cand and n_tok: no candidates without questions, no tokens
+  // without candidates
+  if ((p->n_q == 0 && p->n_cand > 0) || (p->n_cand == 0 && p->n_tok > 0)) return JET_E_SHAPE;
   if (p->n_tok > 0 && p->n_rows == 0) return JET_E_SHAPE;
   if (!p->tok_row && p->n_tok > p->n_rows) return JET_E_SHAPE;
   if (p->n_rows > (1 << 21)) return JET_E_SHAPE;

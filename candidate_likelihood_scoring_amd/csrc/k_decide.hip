@@ -292,6 +292,13 @@ template <bool BIG>
 __global__ __launch_bounds__(BIG ? kDecideThreads : 256) void k_decide(DecideArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int q = blockIdx.x * 4 + wid;
+  // The ends of both offset arrays (a question's own checks see only its interior): with
+  // these and every question's and candidate's checks passed, the candidates partition the
+  // tokens and the questions partition the candidates, so every output is written.
+  if (blockIdx.x == 0 && tid == 0 &&
+      (a.q_cand_off[0] != 0 || a.q_cand_off[a.n_q] != a.n_cand || a.cand_tok_off[0] != 0 ||
+       a.cand_tok_off[a.n_cand] != a.n_tok))
+    flag_or(a.flags, JET_FLAG_BAD_OFFSETS);
   if constexpr (!BIG) {
     if (q < a.n_q) decide_question(a, q, lane);
   } else {

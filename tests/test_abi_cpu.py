@@ -188,6 +188,16 @@ def test_score_rejects_invalid_scalars_without_a_device(lib):
     p.n_cand = 0  # fewer candidates than questions: a question would be empty
     assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -2
     p.n_cand = 1
+    # the offset arrays end at n_cand and n_tok: candidates without a question, or tokens
+    # without a candidate, are a shape error
+    p.n_q = 0
+    assert lib.jet_score_workspace_size(ctypes.byref(p)) == 0
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -2
+    p.n_cand = 0
+    assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), None, 0, None) == -2
+    p.n_tok = 0
+    assert lib.jet_score_workspace_size(ctypes.byref(p)) > 0  # rows only: LSE per row
+    p.n_tok, p.n_cand, p.n_q = 1, 1, 1
     ws = np.zeros(1 << 20, np.uint8)
     mis = ws.ctypes.data + 1
     assert lib.jet_score(ctypes.byref(p), ctypes.byref(o), mis, 1 << 19, None) == -6

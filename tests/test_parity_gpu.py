@@ -699,6 +699,17 @@ def test_bad_indices_set_flags_without_faulting(jet, d):
     q["q_true_idx"] = (K + 3).astype(np.int32)
     out = _run(jet, q)
     assert out["dev_flags"][0] & 8
+    # offset arrays that do not start at 0 or end at n_cand / n_tok, every question and
+    # candidate well formed in itself: a candidate outside every question, or a token outside
+    # every candidate, raises the flag too
+    p2 = wl.make_problem(V=500, d=d, n_q=4, K=(2, 4), lengths=(2, 3), layout="own", seed=43)
+    for key, pos, delta in (("q_cand_off", 0, 1), ("q_cand_off", -1, -1),
+                            ("cand_tok_off", 0, 1), ("cand_tok_off", -1, -1)):
+        q = dict(p2)
+        q[key] = p2[key].copy()
+        q[key][pos] += delta
+        out = _run(jet, q)
+        assert out["dev_flags"][0] == 4, (key, pos, out["dev_flags"][0])
 
 
 def test_debug_validate_rejects_before_launch(jet, monkeypatch):
