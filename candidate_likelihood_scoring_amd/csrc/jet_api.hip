@@ -399,6 +399,7 @@ static jet_status check_restricted(const jet_restricted_problem* p) {
   jet_status st = check_dims(p->h_dtype, p->w_dtype, p->n_rows, p->V, p->d, p->H, p->W, p->T);
   if (st != JET_OK) return st;
   if (p->n_union < 0 || p->n_fields < 0 || p->n_slots < p->n_fields) return JET_E_SHAPE;
+  if (p->n_fields == 0 && p->n_slots > 0) return JET_E_SHAPE;  // slots outside every field
   if (p->n_fields > 0 && (p->n_union < 1 || p->n_rows < 1)) return JET_E_SHAPE;
   if (p->n_union > p->V) return JET_E_SHAPE;
   if (p->n_rows > (1 << 21)) return JET_E_SHAPE;

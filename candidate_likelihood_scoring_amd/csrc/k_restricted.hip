@@ -153,6 +153,10 @@ __global__ __launch_bounds__(256) void k_field_softmax(
     const int id = ids[j];
     if (id < 0 || id >= V) flag_or(flags, JET_FLAG_BAD_UNION);
   }
+  // the offsets' ends: with them and every field's own check, the fields partition the slots
+  if (blockIdx.x == 0 && threadIdx.x == 0 && n_fields > 0 &&
+      (slot_off[0] != 0 || slot_off[n_fields] != n_slots))
+    flag_or(flags, JET_FLAG_BAD_OFFSETS);
   const int lane = threadIdx.x & 63;
   const int f = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (f >= n_fields) return;
@@ -258,6 +262,9 @@ __device__ inline void fields_check(const FieldArgs& a, uint32_t* s_bits, int ti
   }
   for (int j = tid; j < a.n_slots; j += kFieldThreads)
     if (a.slot_uidx[j] < 0 || a.slot_uidx[j] >= a.n_union) bits |= JET_FLAG_BAD_UNION;
+  // the offsets' ends: with them and every field's own check, the fields partition the slots
+  if (tid == 0 && a.n_fields > 0 && (a.slot_off[0] != 0 || a.slot_off[a.n_fields] != a.n_slots))
+    bits |= JET_FLAG_BAD_OFFSETS;
   if (bits) atomicOr(s_bits, bits);
   __syncthreads();
   if (tid == 0) a.flags[0] = (int32_t)*s_bits;

@@ -314,6 +314,23 @@ def test_restricted_one_launch_limits(lib):
     assert need(64, 4097, w_dtype=0) == al(100 * 64 * 4) + al(100 * 32 * 4) + 256
 
 
+def test_restricted_slots_without_fields_rejected(lib):
+    """The field offsets end at n_slots, so slots without a field are a shape error (host
+    check, no device needed); no slots and no fields is a valid empty problem."""
+    h = np.zeros(16, np.float32)
+    rp = _lib.JetRestrictedProblem()
+    rp.H, rp.h_dtype, rp.n_rows = h.ctypes.data, 0, 4
+    rp.W, rp.w_dtype, rp.V, rp.d = h.ctypes.data, 1, 1000, 64
+    rp.union_ids, rp.n_union = h.ctypes.data, 3
+    rp.field_row = rp.field_slot_off = rp.slot_uidx = h.ctypes.data
+    rp.n_fields, rp.n_slots, rp.T = 0, 3, 1.0
+    assert lib.jet_restricted_workspace_size(ctypes.byref(rp)) == 0
+    ro = _lib.JetRestrictedOutputs()
+    assert lib.jet_score_restricted(ctypes.byref(rp), ctypes.byref(ro), None, 0, None) == -2
+    rp.n_slots = 0
+    assert lib.jet_restricted_workspace_size(ctypes.byref(rp)) > 0
+
+
 def test_projection_kernel_choice(lib):
     """The plan's kernel choice depends only on the problem's scalars (host-only call)."""
     from candidate_likelihood_scoring_amd import api

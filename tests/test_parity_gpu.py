@@ -1046,6 +1046,25 @@ def test_restricted_bad_device_indices(jet, case):
                     f"restricted bad indices {case}")
 
 
+@pytest.mark.parametrize("case", [
+    dict(n_fields=12, V=3000, d=256, K=(3, 6), seed=21),
+    dict(n_fields=12, V=3000, d=4096, K=(3, 6), seed=23),
+    dict(n_fields=170, V=9000, d=128, K=(25, 26), seed=24),
+    dict(n_fields=170, V=9000, d=64, K=(25, 26), seed=26, w_dtype="f32"),
+], ids=["fields_nc2", "fields_lds", "two_launch", "f32_gather"])
+def test_restricted_offset_ends_flagged(jet, case):
+    """Field offsets that do not start at 0 or end at n_slots, every field well formed in
+    itself (a slot outside every field): JET_FLAG_BAD_OFFSETS alone, on every restricted
+    kernel."""
+    rp = wl.make_restricted(**case)
+    for pos, delta in ((0, 1), (-1, -1)):
+        rd = jet.restricted_to_device(rp, "cuda")
+        rd["field_slot_off"][pos] += delta
+        out = jet.to_numpy(jet.score_restricted_problem(rd))
+        torch.cuda.synchronize()
+        assert out["dev_flags"][0] == 4, (case, pos, out["dev_flags"][0])
+
+
 # ----------------------------------------------------------------------------------------
 # no stray writes: outputs and workspace padded with a canary that must survive the call
 # ----------------------------------------------------------------------------------------
