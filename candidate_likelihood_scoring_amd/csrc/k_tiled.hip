@@ -10,23 +10,20 @@
 // sweeps a contiguous range of 256-entry vocabulary tiles; each wave computes a 128 x 128
 // quadrant (vocabulary x rows), 256 fp32 accumulators per lane (all AGPRs).  The stages of
 // all the range's vocabulary tiles form one stream, so the next tile's first stages are in
-// flight during an epilogue.  Three kernels:
+// flight during an epilogue.  Two kernels, d any multiple of 64 (64-wide stages, odd
+// counts included):
 //  * k_project_tiled_m16 (bf16 H): 8 x 8 blocks of v_mfma_f32_16x16x32_bf16 per wave;
-//    64-wide stages loaded by the buffer unit straight into two LDS buffers; one barrier
-//    per stage, at its midpoint (see the kernel);
-//  * k_project_tiled_m16x2 (fp32 H as two bf16 planes, hi + lo, d a multiple of 128): the
-//    same kernel with the hi and lo rows of 128 rows as its 256 B-operand rows, both
-//    products of a row accumulated into one accumulator;
-//  * k_project_tiled_bf16 (fp32 H as two planes, d a multiple of 64 only): 4 x 4 blocks of
-//    v_mfma_f32_32x32x16_bf16 per wave, each product issued for hi and lo; 32-wide stages
-//    staged through two register sets into a ring of three LDS buffers.
-// In all, every MFMA is followed by at most one memory instruction (fragment read, LDS
-// write or global load), so with one wave per SIMD the memory traffic overlaps the matrix
-// core instead of stalling its issue in bursts.  The last vocabulary tile (and row tile) is
-// shifted back to end exactly at V (n_rows), so every load is in bounds; the overlap is
-// masked in the epilogue and only the tile's own rows are reported.  LDS chunk (row r,
-// 16-byte chunk c) lives at r * CH + (c ^ f(r)), which keeps the row-wise writes and the
-// fragment reads conflict-free.
+//    stages loaded by the buffer unit straight into two LDS buffers; one barrier per
+//    stage, at its midpoint (see the kernel);
+//  * k_project_tiled_m16x2 (fp32 H as two bf16 planes, hi + lo): the same kernel with the
+//    hi and lo rows of 128 rows as its 256 B-operand rows, both products of a row
+//    accumulated into one accumulator.
+// Every MFMA is followed by at most one memory instruction (fragment read or load), so with
+// one wave per SIMD the memory traffic overlaps the matrix core instead of stalling its
+// issue in bursts.  The last vocabulary tile (and row tile) is shifted back to end exactly
+// at V (n_rows), so every load is in bounds; the overlap is masked in the epilogue and only
+// the tile's own rows are reported.  LDS chunk (row r, 16-byte chunk c) lives at
+// r * 8 + (c ^ swz16(r)), which keeps the fragment reads free of bank conflicts.
 //
 // Workgroup placement: workgroup L runs on XCD L % 8, and each XCD runs about 32 at a time
 // (one per CU).  Launch index L is remapped so that those 32 form an SR x SS block of
@@ -40,23 +37,8 @@ namespace {
 constexpr int TBM = 256;  // vocabulary entries per block tile
 constexpr int TBN = 256;  // rows per block tile
 
-__device__ inline int tm_of(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
-
-// XOR swizzle of 16-byte chunks, a function of row & 15 only: 16 consecutive rows read at
-// one chunk land in 16 different 16-byte bank groups, every aligned 8 rows in 8 different
-// ones, and 32-row tiles 32 * CH apart share one swizzle (so their addresses differ by an
-// immediate offset).
-template <int CH>
-__device__ inline int swz(int r) {
-  return CH == 8 ? ((r ^ ((r >> 3) & 1)) & 7) : (((r >> 1) ^ (r >> 2)) & 3);
-}
-
 __device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ inline u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
 // Load 16 bytes per lane straight into LDS: lane l's bytes land at LDS byte address
@@ -96,319 +78,6 @@ __device__ __forceinline__ void tile_assign(int n_rtiles, int sr, int ss, int sp
   split = js * ss + w % ss;
 }
 
-// Fold the finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
-// this lane's rows (fp32-H kernel, 4 x 4 blocks of 32 x 32); no target logit is captured
-// (k_token_logp computes them after the projection).  The shifted last vocabulary tile skips the entries before
-// v_nom, which the previous tile counted, with a masked copy of the fold.
-__device__ __forceinline__ void tile_epilogue(
-    f32x16 (&acc)[4][4], float (&m_run)[4], float (&s_run)[4], int vt, int V, int wm, int h) {
-  const int v_nom = vt * TBM;
-  const int v0 = min(v_nom, V - TBM);
-  // each block column's accumulators stay pinned in AGPRs until its fold reads them (left
-  // free, the compiler copied them out early and spilled the next stage's loaded operands)
-  if (v0 != v_nom) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
-      float gm = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom) gm = fmaxf(gm, acc[mt][nt][i]);
-      const float mn = fmaxf(m_run[nt], gm);
-      if (mn != -INFINITY) {
-        const float mb = mn * kLog2e;
-        float sum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (v0 + wm * 128 + mt * 32 + tm_of(i, h) >= v_nom)
-              sum += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
-        s_run[nt] = s_run[nt] * exp2f((m_run[nt] - mn) * kLog2e) + sum;
-        m_run[nt] = mn;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt][nt]));
-      float gm = m_run[nt];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) gm = fmaxf(gm, acc[mt][nt][i]);
-      const float mb = gm == -INFINITY ? 0.f : gm * kLog2e;
-      // four partial sums, so that consecutive exponentials do not wait on one another
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ps[i & 3] += exp2_hw(fmaf(acc[mt][nt][i], kLog2e, -mb));
-      s_run[nt] = s_run[nt] * exp2_hw(m_run[nt] * kLog2e - mb) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-      m_run[nt] = gm;
-    }
-  }
-}
-
-// Merge lane halves, then the two vocabulary halves (wm = 0 then 1) of each row, and write
-// the tile's (max, sum) partial for its own rows.
-__device__ __forceinline__ void tile_finish(float (&m_run)[4], float (&s_run)[4],
-                                            float2 (&red)[2][TBN], int tid, int wm, int wn, int n,
-                                            int h, int row0, int row_nom, int split, int n_rows,
-                                            float2* __restrict__ part) {
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const float m2 = __shfl_xor(m_run[nt], 32), s2 = __shfl_xor(s_run[nt], 32);
-    lse_merge(m_run[nt], s_run[nt], m2, s2);
-    if (h == 0) red[wm][wn * 128 + nt * 32 + n] = make_float2(m_run[nt], s_run[nt]);
-  }
-  __syncthreads();
-  {
-    const int r = tid;  // 256 threads, 256 rows
-    float m = red[0][r].x, s = red[0][r].y;
-    lse_merge(m, s, red[1][r].x, red[1][r].y);
-    const int row = row0 + r;
-    if (row >= row_nom) part[(size_t)split * n_rows + row] = make_float2(m, s);
-  }
-}
-
-// Stage shape of the fp32-H kernel: a stage is BK = 32 columns of K for the 256-row head
-// tile and the two 256-row hidden-state planes: CH = BK / 8 16-byte chunks per row, so one
-// load round of 256 threads covers RPI = 256 / CH rows with CH lanes per contiguous row
-// segment.  Three 48 KB buffers fill the LDS ring.
-template <int NP> struct TiledShape;
-template <> struct TiledShape<2> { static constexpr int BK = 32, NBUF = 3; };
-
-template <int NP>
-__global__ __launch_bounds__(256, 1) void k_project_tiled_bf16(
-    const uint16_t* __restrict__ W, int V, int d, const uint16_t* __restrict__ H0,
-    const uint16_t* __restrict__ H1, int n_rows, int n_vtiles, int32_t* __restrict__ flags,
-    float2* __restrict__ part,
-    int n_rtiles, int splits, int sr, int ss, int remap) {
-  constexpr int BK = TiledShape<NP>::BK, NBUF = TiledShape<NP>::NBUF;
-  constexpr int CH = BK / 8;          // 16-byte chunks per row per stage
-  constexpr int KK = BK / 16;         // MFMA k sub-steps per stage
-  constexpr int RPI = 256 / CH;       // tile rows covered by one load round of 256 threads
-  constexpr int LA = TBM / RPI;       // head loads per thread per stage
-  constexpr int LB = TBN / RPI;       // hidden-state loads per plane per thread per stage
-  constexpr int ASZ = TBM * CH;       // 16-byte slots per operand plane per buffer
-  constexpr int BUFSZ = ASZ * (1 + NP);
-  constexpr int NST = LA + NP * LB;   // loads (and LDS stores) per thread per stage
-  constexpr int NRD = 4 + 4 * NP;     // fragment reads per sub-step
-  static_assert((NBUF == 2 || NBUF == 3) && KK % 2 == 0, "stage layout");
-  static_assert(NRD + 2 * ((NST + KK - 1) / KK) <= 16 * NP, "every memory slot needs an MFMA");
-  __shared__ u32x4 lds[NBUF * BUFSZ];
-  __shared__ float2 red[2][TBN];
-
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  const int wm = wid & 1, wn = wid >> 1;
-  const int n = lane & 31, h = lane >> 5;
-  // the first launch index clears the flag word (no launch before this kernel does)
-  if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0;
-  int rt, split;
-  tile_assign(n_rtiles, sr, ss, splits, remap, rt, split);
-  if (rt >= n_rtiles || split >= splits) return;  // padding of the XCD-aware launch
-  const int row_nom = rt * TBN;                    // first row this tile reports
-  const int row0 = min(row_nom, n_rows - TBN);     // rows loaded: [row0, row0 + 256), all valid
-  // consecutive ranges of L tiles (see the split choice); trailing ranges may be empty
-  const int L = (n_vtiles + splits - 1) / splits;
-  const int t0 = min(split * L, n_vtiles);
-  const int t1 = min(t0 + L, n_vtiles);
-  const int nk = d / BK;                           // even
-  const uint32_t rowb = (uint32_t)d * 2;           // bytes per row (head and H planes)
-
-  // load-side mapping: thread tid loads chunk tid % CH of tile rows tid / CH + i * RPI
-  const int lr0 = tid / CH, lc = tid % CH;
-  const uint32_t lvoff = (uint32_t)lr0 * rowb + lc * 16;
-  // Buffer resources based at this workgroup's first H row and first head row, so that
-  // every offset is local to its own tiles (32 bits suffice whatever the operand sizes):
-  // H rows [row0, row0 + 256), head rows [vbase, vend) covering every tile of the range
-  // (a tile starts at min(t * 256, V - 256); an empty range still loads one tile).
-  const int vbase = min(t0 * TBM, V - TBM);
-  const int vend = max(min(t1 * TBM, V), vbase + TBM);
-  const __amdgpu_buffer_rsrc_t rH0 = rsrc_of(H0 + (size_t)row0 * d, (uint32_t)TBN * rowb);
-  const __amdgpu_buffer_rsrc_t rH1 =
-      rsrc_of((NP == 2 ? H1 : H0) + (size_t)row0 * d, (uint32_t)TBN * rowb);
-  const __amdgpu_buffer_rsrc_t rW = rsrc_of(W + (size_t)vbase * d, (uint32_t)(vend - vbase) * rowb);
-  const uint32_t hrow = 0;
-  // LDS write slot: rows lr0 + i * RPI share row & 15, hence one swizzle
-  const int wslot = lr0 * CH + (lc ^ swz<CH>(lr0));
-  // fragment read slots of sub-step kk: row (wm|wn)*128 + t*32 + n, chunk 2 kk + h
-  int ra_slot[KK], rb_slot[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    ra_slot[kk] = (wm * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
-    rb_slot[kk] = ASZ + (wn * 128 + n) * CH + ((2 * kk + h) ^ swz<CH>(n));
-  }
-
-  float m_run[4], s_run[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    m_run[nt] = -INFINITY;
-    s_run[nt] = 0.f;
-  }
-
-  // The stages of all vocabulary tiles of this split form one stream g = 0 .. G - 1
-  // (tile t0 + g / nk, k block g % nk).  Two register sets: at the top of stage g, stage
-  // g + NBUF - 1 (loaded during the previous stage) sits in one set and is written to LDS
-  // buffer (g + NBUF - 1) % NBUF during stage g, while stage g + NBUF is loaded into the
-  // other.  With three buffers, buffer (g + 1) % 3 was completed before the previous
-  // barrier, so the first fragments of stage g + 1 are read before this stage's barrier;
-  // with two they are read right after it.  Past the end the cursor repeats the last stage
-  // (in bounds; never consumed).
-  const int G = (t1 - t0) * nk;
-  int lt = t0, lk = 0, lg = 0;  // load cursor: tile, k block, stream index
-  u32x4 ra[2][LA], rb[2][NP][LB];
-  uint32_t l_ws = 0, l_hs = 0;  // byte offsets of the stage being loaded
-#define JET_CURSOR()                                                                         \
-  {                                                                                          \
-    const uint32_t ko = (uint32_t)lk * (BK * 2);                                             \
-    l_ws = __builtin_amdgcn_readfirstlane((uint32_t)(min(lt * TBM, V - TBM) - vbase) * rowb + ko); \
-    l_hs = __builtin_amdgcn_readfirstlane(hrow + ko);                                        \
-    if (lg + 1 < G) {                                                                        \
-      ++lg;                                                                                  \
-      if (++lk == nk) {                                                                      \
-        lk = 0;                                                                              \
-        ++lt;                                                                                \
-      }                                                                                      \
-    }                                                                                        \
-  }
-  // loads u in [U0, U1) of the stage at the cursor into register set SET (u < LA: head
-  // rows, else plane (u - LA) / LB of the hidden states)
-#define JET_LOADU(SET, U0, U1)                                                               \
-  {                                                                                          \
-    _Pragma("unroll") for (int u = (U0); u < (U1); ++u) {                                    \
-      if (u < LA) ra[SET][u] = bload(rW, lvoff, l_ws + u * RPI * rowb);                      \
-      else                                                                                   \
-        rb[SET][(u - LA) / LB][(u - LA) % LB] =                                              \
-            bload((u - LA) / LB ? rH1 : rH0, lvoff, l_hs + ((u - LA) % LB) * RPI * rowb);    \
-    }                                                                                        \
-  }
-#define JET_LOAD(SET)                                                                        \
-  {                                                                                          \
-    JET_CURSOR();                                                                            \
-    JET_LOADU(SET, 0, NST);                                                                  \
-  }
-  // stores u in [U0, U1) of register set SET into the buffer at slot offset BOFF
-#define JET_STORE(SET, BOFF, U0, U1)                                                         \
-  {                                                                                          \
-    _Pragma("unroll") for (int u = (U0); u < (U1); ++u) {                                    \
-      if (u < LA) lds[(BOFF) + wslot + u * RPI * CH] = ra[SET][u];                           \
-      else                                                                                   \
-        lds[(BOFF) + ASZ * (1 + (u - LA) / LB) + wslot + ((u - LA) % LB) * RPI * CH] =        \
-            rb[SET][(u - LA) / LB][(u - LA) % LB];                                           \
-    }                                                                                        \
-  }
-  bf16x8 fa[2][4], fb[2][NP][4];
-  // fragment read jr (0 .. NRD - 1) of sub-step KK_ into set F, in order of first use:
-  // a0, all b, a1, a2, a3
-#define JET_FRAG1(F, BOFF, KK_, JR)                                                          \
-  {                                                                                          \
-    if ((JR) == 0) {                                                                         \
-      fa[F][0] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_]]);                     \
-    } else if ((JR) <= 4 * NP) {                                                             \
-      const int pb = ((JR) - 1) % NP, tb = ((JR) - 1) / NP;                                  \
-      fb[F][pb][tb] =                                                                        \
-          __builtin_bit_cast(bf16x8, lds[(BOFF) + pb * ASZ + rb_slot[KK_] + tb * 32 * CH]);  \
-    } else {                                                                                 \
-      const int ta = (JR) - 4 * NP;                                                          \
-      fa[F][ta] = __builtin_bit_cast(bf16x8, lds[(BOFF) + ra_slot[KK_] + ta * 32 * CH]);     \
-    }                                                                                        \
-  }
-#define JET_FRAGS(F, BOFF, KK_)                                                              \
-  {                                                                                          \
-    _Pragma("unroll") for (int jr_ = 0; jr_ < NRD; ++jr_) JET_FRAG1(F, BOFF, KK_, jr_);      \
-  }
-  // One stage in issue order.  Sub-step kk runs 16 NP MFMAs from fragment set kk & 1
-  // (vocabulary tile i / (4 NP), row tile (i / NP) % 4, plane i % NP); MFMA i is followed
-  // by memory slot i: first the fragment reads of the next sub-step (set (kk + 1) & 1; for
-  // the last sub-step those of the next stage, with three buffers) with this sub-step's
-  // share of the LDS stores spread evenly among them, then its share of the loads.
-  // SLOAD / SSTORE: the register sets being loaded / stored.  FIRST: the first stage of a
-  // vocabulary tile, whose first MFMA per accumulator block starts from zero.
-#define JET_STAGE(SLOAD, SSTORE, FIRST)                                                      \
-  {                                                                                          \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
-    JET_CURSOR();                                                                            \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
-    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                      \
-      const int u0 = kk * NST / KK, nu = (kk + 1) * NST / KK - u0;                           \
-      const int nrd = (kk + 1 < KK || NBUF == 3) ? NRD : 0;                                  \
-      const int nls = nrd + nu; /* LDS slots */                                              \
-      _Pragma("unroll") for (int i = 0; i < 16 * NP; ++i) {                                  \
-        acc[i / (4 * NP)][(i / NP) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(            \
-            fa[kk & 1][i / (4 * NP)], fb[kk & 1][i % NP][(i / NP) % 4],                      \
-            (FIRST) && kk == 0 && i % NP == 0 ? f32x16{} : acc[i / (4 * NP)][(i / NP) % 4], 0, \
-            0, 0);                                                                           \
-        if (i < nls) {                                                                       \
-          const int nwb = (i * nu) / nls;                                                    \
-          if (((i + 1) * nu) / nls > nwb) {                                                  \
-            JET_STORE(SSTORE, b_st, u0 + nwb, u0 + nwb + 1);                                 \
-          } else if (kk + 1 < KK) {                                                          \
-            JET_FRAG1((kk + 1) & 1, b_cur, kk + 1, i - nwb);                                 \
-          } else {                                                                           \
-            JET_FRAG1(0, b_nxt, 0, i - nwb);                                                 \
-          }                                                                                  \
-        } else if (i - nls < nu) {                                                           \
-          JET_LOADU(SLOAD, u0 + i - nls, u0 + i - nls + 1);                                  \
-        }                                                                                    \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
-      }                                                                                      \
-    }                                                                                        \
-    __syncthreads();                                                                         \
-    if (NBUF == 3) {                                                                         \
-      const int b_old = b_cur;                                                               \
-      b_cur = b_nxt;                                                                         \
-      b_nxt = b_st;                                                                          \
-      b_st = b_old;                                                                          \
-    } else {                                                                                 \
-      const int b_old = b_cur;                                                               \
-      b_cur = b_st;                                                                          \
-      b_st = b_old;                                                                          \
-      JET_FRAGS(0, b_cur, 0);                                                                \
-      __builtin_amdgcn_sched_barrier(0);                                                     \
-    }                                                                                        \
-  }
-
-  // prologue: stages 0 .. NBUF - 2 into buffers 0 .. NBUF - 2, stage NBUF - 1 in flight
-  JET_LOAD(0);
-  JET_STORE(0, 0, 0, NST);
-  if (NBUF == 3) {
-    JET_LOAD(1);
-    JET_STORE(1, BUFSZ, 0, NST);
-  }
-  JET_LOAD((NBUF - 1) & 1);
-  __syncthreads();
-  // slot offsets of the buffers of stages g, g + 1 (three buffers) and g + NBUF - 1
-  int b_cur = 0, b_nxt = BUFSZ, b_st = (NBUF - 1) * BUFSZ;
-  JET_FRAGS(0, b_cur, 0);
-
-  for (int vt = t0; vt < t1; ++vt) {
-    f32x16 acc[4][4];
-    JET_STAGE(NBUF & 1, (NBUF - 1) & 1, true);    // stage g even, first of the tile
-    JET_STAGE((NBUF - 1) & 1, NBUF & 1, false);   // stage g odd
-    for (int kb = 2; kb < nk; kb += 2) {
-      JET_STAGE(NBUF & 1, (NBUF - 1) & 1, false);
-      JET_STAGE((NBUF - 1) & 1, NBUF & 1, false);
-    }
-
-    tile_epilogue(acc, m_run, s_run, vt, V, wm, h);
-  }
-#undef JET_LOAD
-#undef JET_LOADU
-#undef JET_CURSOR
-#undef JET_STORE
-#undef JET_FRAGS
-#undef JET_STAGE
-#undef JET_FRAG1
-
-  tile_finish(m_run, s_run, red, tid, wm, wn, n, h, row0, row_nom, split, n_rows, part);
-}
-
 // ------------------------------------------------------------------------------------
 // bf16 hidden states on v_mfma_f32_16x16x32_bf16.  A stage is 64 columns of K for the
 // 256-row head tile and the 256-row hidden-state tile (8 chunks of 16 bytes per row), two
@@ -434,10 +103,6 @@ __device__ inline int swz16(int r) {
   return (((r >> 2) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 1) & 1);
 }
 
-// Fold a finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
-// this lane's rows (see tile_epilogue).  TWO (fp32 H
-// as two planes): both planes' products of a row are in one accumulator, four block
-// columns per wave (64 rows).
 // Clear the accumulators of block column nt once the epilogue has folded them.  The zeros
 // are written to the accumulator registers and then made opaque to the compiler, so every
 // stage of a tile, the first included, runs one loop body that accumulates in place.
@@ -454,6 +119,11 @@ __device__ __forceinline__ void zero_column(f32x4 (&acc)[8][TWO ? 4 : 8], int nt
   }
 }
 
+// Fold a finished block tile (vocabulary tile vt) into the running (max, sum of exp) of
+// this lane's rows; no target logit is captured (k_token_logp computes them after the
+// projection).  TWO (fp32 H as two planes): both planes' products of a row are in one
+// accumulator, four block columns per wave (64 rows).  The shifted last vocabulary tile
+// masks the entries before v_nom, which the previous tile counted.
 template <bool TWO>
 __device__ __forceinline__ void tile_epilogue16(
     f32x4 (&acc)[8][TWO ? 4 : 8], float (&m_run)[8], float (&s_run)[8], int vt, int V, int wm,
@@ -534,7 +204,7 @@ __device__ __forceinline__ void project_m16(
   const int L = (n_vtiles + splits - 1) / splits;
   const int t0 = min(split * L, n_vtiles);
   const int t1 = min(t0 + L, n_vtiles);
-  const int nk = d / BK;  // even
+  const int nk = d / BK;  // d is a multiple of BK
   const uint32_t rowb = (uint32_t)d * 2;
   // Buffer resources based at this workgroup's first H row and first head row, so that
   // every offset is local to its own tiles (32 bits suffice whatever the operand sizes):
@@ -657,10 +327,13 @@ __device__ __forceinline__ void project_m16(
 #pragma unroll
   for (int nt = 0; nt < NR; ++nt) zero_column<TWO>(acc, nt);
   for (int vt = t0; vt < t1; ++vt) {
-    for (int kb = 0; kb < nk; kb += 2) {
+    // two stages per trip (the buffer index alternates at run time, so an odd count only
+    // adds one stage after the loop)
+    for (int kb = 0; kb + 1 < nk; kb += 2) {
       JET_MSTAGE();
       JET_MSTAGE();
     }
+    if (nk & 1) JET_MSTAGE();
     {
       // lane-derived values recomputed here (from the exec mask, in a form the compiler
       // cannot hoist) instead of being kept live across the stage loop: a spill reload
@@ -727,17 +400,14 @@ __global__ __launch_bounds__(256, 1) void k_project_tiled_m16x2(
 
 }  // namespace
 
-// d must be a multiple of two stages (the stage loop is unrolled by two)
-int tiled_bk(bool hilo) { return hilo ? 2 * TiledShape<2>::BK : 128; }
+// d must be a whole number of 64-wide stages
+int tiled_bk(bool hilo) { return 64; }
 
-// fp32 H runs on the 16 x 16 kernel's two-plane form when d allows its 64-wide stages
-static bool tiled_two_plane_m16(bool hilo, int d) { return hilo && d % 128 == 0; }
-
-int tiled_row_tile(bool hilo, int d) { return tiled_two_plane_m16(hilo, d) ? 128 : TBN; }
+// fp32 H runs as two bf16 planes, 128 real rows per block tile
+int tiled_row_tile(bool hilo, int d) { return hilo ? 128 : TBN; }
 
 const char* tiled_kernel_name(bool hilo, int d) {
-  if (tiled_two_plane_m16(hilo, d)) return "k_project_tiled_m16x2";
-  return hilo ? "k_project_tiled_bf16" : "k_project_tiled_m16";
+  return hilo ? "k_project_tiled_m16x2" : "k_project_tiled_m16";
 }
 
 hipError_t launch_project_tiled(const ScoreArgs& a) {
@@ -750,10 +420,10 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   // Otherwise the plain order P = rt * S + split.  One row tile has no head tile for a block
   // to share, and padding it to a block left 3 of 4 workgroups empty: 467 -> 352 us at
   // 256 rows, V = 248,320, d = 2560.  With 2 or 3 row tiles the blocks' sharing of each head
-  // tile in L2 outweighs their padding (629 against 677 us at 384 rows).  bf16 H takes 8 x 4 blocks (each head tile shared 8 ways; 2%
-  // faster than 4 x 8 on large_batch) when that pads at most 1/16 of the row tiles; the
-  // two-plane kernels, whose H tiles hold two planes, take 4 x 8 (with 8 x 4 they were no
-  // faster at 32 row tiles and 7% slower at 64).
+  // tile in L2 outweighs their padding (629 against 677 us at 384 rows).  bf16 H takes 8 x 4
+  // blocks (each head tile shared 8 ways; 2% faster than 4 x 8 on large_batch) when that pads
+  // at most 1/16 of the row tiles; the two-plane kernel, whose H tiles hold two planes, takes
+  // 4 x 8 (with 8 x 4 it was no faster at 32 row tiles and 7% slower at 64).
   const int S = pl.grid_x, R = pl.n_rtiles;
   int sr = 1, ss = S, remap = 0, total = S * R;
   if (S % 8 == 0 && R >= 2) {
@@ -772,15 +442,10 @@ hipError_t launch_project_tiled(const ScoreArgs& a) {
   // the kernels see rows_k rows (n_rows, or one whole row tile of zero-padded H); partials
   // are strided by rows_k
   const int rk = pl.rows_k;
-  if (pl.hilo && tiled_two_plane_m16(pl.hilo, p->d)) {
+  if (pl.hilo) {
     const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
     const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
     hipLaunchKernelGGL(k_project_tiled_m16x2, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
-                       rk, pl.n_vgroups, a.flags, part, R, S, sr, ss, remap);
-  } else if (pl.hilo) {
-    const uint16_t* hhi = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hhi);
-    const uint16_t* hlo = reinterpret_cast<const uint16_t*>(a.ws + pl.off_hlo);
-    hipLaunchKernelGGL(k_project_tiled_bf16<2>, grid, block, 0, a.stream, W, p->V, p->d, hhi, hlo,
                        rk, pl.n_vgroups, a.flags, part, R, S, sr, ss, remap);
   } else {
     const uint16_t* H = pl.pad_h ? reinterpret_cast<const uint16_t*>(a.ws + pl.off_hpad)

@@ -288,11 +288,19 @@ TILED = [
     dict(V=2500, d=64, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=63, n_extra_rows=250),
     dict(V=4099, d=192, n_q=20, K=(1, 10), lengths=(1, 4), layout="field", seed=64,
          n_extra_rows=400, T=1.7),
-    # fp32 H with d a multiple of 128: the 16 x 16 kernel's two-plane form, 128-row tiles
+    # fp32 H: the 16 x 16 kernel's two-plane form, 128-row tiles
     dict(V=3001, d=128, n_q=30, K=(2, 8), lengths=(1, 6), layout="own", seed=68, n_extra_rows=300),
     dict(V=1283, d=256, n_q=25, K=(1, 12), lengths=(1, 5), layout="prefix", seed=69,
          n_extra_rows=211),
     dict(V=256, d=128, n_q=10, K=(2, 4), lengths=(1, 3), layout="own", seed=70, n_extra_rows=256),
+    # an odd number of 64-wide stages (the extra stage after the stage-pair loop), with two
+    # vocabulary tiles per workgroup so the odd stage is followed by the next tile's stages
+    dict(V=30011, d=192, n_q=40, K=(2, 8), lengths=(1, 6), layout="own", seed=71, h_dtype="bf16",
+         n_extra_rows=300),
+    dict(V=20011, d=320, n_q=30, K=(2, 8), lengths=(1, 6), layout="prefix", seed=72,
+         n_extra_rows=200, T=0.8),
+    dict(V=5003, d=64, n_q=20, K=(2, 8), lengths=(1, 5), layout="field", seed=73, h_dtype="bf16",
+         n_extra_rows=256),
 ]
 
 

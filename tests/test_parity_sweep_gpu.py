@@ -6,7 +6,7 @@ Forty-two problems are drawn from one seed, six per plan family: the streaming k
 H) rows in one pass; the register-staged fallback (bf16 head, d a multiple of neither 64
 nor 128); the fp32 head; the tiled kernels just past the streaming kernel's rows (one
 zero-padded row tile, or two with fp32 H); and the tiled kernels with bf16 H and with fp32
-H past 256 rows.  Each draws its vocabulary size, d, layout (prefix row, one row per
+H past 256 rows, d an even or odd number of 64-wide stages.  Each draws its vocabulary size, d, layout (prefix row, one row per
 field, a row per token), candidate counts and lengths, exact duplicates, temperature and H
 dtype, and asserts the kernel the plan's documented rule picks.  Every output is compared
 element by element over every row a token references plus a sample of unreferenced rows.
@@ -35,8 +35,8 @@ def plan_kernel(p):
         if rows <= (64 if hf else 128) or V < 256:
             return "k_project_wg_bf16"
         return "k_project_tiled_m16x2" if hf else "k_project_tiled_m16"
-    if hf and d % 64 == 0 and rows > 32 and V >= 256:
-        return "k_project_tiled_bf16"
+    if d % 64 == 0 and rows > 32 and V >= 256:
+        return "k_project_tiled_m16x2" if hf else "k_project_tiled_m16"
     return "k_project_small_bf16"
 
 
@@ -69,7 +69,7 @@ def _cases(n=42, seed=4711):
             c.update(d=pick([32, 64, 128, 160]), V=int(rng.integers(100, 30_000)),
                      h_dtype="f32", w_dtype="f32")
         elif fam == "tiled_bf16h":
-            c.update(d=pick([128, 256, 384]), V=int(rng.integers(256, 30_000)), h_dtype="bf16",
+            c.update(d=pick([64, 128, 192, 256, 320, 384]), V=int(rng.integers(256, 30_000)), h_dtype="bf16",
                      w_dtype="bf16", n_q=int(rng.integers(6, 15)), n_extra_rows=int(rng.integers(256, 500)))
         else:
             c.update(d=pick([64, 128, 192, 256, 320]), V=int(rng.integers(256, 30_000)),
