@@ -91,13 +91,13 @@ void make_plan(const jet_problem* p, Plan* pl) {
   // tiled path: enough rows, whole stages, at least one full vocabulary tile (its buffer
   // offsets are local to a workgroup's tiles, so operands of any size take it); fewer rows
   // than one row tile run as one tile with zero rows appended to H
-  const bool stream_d = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
-  const int one_pass_rows = stream_d ? 32 * stream_max_row_tiles(pl->hilo) : 32;
+  const bool streams = pl->variant == VAR_SMALL_BF16 && stream_d(p->d);
+  const int one_pass_rows = streams ? 32 * stream_max_row_tiles(pl->hilo) : 32;
   if (pl->variant == VAR_SMALL_BF16 && p->n_rows > one_pass_rows && p->V >= 256 &&
       p->d % tiled_bk(pl->hilo) == 0)
     pl->variant = VAR_TILED_BF16;
   pl->rows_k = p->n_rows;
-  pl->stream = pl->variant == VAR_SMALL_BF16 && p->d % 128 == 0;
+  pl->stream = pl->variant == VAR_SMALL_BF16 && stream_d(p->d);
   if (pl->variant == VAR_TILED_BF16) {
     pl->row_tile = tiled_row_tile(pl->hilo, p->d);
     pl->rows_k = std::max(p->n_rows, pl->row_tile);

@@ -93,6 +93,7 @@ struct ScoreArgs {
 hipError_t launch_prep(const ScoreArgs& a);
 hipError_t launch_project(const ScoreArgs& a);
 hipError_t launch_project_tiled(const ScoreArgs& a);
+bool stream_d(int d);  // d the streaming kernel takes (a multiple of 64)
 int tiled_bk(bool hilo);
 int tiled_row_tile(bool hilo, int d);
 const char* tiled_kernel_name(bool hilo, int d);

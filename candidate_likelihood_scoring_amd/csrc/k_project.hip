@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 }
 
 // ------------------------------------------------------------------------------------
-// Streaming kernel for d % 128 == 0 (the HBM-bound small-row case).
+// Streaming kernel for d a multiple of 64 (the HBM-bound small-row case).
 //
 // Every global load is lane-contiguous: 16 lanes cover 256 contiguous bytes of one row and
 // an instruction reads four rows, i.e. 8 whole cache lines per 1 KB.  (Loading operands
@@ -225,7 +225,9 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // sixteen consecutive rows at the same c fall into sixteen different 16-byte bank groups,
 // so the row-wise writes and the column-wise fragment reads are both conflict-free.
 // K permutation inside a stage: lane half h, MFMA step j covers k = kb + 64 h + 8 j + e,
-// i.e. chunk 8 h + j of the row, for both operands.  Register stages rotate S deep; loads
+// i.e. chunk 8 h + j of the row, for both operands.  When d % 128 = 64 the last stage holds
+// 64 k: its chunks 8..15 re-read chunks 0..7 of the same head rows (in bounds, lines the
+// stage already fetches) and meet zero H chunks, so they add nothing.  Register stages rotate S deep; loads
 // run S-1 stages ahead and are never predicated (a stage past the end re-reads the last
 // one), so the compiler waits exactly for the stage it consumes.
 // ------------------------------------------------------------------------------------
@@ -237,7 +239,9 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // NR: 32-row tiles of H per workgroup (1, 2 or 4): each head fragment is multiplied into NR
 // accumulator tiles, so the head is read once for 32 NR rows.  The H stage holds NR x 32
 // rows (LDS: 64 KB of head tiles + 2 x NP x NR x 8 KB of H stages, at most 128 KB).
-template <int WPB, int S, bool HF32, bool NT, int NR>
+// HALF: d % 128 = 64, the last stage 64 wide (a separate instance, so that the loads of the
+// d % 128 = 0 instances stay as they were: the run-time test cost binary_enum 15%).
+template <int WPB, int S, bool HF32, bool NT, int NR, bool HALF>
 __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     const uint16_t* __restrict__ W, int V, int d, const void* __restrict__ Hsrc, int n_rows,
     int n_groups, int32_t* __restrict__ flags, float2* __restrict__ part) {
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
   const int rt = blockIdx.y, row0 = rt * 32 * NR;
   const int g0 = (int)((long long)blockIdx.x * n_groups / gridDim.x);
   const int g1 = (int)((long long)(blockIdx.x + 1) * n_groups / gridDim.x);
-  const int nst = d / KC;
+  const int nst = HALF ? (d + KC - 1) / KC : d / KC;  // with HALF the last stage holds 64 k
   u32x4* my = wt[wid];
   float m_run[NR], s_run[NR];
 #pragma unroll
@@ -281,6 +285,8 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
                     : (const char*)((const uint16_t*)Hsrc + (size_t)hrow * d + lch * 8);
   }
   const int h_chunk = HF32 ? ((lane & 31) >> 1) : lch;
+  // lanes whose H values sit in chunks 8..15 of a stage (k 64..127 of it)
+  const bool h_upper = HF32 ? (lane & 31) >= 16 : lch >= 8;
 
   for (int g = g0; g < g1; ++g) {
     const int v0 = g * (WPB * 32) + wid * 32;
@@ -290,14 +296,19 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
     u32x4 R[S][8], Hr[S][HQ];
 #define JET_STAGE_LOAD(SLOT, ST)                                                            \
   {                                                                                         \
-    const int ko_ = (ST) * KC + lch * 8;                                                    \
+    const bool up_ = HALF && (ST) == nst - 1; /* a 64-wide last stage */                    \
+    const int ko_ = (ST) * KC + (up_ ? (lch & 7) : lch) * 8;                                \
     _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                         \
       const u32x4* src_ = reinterpret_cast<const u32x4*>(                                   \
           W + (size_t)min(v0 + 4 * q + lrow, V - 1) * d + ko_);                             \
       R[SLOT][q] = NT ? __builtin_nontemporal_load(src_) : *src_;                           \
     }                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < HQ; ++i) Hr[SLOT][i] =                             \
-        *reinterpret_cast<const u32x4*>(h_src[i] + (size_t)(ST) * KC * (HF32 ? 4 : 2));     \
+    const bool hz_ = up_ && h_upper;                                                        \
+    _Pragma("unroll") for (int i = 0; i < HQ; ++i) {                                        \
+      const u32x4 hv_ = *reinterpret_cast<const u32x4*>(                                    \
+          h_src[i] + ((size_t)(ST) * KC - (hz_ ? 64 : 0)) * (HF32 ? 4 : 2));                \
+      Hr[SLOT][i] = hz_ ? u32x4{0u, 0u, 0u, 0u} : hv_;                                      \
+    }                                                                                       \
   }
 #define JET_STAGE_MMA(SLOT, ST)                                                             \
   {                                                                                         \
@@ -491,17 +502,20 @@ hipError_t launch_project(const ScoreArgs& a) {
   if (pl.variant == VAR_TILED_BF16) return launch_project_tiled(a);
   float2* part = reinterpret_cast<float2*>(a.ws + pl.off_part);
   dim3 grid(pl.grid_x, pl.n_rtiles), block(256);
-  if (pl.variant == VAR_SMALL_BF16 && p->d % 128 == 0) {
+  if (pl.variant == VAR_SMALL_BF16 && stream_d(p->d)) {
     const uint16_t* W = static_cast<const uint16_t*>(p->W);
     dim3 sblock(kStreamWPB * 64);
     // non-temporal head loads unless several row tiles could find a small head in a cache
     const bool nt = pl.n_rtiles == 1 || (size_t)p->V * p->d * 2 >= kStreamNtBytes;
-#define JET_WG(HF, NTV, NRV)                                                                 \
-  hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, (NRV == 1 ? kStreamS : 2), HF, NTV, NRV>), \
+#define JET_WG(HF, NTV, NRV, HALFV)                                                          \
+  hipLaunchKernelGGL((k_project_wg_bf16<kStreamWPB, (NRV == 1 ? kStreamS : 2), HF, NTV, NRV,    \
+                                        HALFV>),                                                \
                      grid, sblock, 0,                                                           \
                      a.stream, W, p->V, p->d, p->H, p->n_rows, pl.n_vgroups, a.flags, part)
+#define JET_WG_H(HF, NTV, NRV) \
+  if (p->d % 128) JET_WG(HF, NTV, NRV, true); else JET_WG(HF, NTV, NRV, false)
 #define JET_WG_NT(HF, NRV) \
-  if (nt) JET_WG(HF, true, NRV); else JET_WG(HF, false, NRV)
+  if (nt) { JET_WG_H(HF, true, NRV); } else { JET_WG_H(HF, false, NRV); }
     if (pl.hilo) {
       if (pl.stream_nr == 1) { JET_WG_NT(true, 1); }
       else if (pl.stream_nr == 2) { JET_WG_NT(true, 2); }
@@ -513,6 +527,7 @@ hipError_t launch_project(const ScoreArgs& a) {
       else return hipErrorInvalidValue;
     }
 #undef JET_WG_NT
+#undef JET_WG_H
 #undef JET_WG
   } else if (pl.variant == VAR_SMALL_BF16) {
     const uint16_t* W = static_cast<const uint16_t*>(p->W);
@@ -538,14 +553,17 @@ hipError_t launch_project(const ScoreArgs& a) {
   return hipGetLastError();
 }
 
+// The streaming kernel takes d in 128-wide stages, the last one 64 wide when d % 128 = 64.
+bool stream_d(int d) { return d % 64 == 0; }
+
 // Vocabulary entries per group and workgroups of the small-row path.
 int small_group_size(int variant, int d) {
   if (variant == VAR_SMALL_F32) return 32;
-  return d % 128 == 0 ? 32 * kStreamWPB : 32 * kSmallNT;
+  return stream_d(d) ? 32 * kStreamWPB : 32 * kSmallNT;
 }
 
 int small_grid(int variant, int d, int n_groups, int max_waves) {
-  if (variant == VAR_SMALL_BF16 && d % 128 == 0) {
+  if (variant == VAR_SMALL_BF16 && stream_d(d)) {
     int wg = max_waves / kStreamWPB;
     return n_groups < wg ? n_groups : wg;
   }

@@ -356,10 +356,12 @@ def test_projection_kernel_choice(lib):
     assert pick(128, 248320, 2560, BF16, BF16) == "k_project_wg_bf16"
     assert pick(129, 248320, 2560, BF16, BF16) == "k_project_tiled_m16"  # one padded row tile
     assert pick(255, 5000, 256, BF16, BF16) == "k_project_tiled_m16"
-    assert pick(40, 5000, 192, F32, BF16) == "k_project_tiled_m16x2"    # no streaming kernel at this d
-    assert pick(40, 5000, 192, BF16, BF16) == "k_project_tiled_m16"
-    assert pick(32, 5000, 192, BF16, BF16) == "k_project_small_bf16"    # one 32-row tile, no streaming
-    assert pick(1000, 5000, 160, BF16, BF16) == "k_project_small_bf16"  # d not whole 64-wide stages
+    assert pick(40, 5000, 192, F32, BF16) == "k_project_wg_bf16"        # a 64-wide last stage
+    assert pick(65, 5000, 192, F32, BF16) == "k_project_tiled_m16x2"
+    assert pick(128, 49152, 960, BF16, BF16) == "k_project_wg_bf16"
+    assert pick(129, 49152, 960, BF16, BF16) == "k_project_tiled_m16"
+    assert pick(32, 5000, 160, BF16, BF16) == "k_project_small_bf16"    # d not whole 64-wide stages
+    assert pick(1000, 5000, 160, BF16, BF16) == "k_project_small_bf16"
     assert pick(300, 255, 256, BF16, BF16) == "k_project_wg_bf16"       # vocabulary below one tile
     assert pick(33, 255, 256, F32, BF16) == "k_project_wg_bf16"
     assert pick(32, 1000, 64, F32, F32) == "k_project_small_f32"

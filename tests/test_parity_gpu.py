@@ -118,12 +118,13 @@ def test_many_candidates(jet, case):
 
 
 @pytest.mark.parametrize("h_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("d", [384, 640])
+@pytest.mark.parametrize("d", [384, 640, 192, 960, 64])
 def test_stream_odd_stage_count(jet, d, h_dtype):
-    """The streaming kernel with an odd number of 128-wide stages (3 and 5): its H stage
-    buffers alternate by stage, so the last stage of one vocabulary group and the first of
-    the next share a buffer.  513 groups over 256 workgroups give every workgroup two or
-    three groups in a row; every output against the oracle (30 field rows: one row tile)."""
+    """The streaming kernel with an odd number of 128-wide stages (3 and 5; with d % 128 =
+    64 the last one 64 wide: 2 stages at d = 192, 8 at 960, 1 at 64): its H stage buffers
+    alternate by stage, so the last stage of one vocabulary group and the first of the next
+    share a buffer.  513 groups over 256 workgroups give every workgroup two or three groups
+    in a row; every output against the oracle (30 field rows: one row tile)."""
     p = wl.make_problem(V=131101, d=d, n_q=30, K=(2, 6), layout="field", seed=95,
                         h_dtype=h_dtype)
     kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
@@ -135,9 +136,10 @@ def test_stream_odd_stage_count(jet, d, h_dtype):
 
 
 # (d, H dtype, rows): the streaming kernel carrying 2 (fp32 H) or 4 (bf16 H) 32-row tiles
-# per workgroup, with full and ragged last tiles and odd stage counts (d = 384, 640)
+# per workgroup, with full and ragged last tiles and odd stage counts (d = 384, 640; a
+# 64-wide last stage at d = 320, 960)
 _STREAM_MULTI = [(256, "f32", 64), (384, "f32", 41), (256, "bf16", 128), (640, "bf16", 97),
-                 (128, "bf16", 70), (384, "bf16", 33)]
+                 (128, "bf16", 70), (384, "bf16", 33), (320, "f32", 50), (960, "bf16", 111)]
 
 
 @pytest.mark.parametrize("d,h_dtype,rows", _STREAM_MULTI,

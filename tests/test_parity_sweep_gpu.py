@@ -2,13 +2,14 @@
 oracle (needs an MI355X).
 
 Forty-two problems are drawn from one seed, six per plan family: the streaming kernel
-(bf16 head, d % 128 == 0) with one 32-row tile and with 33 to 64 (fp32 H) or 128 (bf16
-H) rows in one pass; the register-staged fallback (bf16 head, d a multiple of neither 64
-nor 128); the fp32 head; the tiled kernels just past the streaming kernel's rows (one
-zero-padded row tile, or two with fp32 H); and the tiled kernels with bf16 H and with fp32
-H past 256 rows, d an even or odd number of 64-wide stages.  Each draws its vocabulary size, d, layout (prefix row, one row per
-field, a row per token), candidate counts and lengths, exact duplicates, temperature and H
-dtype, and asserts the kernel the plan's documented rule picks.  Every output is compared
+(bf16 head, d % 64 == 0) with one 32-row tile and with 33 to 64 (fp32 H) or 128 (bf16
+H) rows in one pass; the register-staged fallback (bf16 head, d not a multiple of 64);
+the fp32 head; the tiled kernels just past the streaming kernel's rows (one zero-padded
+row tile, or two with fp32 H); and the tiled kernels with bf16 H and with fp32 H past 256
+rows, d an even or odd number of 64-wide stages.  Each draws its vocabulary size, d,
+layout (prefix row, one row per field, a row per token), candidate counts and lengths,
+exact duplicates, temperature and H dtype, and asserts the kernel the plan's documented
+rule picks.  Every output is compared
 element by element over every row a token references plus a sample of unreferenced rows.
 """
 import numpy as np
@@ -31,11 +32,9 @@ def plan_kernel(p):
     rows, V, d, hf = p["n_rows"], p["V"], p["d"], p["h_dtype"] == "f32"
     if p["w_dtype"] == "f32":
         return "k_project_small_f32"
-    if d % 128 == 0:
+    if d % 64 == 0:
         if rows <= (64 if hf else 128) or V < 256:
             return "k_project_wg_bf16"
-        return "k_project_tiled_m16x2" if hf else "k_project_tiled_m16"
-    if d % 64 == 0 and rows > 32 and V >= 256:
         return "k_project_tiled_m16x2" if hf else "k_project_tiled_m16"
     return "k_project_small_bf16"
 
@@ -52,7 +51,7 @@ def _cases(n=42, seed=4711):
                  n_q=int(rng.integers(1, 6)), n_extra_rows=0)
         hd = pick(["f32", "bf16"])
         if fam == "stream":  # at most 2 questions x 8 candidates x 2 tokens: 32 rows
-            c.update(d=pick([128, 256, 384, 512, 640, 1024]), V=int(rng.integers(300, 120_000)),
+            c.update(d=pick([64, 128, 192, 256, 384, 512, 640, 960, 1024]), V=int(rng.integers(300, 120_000)),
                      h_dtype=hd, w_dtype="bf16", n_q=int(rng.integers(1, 3)),
                      K=(1, int(rng.integers(2, 9))), lengths=(1, int(rng.integers(1, 3))))
         elif fam in ("stream_multi", "tiled_mid"):  # one row per field, then unreferenced rows
@@ -60,8 +59,8 @@ def _cases(n=42, seed=4711):
             lo, hi = (33, top) if fam == "stream_multi" else (top + 1, 255)
             rows = int(rng.integers(lo, hi + 1))
             n_q = int(rng.integers(1, min(rows, 20) + 1))
-            c.update(d=pick([128, 256, 384, 512]), V=int(rng.integers(256, 60_000)), h_dtype=hd,
-                     w_dtype="bf16", layout="field", n_q=n_q, n_extra_rows=rows - n_q)
+            c.update(d=pick([128, 192, 256, 320, 384, 512]), V=int(rng.integers(256, 60_000)),
+                     h_dtype=hd, w_dtype="bf16", layout="field", n_q=n_q, n_extra_rows=rows - n_q)
         elif fam == "fallback":  # never tiled: d is not a multiple of 64
             c.update(d=pick([32, 96, 160, 224, 288]), V=int(rng.integers(300, 60_000)),
                      h_dtype=hd, w_dtype="bf16")
