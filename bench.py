@@ -180,20 +180,22 @@ def _oracle_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
-def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 20.0) -> dict:
+def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 20.0):
     """The fp64 oracle on the host's cores, on a bounded sample of the same workload: whole
     questions (all of them if they fit about budget_s), repeated until about 10 s of work.
-    The head is widened to fp64 once, before timing, so the figure is scoring alone."""
+    The head is widened to fp64 once, before timing, so the figure is scoring alone.
+    Returns the baseline record and the oracle's result on the sample."""
     import numpy as np
 
     import oracle
     cores = _oracle_threads()
     if restricted:
         n = int(p["field_off"][-1])
-        runs, dt = _timed_runs(lambda: oracle.score_restricted(p))
+        res = {}
+        runs, dt = _timed_runs(lambda: res.update(ref=oracle.score_restricted(p)))
         return dict(value=n * runs / dt, unit="scored candidate tokens/s", cores=int(cores), kind="oracle",
                     sample=f"the whole batch ({n} allowed-token slots), {runs} runs, {dt:.2f} s"
-                           f"{_cpu_model()}")
+                           f"{_cpu_model()}"), res["ref"]
     n_tok = len(p["tok_target"])
     tok_row = np.arange(n_tok) if p.get("tok_row") is None else np.asarray(p["tok_row"])
     # Time one question first; then as many whole questions as fit the budget.
@@ -214,13 +216,50 @@ def _cpu_baseline(p: dict, restricted: bool, budget_s: float = 20.0) -> dict:
         sample_q = max(1, int(budget_s / max(probe, 1e-3)))
     qs = list(range(sample_q))
     rows = rows_of(qs) if sample_q < n_q else None
-    runs, dt = _timed_runs(lambda: oracle.score(p, rows=rows, W64=W64))
+    res = {}
+    runs, dt = _timed_runs(lambda: res.update(ref=oracle.score(p, rows=rows, W64=W64)))
     toks = int(co[qo[sample_q]]) if sample_q < n_q else n_tok
     what = ("the whole batch" if sample_q == n_q else f"the first {sample_q} of {n_q} questions")
     n_r = n_rows if rows is None else len(rows)
     return dict(value=toks * runs / dt, unit="scored candidate tokens/s", cores=int(cores), kind="oracle",
                 sample=f"{what}: {toks} tokens on {n_r} predictor rows, {runs} runs, {dt:.2f} s"
-                       f"{_cpu_model()}")
+                       f"{_cpu_model()}"), res["ref"]
+
+
+Q_TOL = 1e-4  # candidate probabilities; decisions are compared where the oracle's top-two gap exceeds it
+
+
+def _parity(p: dict, out: dict, ref: dict, restricted: bool) -> dict:
+    """The benchmark's own outputs (last timed call) against the oracle result the CPU
+    baseline computed, on everything the oracle computed (its sample): largest absolute
+    errors, the stated tolerances, and decisions outside the near-tie band."""
+    import numpy as np
+
+    tl = 1e-4 if p["w_dtype"] == "f32" else 2e-3
+
+    def maxerr(a, b):
+        a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+        m = ~np.isnan(b)
+        return float(np.abs(a[m] - b[m]).max()) if m.any() else 0.0, int(m.sum())
+
+    if restricted:
+        dz, n = maxerr(out["slot_logit"], ref["slot_logit"])
+        dq, _ = maxerr(out["slot_q"], ref["slot_q"])
+        arg, ref_arg, gap = out["field_argmax"], ref["field_argmax"], ref["field_gap"]
+        res = dict(slots=n, max_abs_dlogit=dz, max_abs_dq=dq)
+    else:
+        dl, n = maxerr(out["tok_logp"], ref["tok_logp"])
+        dq, nc = maxerr(out["cand_q"], ref["cand_q"])
+        sel = ~np.isnan(np.asarray(ref["q_expect"], np.float64))
+        arg, ref_arg, gap = out["q_argmax"][sel], ref["q_argmax"][sel], ref["q_gap"][sel]
+        res = dict(tokens=n, candidates=nc, questions=int(sel.sum()), max_abs_dlogp=dl, max_abs_dq=dq)
+    clear = np.asarray(gap) > Q_TOL
+    res.update(decisions_compared=int(clear.sum()),
+               decision_mismatches=int((np.asarray(arg)[clear] != np.asarray(ref_arg)[clear]).sum()),
+               near_ties=int((~clear).sum()), tol_logp=tl, tol_q=Q_TOL)
+    res["within_tolerance"] = bool((res.get("max_abs_dlogp", res.get("max_abs_dlogit", 0.0)) <= tl)
+                                   and dq <= Q_TOL and res["decision_mismatches"] == 0)
+    return res
 
 
 def _bench_calibration(args) -> int:
@@ -518,7 +557,10 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         _log("[bench] timing the fp64 oracle on host cores")
-        cpu = _cpu_baseline(p, restricted)
+        cpu, ref = _cpu_baseline(p, restricted)
+        # the same oracle result, against this run's outputs (the last timed call)
+        got = {k: v.detach().cpu().numpy() for k, v in out.items()}
+        extra["parity_vs_oracle"] = _parity(p, got, ref, restricted)
 
     dtype = "f32" if p["w_dtype"] == "f32" else "bf16"
     config = dict(workload=args.workload, V=V, d=d, rows=rows, scored_tokens=int(n_tokens),
