@@ -61,7 +61,7 @@ enum Variant { VAR_SMALL_BF16 = 0, VAR_SMALL_F32 = 1, VAR_TILED_BF16 = 2 };
 struct Plan {
   int variant;
   bool hilo;          // fp32 H split into bf16 hi + lo
-  bool stream;        // streaming kernel (d % 128 == 0): splits fp32 H itself
+  bool stream;        // streaming kernel (d % 64 == 0): splits fp32 H itself
   int stream_nr;      // streaming kernel: 32-row tiles of H per workgroup (1, 2 or 4)
   int row_tile;       // rows per projection tile
   int rows_k;         // rows the projection kernel sees: n_rows, or one whole row tile of the

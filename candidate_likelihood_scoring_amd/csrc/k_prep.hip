@@ -58,7 +58,7 @@ hipError_t launch_prep(const ScoreArgs& a) {
                                       reinterpret_cast<uint16_t*>(ws + pl.off_hlo), a.stream);
     if (e != hipSuccess) return e;
   }
-  if (pl.pad_h) {  // bf16 H: d is a multiple of 128, so rows are whole 16-byte chunks
+  if (pl.pad_h) {  // bf16 H: d is a multiple of 64, so rows are whole 16-byte chunks
     const long long n16 = (long long)p->n_rows * p->d / 8, n16_out = (long long)pl.rows_k * p->d / 8;
     hipLaunchKernelGGL(k_pad_rows, dim3(split_blocks(n16_out, 256)), dim3(256), 0, a.stream,
                        static_cast<const u32x4*>(p->H), n16, n16_out,
