@@ -227,9 +227,9 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // K permutation inside a stage: lane half h, MFMA step j covers k = kb + 64 h + 8 j + e,
 // i.e. chunk 8 h + j of the row, for both operands.  When d % 128 = 64 the last stage holds
 // 64 k: its chunks 8..15 re-read chunks 0..7 of the same head rows (in bounds, lines the
-// stage already fetches) and meet zero H chunks, so they add nothing.  Register stages rotate S deep; loads
-// run S-1 stages ahead and are never predicated (a stage past the end re-reads the last
-// one), so the compiler waits exactly for the stage it consumes.
+// stage already fetches) and meet zero H chunks, so they add nothing.  Register stages
+// rotate S deep; loads run S-1 stages ahead and are never predicated (a stage past the end
+// re-reads the last one), so the compiler waits exactly for the stage it consumes.
 // ------------------------------------------------------------------------------------
 // NT: head loads carry the non-temporal hint (the head streams through once, with no reuse
 // the caches could serve: one row tile, or a head larger than the last-level cache).
