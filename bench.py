@@ -68,7 +68,8 @@ _TILED_SRC = ["candidate_likelihood_scoring_amd/csrc/k_tiled.hip",
               "candidate_likelihood_scoring_amd/csrc/jet_internal.h",
               "candidate_likelihood_scoring_amd/csrc/jet_api.hip"]
 KERNEL_SOURCES = {"k_project_wg_bf16": _SMALL_SRC, "k_project_small_bf16": _SMALL_SRC,
-                  "k_project_small_f32": _SMALL_SRC, "k_project_tiled_m16": _TILED_SRC,
+                  "k_project_small_f32": _SMALL_SRC, "k_project_wg_f32": _SMALL_SRC,
+                  "k_project_tiled_m16": _TILED_SRC,
                   "k_project_tiled_m16x2": _TILED_SRC}
 
 

@@ -20,8 +20,8 @@ static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace jet {
 
-int small_group_size(int variant, int d);
-int small_grid(int variant, int d, int n_groups, int max_waves);
+int small_group_size(int variant, bool stream);
+int small_grid(int variant, bool stream, int n_groups, int max_waves);
 
 namespace {
 
@@ -39,6 +39,21 @@ constexpr int kSmallWaves = JET_SMALL_WAVES;
 // tile per workgroup 194 us per 32-row tile (1.48 ms at 255 rows), one tiled row tile about
 // 350 us.
 int stream_max_row_tiles(bool hilo) { return hilo ? 2 : 4; }
+
+// fp32 head: the streaming kernel k_project_wg_f32 when it has at least one workgroup per
+// CU (256-entry vocabulary groups x row tiles of 16 rows up to 16 rows, else 32); smaller
+// problems take k_project_small_f32, whose 32-entry groups and k split over four waves
+// spread them over more CUs.  Measured with 8 rows: the streaming kernel 8.2 -> 13.3 us at
+// V = 4096, d = 256 and 23 -> 40 us at V = 16,384, d = 1024 (16 and 64 groups), level at
+// 128 groups, 26 -> 20 us at V = 65,536, d = 256 (256 groups); 109 us against 164 us at
+// V = 128,000, d = 1024 with 4 rows.
+constexpr long long kF32StreamMinWork = 256;
+bool f32_streams(int V, int n_rows) {
+  if (!JET_F32_STREAM) return false;
+  const long long groups = (V + 255) / 256;
+  const long long tiles = n_rows <= 16 ? 1 : (n_rows + 31) / 32;
+  return groups * tiles >= kF32StreamMinWork;
+}
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -97,7 +112,8 @@ void make_plan(const jet_problem* p, Plan* pl) {
       p->d % tiled_bk(pl->hilo) == 0)
     pl->variant = VAR_TILED_BF16;
   pl->rows_k = p->n_rows;
-  pl->stream = pl->variant == VAR_SMALL_BF16 && stream_d(p->d);
+  pl->stream = (pl->variant == VAR_SMALL_BF16 && stream_d(p->d)) ||
+               (pl->variant == VAR_SMALL_F32 && f32_streams(p->V, p->n_rows));
   if (pl->variant == VAR_TILED_BF16) {
     pl->row_tile = tiled_row_tile(pl->hilo, p->d);
     pl->rows_k = std::max(p->n_rows, pl->row_tile);
@@ -126,14 +142,16 @@ void make_plan(const jet_problem* p, Plan* pl) {
     // streaming kernel: the fewest row tiles per workgroup (1, 2, 4) that cover the rows,
     // up to the LDS limit (more rows only with a vocabulary below one tiled tile)
     int nr = 1;
-    if (pl->stream)
+    if (pl->stream && pl->variant == VAR_SMALL_BF16)
       while (nr < stream_max_row_tiles(pl->hilo) && 32 * nr < p->n_rows) nr *= 2;
     pl->stream_nr = nr;
     pl->row_tile = 32 * nr;
+    // fp32 head: up to 16 rows take the 16-row tile (half the matrix work of a 32-row one)
+    if (pl->stream && pl->variant == VAR_SMALL_F32 && p->n_rows <= 16) pl->row_tile = 16;
     pl->n_rtiles = (p->n_rows + pl->row_tile - 1) / pl->row_tile;
-    pl->vgroup = small_group_size(pl->variant, p->d);
+    pl->vgroup = small_group_size(pl->variant, pl->stream);
     pl->n_vgroups = (p->V + pl->vgroup - 1) / pl->vgroup;
-    pl->grid_x = std::max(1, small_grid(pl->variant, p->d, pl->n_vgroups, kSmallWaves));
+    pl->grid_x = std::max(1, small_grid(pl->variant, pl->stream, pl->n_vgroups, kSmallWaves));
   }
   pl->n_parts = pl->grid_x;
   // no target logit is captured by a projection kernel (k_token_logp computes them after
@@ -263,7 +281,7 @@ const char* jet_projection_kernel(const jet_problem* p) {
   make_plan(p, &pl);
   switch (pl.variant) {
     case VAR_TILED_BF16: return tiled_kernel_name(pl.hilo, p->d);
-    case VAR_SMALL_F32: return "k_project_small_f32";
+    case VAR_SMALL_F32: return pl.stream ? "k_project_wg_f32" : "k_project_small_f32";
     default: return pl.stream ? "k_project_wg_bf16" : "k_project_small_bf16";
   }
 }

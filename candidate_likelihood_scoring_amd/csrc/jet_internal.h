@@ -58,10 +58,17 @@ __device__ inline void flag_or(int32_t* flags, uint32_t bit) {
 // ------------------------------------------------------------------------------------
 enum Variant { VAR_SMALL_BF16 = 0, VAR_SMALL_F32 = 1, VAR_TILED_BF16 = 2 };
 
+// fp32 heads take the streaming kernel k_project_wg_f32 (0: the k-split kernel
+// k_project_small_f32, kept for the restricted path's stored logits)
+#ifndef JET_F32_STREAM
+#define JET_F32_STREAM 1
+#endif
+
 struct Plan {
   int variant;
   bool hilo;          // fp32 H split into bf16 hi + lo
-  bool stream;        // streaming kernel (d % 64 == 0): splits fp32 H itself
+  bool stream;        // streaming kernel (bf16 head with d % 64 == 0, or an fp32 head):
+                      // partials row-major; with a bf16 head it splits fp32 H itself
   int stream_nr;      // streaming kernel: 32-row tiles of H per workgroup (1, 2 or 4)
   int row_tile;       // rows per projection tile
   int rows_k;         // rows the projection kernel sees: n_rows, or one whole row tile of the

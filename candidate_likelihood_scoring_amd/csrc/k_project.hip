@@ -385,6 +385,179 @@ __global__ __launch_bounds__(WPB * 64) void k_project_wg_bf16(
 }
 
 // ------------------------------------------------------------------------------------
+// Streaming kernel for an fp32 head (fp32 H).  The loads of the bf16 streaming kernel: 16
+// lanes read 256 contiguous bytes (64 k) of one row and an instruction reads four rows, so
+// every head byte moves in whole cache lines; each wave owns a 32-row head tile per
+// vocabulary group and moves each stage of it through its own LDS tile into the operand
+// layout of the matrix op.  The 32 x 64 stage of H is loaded once per workgroup (four rows
+// per wave) into a double-buffered stage shared by all waves.  LDS chunk (row r, 16-byte
+// chunk c) sits at r * 16 + (c ^ (r & 15)), as in the bf16 kernel.  HALF: d % 64 = 32, the
+// last stage holds 32 k; its chunks 8..15 re-read chunks 0..7 of the same head rows (in
+// bounds) and meet zero H chunks.
+// fp32 matrix ops run at a sixteenth of the bf16 rate: at a full 32-row tile the matrix work
+// of a stage takes about as long as its head bytes take to arrive at HBM speed, so a tile
+// of 16 rows serves up to 16 rows at half the matrix work.
+//   RT = 32: v_mfma_f32_32x32x2f32, lane l supplies row l % 32 and one k of its half l / 32;
+//            K is permuted inside a stage so that half h takes k = 32 h + s at step s.
+//   RT = 16: v_mfma_f32_16x16x4f32 on two 16-entry vocabulary tiles, lane l supplies row
+//            l % 16 and one k of its quarter q = l / 16, k = 16 q + s at step s; output
+//            (m, n) of a 16 x 16 tile sits in lane n + 16 (m / 4), register m % 4.
+// Both operands take the same permutation, and one 16-byte LDS read serves four steps.
+template <int WPB, int S, bool NT, bool HALF, int RT>
+__global__ __launch_bounds__(WPB * 64) void k_project_wg_f32(
+    const float* __restrict__ W, int V, int d, const float* __restrict__ H, int n_rows,
+    int n_groups, int32_t* __restrict__ flags, float2* __restrict__ part) {
+  constexpr int KC = 64;  // k per stage
+  static_assert(WPB == 8, "four H rows per wave per stage");
+  static_assert(RT == 16 || RT == 32, "row tile");
+  __shared__ u32x4 wt[WPB][512];  // per-wave 32-row head tile
+  __shared__ u32x4 hb[2][512];    // H stage, double buffered
+  __shared__ float2 red[WPB][32];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n = lane & 31, half = lane >> 5;
+  const int n16 = lane & 15, quarter = lane >> 4;
+  const int lrow = lane >> 4, lch = lane & 15;
+  const int row0 = blockIdx.y * RT;
+  const int g0 = (int)((long long)blockIdx.x * n_groups / gridDim.x);
+  const int g1 = (int)((long long)(blockIdx.x + 1) * n_groups / gridDim.x);
+  const int nst = HALF ? (d + KC - 1) / KC : d / KC;
+  u32x4* my = wt[wid];
+  float m_run = -INFINITY, s_run = 0.f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flags[0] = 0;
+  // H stage rows 4 wid + lane / 16, chunk lane % 16 (rows past the last, and with RT = 16
+  // stage rows 16..31, repeat a valid row: their products are not used)
+  const int h_r = 4 * wid + lrow;
+  const float* h_src = H + (size_t)min(row0 + h_r, n_rows - 1) * d + lch * 4;
+  const bool h_upper = lch >= 8;  // k 32..63 of a stage
+  const int h_slot = h_r * 16 + (lch ^ (h_r & 15));
+
+  for (int g = g0; g < g1; ++g) {
+    const int v0 = g * (WPB * 32) + wid * 32;
+    f32x16 acc = {};
+    f32x4 acc16[2] = {};
+    u32x4 R[S][8], Hr[S];
+#define JET_F32_LOAD(SLOT, ST)                                                              \
+  {                                                                                         \
+    const bool up_ = HALF && (ST) == nst - 1; /* a 32-wide last stage */                    \
+    const int ko_ = (ST) * KC + (up_ ? (lch & 7) : lch) * 4;                                \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                         \
+      const u32x4* src_ = reinterpret_cast<const u32x4*>(                                   \
+          W + (size_t)min(v0 + 4 * q + lrow, V - 1) * d + ko_);                             \
+      R[SLOT][q] = NT ? __builtin_nontemporal_load(src_) : *src_;                           \
+    }                                                                                       \
+    const bool hz_ = up_ && h_upper;                                                        \
+    const u32x4 hv_ =                                                                       \
+        *reinterpret_cast<const u32x4*>(h_src + (size_t)(ST) * KC - (hz_ ? 32 : 0));        \
+    Hr[SLOT] = hz_ ? u32x4{0u, 0u, 0u, 0u} : hv_;                                           \
+  }
+#define JET_F32_MMA(SLOT, ST)                                                               \
+  {                                                                                         \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                         \
+      const int r = 4 * q + lrow;                                                           \
+      my[r * 16 + (lch ^ (r & 15))] = R[SLOT][q];                                            \
+    }                                                                                       \
+    u32x4* hbuf = &hb[(ST) & 1][0];                                                         \
+    hbuf[h_slot] = Hr[SLOT];                                                                \
+    __syncthreads();                                                                        \
+    if constexpr (RT == 32) {                                                               \
+      _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                       \
+        const int c = ((half * 8 + j) ^ (n & 15)) + n * 16;                                  \
+        const u32x4 a4 = my[c], b4 = hbuf[c];                                               \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e)                                       \
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a4[e]),                \
+                                                     __uint_as_float(b4[e]), acc, 0, 0, 0); \
+      }                                                                                     \
+    } else {                                                                                \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
+        const int c = ((quarter * 4 + j) ^ n16) + n16 * 16;                                  \
+        const u32x4 a0 = my[c], a1 = my[c + 256], b4 = hbuf[c];                             \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                     \
+          acc16[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a0[e]),           \
+                                                          __uint_as_float(b4[e]), acc16[0], \
+                                                          0, 0, 0);                         \
+          acc16[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a1[e]),           \
+                                                          __uint_as_float(b4[e]), acc16[1], \
+                                                          0, 0, 0);                         \
+        }                                                                                   \
+      }                                                                                     \
+    }                                                                                       \
+  }
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      JET_F32_LOAD(s, min(s, nst - 1));
+    }
+    // main loop over a multiple of S stages, so that no load sits behind a condition
+    const int nmain = nst - nst % S;
+    for (int st0 = 0; st0 < nmain; st0 += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        JET_F32_LOAD((s + S - 1) % S, min(st0 + s + S - 1, nst - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        JET_F32_MMA(s, st0 + s);
+      }
+    }
+    // the last nst % S (< S) stages are already in slots 0 .. nst % S - 1
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nst - nmain) JET_F32_MMA(s, nmain + s);  // uniform over the workgroup
+#undef JET_F32_MMA
+#undef JET_F32_LOAD
+    if constexpr (RT == 32) {
+      Acc<1> one;
+      one.t[0] = acc;
+      epilogue_lse<1>(one, v0, V, half, m_run, s_run);
+    } else {
+      // register i of tile t: vocabulary entry v0 + 16 t + 4 quarter + i, row n16
+      float gm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v0 + 16 * t + 4 * quarter + i < V) gm = fmaxf(gm, acc16[t][i]);
+      const float mn = fmaxf(m_run, gm);
+      if (mn != -INFINITY) {
+        const float mb = mn * kLog2e;
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v0 + 16 * t + 4 * quarter + i < V) sum += exp2f(fmaf(acc16[t][i], kLog2e, -mb));
+        s_run = s_run * exp2f((m_run - mn) * kLog2e) + sum;
+        m_run = mn;
+      }
+    }
+    // the H stage buffer is hb[stage & 1] and the stage count restarts with every group: with
+    // an odd count the group's last stage and the next group's first share buffer 0 (one
+    // barrier per group, uniform)
+    if (nst & 1) __syncthreads();
+  }
+  if constexpr (RT == 32) {
+    store_partial<WPB, true>(m_run, s_run, n, half, wid, row0, n_rows, part, red);
+  } else {
+    // lanes n16, n16 + 16, n16 + 32 and n16 + 48 hold row n16: merge them, then the waves
+    // in wave order
+#pragma unroll
+    for (int x = 16; x <= 32; x *= 2) {
+      const float m2 = __shfl_xor(m_run, x);
+      const float s2 = __shfl_xor(s_run, x);
+      lse_merge(m_run, s_run, m2, s2);
+    }
+    if (lane < 16) red[wid][lane] = make_float2(m_run, s_run);
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      float m = red[0][n16].x, s = red[0][n16].y;
+#pragma unroll
+      for (int w = 1; w < WPB; ++w) lse_merge(m, s, red[w][n16].x, red[w][n16].y);
+      const int row = row0 + n16;
+      if (row < n_rows) part[(size_t)row * gridDim.x + blockIdx.x] = make_float2(m, s);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // fp32 head and fp32 hidden states: v_mfma_f32_32x32x2_f32 takes one k per lane half.
 // A workgroup takes one 32-entry vocabulary group at a time and its four waves split the
 // k range: wave w takes the 16-wide blocks w, w + 4, ...; in a block, lane half h loads 8
@@ -542,6 +715,23 @@ hipError_t launch_project(const ScoreArgs& a) {
                          a.stream, W, p->V, p->d, h, nullptr, p->n_rows, pl.n_vgroups, a.flags,
                          part);
     }
+  } else if (pl.variant == VAR_SMALL_F32 && pl.stream) {
+    const float* W = static_cast<const float*>(p->W);
+    const float* H = static_cast<const float*>(p->H);
+    dim3 sblock(kStreamWPB * 64);
+    const bool nt = pl.n_rtiles == 1 || (size_t)p->V * p->d * 4 >= kStreamNtBytes;
+#define JET_WF(NTV, HALFV, RTV)                                                                \
+  hipLaunchKernelGGL((k_project_wg_f32<kStreamWPB, kStreamS, NTV, HALFV, RTV>), grid, sblock,   \
+                     0, a.stream, W, p->V, p->d, H, p->n_rows, pl.n_vgroups, a.flags, part)
+#define JET_WF_H(NTV, RTV) \
+  if (p->d % 64) JET_WF(NTV, true, RTV); else JET_WF(NTV, false, RTV)
+#define JET_WF_NT(RTV) \
+  if (nt) { JET_WF_H(true, RTV); } else { JET_WF_H(false, RTV); }
+    if (pl.row_tile == 16) { JET_WF_NT(16); }
+    else { JET_WF_NT(32); }
+#undef JET_WF_NT
+#undef JET_WF_H
+#undef JET_WF
   } else if (pl.variant == VAR_SMALL_F32) {
     hipLaunchKernelGGL((k_project_small_f32<false>), grid, block, 0, a.stream,
                        static_cast<const float*>(p->W), p->V, p->d,
@@ -557,13 +747,13 @@ hipError_t launch_project(const ScoreArgs& a) {
 bool stream_d(int d) { return d % 64 == 0; }
 
 // Vocabulary entries per group and workgroups of the small-row path.
-int small_group_size(int variant, int d) {
-  if (variant == VAR_SMALL_F32) return 32;
-  return stream_d(d) ? 32 * kStreamWPB : 32 * kSmallNT;
+int small_group_size(int variant, bool stream) {
+  if (stream) return 32 * kStreamWPB;
+  return variant == VAR_SMALL_F32 ? 32 : 32 * kSmallNT;
 }
 
-int small_grid(int variant, int d, int n_groups, int max_waves) {
-  if (variant == VAR_SMALL_BF16 && stream_d(d)) {
+int small_grid(int variant, bool stream, int n_groups, int max_waves) {
+  if (stream) {
     int wg = max_waves / kStreamWPB;
     return n_groups < wg ? n_groups : wg;
   }

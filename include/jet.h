@@ -176,7 +176,7 @@ JET_API jet_status jet_score_noalloc(const jet_problem* p, const jet_outputs* o,
 /* Name of the projection kernel jet_score launches for this problem (the plan depends
  * only on the problem's scalars), as profilers report it: "k_project_tiled_m16",
  * "k_project_tiled_m16x2", "k_project_wg_bf16", "k_project_small_bf16" or
- * "k_project_small_f32".  NULL when the problem is invalid.  Host only; the string is
+ * "k_project_wg_f32".  NULL when the problem is invalid.  Host only; the string is
  * static. */
 JET_API const char* jet_projection_kernel(const jet_problem* p);
 

@@ -364,7 +364,13 @@ def test_projection_kernel_choice(lib):
     assert pick(1000, 5000, 160, BF16, BF16) == "k_project_small_bf16"
     assert pick(300, 255, 256, BF16, BF16) == "k_project_wg_bf16"       # vocabulary below one tile
     assert pick(33, 255, 256, F32, BF16) == "k_project_wg_bf16"
+    # fp32 head: streaming with at least 256 (256-entry group, row tile) pairs
     assert pick(32, 1000, 64, F32, F32) == "k_project_small_f32"
+    assert pick(8, 32768, 256, F32, F32) == "k_project_small_f32"   # 128 groups
+    assert pick(16, 65536, 96, F32, F32) == "k_project_wg_f32"      # 256 groups, one 16-row tile
+    assert pick(17, 65280, 96, F32, F32) == "k_project_small_f32"   # 255 groups, one 32-row tile
+    assert pick(33, 32768, 256, F32, F32) == "k_project_wg_f32"     # 128 groups x 2 row tiles
+    assert pick(5000, 1000, 96, F32, F32) == "k_project_wg_f32"     # 4 groups x 157 row tiles
     # operands past 4 GiB keep the matrix-core kernels (offsets local to each workgroup)
     assert pick(300, 262144, 8192, BF16, BF16) == "k_project_tiled_m16"   # head of 4 GiB
     assert pick(300, 300007, 8192, BF16, BF16) == "k_project_tiled_m16"   # 4.9 GB head

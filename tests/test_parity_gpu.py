@@ -158,6 +158,32 @@ def test_stream_row_tiles_per_workgroup(jet, d, h_dtype, rows):
     log(f"[gpu] errs {compare(p, out, jo.score(p), f'stream_multi_{d}_{h_dtype}_{rows}')}")
 
 
+# fp32 head (V, d, rows), each with at least 256 (vocabulary group, row tile) pairs so that
+# the streaming kernel takes it: last stage 32 wide (d % 64 = 32) or whole; 1 to 16 stages
+# (odd and even counts, each remainder of the 3-slot pipeline; odd counts also with several
+# groups per workgroup, V > 65,536); the 16-row tile (1 to 16 rows) and 32-row tiles, the
+# last ragged; vocabularies of one entry, below one 256-entry group and with a one-entry
+# last group; a head past the last-level cache (non-temporal loads)
+_F32_STREAM = [(1, 32, 8200), (255, 96, 8192), (70001, 96, 1), (131101, 320, 16),
+               (65537, 64, 17), (30011, 160, 70), (100003, 1024, 5), (128000, 1024, 4),
+               (3001, 64, 2100), (257, 256, 4100), (140000, 192, 40), (90001, 64, 9)]
+
+
+@pytest.mark.parametrize("V,d,rows", _F32_STREAM, ids=[f"V{v}_d{d}_{r}" for v, d, r in _F32_STREAM])
+def test_f32_head_stream(jet, V, d, rows):
+    """fp32 head and fp32 H: the streaming kernel (one row tile per workgroup, 16 rows with
+    v_mfma_f32_16x16x4f32 up to 16 rows, else 32 with v_mfma_f32_32x32x2f32; 64 k per stage
+    through LDS), one question per row (single-token fields); every output against the
+    oracle at the fp32 tolerance, on every row."""
+    p = wl.make_problem(V=V, d=d, n_q=rows, K=1 if V == 1 else (1, 6), layout="field",
+                        seed=500 + d + rows, w_dtype="f32")
+    kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
+    log(f"[gpu] f32 head V={V} d={d} rows={p['n_rows']} ({kern})")
+    assert kern == "k_project_wg_f32" and p["n_rows"] == rows
+    out = _run(jet, p)
+    log(f"[gpu] errs {compare(p, out, jo.score(p), f'f32_stream_{V}_{d}_{rows}')}")
+
+
 @pytest.mark.parametrize("h_dtype,rows", [("f32", 150), ("bf16", 300)])
 def test_stream_small_vocab_many_rows(jet, h_dtype, rows):
     """A vocabulary below one tiled tile (V = 200) keeps many rows on the streaming kernel:

@@ -4,13 +4,15 @@ oracle (needs an MI355X).
 Forty-two problems are drawn from one seed, six per plan family: the streaming kernel
 (bf16 head, d % 64 == 0) with one 32-row tile and with 33 to 64 (fp32 H) or 128 (bf16
 H) rows in one pass; the register-staged fallback (bf16 head, d not a multiple of 64);
-the fp32 head; the tiled kernels just past the streaming kernel's rows (one zero-padded
-row tile, or two with fp32 H); and the tiled kernels with bf16 H and with fp32 H past 256
-rows, d an even or odd number of 64-wide stages.  Each draws its vocabulary size, d,
-layout (prefix row, one row per field, a row per token), candidate counts and lengths,
-exact duplicates, temperature and H dtype, and asserts the kernel the plan's documented
-rule picks.  Every output is compared
-element by element over every row a token references plus a sample of unreferenced rows.
+the fp32 head on small problems (the k-split kernel); the tiled kernels just past the
+streaming kernel's rows (one zero-padded row tile, or two with fp32 H); and the tiled
+kernels with bf16 H and with fp32 H past 256 rows, d an even or odd number of 64-wide
+stages.  Six more, from a second seed, are fp32 heads large enough for the fp32
+streaming kernel.  Each draws its vocabulary size, d, layout (prefix row, one row per
+field, a row per token), candidate counts and lengths, exact duplicates, temperature and
+H dtype, and asserts the kernel the plan's documented rule picks.  Every output is
+compared element by element over every row a token references plus a sample of
+unreferenced rows.
 """
 import numpy as np
 import pytest
@@ -30,8 +32,9 @@ FAMILIES = ("stream", "stream_multi", "fallback", "f32_head", "tiled_mid", "tile
 def plan_kernel(p):
     """The projection kernel of the plan's rule, from the problem's scalars."""
     rows, V, d, hf = p["n_rows"], p["V"], p["d"], p["h_dtype"] == "f32"
-    if p["w_dtype"] == "f32":
-        return "k_project_small_f32"
+    if p["w_dtype"] == "f32":  # streaming with one workgroup per CU: 256-entry groups x row tiles
+        tiles = 1 if rows <= 16 else -(-rows // 32)
+        return "k_project_wg_f32" if -(-V // 256) * tiles >= 256 else "k_project_small_f32"
     if d % 64 == 0:
         if rows <= (64 if hf else 128) or V < 256:
             return "k_project_wg_bf16"
@@ -78,7 +81,25 @@ def _cases(n=42, seed=4711):
     return out
 
 
-CASES = _cases()
+def _f32_stream_cases(n=6, seed=4712):
+    """fp32 heads large enough for the streaming kernel: V of 65,536 to 200,000 (256 to 782
+    groups), 1 to 64 rows (the 16-row tile, one and two 32-row tiles), d with a 32-wide
+    last stage or whole stages."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        pick = lambda xs: xs[int(rng.integers(0, len(xs)))]  # noqa: E731
+        rows = (1, int(rng.integers(2, 17)), int(rng.integers(17, 65)))[i % 3]
+        n_q = int(rng.integers(1, min(rows, 12) + 1))
+        out.append(("f32_stream", dict(
+            T=float(pick([0.5, 1.0, 2.0])), layout="field", dups=int(rng.integers(0, 3)),
+            seed=9100 + i, name=f"sweep_f32_stream{i}", K=(1, int(rng.integers(2, 13))),
+            n_q=n_q, n_extra_rows=rows - n_q, d=(32, 320, 96, 192, 64, 128)[i % 6],
+            V=int(rng.integers(65_536, 200_000)), h_dtype="f32", w_dtype="f32")))
+    return out
+
+
+CASES = _cases() + _f32_stream_cases()
 
 
 @pytest.mark.parametrize("fam,case", CASES, ids=[c["name"] for _, c in CASES])
