@@ -137,6 +137,45 @@ def _per_call_ms(fn, stream, n: int):
     return ms[len(ms) // 2], ms[0]
 
 
+def _graph_call_ms(step, stream, n: int, outputs: dict, calls: int = 1):
+    """`calls` back-to-back calls captured in one HIP graph (on a side stream, as capture
+    requires) and replayed n times on the bench's stream, each replay bracketed by its own
+    events: median and minimum per call.  The replays' outputs must equal an eager call's
+    bit for bit."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    side_h = side.cuda_stream
+    with torch.cuda.stream(side):
+        step(s=side_h)
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outputs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(calls):
+            step(s=side_h)
+    torch.cuda.synchronize()
+    for v in outputs.values():
+        v.fill_(-7)
+    pairs = []
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    for k, v in outputs.items():  # bit patterns (an unset q_true is NaN)
+        same = (torch.equal(v.view(torch.int32), eager[k].view(torch.int32))
+                if v.dtype == torch.float32 else torch.equal(v, eager[k]))
+        assert same, f"graph replay differs from the eager call in {k}"
+    ms = sorted(a.elapsed_time(b) / calls for a, b in pairs)
+    del g
+    return ms[len(ms) // 2], ms[0]
+
+
 def _full_path_step(p: dict, dev, lib, stream):
     """A jet_score step over the restricted problem's fields posed as single-token
     candidates of a full-vocabulary problem (same H, head, ids and T), for the restricted
@@ -425,8 +464,8 @@ def main(argv=None) -> int:
         for name, _ in o._fields_:
             setattr(o, name, out[name].data_ptr())
 
-        def step(ev=None):
-            st = lib.jet_score_restricted(ctypes.byref(prob), ctypes.byref(o), base, size, sh)
+        def step(ev=None, s=sh):
+            st = lib.jet_score_restricted(ctypes.byref(prob), ctypes.byref(o), base, size, s)
             if st:
                 raise _lib.JetError(st, "jet_score_restricted")
 
@@ -440,9 +479,9 @@ def main(argv=None) -> int:
         out = api.alloc_outputs(prob, dev, optional=True)
         o = api._outputs_struct(out)
 
-        def step(ev=None):
+        def step(ev=None, s=sh):
             if ev is None:
-                st = lib.jet_score(ctypes.byref(prob), ctypes.byref(o), base, size, sh)
+                st = lib.jet_score(ctypes.byref(prob), ctypes.byref(o), base, size, s)
             else:
                 st = lib.jet_score_profiled(ctypes.byref(prob), ctypes.byref(o), base, size, sh,
                                             ev[0], ev[1])
@@ -487,6 +526,12 @@ def main(argv=None) -> int:
         med, mn = _per_call_ms(step, stream, args.steps)
         extra["call_ms_median"] = round(med, 5)
         extra["call_ms_min"] = round(mn, 5)
+        # the same call replayed from a captured HIP graph, one call per graph and 20
+        outs = {k: v for k, v in out.items() if k != "dev_flags"}
+        for calls, key in ((1, "graph_call_ms"), (20, "graph20_call_ms")):
+            gmed, gmn = _graph_call_ms(step, stream, args.steps, outs, calls)
+            extra[key + "_median"] = round(gmed, 5)
+            extra[key + "_min"] = round(gmn, 5)
     if restricted:
         # the same fields through the full-vocabulary path (one jet_score call)
         _log("[bench] timing the full-vocabulary path on the same fields")
