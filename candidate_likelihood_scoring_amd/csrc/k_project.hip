@@ -2,7 +2,7 @@
 // ("small-row" kernels, HBM-bound on the head).
 //
 // What it computes (JET paper, Eq. 1-2; FastJEV Sec. 3.3, candidate-preserving readout):
-// for each row r of a 32-row tile and every vocabulary entry v, z[r,v] = <H[r], W[v]>
+// for each row r of a row tile and every vocabulary entry v, z[r,v] = <H[r], W[v]>
 // with fp32 accumulation on the matrix cores; the logits stay in registers and never
 // reach memory (the JET paper's GPU scoring likewise hands back only the candidates'
 // log-probabilities).  Each wave folds its logits into a running (max, sum of exp) per row;
