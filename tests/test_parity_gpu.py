@@ -121,10 +121,11 @@ def test_many_candidates(jet, case):
 @pytest.mark.parametrize("d", [384, 640, 192, 960, 64])
 def test_stream_odd_stage_count(jet, d, h_dtype):
     """The streaming kernel with an odd number of 128-wide stages (3 and 5; with d % 128 =
-    64 the last one 64 wide: 2 stages at d = 192, 8 at 960, 1 at 64): its H stage buffers
-    alternate by stage, so the last stage of one vocabulary group and the first of the next
-    share a buffer.  513 groups over 256 workgroups give every workgroup two or three groups
-    in a row; every output against the oracle (30 field rows: one row tile)."""
+    64 the last one 64 wide: 2 stages at d = 192, 8 at 960, 1 at 64): with one row tile its
+    H stage buffers alternate by pairs of stages (2, 3, 1, 4 and 1 pairs here), so with an
+    odd pair count the last stage of one vocabulary group and the first of the next share a
+    buffer.  513 groups over 256 workgroups give every workgroup two or three groups in a
+    row; every output against the oracle (30 field rows: one row tile)."""
     p = wl.make_problem(V=131101, d=d, n_q=30, K=(2, 6), layout="field", seed=95,
                         h_dtype=h_dtype)
     kern = api.projection_kernel(api.make_problem(**jet.to_device(p, "cuda")))
