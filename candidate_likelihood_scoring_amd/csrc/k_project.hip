@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256) void k_project_small_bf16(
 // Its first workgroup clears the flag word (no launch before it does).
 // NR: 32-row tiles of H per workgroup (1, 2 or 4): each head fragment is multiplied into NR
 // accumulator tiles, so the head is read once for 32 NR rows.  The H stage holds NR x 32
-// rows (LDS: 64 KB of head tiles + 2 x NP x NR x 8 KB of H stages, at most 128 KB).
+// rows (LDS: 64 KB of head tiles + 2 x NP x NR x 8 KB of H stages, twice that with PAIR;
+// at most 128 KB).
 // HALF: d % 128 = 64, the last stage 64 wide (a separate instance, so that the loads of the
 // d % 128 = 0 instances stay as they were: the run-time test cost binary_enum 15%).
 // PAIR (one row tile): the per-stage barrier only guards the shared H stage, so two H stages
